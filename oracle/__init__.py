@@ -1,0 +1,186 @@
+"""fp64 CPU oracle for batched draft-verify rejection sampling.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  The product
+library never loads it, and it imports nothing from the product package.
+
+The arithmetic lives in ``spec_verify_oracle.c`` (plain C, fp64, single
+threaded); this module only compiles it with gcc and marshals numpy arrays.
+``run(..., threads=n)`` splits the batch into contiguous request ranges and
+calls the C routine on each range from a thread pool: requests are independent,
+so the result does not depend on ``n``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spec_verify_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+# fault bits (same meaning as the OF_* constants of the C source)
+FAULT_DRAFT_ID = 1
+FAULT_TEMPERATURE = 2
+FAULT_TOP_P = 4
+FAULT_TARGET_ROW = 8
+FAULT_DRAFT_ROW = 16
+FAULT_DRAFT_MASS = 32
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/liboracle.so``."""
+    global _lib
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+        _lib = None
+    return _LIB
+
+
+def _bind(path):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.oracle_spec_verify.restype = ctypes.c_int
+    lib.oracle_spec_verify.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int] + [P] * 2 + \
+        [P, ctypes.c_int] + [P] * 12
+    lib.oracle_target_probs.restype = ctypes.c_int
+    lib.oracle_target_probs.argtypes = [ctypes.c_int, P, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                        ctypes.c_double, P, P]
+    lib.oracle_draft_probs.restype = ctypes.c_int
+    lib.oracle_draft_probs.argtypes = [ctypes.c_int, P, ctypes.c_double, ctypes.c_int, ctypes.c_double, P, P]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = _bind(_LIB)
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=None, top_p=None,
+        u_accept=None, u_sample=None, threads: int = 1, _lib_override=None) -> dict:
+    """Verify a batch on the CPU.
+
+    ``dtype`` is "f32" (``target_logits`` float32) or "bf16" (``target_logits``
+    uint16 bit patterns).  Returns a dict with tokens [N,gmax+1], num_accepted
+    [N], p_y / q_y [N,gmax] (NaN where not computed), resid_mass [N], margin [N]
+    and fault [N].
+    """
+    lib = _lib_override or _load()
+    ids = _c(draft_ids, np.int32)
+    N, gmax = ids.shape
+    dt = {"f32": 0, "bf16": 1}[dtype]
+    tl = _c(target_logits, np.uint16 if dt == 1 else np.float32)
+    V = tl.shape[-1]
+    assert tl.shape == (N, gmax + 1, V), tl.shape
+    q = _c(draft_probs, np.float32)
+    if q is not None:
+        assert q.shape == (N, gmax, V), q.shape
+    T = _c(temperature, np.float32)
+    k = _c(top_k, np.int32)
+    p = _c(top_p, np.float32)
+    ua = _c(u_accept, np.float32) if u_accept is not None else np.zeros((N, gmax), np.float32)
+    us = _c(u_sample, np.float32) if u_sample is not None else np.zeros((N,), np.float32)
+    out = dict(tokens=np.empty((N, gmax + 1), np.int32), num_accepted=np.empty((N,), np.int32),
+               p_y=np.empty((N, gmax), np.float64), q_y=np.empty((N, gmax), np.float64),
+               resid_mass=np.empty((N,), np.float64), margin=np.empty((N,), np.float64),
+               fault=np.empty((N,), np.int32))
+
+    def sl(a, lo):
+        return None if a is None else a[lo:].ctypes.data
+
+    def one(lo, hi):
+        n = hi - lo
+        if n <= 0:
+            return 0
+        return lib.oracle_spec_verify(n, gmax, V, sl(ids, lo), sl(q, lo), sl(tl, lo), dt, sl(T, lo), sl(k, lo),
+                                      sl(p, lo), sl(ua, lo), sl(us, lo), sl(out["tokens"], lo),
+                                      sl(out["num_accepted"], lo), sl(out["p_y"], lo), sl(out["q_y"], lo),
+                                      sl(out["resid_mass"], lo), sl(out["margin"], lo), sl(out["fault"], lo))
+
+    threads = max(1, min(int(threads), N)) if N else 1
+    if threads == 1:
+        rc = [one(0, N)]
+    else:
+        bounds = np.linspace(0, N, threads + 1).astype(int)
+        with ThreadPoolExecutor(threads) as ex:
+            rc = list(ex.map(lambda t: one(bounds[t], bounds[t + 1]), range(threads)))
+    if any(rc):
+        raise ValueError("oracle rejected the shapes or dtype")
+    return out
+
+
+def target_probs(row, dtype, T=1.0, top_k=0, top_p=1.0, _lib_override=None):
+    """p' of one target row as V doubles; returns (probs, fault, topp_margin)."""
+    lib = _lib_override or _load()
+    dt = {"f32": 0, "bf16": 1}[dtype]
+    r = _c(row, np.uint16 if dt == 1 else np.float32)
+    out = np.zeros(r.shape[0], np.float64)
+    m = np.zeros(1, np.float64)
+    f = lib.oracle_target_probs(r.shape[0], _ptr(r), dt, float(T), int(top_k), float(top_p), _ptr(out), _ptr(m))
+    return out, f, float(m[0])
+
+
+def draft_probs(row, T=1.0, top_k=0, top_p=1.0, _lib_override=None):
+    """q' of one draft row as V doubles; returns (probs, fault, topp_margin)."""
+    lib = _lib_override or _load()
+    r = _c(row, np.float32)
+    out = np.zeros(r.shape[0], np.float64)
+    m = np.zeros(1, np.float64)
+    f = lib.oracle_draft_probs(r.shape[0], _ptr(r), float(T), int(top_k), float(top_p), _ptr(out), _ptr(m))
+    return out, f, float(m[0])
+
+
+class Variant:
+    """The same interface bound to another build of the oracle source (used to
+    check that the pins reject deliberately altered copies of it)."""
+
+    def __init__(self, so_path):
+        self._lib = _bind(so_path)
+        for name in ("FAULT_DRAFT_ID", "FAULT_TEMPERATURE", "FAULT_TOP_P", "FAULT_TARGET_ROW",
+                     "FAULT_DRAFT_ROW", "FAULT_DRAFT_MASS"):
+            setattr(self, name, globals()[name])
+
+    def run(self, *a, **k):
+        return run(*a, _lib_override=self._lib, **k)
+
+    def target_probs(self, *a, **k):
+        return target_probs(*a, _lib_override=self._lib, **k)
+
+    def draft_probs(self, *a, **k):
+        return draft_probs(*a, _lib_override=self._lib, **k)
+
+
+def build_variant(source_text: str, out_dir: str) -> "Variant":
+    """Compile an altered copy of the oracle source and bind it."""
+    src = os.path.join(out_dir, "variant.c")
+    so = os.path.join(out_dir, "libvariant.so")
+    with open(src, "w") as f:
+        f.write(source_text)
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", so, src, "-lm"])
+    return Variant(so)
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()

@@ -1,0 +1,134 @@
+/*
+ * spec_verify.h -- C ABI of the batched draft-verify rejection sampler for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (zwjcode.cn, "生成 4 个 Token 为何不一定要跑 4 次大模型？
+ * Speculative Decoding 的提议、验证与接受", sections 02-07; pinghaoyang.com.cn,
+ * "vLLM 源码完全拆解（十）：投机解码——草稿模型、批量验证与 token 接受流水线",
+ * section "拒绝采样：RejectionSampler 的两个分支" and its greedy / random kernel
+ * subsections):
+ *
+ *   For each request i with gamma_i draft tokens y_0..y_{gamma_i-1}:
+ *   1. gamma_i is the index of the first negative entry of draft_ids[i, :]
+ *      (gmax if none); later entries are ignored.
+ *   2. Greedy requests (temperature 0): t_j = argmax of target row j (lowest
+ *      id on ties); accept while y_j == t_j; A = first mismatch (or gamma_i);
+ *      the output is y_0..y_{A-1}, t_A.
+ *   3. Sampled requests (temperature T > 0): p'_j = softmax(l_j / T) restricted
+ *      to the top-k / top-p kept set and renormalised; q'_j = q_j^(1/T)
+ *      restricted by the same rule (own thresholds) and renormalised, or the
+ *      one-hot of y_j when draft_probs is NULL.  Top-k keeps every value tied
+ *      with the k-th largest; top-p keeps the smallest set of whole tie groups,
+ *      largest values first, whose mass reaches top_p of the top-k mass.
+ *      Position j is accepted iff u_accept[i,j] * q'_j(y_j) < p'_j(y_j).
+ *      A = first rejected position (or gamma_i).  If A < gamma_i the token at
+ *      A is drawn from w = max(0, p'_A - q'_A) (p'_A when that is all zero);
+ *      otherwise the bonus token is drawn from w = p'_{gamma_i}.  The draw is
+ *      z = min{x : C_x > u_sample[i] * S} with C the running sum of w over
+ *      ascending token id and S = sum(w) (if rounding leaves no such x, the
+ *      largest x with w_x > 0).
+ *   4. out_tokens[i, :] = y_0..y_{A-1}, z, then -1 up to gmax + 1 entries;
+ *      out_num_accepted[i] = A.
+ *
+ * Data faults are reported per request, never by aborting the launch: the
+ * request's out_tokens row is all -1 and out_num_accepted[i] = -1.  Faults:
+ * a draft id >= V before the first negative id; a temperature that is NaN,
+ * negative, infinite or subnormal; on a sampled request a top_p that is NaN or
+ * <= 0; a read target row (rows 0..gamma_i) holding NaN or +inf or no finite
+ * value; on a sampled request with draft_probs, a read draft row (rows
+ * 0..gamma_i-1) holding NaN, +-inf or an entry with its sign bit set, or
+ * whose kept mass is zero.  Rows beyond those are never read (they may hold
+ * anything, including NaN).  top_k <= 0 or >= V and top_p >= 1 switch the
+ * filter off.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* target_logits element types */
+#define SPEC_VERIFY_F32 0  /* IEEE binary32                          */
+#define SPEC_VERIFY_BF16 1 /* bfloat16 bit patterns (uint16 storage) */
+
+/* return codes (nothing is enqueued unless SPEC_VERIFY_OK is returned) */
+#define SPEC_VERIFY_OK 0
+#define SPEC_VERIFY_ERR_NULL 1      /* a required pointer is NULL                        */
+#define SPEC_VERIFY_ERR_SHAPE 2     /* N < 0, gmax outside [0, 64], V < 1, or too large  */
+#define SPEC_VERIFY_ERR_DTYPE 3     /* unknown logits_dtype                              */
+#define SPEC_VERIFY_ERR_WORKSPACE 4 /* workspace_bytes below spec_verify_workspace_size  */
+#define SPEC_VERIFY_ERR_HIP 5       /* a HIP runtime call failed (launch, allocation)     */
+
+/* fault bits of the diagnostic fault output */
+#define SPEC_VERIFY_FAULT_DRAFT_ID 1
+#define SPEC_VERIFY_FAULT_TEMPERATURE 2
+#define SPEC_VERIFY_FAULT_TOP_P 4
+#define SPEC_VERIFY_FAULT_TARGET_ROW 8
+#define SPEC_VERIFY_FAULT_DRAFT_ROW 16
+#define SPEC_VERIFY_FAULT_DRAFT_MASS 32
+
+/*
+ * Bytes of device workspace one call with these sizes needs.  The layout is
+ * private to the library; its contents do not need initialising and are not
+ * meaningful after the call.
+ */
+size_t spec_verify_workspace_size(int N, int gmax, int V);
+
+/*
+ * Verify a batch.  All array arguments are DEVICE pointers owned by the
+ * caller, row-major with the vocabulary contiguous:
+ *   draft_ids         int32   [N, gmax]        -1 (any negative) pads
+ *   draft_probs       float32 [N, gmax, V]     or NULL: draft-free (n-gram) drafts
+ *   target_logits     f32/bf16 [N, gmax+1, V]  row gamma_i is the bonus position
+ *   temperature       float32 [N]              or NULL: 1.0 for every request
+ *   top_k             int32   [N]              or NULL: off
+ *   top_p             float32 [N]              or NULL: off
+ *   u_accept          float32 [N, gmax]        uniforms in [0, 1) (may be NULL if gmax == 0)
+ *   u_sample          float32 [N]              uniforms in [0, 1)
+ *   out_tokens        int32   [N, gmax+1]      written
+ *   out_num_accepted  int32   [N]              written
+ * workspace: device memory of at least spec_verify_workspace_size(N, gmax, V)
+ * bytes, or NULL to let the library use a buffer it allocates once per device
+ * (grown when needed and kept until the process ends; the allocation may
+ * synchronise the device).  stream: a hipStream_t, or NULL for the default
+ * stream.  The call only enqueues work on the stream and returns; it never
+ * waits for the device.  Calls that share a workspace must be ordered on one
+ * stream.  N == 0 is a valid empty batch.  Inputs are read only; outputs must
+ * not alias inputs or the workspace.
+ */
+int spec_verify(int N, int gmax, int V, const int32_t *draft_ids, const float *draft_probs,
+                const void *target_logits, int logits_dtype, const float *temperature,
+                const int32_t *top_k, const float *top_p, const float *u_accept,
+                const float *u_sample, int32_t *out_tokens, int32_t *out_num_accepted,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * spec_verify plus diagnostic outputs, each an optional DEVICE pointer:
+ *   p_y         float64 [N, gmax]  p'_j(y_j) for j < gamma_i of sampled requests
+ *   q_y         float64 [N, gmax]  q'_j(y_j) (1 for draft-free requests)
+ *   resid_mass  float64 [N]        S of the final draw (sampled requests)
+ *   fault       int32   [N]        fault bits (0: none)
+ * Entries that do not apply are written as NaN (p_y, q_y, resid_mass).
+ */
+int spec_verify_diag(int N, int gmax, int V, const int32_t *draft_ids, const float *draft_probs,
+                     const void *target_logits, int logits_dtype, const float *temperature,
+                     const int32_t *top_k, const float *top_p, const float *u_accept,
+                     const float *u_sample, int32_t *out_tokens, int32_t *out_num_accepted,
+                     double *p_y, double *q_y, double *resid_mass, int32_t *fault,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable text of a return code (static storage). */
+const char *spec_verify_status_string(int status);
+
+/* ABI version of this header: 1. */
+int spec_verify_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,165 @@
+"""MI355X batched draft-verify rejection sampler.
+
+Python binding of the C ABI in include/spec_verify.h.  It only marshals
+arguments: every step of the verification runs in the HIP kernels of
+``libspecverify.so``.  PyTorch supplies device memory and the stream.  There
+is no fallback: if the library is not built, importing the binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so the library binds to the HIP runtime torch uses
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+F32 = 0
+BF16 = 1
+STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "bad dtype", 4: "workspace too small", 5: "HIP error"}
+FAULT_DRAFT_ID = 1
+FAULT_TEMPERATURE = 2
+FAULT_TOP_P = 4
+FAULT_TARGET_ROW = 8
+FAULT_DRAFT_ROW = 16
+FAULT_DRAFT_MASS = 32
+
+EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_workspace_size", "spec_verify_status_string",
+           "spec_verify_version")
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libspecverify.so is not built (%s); run __graft_entry__.build() or "
+            "python rejection_sampling_verify_13_amd/build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.spec_verify.restype = I
+    lib.spec_verify.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P, P, P, P, Z, P]
+    lib.spec_verify_diag.restype = I
+    lib.spec_verify_diag.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.spec_verify_workspace_size.restype = Z
+    lib.spec_verify_workspace_size.argtypes = [I, I, I]
+    lib.spec_verify_status_string.restype = ctypes.c_char_p
+    lib.spec_verify_status_string.argtypes = [I]
+    lib.spec_verify_version.restype = I
+    lib.spec_verify_version.argtypes = []
+    return lib
+
+
+lib = _load()
+
+
+def workspace_size(N: int, gmax: int, V: int) -> int:
+    return int(lib.spec_verify_workspace_size(N, gmax, V))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, top_p=None, u_accept=None,
+           u_sample=None, *, out_tokens=None, out_num_accepted=None, workspace=None, stream=None, diag=False):
+    """Verify a batch on the GPU.
+
+    draft_ids int32 [N, gmax] (-1 padded), draft_probs float32 [N, gmax, V] or
+    None, target_logits bfloat16/float32 [N, gmax+1, V], temperature float32
+    [N] or None, top_k int32 [N] or None, top_p float32 [N] or None, u_accept
+    float32 [N, gmax], u_sample float32 [N]; all on one CUDA (HIP) device.
+    Returns (out_tokens int32 [N, gmax+1], out_num_accepted int32 [N]) and,
+    with diag=True, a dict of p_y, q_y [N, gmax] float64, resid_mass [N]
+    float64 and fault [N] int32.  The work is enqueued on ``stream`` (default:
+    torch's current stream); nothing synchronises.
+    """
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [N, gmax+1, V]")
+    N, G1, V = target_logits.shape
+    G = G1 - 1
+    dev = target_logits.device
+    if target_logits.dtype == torch.bfloat16:
+        dt = BF16
+    elif target_logits.dtype == torch.float32:
+        dt = F32
+    else:
+        raise TypeError("target_logits must be bfloat16 or float32")
+    if not target_logits.is_contiguous():
+        raise ValueError("target_logits must be contiguous")
+    _check(draft_ids, "draft_ids", torch.int32, (N, G), dev)
+    _check(draft_probs, "draft_probs", torch.float32, (N, G, V), dev)
+    _check(temperature, "temperature", torch.float32, (N,), dev)
+    _check(top_k, "top_k", torch.int32, (N,), dev)
+    _check(top_p, "top_p", torch.float32, (N,), dev)
+    _check(u_accept, "u_accept", torch.float32, (N, G), dev)
+    _check(u_sample, "u_sample", torch.float32, (N,), dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((N, G + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((N,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", torch.int32, (N, G + 1), dev)
+    _check(out_num_accepted, "out_num_accepted", torch.int32, (N,), dev)
+    if workspace is None:
+        workspace = torch.empty((workspace_size(N, G, V),), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    with torch.cuda.device(dev):
+        if diag:
+            d = dict(p_y=torch.empty((N, G), dtype=torch.float64, device=dev),
+                     q_y=torch.empty((N, G), dtype=torch.float64, device=dev),
+                     resid_mass=torch.empty((N,), dtype=torch.float64, device=dev),
+                     fault=torch.empty((N,), dtype=torch.int32, device=dev))
+            rc = lib.spec_verify_diag(N, G, V, _ptr(draft_ids), _ptr(draft_probs), _ptr(target_logits), dt,
+                                      _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(u_accept), _ptr(u_sample),
+                                      _ptr(out_tokens), _ptr(out_num_accepted), _ptr(d["p_y"]), _ptr(d["q_y"]),
+                                      _ptr(d["resid_mass"]), _ptr(d["fault"]), _ptr(workspace), ws_bytes, sptr)
+        else:
+            rc = lib.spec_verify(N, G, V, _ptr(draft_ids), _ptr(draft_probs), _ptr(target_logits), dt,
+                                 _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(u_accept), _ptr(u_sample),
+                                 _ptr(out_tokens), _ptr(out_num_accepted), _ptr(workspace), ws_bytes, sptr)
+    if rc != 0:
+        raise SpecVerifyError("spec_verify failed: %s" % lib.spec_verify_status_string(rc).decode())
+    if diag:
+        return out_tokens, out_num_accepted, d
+    return out_tokens, out_num_accepted
+
+
+def to_device(batch: dict, device="cuda"):
+    """Move a numpy batch (the layout of the workloads module) to torch tensors."""
+    import numpy as np
+    out = {}
+    for k in ("draft_ids", "draft_probs", "temperature", "top_k", "top_p", "u_accept", "u_sample"):
+        v = batch.get(k)
+        out[k] = None if v is None else torch.from_numpy(np.ascontiguousarray(v)).to(device)
+    tl = batch["target_logits"]
+    if batch["dtype"] == "bf16":
+        out["target_logits"] = torch.from_numpy(np.ascontiguousarray(tl).view(np.int16)).to(device).view(torch.bfloat16)
+    else:
+        out["target_logits"] = torch.from_numpy(np.ascontiguousarray(tl)).to(device)
+    return out
+
+
+def verify_batch(dev_batch: dict, **kw):
+    """verify() with the arguments taken from a to_device() dict."""
+    return verify(dev_batch["draft_ids"], dev_batch["draft_probs"], dev_batch["target_logits"],
+                  dev_batch["temperature"], dev_batch["top_k"], dev_batch["top_p"], dev_batch["u_accept"],
+                  dev_batch["u_sample"], **kw)

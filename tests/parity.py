@@ -1,0 +1,108 @@
+"""Helpers shared by the GPU parity tests: run a batch through the HIP library
+and through the CPU oracle, and compare the two by the stated tolerances.
+
+Tolerances: token ids and num_accepted bit-exact on every request the oracle
+does not flag as ambiguous; a request is ambiguous when one of its decisions
+lies within 1e-6 of a boundary (|u - p'/q'| at a read position, |u - C_x/S| of
+the draw, the top-p cut fraction); ambiguous requests must stay below 1e-4 of
+the rows compared (at least one allowed per comparison only when 1e-4 of the
+rows rounds up to one).  p'(y) and q'(y) must agree within 1e-5 absolute.
+Fault bits must agree exactly.
+"""
+import math
+import sys
+
+import numpy as np
+
+MARGIN = 1e-6
+PROB_ATOL = 1e-5
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_run(batch, diag=True, stream=None):
+    """Run a numpy batch on cuda:0; mixed dense / draft-free batches go as two
+    calls on contiguous halves, on the same stream."""
+    import torch
+    import rejection_sampling_verify_13_amd as sv
+    import workloads as W
+    parts = [batch]
+    if batch["draft_probs"] is not None and "has_q" in batch and not batch["has_q"].all():
+        parts = W.split_by_q(batch)
+    outs = []
+    for p in parts:
+        d = sv.to_device(p)
+        if diag:
+            t, n, dg = sv.verify_batch(d, diag=True, stream=stream)
+            outs.append(dict(tokens=t, num_accepted=n, **dg))
+        else:
+            t, n = sv.verify_batch(d, stream=stream)
+            outs.append(dict(tokens=t, num_accepted=n))
+    torch.cuda.synchronize()
+    res = {}
+    for k in outs[0]:
+        res[k] = np.concatenate([o[k].cpu().numpy() for o in outs], axis=0)
+    return res
+
+
+def oracle_run(batch, threads=8):
+    import oracle
+    import workloads as W
+    parts = [batch]
+    if batch["draft_probs"] is not None and "has_q" in batch and not batch["has_q"].all():
+        parts = W.split_by_q(batch)
+    outs = [oracle.run(p["draft_ids"], p["draft_probs"], p["target_logits"], p["dtype"], p["temperature"],
+                       p["top_k"], p["top_p"], p["u_accept"], p["u_sample"], threads=threads) for p in parts]
+    return {k: np.concatenate([o[k] for o in outs], axis=0) for k in outs[0]}
+
+
+def compare(g, o, rows=None, label=""):
+    """Assert parity of GPU results g with oracle results o; return counts."""
+    N = o["tokens"].shape[0]
+    if rows is None:
+        rows = max(1, N)
+    amb = (o["margin"] < MARGIN) & (o["fault"] == 0)
+    fault_mismatch = np.nonzero(g["fault"] != o["fault"])[0] if "fault" in g else np.array([], int)
+    assert len(fault_mismatch) == 0, "%s fault bits differ at requests %s: gpu %s oracle %s" % (
+        label, fault_mismatch[:10], g["fault"][fault_mismatch[:10]], o["fault"][fault_mismatch[:10]])
+    tok_bad = np.nonzero(~amb & ((g["tokens"] != o["tokens"]).any(axis=1) | (g["num_accepted"] != o["num_accepted"])))[0]
+    if len(tok_bad):
+        i = tok_bad[0]
+        raise AssertionError("%s %d token mismatches (first request %d): gpu %s/%d oracle %s/%d margin %.3g" % (
+            label, len(tok_bad), i, g["tokens"][i], g["num_accepted"][i], o["tokens"][i], o["num_accepted"][i],
+            o["margin"][i]))
+    allowed = max(0, math.ceil(1e-4 * rows))
+    assert amb.sum() <= allowed, "%s %d ambiguous requests, allowed %d" % (label, amb.sum(), allowed)
+    worst = 0.0
+    if "p_y" in g:
+        for key in ("p_y", "q_y"):
+            a, b = g[key], o[key]
+            both = ~np.isnan(b) & (o["fault"][:, None] == 0)
+            assert not np.isnan(a[both]).any(), "%s %s missing on GPU" % (label, key)
+            if both.any():
+                d = np.abs(a[both] - b[both]).max()
+                worst = max(worst, d)
+                assert d <= PROB_ATOL, "%s %s differs by %.3g" % (label, key, d)
+    return dict(requests=N, ambiguous=int(amb.sum()), faults=int((o["fault"] != 0).sum()), max_prob_err=worst)
+
+
+def check_layout(batch, g):
+    """Properties that hold for every request at any size: -1 padding after
+    the committed tokens, the accepted prefix equals the drafts, ids in range,
+    num_accepted within the draft length."""
+    ids = batch["draft_ids"]
+    N, G = ids.shape
+    V = batch["target_logits"].shape[-1]
+    gam = np.full(N, G) if G == 0 else np.where((ids < 0).any(axis=1), np.argmax(ids < 0, axis=1), G)
+    A = g["num_accepted"]
+    ok = A >= 0
+    assert (A[ok] <= gam[ok]).all()
+    for i in np.nonzero(ok)[0]:
+        a = A[i]
+        assert (g["tokens"][i, :a] == ids[i, :a]).all()
+        assert 0 <= g["tokens"][i, a] < V
+        assert (g["tokens"][i, a + 1:] == -1).all()
+    assert (g["tokens"][~ok] == -1).all()

@@ -1,0 +1,295 @@
+"""GPU parity: the HIP path against the CPU oracle, request by request.
+
+Reduced-size cases span several 2048-token workgroup steps and a ragged tail
+(V not a multiple of the step; V not a multiple of 8 takes the scalar-load
+path); full-size cases run the whole workload on the GPU exactly as the
+benchmark does and compare a seeded sample of requests with the oracle, plus
+layout properties of every request.  Every case prints its name before it
+touches the GPU.
+"""
+import numpy as np
+import pytest
+
+from conftest import floats, ints, read_golden
+from parity import check_layout, compare, gpu_run, log, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+import workloads as W  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rejection_sampling_verify_13_amd  # noqa: F401  (raises if the library is missing)
+    import oracle
+    oracle.build(force=False)
+
+
+def one_request(ids, q, logits, T=1.0, k=0, p=1.0, ua=None, us=0.5, dtype="f32"):
+    ids = np.asarray(ids, np.int32).reshape(1, -1)
+    g = ids.shape[1]
+    return dict(draft_ids=ids, draft_probs=None if q is None else np.asarray(q, np.float32)[None],
+                target_logits=np.asarray(logits, np.float32 if dtype == "f32" else np.uint16)[None], dtype=dtype,
+                temperature=np.array([T], np.float32), top_k=np.array([k], np.int32), top_p=np.array([p], np.float32),
+                u_accept=np.asarray(ua if ua is not None else np.zeros(g), np.float32).reshape(1, g),
+                u_sample=np.array([us], np.float32))
+
+
+def stack(reqs):
+    out = {}
+    for k in reqs[0]:
+        v = reqs[0][k]
+        out[k] = v if not isinstance(v, np.ndarray) else np.concatenate([r[k] for r in reqs], axis=0)
+    return out
+
+
+def parity(batch, label, rows=None):
+    log("[parity] %s: N=%d gmax=%d V=%d dtype=%s" % (label, batch["draft_ids"].shape[0], batch["draft_ids"].shape[1],
+                                                       batch["target_logits"].shape[-1], batch["dtype"]))
+    g = gpu_run(batch)
+    o = oracle_run(batch)
+    res = compare(g, o, rows=rows, label=label)
+    check_layout(batch, g)
+    log("[parity] %s ok %s" % (label, res))
+    return g, o, res
+
+
+# ------------------------------------------------------------------------------------------
+# the pages' examples on the GPU
+# ------------------------------------------------------------------------------------------
+
+def test_worked_example_on_gpu():
+    g = read_golden("worked_example_two_token.txt")
+    logits = np.log(np.array(floats(g["target_probs"])))
+    reqs = [one_request(ints(g["draft_ids"]), floats(g["draft_probs"]), logits, ua=[float(g["u_accept"])], us=us)
+            for us in np.linspace(0, 1, 16, endpoint=False)]
+    b = stack(reqs)
+    log("[parity] worked example")
+    r = gpu_run(b)
+    for t in range(len(reqs)):
+        assert list(r["tokens"][t]) == ints(g["expect_tokens"])
+        assert r["num_accepted"][t] == int(g["expect_num_accepted"])
+        assert r["p_y"][t, 0] / r["q_y"][t, 0] == pytest.approx(float(g["expect_alpha"]), abs=1e-6)
+        assert r["resid_mass"][t] == pytest.approx(0.4, abs=1e-6)
+    compare(r, oracle_run(b), label="worked example")
+
+
+def test_exercise_on_gpu():
+    g = read_golden("exercise_three_token.txt")
+    logits = np.log(np.array(floats(g["target_probs"])))
+    us_list = [u for u in np.linspace(0, 1, 24, endpoint=False) if abs(u - 2 / 3) > 1e-3]
+    b = stack([one_request(ints(g["draft_ids"]), floats(g["draft_probs"]), logits, ua=[0.41], us=u) for u in us_list])
+    log("[parity] exercise")
+    r = gpu_run(b)
+    for t, u in enumerate(us_list):
+        assert r["num_accepted"][t] == 0
+        assert r["tokens"][t, 0] == (1 if u < 2 / 3 else 2)
+
+
+def test_greedy_example_on_gpu():
+    g = read_golden("greedy_example.txt")
+    V = int(g["V"])
+    rng = np.random.default_rng(0)
+    rows = []
+    for a in ints(g["target_argmax"]):
+        l = rng.standard_normal(V).astype(np.float32)
+        l[a] = l.max() + 1
+        rows.append(l)
+    logits = np.array(rows)
+    b = stack([one_request(ints(g["draft_ids"]), None, logits, T=0.0),
+               one_request(ints(g["all_match_draft_ids"]), None, logits, T=0.0)])
+    log("[parity] greedy example")
+    r = gpu_run(b)
+    assert list(r["tokens"][0]) == ints(g["expect_tokens"]) and r["num_accepted"][0] == 2
+    assert list(r["tokens"][1]) == ints(g["all_match_expect_tokens"]) and r["num_accepted"][1] == 4
+
+
+# ------------------------------------------------------------------------------------------
+# reduced-size workloads: every request compared
+# ------------------------------------------------------------------------------------------
+
+SMALL = {
+    "cfg1": W.config(1),
+    "cfg2_small": W.config(2, N=24, V=5000),
+    "cfg3_small": W.config(3, N=16, V=12000),
+    "cfg3_small_f32": W.config(3, N=12, V=9000, dtype="f32"),
+    "cfg4_small": W.config(4, N=40, V=7000, greedy_count=10),
+    "cfg5_small": W.config(5, N=48, V=6144),
+    "unaligned_bf16": W.config(2, N=16, V=4999),
+    "unaligned_f32_topk": W.config(3, N=10, V=3001, dtype="f32"),
+    "null_q_topk": W.config(3, N=12, V=8000, q_mode="null"),
+    "top_p_only": W.config(2, N=16, V=6000, top_p=0.8),
+    "large_k_general_path": W.config(3, N=8, V=6000, top_k=300, top_p=1.0),
+    "large_k_top_p": W.config(3, N=8, V=6000, top_k=500, top_p=0.7),
+    "top_k_one": W.config(2, N=16, V=3000, top_k=1),
+    "k_128_edge": W.config(3, N=8, V=4096, top_k=128, top_p=0.95),
+    "greedy_all": W.config(4, N=24, V=5000, greedy_count=24),
+    "low_temperature": W.config(2, N=16, V=4000, temperature=0.05),
+    "high_temperature": W.config(2, N=16, V=4000, temperature=3.0),
+    "gamma_zero": W.config(2, N=12, gmax=0, V=3000),
+    "gamma_max_64": W.config(2, N=3, gmax=64, V=2048),
+    "tiny_vocab": W.config(1, N=20, V=3),
+    "vocab_one": W.config(1, N=6, V=1),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(name):
+    b = W.generate(SMALL[name], threads=8)
+    parity(b, name)
+
+
+def test_mixed_per_request_parameters():
+    rng = np.random.default_rng(5)
+    b = W.generate(W.config(3, N=40, V=7000, top_k=0, top_p=1.0), threads=8)
+    b["temperature"] = rng.choice([0.0, 0.5, 1.0, 1.7], 40).astype(np.float32)
+    b["top_k"] = rng.choice([0, 1, 5, 50, 128, 129, 400, 7000, -3], 40).astype(np.int32)
+    b["top_p"] = rng.choice([1.0, 0.95, 0.5, 0.1, 2.0], 40).astype(np.float32)
+    parity(b, "mixed parameters")
+
+
+def test_draft_equals_target_accepts_all():
+    b = W.generate(W.config(1, N=16, V=2048), threads=8)
+    l = b["target_logits"][:, :-1].astype(np.float64)
+    e = np.exp(l - l.max(axis=2, keepdims=True))
+    b["draft_probs"] = (e / e.sum(axis=2, keepdims=True)).astype(np.float32)
+    g, o, _ = parity(b, "q equals p")
+    amb = o["margin"] < 1e-6
+    assert (g["num_accepted"][~amb] == b["draft_ids"].shape[1]).all()
+
+
+def test_one_hot_q_equals_null_q():
+    b = W.generate(W.config(2, N=16, V=3000), threads=8)
+    oh = np.zeros_like(b["draft_probs"])
+    for i in range(16):
+        for j in range(4):
+            oh[i, j, b["draft_ids"][i, j]] = 1.0
+    g1 = gpu_run(dict(b, draft_probs=oh))
+    g2 = gpu_run(dict(b, draft_probs=None, has_q=np.zeros(16, bool)))
+    np.testing.assert_array_equal(g1["tokens"], g2["tokens"])
+    np.testing.assert_array_equal(g1["num_accepted"], g2["num_accepted"])
+
+
+def test_batch_composition_does_not_matter():
+    # one request's result must not depend on its neighbours (no crosstalk)
+    b = W.generate(W.config(5, N=32, V=4096), threads=8)
+    full = gpu_run(b)
+    for lo, hi in ((0, 1), (5, 9), (16, 17), (20, 32)):
+        sub = {k: (v[lo:hi] if isinstance(v, np.ndarray) and v.shape[:1] == (32,) else v) for k, v in b.items()}
+        if sub["draft_probs"] is not None:
+            sub["draft_probs"] = b["draft_probs"][lo:hi]
+        r = gpu_run(sub)
+        np.testing.assert_array_equal(r["tokens"], full["tokens"][lo:hi])
+
+
+def test_repeat_calls_are_identical():
+    b = W.generate(W.config(3, N=16, V=20000), threads=8)
+    r1, r2 = gpu_run(b), gpu_run(b)
+    for k in ("tokens", "num_accepted", "p_y", "q_y", "resid_mass", "fault"):
+        np.testing.assert_array_equal(r1[k], r2[k])
+
+
+# ------------------------------------------------------------------------------------------
+# faults and special values
+# ------------------------------------------------------------------------------------------
+
+def test_fault_injection():
+    base = W.generate(W.config(2, N=16, V=2048), threads=8)
+    b = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in base.items()}
+    nan16, inf16, ninf16 = np.uint16(0x7FC0), np.uint16(0x7F80), np.uint16(0xFF80)
+    b["draft_ids"][0, 2] = 2048                 # id out of range
+    b["temperature"][1] = -1.0                  # bad temperature
+    b["temperature"][2] = np.nan
+    b["top_p"][3] = 0.0                         # bad top_p
+    b["target_logits"][4, 1, 77] = nan16        # NaN in a read target row
+    b["target_logits"][5, 4, 5] = inf16         # +inf in the bonus row
+    b["target_logits"][6, 2, :] = ninf16        # no finite value
+    b["target_logits"][7, 0, 9] = ninf16        # a single -inf is fine
+    b["draft_probs"][8, 3, 100] = -1e-3         # negative draft probability
+    b["draft_probs"][9, 0, :] = 0.0             # zero draft mass
+    b["draft_probs"][10, 1, 5] = np.inf
+    b["temperature"][11] = 0.0                  # greedy: NaN in q rows is never read
+    b["draft_probs"][11, 0, 3] = np.nan
+    b["temperature"][12] = 0.0
+    b["target_logits"][12, 3, 4] = nan16        # greedy: NaN in a target row is a fault
+    b["draft_ids"][13, 1] = -1                  # padding: later rows are never read
+    b["target_logits"][13, 2:, :] = nan16
+    b["draft_probs"][13, 1:, :] = np.nan
+    b["temperature"][14] = 1e-40                # subnormal temperature
+    g, o, _ = parity(b, "fault injection")
+    assert o["fault"][[0, 1, 2, 3, 4, 5, 6, 8, 9, 10, 12, 14]].all()
+    assert (o["fault"][[7, 11, 13, 15]] == 0).all()
+
+
+def test_special_rows():
+    V = 2048
+    rng = np.random.default_rng(9)
+    reqs = []
+    l = (rng.standard_normal((3, V)) * 3).astype(np.float32)
+    q = np.full((2, V), 1.0 / V, np.float32)
+    # all logits equal (maximal ties) with top-k / top-p
+    flat = np.zeros((3, V), np.float32)
+    reqs.append(one_request([3, 7], q, flat, k=5, p=0.5, ua=[0.3, 0.9], us=0.77))
+    reqs.append(one_request([3, 7], q, flat, k=0, p=0.3, ua=[0.3, 0.9], us=0.21))
+    # mostly -inf rows (masked vocabulary)
+    masked = np.full((3, V), -np.inf, np.float32)
+    masked[:, [1, 500, 1999]] = [[1, 2, 3], [0, 0, 5], [2, 2, 2]]
+    qm = np.zeros((2, V), np.float32)
+    qm[:, [1, 500, 1999, 7]] = 0.25
+    reqs.append(one_request([500, 7], qm, masked, ua=[0.1, 0.5], us=0.6))
+    reqs.append(one_request([1999, 1], qm, masked, T=0.0))
+    # draft token outside the target's top-k (p'(y) = 0): rejected
+    reqs.append(one_request([int(np.argmin(l[0])), 1], q, l, k=10, ua=[0.0, 0.0], us=0.4))
+    # huge logits (no overflow relative to the max)
+    big = l * 1e4
+    reqs.append(one_request([1, 2], q, big, ua=[0.5, 0.5], us=0.5))
+    b = stack(reqs)
+    parity(b, "special rows")
+
+
+# ------------------------------------------------------------------------------------------
+# full workloads, launched exactly as the benchmark does, sampled requests checked
+# ------------------------------------------------------------------------------------------
+
+FULL_SAMPLE = 24
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled(cfg):
+    spec = W.config(cfg)
+    log("[parity] full config %d: N=%d gmax=%d V=%d (generating)" % (cfg, spec.N, spec.gmax, spec.V))
+    b = W.generate(spec, threads=16)
+    log("[parity] full config %d: running on the GPU" % cfg)
+    g = gpu_run(b)
+    check_layout(b, g)
+    rng = np.random.default_rng(77 + cfg)
+    if cfg == 5:  # both halves: dense q first, then draft-free
+        h = spec.N // 2
+        pick = np.concatenate([np.sort(rng.choice(h, FULL_SAMPLE // 2, replace=False)),
+                               h + np.sort(rng.choice(h, FULL_SAMPLE // 2, replace=False))])
+    else:
+        pick = np.sort(rng.choice(spec.N, size=min(FULL_SAMPLE, spec.N), replace=False))
+    sub = W.generate(spec, requests=pick, threads=16)
+    for k in ("draft_ids", "u_accept", "u_sample", "temperature"):
+        np.testing.assert_array_equal(sub[k], b[k][pick])
+    log("[parity] full config %d: oracle on %d sampled requests" % (cfg, len(pick)))
+    o = oracle_run(sub, threads=16)
+    gs = {k: v[pick] for k, v in g.items()}
+    res = compare(gs, o, rows=len(pick) * (spec.gmax + 1), label="config %d" % cfg)
+    # greedy requests: every one of them checked against numpy's argmax
+    greedy = np.nonzero(b["temperature"] == 0)[0]
+    for i in greedy:
+        gam = int(b["gamma"][i])
+        tl = b["target_logits"][i, : gam + 1]
+        am = np.argmax(W.bf16_bits_to_f32(tl) if b["dtype"] == "bf16" else tl, axis=1)
+        A = gam
+        for j in range(gam):
+            if b["draft_ids"][i, j] != am[j]:
+                A = j
+                break
+        assert g["num_accepted"][i] == A and g["tokens"][i, A] == am[A]
+    assert (g["fault"] == 0).all()
+    log("[parity] full config %d ok %s, greedy checked %d" % (cfg, res, len(greedy)))

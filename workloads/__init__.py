@@ -105,8 +105,10 @@ def _batch_params(spec: Spec):
     return gam.astype(np.int64), T
 
 
-def generate(spec: Spec, requests=None) -> dict:
-    """Build the batch (or the listed subset of its requests, in that order)."""
+def generate(spec: Spec, requests=None, threads: int = 1) -> dict:
+    """Build the batch (or the listed subset of its requests, in that order).
+
+    Requests are independent streams, so ``threads`` only changes the speed."""
     gam_all, T_all = _batch_params(spec)
     idx = np.arange(spec.N) if requests is None else np.asarray(requests, dtype=np.int64)
     n, G, V = len(idx), spec.gmax, spec.V
@@ -118,8 +120,10 @@ def generate(spec: Spec, requests=None) -> dict:
     ua = np.empty((n, G), np.float32)
     us = np.empty((n,), np.float32)
     has_q = np.zeros(n, bool)
-    for r, i in enumerate(idx):
-        rng = spec.request_rng(int(i))
+
+    def one(r):
+        i = int(idx[r])
+        rng = spec.request_rng(i)
         g = int(gam_all[i])
         T = float(T_all[i])
         Td = T if T > 0 else 1.0
@@ -165,6 +169,14 @@ def generate(spec: Spec, requests=None) -> dict:
             ids[r, j] = y
         ua[r] = uniforms(rng, (G,))
         us[r] = uniforms(rng, ())
+
+    if threads > 1 and n > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(min(threads, n)) as ex:
+            list(ex.map(one, range(n)))
+    else:
+        for r in range(n):
+            one(r)
     out = dict(draft_ids=ids, draft_probs=q, target_logits=logits, dtype=spec.dtype,
                temperature=T_all[idx].copy(), top_k=np.full(n, spec.top_k, np.int32),
                top_p=np.full(n, spec.top_p, np.float32), u_accept=ua, u_sample=us, has_q=has_q,

@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the batched draft-verify rejection sampler on one MI355X.
+
+One step = one spec_verify call (row pass + per-request finish) over the
+whole batch of the workload.  The default workload is N = 256 requests,
+gamma = 5 drafts, V = 128256, bf16 target logits, fp32 draft probabilities,
+top_k = 50 / top_p = 0.9 on both distributions, T = 1 (the N=256, V=128256
+configuration).  Inputs are seeded synthetic tensors resident in HBM before
+the timed region; two copies of them alternate between steps so that no step
+reads data the previous step left in the 256 MB Infinity Cache.
+
+Prints one JSON line: verified draft positions per second (sum of gamma_i per
+step / time), the roofline of the dominant kernel (the row pass, timed with
+HIP events on its stream), and the CPU oracle timed on a bounded sample of the
+same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+SRC = os.path.join(ROOT, "rejection_sampling_verify_13_amd", "csrc", "spec_verify.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "row_kernel_counters.md")
+
+
+def source_digest():
+    with open(SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def workload_bytes(batch):
+    """Algorithmic HBM bytes of one step: every real target row once (rows
+    0..gamma_i), every real draft row once (rows 0..gamma_i-1 of sampled
+    requests that carry draft probabilities), plus the small per-request
+    arrays and outputs."""
+    import numpy as np
+    V = batch["target_logits"].shape[-1]
+    s_l = 2 if batch["dtype"] == "bf16" else 4
+    gam = batch["gamma"].astype(np.int64)
+    N, G = batch["draft_ids"].shape
+    sampled = batch["temperature"] > 0
+    with_q = sampled & batch["has_q"] if batch["draft_probs"] is not None else np.zeros(N, bool)
+    target = int((gam + 1).sum()) * V * s_l
+    draft = int(gam[with_q].sum()) * V * 4
+    small = N * G * 4 * 2 + N * 4 * 4 + N * (G + 1) * 4 + N * 4
+    return target + draft + small, target, draft
+
+
+def traffic_from_profile(digest, workload):
+    """HBM bytes per row-kernel launch from the committed counter summary, if
+    it was taken on this exact kernel source and workload; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    text = open(COUNTERS).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*(\d+)\s+source:\s*(\w+)\s+workload:\s*(\S+)", text)
+    if not m or m.group(2) != digest or m.group(3) != workload:
+        return None
+    return int(m.group(1))
+
+
+def cpu_baseline(spec, n_req, threads):
+    import numpy as np
+    import oracle
+    import workloads as W
+    oracle.build(force=False)
+    sub = W.generate(spec, requests=range(n_req), threads=threads)
+    t0 = time.perf_counter()
+    oracle.run(sub["draft_ids"], sub["draft_probs"], sub["target_logits"], sub["dtype"], sub["temperature"],
+               sub["top_k"], sub["top_p"], sub["u_accept"], sub["u_sample"], threads=threads)
+    dt = time.perf_counter() - t0
+    pos = int(np.asarray(sub["gamma"]).sum())
+    return dict(value=pos / dt, unit="positions/s", cores=threads, kind="oracle",
+                sample="first %d of %d requests of the same workload (%d verified positions), fp64 C oracle, "
+                       "%d threads over requests, %.2f s wall" % (n_req, spec.N, pos, threads, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
+    ap.add_argument("--cpu-sample", type=int, default=96, help="requests timed on the CPU oracle (0: skip)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, run a plain elementwise copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the verify path is measured on one MI355X and no "
+              "multi-GPU run is part of this build (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as W
+    import rejection_sampling_verify_13_amd as sv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = W.config(args.config)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    print("[bench] generating workload %d (N=%d gmax=%d V=%d)" % (args.config, spec.N, spec.gmax, spec.V),
+          file=sys.stderr, flush=True)
+    batch = W.generate(spec, threads=threads)
+    parts = W.split_by_q(batch) if (batch["draft_probs"] is not None and not batch["has_q"].all()) else [batch]
+    B_alg, B_target, B_draft = workload_bytes(batch)
+    positions = int(batch["gamma"].sum())
+    rows = int((batch["gamma"] + 1).sum())
+
+    # two resident copies of the inputs, alternated between steps
+    sets = []
+    for _ in range(2):
+        ps = []
+        for p in parts:
+            d = sv.to_device(p, dev)
+            Np, Gp = p["draft_ids"].shape
+            Vp = p["target_logits"].shape[-1]
+            d["ws"] = torch.empty((sv.workspace_size(Np, Gp, Vp),), dtype=torch.uint8, device=dev)
+            d["out_t"] = torch.empty((Np, Gp + 1), dtype=torch.int32, device=dev)
+            d["out_n"] = torch.empty((Np,), dtype=torch.int32, device=dev)
+            ps.append(d)
+        sets.append(ps)
+    del batch["target_logits"], batch["draft_probs"]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(k, events=None):
+        for pi, d in enumerate(sets[k % 2]):
+            ev = None
+            if events is not None:
+                ev = events[pi]
+            sv.verify(d["draft_ids"], d["draft_probs"], d["target_logits"], d["temperature"], d["top_k"], d["top_p"],
+                      d["u_accept"], d["u_sample"], out_tokens=d["out_t"], out_num_accepted=d["out_n"],
+                      workspace=d["ws"], stream=stream, events=ev)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in parts] for _ in range(K)]
+    for per_step in evs:  # torch creates an event's handle on its first record
+        for trio in per_step:
+            for e in trio:
+                e.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    row_ms = np.array([sum(e[0].elapsed_time(e[1]) for e in evs[k]) for k in range(K)])
+    fin_ms = np.array([sum(e[1].elapsed_time(e[2]) for e in evs[k]) for k in range(K)])
+    ms_per_step = wall * 1e3 / K
+    value = positions * K / wall
+
+    digest = source_digest()
+    workload_name = "cfg%d" % args.config
+    traffic = traffic_from_profile(digest, workload_name)
+    row_avg_s = float(row_ms.mean()) * 1e-3
+    achieved = B_alg / row_avg_s / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    kernel="row_kernel", kernel_avg_us=round(row_avg_s * 1e6, 2),
+                    finish_kernel_avg_us=round(float(fin_ms.mean()) * 1e3, 2),
+                    algorithmic_bytes_per_launch=B_alg)
+
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if args.cpu_sample > 0:
+        n_req = min(args.cpu_sample, spec.N)
+        print("[bench] timing the CPU oracle on %d requests" % n_req, file=sys.stderr, flush=True)
+        cpu = cpu_baseline(spec, n_req, threads)
+
+    desc = {1: "tiny fp32: N=4 gamma=4 V=1024",
+            2: "N=64 gamma=4 V=32000 bf16 T=0.8",
+            3: "N=256 gamma=5 V=128256 bf16 top_k=50 top_p=0.9 T=1",
+            4: "N=512 gamma=8 V=151936 bf16 25% greedy, T~U[0.5,1.2]",
+            5: "N=1024 ragged gamma in 0..7 V=128256 bf16, half draft-free"}[args.config]
+    out = {
+        "metric": "verified draft positions/sec and achieved HBM GB/s (% of peak), 1 MI355X",
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": desc, "requests": spec.N, "gamma": spec.gmax, "vocab": spec.V,
+                   "target_logits": spec.dtype, "draft_probs": "f32" if spec.q_mode != "null" else None,
+                   "verified_positions_per_step": positions, "rows_per_step": rows,
+                   "algorithmic_bytes_per_step": B_alg, "target_bytes": B_target, "draft_bytes": B_draft},
+        "hbm_gbps_step": round(B_alg / (ms_per_step * 1e-3) / 1e9, 1),
+        "hbm_frac_step": round(B_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "rows_per_s": round(rows * K / wall, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source": digest,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

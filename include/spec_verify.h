@@ -121,6 +121,21 @@ int spec_verify_diag(int N, int gmax, int V, const int32_t *draft_ids, const flo
                      double *p_y, double *q_y, double *resid_mass, int32_t *fault,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * spec_verify_diag plus three optional hipEvent_t handles (created by the
+ * caller, may be NULL) that are recorded on `stream`: ev_start before the
+ * row pass, ev_mid between the row pass and the per-request finish, ev_end
+ * after it.  For timing the two phases; results are identical to
+ * spec_verify_diag.
+ */
+int spec_verify_timed(int N, int gmax, int V, const int32_t *draft_ids, const float *draft_probs,
+                      const void *target_logits, int logits_dtype, const float *temperature,
+                      const int32_t *top_k, const float *top_p, const float *u_accept,
+                      const float *u_sample, int32_t *out_tokens, int32_t *out_num_accepted,
+                      double *p_y, double *q_y, double *resid_mass, int32_t *fault,
+                      void *workspace, size_t workspace_bytes, void *stream,
+                      void *ev_start, void *ev_mid, void *ev_end);
+
 /* Human-readable text of a return code (static storage). */
 const char *spec_verify_status_string(int status);
 

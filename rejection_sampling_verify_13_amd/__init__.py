@@ -25,8 +25,8 @@ FAULT_TARGET_ROW = 8
 FAULT_DRAFT_ROW = 16
 FAULT_DRAFT_MASS = 32
 
-EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_workspace_size", "spec_verify_status_string",
-           "spec_verify_version")
+EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_timed", "spec_verify_workspace_size",
+           "spec_verify_status_string", "spec_verify_version")
 
 
 class SpecVerifyError(RuntimeError):
@@ -44,6 +44,8 @@ def _load():
     lib.spec_verify.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P, P, P, P, Z, P]
     lib.spec_verify_diag.restype = I
     lib.spec_verify_diag.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.spec_verify_timed.restype = I
+    lib.spec_verify_timed.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P, Z, P, P, P, P]
     lib.spec_verify_workspace_size.restype = Z
     lib.spec_verify_workspace_size.argtypes = [I, I, I]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
@@ -78,7 +80,8 @@ def _check(t, name, dtype, shape, device):
 
 
 def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, top_p=None, u_accept=None,
-           u_sample=None, *, out_tokens=None, out_num_accepted=None, workspace=None, stream=None, diag=False):
+           u_sample=None, *, out_tokens=None, out_num_accepted=None, workspace=None, stream=None, diag=False,
+           events=None):
     """Verify a batch on the GPU.
 
     draft_ids int32 [N, gmax] (-1 padded), draft_probs float32 [N, gmax, V] or
@@ -88,7 +91,9 @@ def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, 
     Returns (out_tokens int32 [N, gmax+1], out_num_accepted int32 [N]) and,
     with diag=True, a dict of p_y, q_y [N, gmax] float64, resid_mass [N]
     float64 and fault [N] int32.  The work is enqueued on ``stream`` (default:
-    torch's current stream); nothing synchronises.
+    torch's current stream); nothing synchronises.  ``events`` = (start, mid,
+    end) torch.cuda.Event objects (or None) are recorded on the stream before
+    the row pass, between the two kernels and after the finish kernel.
     """
     if target_logits.dim() != 3:
         raise ValueError("target_logits must be [N, gmax+1, V]")
@@ -123,7 +128,13 @@ def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, 
         stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
     with torch.cuda.device(dev):
-        if diag:
+        if events is not None:
+            evp = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in events]
+            rc = lib.spec_verify_timed(N, G, V, _ptr(draft_ids), _ptr(draft_probs), _ptr(target_logits), dt,
+                                       _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(u_accept), _ptr(u_sample),
+                                       _ptr(out_tokens), _ptr(out_num_accepted), None, None, None, None,
+                                       _ptr(workspace), ws_bytes, sptr, *evp)
+        elif diag:
             d = dict(p_y=torch.empty((N, G), dtype=torch.float64, device=dev),
                      q_y=torch.empty((N, G), dtype=torch.float64, device=dev),
                      resid_mass=torch.empty((N,), dtype=torch.float64, device=dev),

@@ -9,24 +9,29 @@
 // top-p preprocessing, -1 placeholders, draft-free residual with the draft
 // token's cell removed).  The exact contract is stated in include/spec_verify.h.
 //
-// Two kernels per call, both on the caller's stream:
-//   row_kernel    one 256-thread workgroup per (request, position) row.  It
-//                 streams the target-logit row and, at draft positions of
-//                 sampled requests, the draft-probability row once with 16-byte
-//                 nontemporal loads, and reduces: row max, sum of exp over the
-//                 row (fp32 terms, fp64 accumulation), sum of q^(1/T), draft-row
-//                 validity, greedy argmax.  With top-k active (k <= kKFast) each
-//                 wave keeps an LDS candidate buffer behind a rising threshold
-//                 that never exceeds the true k-th largest value, so one pass
-//                 yields the kept set; other filter settings use a radix select
-//                 that re-reads the row.  p'(y) and q'(y) are evaluated in fp64
-//                 and the acceptance flag u * q'(y) < p'(y) is stored.
-//   finish_kernel one workgroup per request: ballot over the acceptance flags
-//                 gives the first rejection A; greedy requests take the stored
-//                 argmax, sampled ones draw by inverse CDF over ascending token
-//                 id, either from the stored kept list of row A (filters active)
-//                 or by two passes over row A (chunk sums, then the crossing
-//                 chunk).  Outputs are written in the -1 padded layout.
+// Work per call, all on the caller's stream:
+//   clear_kernel  zeroes one completion counter per request.
+//   row_kernel    one 256-thread workgroup per (request, position) row, grid in
+//                 request-major order.  It streams the target-logit row and, at
+//                 draft positions of sampled requests, the draft-probability
+//                 row once (16-byte nontemporal loads, the next step's loads in
+//                 flight while the current step is reduced) and computes: row
+//                 max, sum of exp over the row (fp32 terms, fp64 accumulation),
+//                 sum of q^(1/T), draft-row validity, greedy argmax.  With
+//                 top-k active (k <= kKFast) every lane whose 8-token chunk
+//                 holds a value at or above its wave's threshold appends the
+//                 whole chunk to an LDS buffer; the threshold is raised to the
+//                 k-th largest buffered chunk maximum whenever the buffer fills,
+//                 which never exceeds the true k-th largest value, so one pass
+//                 yields every token of the top-k set.  Other filter settings
+//                 use a radix select that re-reads the row.  p'(y) and q'(y)
+//                 are evaluated in fp64 and the flag u * q'(y) < p'(y) stored.
+//                 The last workgroup of a request to finish (atomic counter)
+//                 then finds the first rejection A by ballot and draws the
+//                 replacement or bonus token by inverse CDF over ascending
+//                 token id: from the stored kept list of row A when filters are
+//                 active, otherwise by two passes over row A (chunk sums, then
+//                 the crossing chunk).  Outputs are written -1 padded.
 //
 // Compile: hipcc --offload-arch=gfx950 -O3 -shared -fPIC
 //          -Xclang -target-feature -Xclang -packed-fp32-ops
@@ -49,9 +54,10 @@ constexpr int kBlock = 256;             // threads per workgroup (4 waves)
 constexpr int kWaves = kBlock / 64;
 constexpr int kCh = 8;                  // tokens per thread per step
 constexpr int kStep = kBlock * kCh;     // tokens per workgroup step (2048)
-constexpr int kWcap = 384;              // candidate slots per wave and distribution
-constexpr int kKFast = 128;             // largest top_k served by the candidate buffers
-constexpr int kListMax = 512;           // merged kept-set capacity (LDS)
+constexpr int kCap = 256;               // buffered chunks per wave and distribution
+constexpr int kKFast = 64;              // largest top_k served by the chunk buffers
+constexpr int kListMax = 512;           // merged candidate tokens (LDS)
+constexpr int kSegMax = kListMax / kWaves;
 constexpr int kLcap = kListMax;         // kept-list entries stored per row
 constexpr int kMaxChunks = 512;         // chunk sums held by the draw
 constexpr int kMaxGamma = 64;
@@ -66,13 +72,13 @@ enum {
   kFaultDraftMass = SPEC_VERIFY_FAULT_DRAFT_MASS,
 };
 
-// Per-row results of row_kernel (64 bytes).
+// Per-row results (64 bytes).
 struct RowStats {
   float m;        // max logit of the row
   float cut_p;    // target token kept iff logit >= cut_p
   float cut_q;    // draft token kept iff q >= cut_q
   int argmax;     // greedy rows: lowest id of the max logit
-  double z;       // sum over the kept set of exp((l - m) / T)
+  double z;       // sum over the kept set of 2^((l - m) * c), c = log2(e) / T in fp32
   double r;       // sum over the kept set of q^(1/T)
   double p_y;     // p'(y) at a draft position
   double q_y;     // q'(y) at a draft position
@@ -85,7 +91,7 @@ static_assert(sizeof(RowStats) == 64, "RowStats layout");
 struct ListEntry {
   int id;
   float val;      // the logit
-  double e;       // exp((l - m) / T)
+  double e;       // 2^((l - m) * c)
 };
 
 struct Args {
@@ -106,70 +112,103 @@ struct Args {
   int32_t* d_fault;
   RowStats* stats;
   ListEntry* lists;
+  unsigned int* done;   // completion counter per request
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Row data is read through global-address-space pointers so that loads are
+// global (not flat) instructions: they then count only against the vector
+// memory counter and the next step's loads stay in flight across LDS work.
+#define GLOBAL_AS __attribute__((address_space(1)))
+#define LDS_AS __attribute__((address_space(3)))
+#define CONST_AS __attribute__((address_space(4)))
+template <class T>
+__device__ inline const GLOBAL_AS T* gptr(const T* p) {
+  return (const GLOBAL_AS T*)p;
+}
+
 // ------------------------------------------------------------------------------------------
-// element access
+// element access: one "step" is 8 consecutive tokens of a lane, kept raw until reduced
 // ------------------------------------------------------------------------------------------
 
 struct Bf16 {
   typedef uint16_t T;
-  static constexpr int kKeyBits = 16;
-  __device__ static float at(const uint16_t* p, size_t x) { return __uint_as_float((uint32_t)p[x] << 16); }
-  __device__ static void load8(const uint16_t* p, float v[8]) {
-    u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
-    v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
-    v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
-    v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
+  struct Raw {
+    u32x4 a;
+  };
+  __device__ static float at(const uint16_t* p, size_t x) { return __uint_as_float((uint32_t)gptr(p)[x] << 16); }
+  __device__ static Raw load(const uint16_t* p) {
+    Raw r;
+    r.a = __builtin_nontemporal_load(gptr(reinterpret_cast<const u32x4*>(p)));
+    return r;
+  }
+  // tokens at or past V read as -inf
+  __device__ static Raw gather(const uint16_t* p, int base, int V) {
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t lo = (base + 2 * t < V) ? (uint32_t)gptr(p)[base + 2 * t] : 0xff80u;
+      const uint32_t hi = (base + 2 * t + 1 < V) ? (uint32_t)gptr(p)[base + 2 * t + 1] : 0xff80u;
+      w[t] = lo | (hi << 16);
+    }
+    Raw r;
+    r.a = u32x4{w[0], w[1], w[2], w[3]};
+    return r;
+  }
+  __device__ static void unpack(const Raw& r, float v[8]) {
+    v[0] = __uint_as_float(r.a.x << 16); v[1] = __uint_as_float(r.a.x & 0xffff0000u);
+    v[2] = __uint_as_float(r.a.y << 16); v[3] = __uint_as_float(r.a.y & 0xffff0000u);
+    v[4] = __uint_as_float(r.a.z << 16); v[5] = __uint_as_float(r.a.z & 0xffff0000u);
+    v[6] = __uint_as_float(r.a.w << 16); v[7] = __uint_as_float(r.a.w & 0xffff0000u);
   }
 };
 
 struct F32 {
   typedef float T;
-  static constexpr int kKeyBits = 32;
-  __device__ static float at(const float* p, size_t x) { return p[x]; }
-  __device__ static void load8(const float* p, float v[8]) {
-    u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
-    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  struct Raw {
+    u32x4 a, b;
+  };
+  __device__ static float at(const float* p, size_t x) { return gptr(p)[x]; }
+  __device__ static Raw load(const float* p) {
+    Raw r;
+    r.a = __builtin_nontemporal_load(gptr(reinterpret_cast<const u32x4*>(p)));
+    r.b = __builtin_nontemporal_load(gptr(reinterpret_cast<const u32x4*>(p)) + 1);
+    return r;
+  }
+  // tokens at or past V read as `fill` (-inf for logits, 0 for probabilities)
+  __device__ static Raw gather(const float* p, int base, int V, uint32_t fill) {
+    uint32_t w[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) w[t] = (base + t < V) ? __float_as_uint(gptr(p)[base + t]) : fill;
+    Raw r;
+    r.a = u32x4{w[0], w[1], w[2], w[3]};
+    r.b = u32x4{w[4], w[5], w[6], w[7]};
+    return r;
+  }
+  __device__ static Raw gather(const float* p, int base, int V) { return gather(p, base, V, 0xff800000u); }
+  __device__ static void unpack(const Raw& r, float v[8]) {
+    v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y); v[2] = __uint_as_float(r.a.z);
+    v[3] = __uint_as_float(r.a.w); v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+    v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+  }
+  __device__ static void bits(const Raw& r, uint32_t u[8]) {
+    u[0] = r.a.x; u[1] = r.a.y; u[2] = r.a.z; u[3] = r.a.w;
+    u[4] = r.b.x; u[5] = r.b.y; u[6] = r.b.z; u[7] = r.b.w;
   }
 };
 
-// Logits of one step: 8 consecutive tokens from `base`; positions at or past V
-// read as -inf (no mass, never kept by a finite threshold, never an argmax).
+// One step of logits: vector load when every row start is 16-byte aligned
+// (the tail step masks tokens past V to -inf), scalar loads otherwise.
 template <class LT, bool VEC>
-__device__ inline void load_logits(const typename LT::T* row, int base, int V, float v[8]) {
-  if (VEC) {
-    if (base < V) {
-      LT::load8(row + base, v);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = -INFINITY;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (base + e < V) ? LT::at(row, (size_t)(base + e)) : -INFINITY;
-  }
+__device__ inline typename LT::Raw load_logits(const typename LT::T* row, int base, int V) {
+  if (VEC && base + kCh <= V) return LT::load(row + base);
+  return LT::gather(row, base, V);
 }
-
-// Draft probabilities of one step; positions at or past V read as 0.
 template <bool VEC>
-__device__ inline void load_q(const float* row, int base, int V, float v[8]) {
-  if (VEC) {
-    if (base < V) {
-      F32::load8(row + base, v);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (base + e < V) ? row[base + e] : 0.f;
-  }
+__device__ inline F32::Raw load_probs(const float* row, int base, int V) {
+  if (VEC && base + kCh <= V) return F32::load(row + base);
+  return F32::gather(row, base, V, 0u);
 }
 
 // order-preserving 32-bit key of a float; -0 and +0 share a key
@@ -182,10 +221,18 @@ __device__ inline float okey_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// 3-input max without canonicalising the operands (NaN operands are ignored
+// unless all are NaN; NaN rows are caught through the exponential sums).
+__device__ inline float fmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ inline float max8(const float v[8]) {
-  float a = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3]));
-  float b = __builtin_fmaxf(__builtin_fmaxf(v[4], v[5]), __builtin_fmaxf(v[6], v[7]));
-  return __builtin_fmaxf(a, b);
+  return fmax3(fmax3(v[0], v[1], v[2]), fmax3(v[3], v[4], v[5]), fmax3(v[6], v[7], v[7]));
+}
+__device__ inline uint32_t max8u(const uint32_t u[8]) {
+  return max(max(max(u[0], u[1]), max(u[2], u[3])), max(max(u[4], u[5]), max(u[6], u[7])));
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -195,6 +242,41 @@ __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ inline double temper_q(float q, float T) {
   return T == 1.f ? (double)q : pow((double)q, 1.0 / (double)T);
 }
+// 2^((l - m) * c) in fp64 with the fp32 scale c used by the streaming sums
+__device__ inline double mass_p(float l, float m, float c) {
+  return exp2(((double)l - (double)m) * (double)c);
+}
+
+// ------------------------------------------------------------------------------------------
+// hand-off of row results to the request's finishing workgroup
+//
+// Row statistics and kept lists are written with agent-scope atomic stores and
+// read back with agent-scope atomic loads: on gfx950 these are global stores /
+// loads with the device-coherence bit, which write through and read past the
+// per-XCD L2, so the finishing workgroup (possibly on another XCD) sees them
+// without a cache-wide write-back or invalidate.  Each writer waits for its
+// stores to complete before the workgroup barrier that precedes the counter
+// increment.
+// ------------------------------------------------------------------------------------------
+
+template <class T>
+__device__ inline void publish(T* dst, const T& v) {
+  static_assert(sizeof(T) % 8 == 0, "published records are whole 8-byte words");
+  const uint64_t* src = reinterpret_cast<const uint64_t*>(&v);
+  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
+#pragma unroll
+  for (int t = 0; t < (int)(sizeof(T) / 8); ++t) __hip_atomic_store(d + t, src[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ inline T fetch(const T* src) {
+  static_assert(sizeof(T) % 8 == 0, "published records are whole 8-byte words");
+  T v;
+  uint64_t* d = reinterpret_cast<uint64_t*>(&v);
+  const uint64_t* s = reinterpret_cast<const uint64_t*>(src);
+#pragma unroll
+  for (int t = 0; t < (int)(sizeof(T) / 8); ++t) d[t] = __hip_atomic_load(s + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
 
 // ------------------------------------------------------------------------------------------
 // wave / block helpers
@@ -202,6 +284,7 @@ __device__ inline double temper_q(float q, float T) {
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 __device__ inline uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
+__device__ inline int mbcnt(uint64_t m) { return __popcll(m & lanemask_lt()); }
 
 __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -217,11 +300,6 @@ __device__ inline double wave_sum_d(double v) {
 __device__ inline float wave_max_f(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ inline float wave_min_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = __builtin_fminf(v, __shfl_xor(v, o));
   return v;
 }
 __device__ inline uint32_t wave_max_u(uint32_t v) {
@@ -260,14 +338,6 @@ __device__ inline float block_max_f(float v, float* red) {
   if (lane_id() == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   float r = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
-  __syncthreads();
-  return r;
-}
-__device__ inline float block_min_f(float v, float* red) {
-  v = wave_min_f(v);
-  if (lane_id() == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = __builtin_fminf(__builtin_fminf(red[0], red[1]), __builtin_fminf(red[2], red[3]));
   __syncthreads();
   return r;
 }
@@ -352,129 +422,102 @@ __device__ inline Req load_req(const Args& a, int i) {
 }
 
 // ------------------------------------------------------------------------------------------
-// candidate buffers (top-k by rising threshold)
+// chunk buffers for top-k (rising threshold, whole 8-token chunks)
 // ------------------------------------------------------------------------------------------
 
-struct Cand {
-  float* val;     // this wave's slots in LDS
-  int* id;
-  int cnt;        // wave-uniform
-  float thr;      // wave-uniform: never above the k-th largest value seen
-  bool overflow;  // wave-uniform: too many ties to stay within the slots
+// A buffered chunk is 8 consecutive tokens of one lane: the order key of its
+// largest value and its first token id.  Values are re-read from the row only
+// for the few chunks that survive to the end of the pass.
+struct ChunkBuf {
+  uint32_t key[kCap];
+  int base[kCap];
 };
 
-// Key of the k-th largest entry (by okey) over up to four LDS segments
-// vals[s * stride .. + cnt[s]).  Requires 1 <= k <= total entries.  All 64
-// lanes of the calling wave must be active.
-__device__ uint32_t wave_kth_key(const float* vals, int stride, const int cnt[4], int nseg, int k, int key_bits,
-                                 uint32_t* hist) {
+// Wave-uniform state of one buffer.
+struct ChunkState {
+  int cnt;
+  uint32_t thr;   // order key; chunks whose maximum key is below it are not buffered
+  bool ovf;
+};
+
+// Key of the k-th largest of the buffered chunk maxima (1 <= k <= cnt).
+__device__ inline uint32_t wave_kth_chunk_key(const LDS_AS ChunkBuf* b, int cnt, int k) {
   const int lane = lane_id();
-  uint32_t prefix = 0, above = 0;
-  for (int shift = 24; shift >= 32 - key_bits; shift -= 8) {
-    for (int b = lane; b < 256; b += 64) hist[b] = 0u;
-    wave_lds_sync();
-    const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
-    for (int s = 0; s < nseg; ++s) {
-      for (int e = lane; e < cnt[s]; e += 64) {
-        uint32_t key = okey(vals[s * stride + e]);
-        if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-    }
-    wave_lds_sync();
-    uint32_t h0 = hist[lane * 4], h1 = hist[lane * 4 + 1], h2 = hist[lane * 4 + 2], h3 = hist[lane * 4 + 3];
-    uint32_t local = h0 + h1 + h2 + h3, suf = local;
+  uint32_t key[kCap / 64];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      uint32_t t = (uint32_t)__shfl_down((int)suf, o);
-      if (lane + o < 64) suf += t;
-    }
-    uint64_t okm = __ballot(above + suf >= (uint32_t)k);
-    const int L = 63 - __clzll((long long)okm);
-    uint32_t cum = (uint32_t)__shfl((int)(above + suf - local), L);
-    uint32_t b3 = (uint32_t)__shfl((int)h3, L), b2 = (uint32_t)__shfl((int)h2, L), b1 = (uint32_t)__shfl((int)h1, L);
-    int d;
-    if (cum + b3 >= (uint32_t)k) {
-      d = 3;
-    } else {
-      cum += b3;
-      if (cum + b2 >= (uint32_t)k) {
-        d = 2;
-      } else {
-        cum += b2;
-        if (cum + b1 >= (uint32_t)k) {
-          d = 1;
-        } else {
-          cum += b1;
-          d = 0;
-        }
-      }
-    }
-    prefix |= (uint32_t)(L * 4 + d) << shift;
-    above = cum;
-    wave_lds_sync();
+  for (int t = 0; t < kCap / 64; ++t) key[t] = lane + 64 * t < cnt ? b->key[lane + 64 * t] : 0u;
+  uint32_t P = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t T = P | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int t = 0; t < kCap / 64; ++t) c += __popcll(__ballot(key[t] >= T));
+    if (c >= k) P = T;
   }
-  return prefix;
+  return P;
 }
 
-// Raise the wave's threshold to the k-th largest buffered value and drop the
-// entries below it.
-__device__ void cand_refresh(Cand& c, int k, int key_bits, uint32_t* hist) {
+// Raise the threshold to the k-th largest buffered chunk maximum and keep only
+// the chunks at or above it (their count is >= k, ties included).  Plain
+// values in and out, so callers keep their state in registers.
+__device__ __noinline__ ChunkState chunk_refresh(LDS_AS ChunkBuf* b, ChunkState s, int k) {
   const int lane = lane_id();
-  int cnts[4] = {c.cnt, 0, 0, 0};
-  const float thr = okey_value(wave_kth_key(c.val, 0, cnts, 1, k, key_bits, hist));
+  const uint32_t thr = wave_kth_chunk_key(b, s.cnt, k);
+  uint32_t key[kCap / 64];
+  int base[kCap / 64];
+#pragma unroll
+  for (int t = 0; t < kCap / 64; ++t) {
+    const bool h = lane + 64 * t < s.cnt;
+    key[t] = h ? b->key[lane + 64 * t] : 0u;
+    base[t] = h ? b->base[lane + 64 * t] : 0;
+  }
+  wave_lds_sync();
   int n = 0;
-  for (int base = 0; base < c.cnt; base += 64) {
-    const int e = base + lane;
-    float v = 0.f;
-    int ix = 0;
-    bool keep = false;
-    if (e < c.cnt) {
-      v = c.val[e];
-      ix = c.id[e];
-      keep = v >= thr;
-    }
-    wave_lds_sync();
+#pragma unroll
+  for (int t = 0; t < kCap / 64; ++t) {
+    const bool keep = lane + 64 * t < s.cnt && key[t] >= thr;
     const uint64_t m = __ballot(keep);
     if (keep) {
-      const int pos = n + __popcll(m & lanemask_lt());
-      c.val[pos] = v;
-      c.id[pos] = ix;
+      const int p = n + mbcnt(m);
+      b->key[p] = key[t];
+      b->base[p] = base[t];
     }
     n += __popcll(m);
-    wave_lds_sync();
   }
-  c.cnt = n;
-  c.thr = thr;
-  if (n > kWcap - 64) c.overflow = true;
+  wave_lds_sync();
+  s.cnt = n;
+  s.thr = thr;
+  if (s.cnt > kCap - 64) s.ovf = true;
+  return s;
 }
 
-// Offer the 8 values of one step (tokens base..base+7, the first nvalid real).
-__device__ void cand_insert(Cand& c, const float v[8], int base, int nvalid, int k, int key_bits, uint32_t* hist) {
-  const int lane = lane_id();
-  for (int e = 0; e < 8; ++e) {
-    if (c.cnt > kWcap - 64) {
-      cand_refresh(c, k, key_bits, hist);
-      if (c.overflow) return;
-    }
-    const bool pass = e < nvalid && v[e] >= c.thr;
-    const uint64_t m = __ballot(pass);
-    if (pass) {
-      const int pos = c.cnt + __popcll(m & lanemask_lt());
-      c.val[pos] = v[e];
-      c.id[pos] = base + e;
-    }
-    c.cnt += __popcll(m);
+// Offer this lane's chunk (maximum key `key`, first token `base`).
+__device__ inline void chunk_offer(LDS_AS ChunkBuf* b, ChunkState& s, int k, bool valid, uint32_t key, int base) {
+  bool ins = valid && key >= s.thr;
+  uint64_t m = __ballot(ins);
+  if (!m || s.ovf) return;
+  int n = __popcll(m);
+  if (s.cnt + n > kCap) {
+    s = chunk_refresh(b, s, k);
+    if (s.ovf) return;
+    ins = valid && key >= s.thr;
+    m = __ballot(ins);
+    n = __popcll(m);
   }
-  (void)lane;
+  if (ins) {
+    const int p = s.cnt + mbcnt(m);
+    b->key[p] = key;
+    b->base[p] = base;
+  }
+  s.cnt += n;
 }
 
 // ------------------------------------------------------------------------------------------
-// radix select over a row in global memory (filters the candidate path does not serve)
+// radix select over a row in global memory (filters the chunk buffers do not serve)
 // ------------------------------------------------------------------------------------------
 
 struct SelectOut {
   uint32_t key;   // selected key
-  double w;       // weight of keys >= selected key
   bool reached;   // false: the total weight above lo stays below the target
 };
 
@@ -513,22 +556,21 @@ __device__ SelectOut block_select(KW kw, int V, uint32_t lo, double target, int 
       } else {
         const int L = 63 - __clzll((long long)okm);
         double cum = __shfl(above + suf - local, L);
-        const double b3 = __shfl(h3, L), b2 = __shfl(h2, L), b1 = __shfl(h1, L), b0 = __shfl(h0, L);
+        const double b3 = __shfl(h3, L), b2 = __shfl(h2, L), b1 = __shfl(h1, L);
         int d;
-        double wsel;
         if (cum + b3 >= target) {
-          d = 3; wsel = cum + b3;
+          d = 3;
         } else {
           cum += b3;
           if (cum + b2 >= target) {
-            d = 2; wsel = cum + b2;
+            d = 2;
           } else {
             cum += b2;
             if (cum + b1 >= target) {
-              d = 1; wsel = cum + b1;
+              d = 1;
             } else {
               cum += b1;
-              d = 0; wsel = cum + b0;
+              d = 0;
             }
           }
         }
@@ -536,7 +578,6 @@ __device__ SelectOut block_select(KW kw, int V, uint32_t lo, double target, int 
           s_u[0] = (uint32_t)(L * 4 + d);
           s_u[1] = 0u;
           s_d[0] = cum;
-          s_d[1] = wsel;
         }
       }
     }
@@ -544,13 +585,11 @@ __device__ SelectOut block_select(KW kw, int V, uint32_t lo, double target, int 
     if (s_u[1]) {
       out.reached = false;
       out.key = lo;
-      out.w = 0.0;
       __syncthreads();
       return out;
     }
     prefix |= s_u[0] << shift;
     above = s_d[0];
-    out.w = s_d[1];
     __syncthreads();
   }
   out.key = prefix;
@@ -571,363 +610,24 @@ __device__ double block_sum_above(KW kw, int V, uint32_t lo, double* red) {
 }
 
 // ------------------------------------------------------------------------------------------
-// kept set from the candidate buffers
-// ------------------------------------------------------------------------------------------
-
-struct Kept {
-  float cut;      // keep iff value >= cut
-  double mass;    // kept mass
-  int n;          // entries in the LDS list (values >= k-th largest)
-  bool ok;        // false: list capacity exceeded, use the radix select
-};
-
-// Merge the wave buffers of one distribution, find the k-th largest value,
-// collect the entries at or above it into the LDS list, weigh them with
-// mass(value) in fp64 and apply top-p over whole tie groups.
-template <class MassFn>
-__device__ Kept kept_from_candidates(float (*cval)[kWcap], int (*cid)[kWcap], const int* wcnt, int k, float top_p,
-                                     bool pact, int key_bits, MassFn mass, uint32_t* hist, float* lval, int* lid,
-                                     double* lmass, double* red_d, float* red_f, int* s_i) {
-  const int tid = threadIdx.x, lane = lane_id();
-  Kept out;
-  if (tid < 64) {
-    const int cnts[4] = {wcnt[0], wcnt[1], wcnt[2], wcnt[3]};
-    const float kth = okey_value(wave_kth_key(&cval[0][0], kWcap, cnts, kWaves, k, key_bits, hist));
-    int n = 0;
-    bool ok = true;
-    for (int s = 0; s < kWaves && ok; ++s) {
-      for (int base = 0; base < cnts[s]; base += 64) {
-        const int e = base + lane;
-        const bool keep = e < cnts[s] && cval[s][e] >= kth;
-        const uint64_t m = __ballot(keep);
-        if (n + __popcll(m) > kListMax) {
-          ok = false;
-          break;
-        }
-        if (keep) {
-          const int pos = n + __popcll(m & lanemask_lt());
-          lval[pos] = cval[s][e];
-          lid[pos] = cid[s][e];
-        }
-        n += __popcll(m);
-      }
-    }
-    if (lane == 0) {
-      s_i[0] = ok ? n : -1;
-      red_f[0] = kth;
-    }
-  }
-  __syncthreads();
-  const int n = s_i[0];
-  const float kth = red_f[0];
-  __syncthreads();
-  if (n < 0) {
-    out.ok = false;
-    return out;
-  }
-  out.ok = true;
-  out.n = n;
-  for (int t = tid; t < n; t += kBlock) lmass[t] = mass(lval[t]);
-  __syncthreads();
-  double zk = 0.0;
-  for (int t = tid; t < n; t += kBlock) zk += lmass[t];
-  zk = block_sum_d(zk, red_d);
-  float cut = kth;
-  if (pact) {
-    const double target = (double)top_p * zk;
-    float best = -INFINITY;
-    for (int t = tid; t < n; t += kBlock) {
-      const float v = lval[t];
-      double cum = 0.0;
-      for (int u = 0; u < n; ++u) cum += (lval[u] >= v) ? lmass[u] : 0.0;
-      if (cum >= target) best = __builtin_fmaxf(best, v);
-    }
-    best = block_max_f(best, red_f);
-    cut = (best == -INFINITY) ? kth : best;  // never reached by rounding: keep the whole top-k set
-  }
-  double zc = 0.0;
-  for (int t = tid; t < n; t += kBlock) zc += (lval[t] >= cut) ? lmass[t] : 0.0;
-  out.mass = block_sum_d(zc, red_d);
-  out.cut = cut;
-  return out;
-}
-
-// ------------------------------------------------------------------------------------------
-// row kernel
+// shared memory
 // ------------------------------------------------------------------------------------------
 
 struct RowShared {
-  float cval[2][kWaves][kWcap];
-  int cid[2][kWaves][kWcap];
-  uint32_t hist[kWaves][256];
+  ChunkBuf pb[kWaves];
+  ChunkBuf qb[kWaves];
   float lval[kListMax];
   int lid[kListMax];
   double lmass[kListMax];
+  ChunkState ps[kWaves], qs[kWaves];
   double red_d[kWaves];
   float red_f[kWaves];
   uint32_t red_u[kWaves];
   int red_i[kWaves];
-  int wcnt[2][kWaves];
-  int wovf[2][kWaves];
   double sel_d[2];
   uint32_t sel_u[2];
-  int misc[4];
+  int misc[8];
 };
-
-template <class LT, bool VEC>
-__global__ __launch_bounds__(kBlock) void row_kernel(Args a) {
-  __shared__ RowShared sh;
-  typedef typename LT::T ET;
-  const int N = a.N, G = a.G, V = a.V;
-  const int j = blockIdx.x / N, i = blockIdx.x - j * N;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const Req rq = load_req(a, i);
-  if (rq.fault || j > rq.gamma) return;
-  const size_t row = (size_t)i * (G + 1) + j;
-  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + row * (size_t)V;
-  RowStats* st = a.stats + row;
-  const bool draft_pos = j < rq.gamma;
-  const int y = draft_pos ? a.ids[(size_t)i * G + j] : -1;
-  const int nsteps = (V + kStep - 1) / kStep;
-
-  if (rq.greedy) {
-    // argmax, lowest id among equal maxima; NaN / +inf / no finite value is a fault
-    float best = -INFINITY;
-    int bidx = -1;
-    bool nan = false;
-    for (int s = 0; s < nsteps; ++s) {
-      const int base = s * kStep + tid * kCh;
-      float v[8];
-      load_logits<LT, VEC>(lrow, base, V, v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) nan |= (v[e] != v[e]);
-      const float cm = max8(v);
-      if (cm > best) {
-        int f = 7;
-#pragma unroll
-        for (int e = 7; e >= 0; --e)
-          if (v[e] == cm) f = e;
-        best = cm;
-        bidx = base + f;
-      }
-    }
-    const float gbest = block_max_f(best, sh.red_f);
-    int cand = (best == gbest && bidx >= 0) ? bidx : INT_MAX;
-    cand = block_min_i(cand, sh.red_i);
-    const int anynan = block_max_i(nan ? 1 : 0, sh.red_i);
-    if (tid == 0) {
-      int fault = 0;
-      if (anynan || gbest == INFINITY || cand == INT_MAX) fault = kFaultTargetRow;
-      RowStats s;
-      s.m = gbest;
-      s.cut_p = -INFINITY;
-      s.cut_q = -INFINITY;
-      s.argmax = cand == INT_MAX ? -1 : cand;
-      s.z = 0.0;
-      s.r = 0.0;
-      s.p_y = NAN;
-      s.q_y = NAN;
-      s.flags = ((draft_pos && y == cand) ? 1 : 0) | (fault << 8);
-      s.nlist = -1;
-      s.pad[0] = s.pad[1] = 0;
-      *st = s;
-    }
-    return;
-  }
-
-  const bool has_q = a.q != nullptr && draft_pos;
-  const float* qrow = has_q ? a.q + ((size_t)i * G + j) * (size_t)V : nullptr;
-  const float T = rq.T;
-  const float c = kLog2e / T;
-  const float invT = 1.f / T;
-  const bool temper = T != 1.f;
-  const bool filt = rq.kact || rq.pact;
-  const bool fast = rq.kact && rq.k <= kKFast;
-
-  // ---- one streaming pass over the row pair ----
-  float m_t = -FLT_MAX;
-  double z_t = 0.0, r_t = 0.0;
-  uint32_t qbad = 0u;
-  Cand cp{&sh.cval[0][wave][0], &sh.cid[0][wave][0], 0, -INFINITY, false};
-  Cand cq{&sh.cval[1][wave][0], &sh.cid[1][wave][0], 0, -INFINITY, false};
-  for (int s = 0; s < nsteps; ++s) {
-    const int base = s * kStep + tid * kCh;
-    float lv[8], qv[8];
-    load_logits<LT, VEC>(lrow, base, V, lv);
-    if (has_q) load_q<VEC>(qrow, base, V, qv);
-    const float cm = max8(lv);
-    if (cm > m_t) {
-      z_t *= (double)fast_exp2((m_t - cm) * c);
-      m_t = cm;
-    }
-    float zs = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) zs += fast_exp2((lv[e] - m_t) * c);
-    z_t += (double)zs;
-    if (has_q) {
-      float rs = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qbad = max(qbad, __float_as_uint(qv[e]));
-        rs += temper ? fast_exp2(fast_log2(qv[e]) * invT) : qv[e];
-      }
-      r_t += (double)rs;
-    }
-    if (fast) {
-      const int nvalid = VEC ? (base < V ? 8 : 0) : max(0, min(8, V - base));
-      if (!cp.overflow && __ballot(cm >= cp.thr)) cand_insert(cp, lv, base, nvalid, rq.k, LT::kKeyBits, sh.hist[wave]);
-      if (has_q && !cq.overflow && __ballot(max8(qv) >= cq.thr))
-        cand_insert(cq, qv, base, nvalid, rq.k, 32, sh.hist[wave]);
-    }
-  }
-
-  // ---- block totals ----
-  const float m = block_max_f(m_t, sh.red_f);
-  const double zpart = z_t * exp2(((double)m_t - (double)m) * (double)c);
-  const double Z = block_sum_d(zpart, sh.red_d);
-  const double R = has_q ? block_sum_d(r_t, sh.red_d) : 0.0;
-  const uint32_t qb = has_q ? block_max_u(qbad, sh.red_u) : 0u;
-  int fault = 0;
-  if (!(Z > 0.0) || isinf(Z)) fault |= kFaultTargetRow;
-  if (has_q && qb >= 0x7f800000u) fault |= kFaultDraftRow;
-
-  float cut_p = -INFINITY, cut_q = -INFINITY;
-  double Zk = Z, Rk = R;
-  int nlist = -1;
-  if (!fault && filt) {
-    if (fast && lane == 0) {
-      sh.wcnt[0][wave] = cp.cnt;
-      sh.wovf[0][wave] = cp.overflow;
-      sh.wcnt[1][wave] = cq.cnt;
-      sh.wovf[1][wave] = cq.overflow;
-    }
-    __syncthreads();
-    // target
-    bool done = false;
-    if (fast && !(sh.wovf[0][0] | sh.wovf[0][1] | sh.wovf[0][2] | sh.wovf[0][3])) {
-      const double mm = (double)m, TT = (double)T;
-      Kept kp = kept_from_candidates(sh.cval[0], sh.cid[0], sh.wcnt[0], rq.k, rq.p, rq.pact, LT::kKeyBits,
-                                     [&](float v) { return exp(((double)v - mm) / TT); }, sh.hist[0], sh.lval,
-                                     sh.lid, sh.lmass, sh.red_d, sh.red_f, sh.misc);
-      if (kp.ok) {
-        done = true;
-        cut_p = kp.cut;
-        Zk = kp.mass;
-        nlist = kp.n;
-        ListEntry* L = a.lists + row * kLcap;
-        for (int t = tid; t < kp.n; t += kBlock) {
-          ListEntry e;
-          e.id = sh.lid[t];
-          e.val = sh.lval[t];
-          e.e = sh.lmass[t];
-          L[t] = e;
-        }
-      }
-      __syncthreads();
-    }
-    if (!done) {
-      auto kw = [&](int x, uint32_t& key, double& w) {
-        const float l = LT::at(lrow, (size_t)x);
-        key = okey(l);
-        w = (double)fast_exp2((l - m) * c);
-      };
-      auto kc = [&](int x, uint32_t& key, double& w) {
-        key = okey(LT::at(lrow, (size_t)x));
-        w = 1.0;
-      };
-      uint32_t lo = 0u;
-      if (rq.kact) lo = block_select(kc, V, 0u, (double)rq.k, LT::kKeyBits, sh.lmass, sh.sel_d, sh.sel_u).key;
-      const double zk = rq.kact ? block_sum_above(kw, V, lo, sh.red_d) : Z;
-      uint32_t cutk = lo;
-      double zc = zk;
-      if (rq.pact) {
-        SelectOut so = block_select(kw, V, lo, (double)rq.p * zk, LT::kKeyBits, sh.lmass, sh.sel_d, sh.sel_u);
-        if (so.reached) {
-          cutk = so.key;
-          zc = block_sum_above(kw, V, cutk, sh.red_d);
-        }
-      }
-      cut_p = (cutk == 0u) ? -INFINITY : okey_value(cutk);
-      Zk = zc;
-    }
-    // draft
-    if (has_q) {
-      bool qdone = false;
-      if (fast && !(sh.wovf[1][0] | sh.wovf[1][1] | sh.wovf[1][2] | sh.wovf[1][3])) {
-        Kept kq = kept_from_candidates(sh.cval[1], sh.cid[1], sh.wcnt[1], rq.k, rq.p, rq.pact, 32,
-                                       [&](float v) { return temper_q(v, T); }, sh.hist[0], sh.lval, sh.lid,
-                                       sh.lmass, sh.red_d, sh.red_f, sh.misc);
-        if (kq.ok) {
-          qdone = true;
-          cut_q = kq.cut;
-          Rk = kq.mass;
-        }
-        __syncthreads();
-      }
-      if (!qdone) {
-        auto kw = [&](int x, uint32_t& key, double& w) {
-          const float q = qrow[x];
-          key = okey(q);
-          w = temper ? (double)fast_exp2(fast_log2(q) * invT) : (double)q;
-        };
-        auto kc = [&](int x, uint32_t& key, double& w) {
-          key = okey(qrow[x]);
-          w = 1.0;
-        };
-        uint32_t lo = 0u;
-        if (rq.kact) lo = block_select(kc, V, 0u, (double)rq.k, 32, sh.lmass, sh.sel_d, sh.sel_u).key;
-        const double rk = rq.kact ? block_sum_above(kw, V, lo, sh.red_d) : R;
-        uint32_t cutk = lo;
-        double rc = rk;
-        if (rq.pact) {
-          SelectOut so = block_select(kw, V, lo, (double)rq.p * rk, 32, sh.lmass, sh.sel_d, sh.sel_u);
-          if (so.reached) {
-            cutk = so.key;
-            rc = block_sum_above(kw, V, cutk, sh.red_d);
-          }
-        }
-        cut_q = (cutk == 0u) ? -INFINITY : okey_value(cutk);
-        Rk = rc;
-      }
-    }
-  }
-  if (!fault && has_q && !(Rk > 0.0)) fault |= kFaultDraftMass;
-
-  if (tid == 0) {
-    RowStats s;
-    s.m = m;
-    s.cut_p = cut_p;
-    s.cut_q = cut_q;
-    s.argmax = -1;
-    s.z = Zk;
-    s.r = Rk;
-    s.p_y = NAN;
-    s.q_y = NAN;
-    int acc = 0;
-    if (draft_pos && !fault) {
-      const float ly = LT::at(lrow, (size_t)y);
-      const double e = (ly >= cut_p) ? exp(((double)ly - (double)m) / (double)T) : 0.0;
-      const double py = e / Zk;
-      double qy = 1.0;
-      if (a.q != nullptr) {
-        const float qv = qrow[y];
-        qy = (qv >= cut_q) ? temper_q(qv, T) / Rk : 0.0;
-      }
-      const double u = (double)a.u_accept[(size_t)i * G + j];
-      acc = (u * qy < py) ? 1 : 0;
-      s.p_y = py;
-      s.q_y = qy;
-    }
-    s.flags = acc | (fault << 8);
-    s.nlist = nlist;
-    s.pad[0] = s.pad[1] = 0;
-    *st = s;
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// finish kernel: first rejection, draw, outputs
-// ------------------------------------------------------------------------------------------
 
 struct FinShared {
   double wsum[kWaves][kMaxChunks];
@@ -939,8 +639,406 @@ struct FinShared {
   double miscd[4];
 };
 
+union KernelShared {
+  RowShared row;
+  FinShared fin;
+};
+
+// ------------------------------------------------------------------------------------------
+// kept set from the chunk buffers
+// ------------------------------------------------------------------------------------------
+
+struct Kept {
+  float cut;      // keep iff value >= cut
+  double mass;    // kept mass
+  int n;          // list entries (values >= the k-th largest)
+  bool ok;        // false: capacity exceeded, use the radix select
+};
+
+// After the stream: each wave prunes its buffer to its k-th largest chunk
+// maximum; every token of the buffered chunks at or above the best wave
+// threshold L (a lower bound of the true k-th largest value) is re-read from
+// the row into the LDS list; the exact k-th largest value is found there, the
+// tokens at or above it are weighed in fp64 (target: 2^((l - m) * c); draft:
+// q^(1/T)) and top-p is applied over whole tie groups.  `row` is the target
+// row (bf16 or fp32 per `bf16`) or the draft row (fp32); VEC rows are 16-byte
+// aligned with V a multiple of 8.
+struct KeptArgs {
+  const void* row;
+  int V;
+  bool bf16;      // row holds bfloat16 (else fp32)
+  bool draft;     // weights q^(1/T) (else 2^((l - m) * c))
+  float m, c, T;
+  int k;
+  float top_p;
+  bool pact;
+};
+
+__device__ inline float row_value(const KeptArgs& ka, int x) {
+  return ka.bf16 ? Bf16::at(reinterpret_cast<const uint16_t*>(ka.row), (size_t)x)
+                 : F32::at(reinterpret_cast<const float*>(ka.row), (size_t)x);
+}
+
+__device__ __noinline__ Kept kept_from_chunks(KeptArgs ka, LDS_AS ChunkBuf* bufs, LDS_AS ChunkState* states,
+                                              LDS_AS float* lval, LDS_AS int* lid, LDS_AS double* lmass,
+                                              LDS_AS double* red_d, LDS_AS float* red_f, LDS_AS int* misc) {
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  const int k = ka.k;
+  Kept out;
+  LDS_AS ChunkBuf* b = bufs + w;
+  ChunkState s;
+  s.cnt = states[w].cnt;
+  s.thr = states[w].thr;
+  s.ovf = states[w].ovf;
+  if (s.cnt > k && !s.ovf) {
+    s = chunk_refresh(b, s, k);
+    s.ovf = false;  // no insertion follows: a full buffer is fine here
+  }
+  __syncthreads();
+  if (lane == 0) {
+    states[w].cnt = s.cnt;
+    states[w].thr = s.thr;
+    states[w].ovf = s.ovf;
+  }
+  __syncthreads();
+  bool ovf = false;
+  uint32_t L = 0u;
+  for (int v = 0; v < kWaves; ++v) {
+    ovf |= states[v].ovf;
+    L = max(L, states[v].thr);
+  }
+  if (ovf) {
+    out.ok = false;
+    return out;
+  }
+  const float Lf = okey_value(L);
+  // wave w re-reads the tokens of its chunks whose maximum reaches L
+  int n = 0;
+  bool fits = true;
+  for (int e0 = 0; e0 < s.cnt; e0 += 64) {
+    const int e = e0 + lane;
+    const bool mine = e < s.cnt && b->key[e] >= L;
+    const int cb = mine ? b->base[e] : 0;
+    float v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = (mine && cb + t < ka.V) ? row_value(ka, cb + t) : -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const bool take = mine && cb + t < ka.V && v[t] >= Lf;
+      const uint64_t m = __ballot(take);
+      if (n + __popcll(m) > kSegMax) fits = false;
+      if (take && fits) {
+        const int p = w * kSegMax + n + mbcnt(m);
+        lval[p] = v[t];
+        lid[p] = cb + t;
+      }
+      n += __popcll(m);
+    }
+  }
+  if (lane == 0) misc[w] = fits ? n : -1;
+  __syncthreads();
+  int off[kWaves + 1];
+  off[0] = 0;
+  bool ok = true;
+  for (int v = 0; v < kWaves; ++v) {
+    ok &= misc[v] >= 0;
+    off[v + 1] = off[v] + (misc[v] >= 0 ? misc[v] : 0);
+  }
+  if (!ok) {
+    __syncthreads();
+    out.ok = false;
+    return out;
+  }
+  // make the list contiguous (all reads before any write)
+  const int my = misc[w];
+  float tv0 = 0.f, tv1 = 0.f;
+  int ti0 = 0, ti1 = 0;
+  if (lane < my) { tv0 = lval[w * kSegMax + lane]; ti0 = lid[w * kSegMax + lane]; }
+  if (lane + 64 < my) { tv1 = lval[w * kSegMax + lane + 64]; ti1 = lid[w * kSegMax + lane + 64]; }
+  __syncthreads();
+  if (lane < my) { lval[off[w] + lane] = tv0; lid[off[w] + lane] = ti0; }
+  if (lane + 64 < my) { lval[off[w] + lane + 64] = tv1; lid[off[w] + lane + 64] = ti1; }
+  __syncthreads();
+  const int total = off[kWaves];
+  // exact k-th largest value of the list (which holds every value at or above it)
+  float kth = -INFINITY;
+  for (int t = tid; t < total; t += kBlock) {
+    const float v = lval[t];
+    int gt = 0, ge = 0;
+    for (int u = 0; u < total; ++u) {
+      gt += lval[u] > v;
+      ge += lval[u] >= v;
+    }
+    if (gt < k && k <= ge) kth = v;
+  }
+  kth = block_max_f(kth, (float*)red_f);
+  // tokens at or above the k-th largest, in list order
+  int nk = 0;
+  if (tid < 64) {
+    for (int base = 0; base < total; base += 64) {
+      const int e = base + lane;
+      float v = 0.f;
+      int id = 0;
+      bool take = false;
+      if (e < total) {
+        v = lval[e];
+        id = lid[e];
+        take = v >= kth;
+      }
+      wave_lds_sync();
+      const uint64_t m = __ballot(take);
+      if (take) {
+        lval[nk + mbcnt(m)] = v;
+        lid[nk + mbcnt(m)] = id;
+      }
+      nk += __popcll(m);
+      wave_lds_sync();
+    }
+    if (lane == 0) misc[kWaves] = nk;
+  }
+  __syncthreads();
+  nk = misc[kWaves];
+  for (int t = tid; t < nk; t += kBlock) lmass[t] = ka.draft ? temper_q(lval[t], ka.T) : mass_p(lval[t], ka.m, ka.c);
+  __syncthreads();
+  double zk = 0.0;
+  for (int t = tid; t < nk; t += kBlock) zk += lmass[t];
+  zk = block_sum_d(zk, (double*)red_d);
+  float cut = kth;
+  if (ka.pact) {
+    const double target = (double)ka.top_p * zk;
+    float best = -INFINITY;
+    for (int t = tid; t < nk; t += kBlock) {
+      const float v = lval[t];
+      double cum = 0.0;
+      for (int u = 0; u < nk; ++u) cum += (lval[u] >= v) ? lmass[u] : 0.0;
+      if (cum >= target) best = __builtin_fmaxf(best, v);
+    }
+    best = block_max_f(best, (float*)red_f);
+    cut = (best == -INFINITY) ? kth : best;  // never reached by rounding: keep the whole top-k set
+  }
+  double zc = 0.0;
+  for (int t = tid; t < nk; t += kBlock) zc += (lval[t] >= cut) ? lmass[t] : 0.0;
+  out.mass = block_sum_d(zc, (double*)red_d);
+  out.cut = cut;
+  out.n = nk;
+  out.ok = true;
+  return out;
+}
+
+// Filters the chunk buffers do not serve: radix selects that re-read the row.
+// Returns the cut value (-inf: keep all) and the kept mass in *mass.
+struct GeneralArgs {
+  const void* row;
+  int V;
+  bool bf16, draft;
+  float m, c, invT;
+  bool temper;
+  int k;
+  bool kact;
+  float top_p;
+  bool pact;
+  double total;   // unfiltered mass of the row
+};
+
+struct Filtered {
+  float cut;
+  double mass;
+};
+
+__device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hist, LDS_AS double* sel_d,
+                                                LDS_AS uint32_t* sel_u, LDS_AS double* red) {
+  KeptArgs ka;
+  ka.row = g.row;
+  ka.V = g.V;
+  ka.bf16 = g.bf16;
+  auto weight = [&](float v) -> double {
+    return g.draft ? (g.temper ? (double)fast_exp2(fast_log2(v) * g.invT) : (double)v)
+                   : (double)fast_exp2((v - g.m) * g.c);
+  };
+  auto kw = [&](int x, uint32_t& key, double& w) {
+    const float v = row_value(ka, x);
+    key = okey(v);
+    w = weight(v);
+  };
+  auto kc = [&](int x, uint32_t& key, double& w) {
+    key = okey(row_value(ka, x));
+    w = 1.0;
+  };
+  uint32_t lo = 0u;
+  if (g.kact)
+    lo = block_select(kc, g.V, 0u, (double)g.k, 32, (double*)hist, (double*)sel_d, (uint32_t*)sel_u).key;
+  const double zk = g.kact ? block_sum_above(kw, g.V, lo, (double*)red) : g.total;
+  uint32_t cutk = lo;
+  double zc = zk;
+  if (g.pact) {
+    SelectOut so = block_select(kw, g.V, lo, (double)g.top_p * zk, 32, (double*)hist, (double*)sel_d,
+                                (uint32_t*)sel_u);
+    if (so.reached) {
+      cutk = so.key;
+      zc = block_sum_above(kw, g.V, cutk, (double*)red);
+    }
+  }
+  Filtered f;
+  f.cut = (cutk == 0u) ? -INFINITY : okey_value(cutk);
+  f.mass = zc;
+  return f;
+}
+
+// ------------------------------------------------------------------------------------------
+// streaming passes
+// ------------------------------------------------------------------------------------------
+
+// Stream `nfull` full steps keeping D steps of loads in flight: load(s)
+// returns the raw data of step s, proc(raw, s) reduces it.  In the steady
+// state every refill is unconditional, so the compiler's wait counters let
+// the D - 1 younger loads stay outstanding while the oldest is reduced.
+template <int D, class Raw, class Load, class Proc>
+__device__ __forceinline__ void ring_stream(int nfull, Load load, Proc proc) {
+  Raw ring[D];
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < nfull) ring[u] = load(u);
+  int s0 = 0;
+  for (; s0 + 2 * D <= nfull; s0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const Raw cur = ring[u];
+      ring[u] = load(s0 + u + D);
+      proc(cur, s0 + u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    const int s = s0 + u;
+    if (s < nfull) {
+      const Raw cur = ring[u];
+      if (s + D < nfull) ring[u] = load(s + D);
+      proc(cur, s);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    const int s = s0 + D + u;
+    if (s < nfull) proc(ring[u], s);
+  }
+}
+
+template <class LR>
+struct StepRaw {
+  LR l;
+  F32::Raw q;
+};
+
+struct StochState {
+  float m;          // running max of this thread's logits
+  double z;         // sum of 2^((l - m) * c) over this thread's logits
+  double r;         // sum of q^(1/T)
+  uint32_t qbad;    // max raw bits of q (>= 0x7f800000: NaN, inf or sign bit)
+  ChunkState ps, qs;
+};
+
+// QM: 0 no draft row, 1 draft row at T = 1, 2 draft row at T != 1.
+template <class LT, bool VEC, int QM, bool CAND>
+__device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, const float* qrow, int V, float c, float invT, int k,
+                                  RowShared& sh, StochState& st) {
+  typedef typename LT::Raw LR;
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int nsteps = (V + kStep - 1) / kStep;
+  auto process = [&](const LR& lr, const F32::Raw& qr, int base) {
+    const bool valid = base < V;
+    float v[8];
+    LT::unpack(lr, v);
+    const float cm = max8(v);
+    if (cm > st.m) {
+      st.z *= (double)fast_exp2((st.m - cm) * c);
+      st.m = cm;
+    }
+    float e[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) e[t] = fast_exp2((v[t] - st.m) * c);
+    st.z += (double)(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+    uint32_t qmax = 0u;
+    if (QM) {
+      uint32_t u[8];
+      F32::bits(qr, u);
+      qmax = max8u(u);
+      st.qbad = max(st.qbad, qmax);
+      float r[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float qv = __uint_as_float(u[t]);
+        r[t] = (QM == 1) ? qv : fast_exp2(fast_log2(qv) * invT);
+      }
+      st.r += (double)(((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7])));
+    }
+    if (CAND) {
+      chunk_offer((LDS_AS ChunkBuf*)&sh.pb[w], st.ps, k, valid, okey(cm), base);
+      if (QM) chunk_offer((LDS_AS ChunkBuf*)&sh.qb[w], st.qs, k, valid, qmax | 0x80000000u, base);  // okey of q >= 0
+    }
+  };
+  // full steps (every lane's 8 tokens inside the row, vector loads only)
+  const int nfull = VEC ? V / kStep : 0;
+  const int base0 = tid * kCh;
+  ring_stream<QM ? 4 : 8, StepRaw<LR>>(
+      nfull,
+      [&](int s) {
+        StepRaw<LR> r;
+        r.l = LT::load(lrow + base0 + s * kStep);
+        if (QM) r.q = F32::load(qrow + base0 + s * kStep);
+        return r;
+      },
+      [&](const StepRaw<LR>& r, int s) { process(r.l, r.q, base0 + s * kStep); });
+  int base = base0 + nfull * kStep;
+  // the ragged tail (and every step of rows that are not 16-byte aligned)
+  for (int s = nfull; s < nsteps; ++s) {
+    const LR lr = load_logits<LT, VEC>(lrow, base, V);
+    F32::Raw qr{};
+    if (QM) qr = load_probs<VEC>(qrow, base, V);
+    process(lr, qr, base);
+    base += kStep;
+  }
+}
+
+// Greedy rows: argmax (lowest id among equal maxima) and a running sum that
+// flags NaN / +inf for an exact re-check.
+template <class LT, bool VEC>
+__device__ void stream_greedy(const typename LT::T* lrow, int V, float& best, int& bidx, float& acc) {
+  typedef typename LT::Raw LR;
+  const int tid = threadIdx.x;
+  const int nsteps = (V + kStep - 1) / kStep;
+  auto process = [&](const LR& lr, int base) {
+    float v[8];
+    LT::unpack(lr, v);
+    if (base < V) {
+      acc += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+      const float cm = max8(v);
+      if (cm > best) {
+        int f = 7;
+#pragma unroll
+        for (int t = 7; t >= 0; --t)
+          if (v[t] == cm) f = t;
+        best = cm;
+        bidx = base + f;
+      }
+    }
+  };
+  const int nfull = VEC ? V / kStep : 0;
+  const int base0 = tid * kCh;
+  ring_stream<8, LR>(
+      nfull, [&](int s) { return LT::load(lrow + base0 + s * kStep); },
+      [&](const LR& r, int s) { process(r, base0 + s * kStep); });
+  int base = base0 + nfull * kStep;
+  for (int s = nfull; s < nsteps; ++s) {
+    process(load_logits<LT, VEC>(lrow, base, V), base);
+    base += kStep;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// per-request finish (run by the last workgroup of the request)
+// ------------------------------------------------------------------------------------------
+
 // Draw weights of one step (mode 0: p'; 1: max(0, p' - q'); 2: p' with y removed).
-template <bool VEC>
 __device__ inline void step_weights(const float lv[8], const float qv[8], int base, int mode, float m, float c,
                                     float invZ, float cut_p, float cut_q, float invR, float invT, bool temper, int yA,
                                     float w[8]) {
@@ -960,11 +1058,12 @@ __device__ inline void step_weights(const float lv[8], const float qv[8], int ba
 }
 
 template <class LT, bool VEC>
-__global__ __launch_bounds__(kBlock) void finish_kernel(Args a) {
-  __shared__ FinShared sh;
+__device__ __noinline__ void finish_request(const CONST_AS Args* ap, int i, LDS_AS FinShared* sh) {
+  Args a;
+  __builtin_memcpy(&a, (const Args*)ap, sizeof(Args));
   typedef typename LT::T ET;
+  typedef typename LT::Raw LR;
   const int G = a.G, V = a.V;
-  const int i = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const Req rq = load_req(a, i);
   int32_t* out = a.out_tokens + (size_t)i * (G + 1);
@@ -974,20 +1073,20 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(Args a) {
   if (!fault) {
     if (wave == 0) {
       int f = 0;
-      for (int jj = lane; jj <= rq.gamma; jj += 64) f |= st[jj].flags >> 8;
+      for (int jj = lane; jj <= rq.gamma; jj += 64) f |= fetch(st + jj).flags >> 8;
       f = wave_or_i(f);
-      const bool acc = lane < rq.gamma && (st[lane].flags & 1);
+      const bool acc = lane < rq.gamma && (fetch(st + lane).flags & 1);
       const uint64_t accm = __ballot(acc);
       const uint64_t within = rq.gamma >= 64 ? ~0ull : ((1ull << rq.gamma) - 1ull);
       const uint64_t rej = ~accm & within;
       if (lane == 0) {
-        sh.misc[0] = f;
-        sh.misc[1] = rej ? (__ffsll((unsigned long long)rej) - 1) : rq.gamma;
+        sh->misc[0] = f;
+        sh->misc[1] = rej ? (__ffsll((unsigned long long)rej) - 1) : rq.gamma;
       }
     }
     __syncthreads();
-    fault = sh.misc[0];
-    A = sh.misc[1];
+    fault = sh->misc[0];
+    A = sh->misc[1];
     __syncthreads();
   }
 
@@ -1008,9 +1107,9 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(Args a) {
   int z;
   double S_out = NAN;
   if (rq.greedy) {
-    z = st[A].argmax;
+    z = fetch(st + A).argmax;
   } else {
-    const RowStats sa = st[A];
+    const RowStats sa = fetch(st + A);
     const bool resid = A < rq.gamma;
     const int yA = resid ? a.ids[(size_t)i * G + A] : -1;
     int mode = resid ? (a.q ? 1 : 2) : 0;
@@ -1021,12 +1120,12 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(Args a) {
     const double us = (double)a.u_sample[i];
 
     if (sa.nlist >= 0) {
-      // ---- kept list of row A: all tokens with p' > 0 are in it ----
+      // ---- kept list of row A: every token with p' > 0 is in it ----
       const ListEntry* L = a.lists + row * kLcap;
       const int n = sa.nlist;
       double part = 0.0;
       for (int t = tid; t < n; t += kBlock) {
-        const ListEntry e = L[t];
+        const ListEntry e = fetch(L + t);
         const double p = (e.val >= sa.cut_p) ? e.e / sa.z : 0.0;
         double w = p;
         if (mode == 1) {
@@ -1036,33 +1135,33 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(Args a) {
         } else if (mode == 2) {
           w = (e.id == yA) ? 0.0 : p;
         }
-        sh.lw[t] = w;
-        sh.lwid[t] = e.id;
+        sh->lw[t] = w;
+        sh->lwid[t] = e.id;
         part += w;
       }
-      double S = block_sum_d(part, sh.red_d);
+      double S = block_sum_d(part, (double*)sh->red_d);
       if (S == 0.0) {
         part = 0.0;
         for (int t = tid; t < n; t += kBlock) {
-          const ListEntry e = L[t];
+          const ListEntry e = fetch(L + t);
           const double p = (e.val >= sa.cut_p) ? e.e / sa.z : 0.0;
-          sh.lw[t] = p;
+          sh->lw[t] = p;
           part += p;
         }
-        S = block_sum_d(part, sh.red_d);
+        S = block_sum_d(part, (double*)sh->red_d);
       }
       const double tau = us * S;
       int best = INT_MAX, last = -1;
       for (int t = tid; t < n; t += kBlock) {
-        if (!(sh.lw[t] > 0.0)) continue;
-        const int id = sh.lwid[t];
+        if (!(sh->lw[t] > 0.0)) continue;
+        const int id = sh->lwid[t];
         double cum = 0.0;
-        for (int u = 0; u < n; ++u) cum += (sh.lwid[u] <= id) ? sh.lw[u] : 0.0;
+        for (int u = 0; u < n; ++u) cum += (sh->lwid[u] <= id) ? sh->lw[u] : 0.0;
         if (cum > tau) best = min(best, id);
         last = max(last, id);
       }
-      best = block_min_i(best, sh.red_i);
-      last = block_max_i(last, sh.red_i);
+      best = block_min_i(best, (int*)sh->red_i);
+      last = block_max_i(last, (int*)sh->red_i);
       z = (best != INT_MAX) ? best : last;
       S_out = S;
     } else {
@@ -1078,57 +1177,73 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(Args a) {
       int last = -1;
       for (int attempt = 0; attempt < 2; ++attempt) {
         last = -1;
-        for (int ch = 0; ch < nch; ++ch) {
-          double csum = 0.0;
-          for (int s = ch * spc; s < min(nsteps, (ch + 1) * spc); ++s) {
-            const int base = s * kStep + tid * kCh;
-            float lv[8], qv[8], w[8];
-            load_logits<LT, VEC>(lrow, base, V, lv);
-            if (mode == 1) load_q<VEC>(qrow, base, V, qv);
-            step_weights<VEC>(lv, qv, base, mode, m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w);
-            double ts = 0.0;
+        double csum = 0.0;
+        auto step = [&](const LR& lr, const F32::Raw& qr, int base, int s) {
+          float lv[8], qv[8], w[8];
+          LT::unpack(lr, lv);
+          F32::unpack(qr, qv);
+          step_weights(lv, qv, base, mode, m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w);
+          double ts = 0.0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              ts += (double)w[e];
-              if (w[e] > 0.f) last = base + e;
-            }
-            csum += wave_sum_d(ts);
+          for (int e = 0; e < 8; ++e) {
+            ts += (double)w[e];
+            if (w[e] > 0.f) last = base + e;
           }
-          if (lane == 0) sh.wsum[wave][ch] = csum;
+          csum += wave_sum_d(ts);
+          if ((s + 1) % spc == 0 || s + 1 == nsteps) {
+            if (lane == 0) sh->wsum[wave][s / spc] = csum;
+            csum = 0.0;
+          }
+        };
+        const int nfull = VEC ? V / kStep : 0;
+        const int base0 = tid * kCh;
+        ring_stream<4, StepRaw<LR>>(
+            nfull,
+            [&](int s) {
+              StepRaw<LR> r;
+              r.l = LT::load(lrow + base0 + s * kStep);
+              r.q = F32::Raw{};
+              if (mode == 1) r.q = F32::load(qrow + base0 + s * kStep);
+              return r;
+            },
+            [&](const StepRaw<LR>& r, int s) { step(r.l, r.q, base0 + s * kStep, s); });
+        int base = base0 + nfull * kStep;
+        for (int s = nfull; s < nsteps; ++s) {
+          step(load_logits<LT, VEC>(lrow, base, V), mode == 1 ? load_probs<VEC>(qrow, base, V) : F32::Raw{}, base, s);
+          base += kStep;
         }
         __syncthreads();
-        // chunk totals in a fixed order, then the sum
         if (tid == 0) {
           double tot = 0.0;
-          for (int ch = 0; ch < nch; ++ch) tot += ((sh.wsum[0][ch] + sh.wsum[1][ch]) + (sh.wsum[2][ch] + sh.wsum[3][ch]));
-          sh.miscd[0] = tot;
+          for (int ch = 0; ch < nch; ++ch) tot += ((sh->wsum[0][ch] + sh->wsum[1][ch]) + (sh->wsum[2][ch] + sh->wsum[3][ch]));
+          sh->miscd[0] = tot;
         }
         __syncthreads();
-        S = sh.miscd[0];
+        S = sh->miscd[0];
         __syncthreads();
         if (S > 0.0 || mode == 0) break;
         mode = 0;  // zero residual: draw from p'
       }
-      last = block_max_i(last, sh.red_i);
+      last = block_max_i(last, (int*)sh->red_i);
       const double tau = us * S;
       // the chunk holding the crossing (serial over at most kMaxChunks totals)
       if (tid == 0) {
         double pre = 0.0;
         int found = -1;
         for (int ch = 0; ch < nch; ++ch) {
-          const double cs = (sh.wsum[0][ch] + sh.wsum[1][ch]) + (sh.wsum[2][ch] + sh.wsum[3][ch]);
+          const double cs = (sh->wsum[0][ch] + sh->wsum[1][ch]) + (sh->wsum[2][ch] + sh->wsum[3][ch]);
           if (pre + cs > tau && cs > 0.0) {
             found = ch;
             break;
           }
           pre += cs;
         }
-        sh.misc[2] = found;
-        sh.miscd[1] = pre;
+        sh->misc[2] = found;
+        sh->miscd[1] = pre;
       }
       __syncthreads();
-      const int found = sh.misc[2];
-      double pre = sh.miscd[1];
+      const int found = sh->misc[2];
+      double pre = sh->miscd[1];
       __syncthreads();
       if (found < 0) {
         z = last;
@@ -1139,14 +1254,14 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(Args a) {
         for (int s = found * spc; s < min(nsteps, (found + 1) * spc); ++s) {
           const int base = s * kStep + tid * kCh;
           float lv[8], qv[8], w[8];
-          load_logits<LT, VEC>(lrow, base, V, lv);
-          if (mode == 1) load_q<VEC>(qrow, base, V, qv);
-          step_weights<VEC>(lv, qv, base, mode, m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w);
+          LT::unpack(load_logits<LT, VEC>(lrow, min(base, V), V), lv);
+          F32::unpack(mode == 1 ? load_probs<VEC>(qrow, min(base, V), V) : F32::Raw{}, qv);
+          step_weights(lv, qv, base, mode, m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w);
           double ts = 0.0;
 #pragma unroll
           for (int e = 0; e < 8; ++e) ts += (double)w[e];
           double total;
-          const double ex = pre + block_exscan_d(ts, sh.red_d, &total);
+          const double ex = pre + block_exscan_d(ts, (double*)sh->red_d, &total);
           if (ts > 0.0 && ex <= tau) {
             double acc = ex;
             int zz = -1, lastpos = -1;
@@ -1161,12 +1276,12 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(Args a) {
           }
           pre += total;
         }
-        const int win = block_max_i(bestkey, sh.red_i);
-        if (tid == 0) sh.misc[3] = -1;
+        const int win = block_max_i(bestkey, (int*)sh->red_i);
+        if (tid == 0) sh->misc[3] = -1;
         __syncthreads();
-        if (win >= 0 && bestkey == win) sh.misc[3] = bestz;
+        if (win >= 0 && bestkey == win) sh->misc[3] = bestz;
         __syncthreads();
-        z = sh.misc[3];
+        z = sh->misc[3];
         if (z < 0) z = last;
       }
       S_out = S;
@@ -1185,9 +1300,283 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(Args a) {
     if (a.d_resid) a.d_resid[i] = S_out;
   }
   if (a.d_py)
-    for (int t = tid; t < G; t += kBlock) a.d_py[(size_t)i * G + t] = (t < rq.gamma && !rq.greedy) ? st[t].p_y : NAN;
+    for (int t = tid; t < G; t += kBlock)
+      a.d_py[(size_t)i * G + t] = (t < rq.gamma && !rq.greedy) ? fetch(st + t).p_y : NAN;
   if (a.d_qy)
-    for (int t = tid; t < G; t += kBlock) a.d_qy[(size_t)i * G + t] = (t < rq.gamma && !rq.greedy) ? st[t].q_y : NAN;
+    for (int t = tid; t < G; t += kBlock)
+      a.d_qy[(size_t)i * G + t] = (t < rq.gamma && !rq.greedy) ? fetch(st + t).q_y : NAN;
+}
+
+// ------------------------------------------------------------------------------------------
+// row processing
+// ------------------------------------------------------------------------------------------
+
+template <class LT, bool VEC>
+__device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, int j, RowShared& sh) {
+  typedef typename LT::T ET;
+  const int G = a.G, V = a.V, tid = threadIdx.x;
+  const size_t row = (size_t)i * (G + 1) + j;
+  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + row * (size_t)V;
+  float best = -INFINITY, acc = 0.f;
+  int bidx = -1;
+  stream_greedy<LT, VEC>(lrow, V, best, bidx, acc);
+  const float gbest = block_max_f(best, sh.red_f);
+  int cand = (best == gbest && bidx >= 0) ? bidx : INT_MAX;
+  cand = block_min_i(cand, sh.red_i);
+  // the running sum is finite unless the row holds NaN, an infinity, or
+  // values whose sum overflows: then look exactly for NaN / +inf
+  const int suspicious = block_max_i(isfinite(acc) ? 0 : 1, sh.red_i);
+  int bad = 0;
+  if (suspicious) {
+    for (int x = tid; x < V; x += kBlock) {
+      const float l = LT::at(lrow, (size_t)x);
+      bad |= (l != l) || (l == INFINITY);
+    }
+    bad = block_max_i(bad, sh.red_i);
+  }
+  if (tid == 0) {
+    const int fault = (bad || gbest == INFINITY || cand == INT_MAX) ? kFaultTargetRow : 0;
+    const int y = j < rq.gamma ? a.ids[(size_t)i * G + j] : -1;
+    RowStats s;
+    s.m = gbest;
+    s.cut_p = -INFINITY;
+    s.cut_q = -INFINITY;
+    s.argmax = cand == INT_MAX ? -1 : cand;
+    s.z = 0.0;
+    s.r = 0.0;
+    s.p_y = NAN;
+    s.q_y = NAN;
+    s.flags = ((j < rq.gamma && y == cand) ? 1 : 0) | (fault << 8);
+    s.nlist = -1;
+    s.pad[0] = s.pad[1] = 0;
+    publish(a.stats + row, s);
+  }
+}
+
+template <class LT, bool VEC>
+__device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int i, int j, RowShared& sh) {
+  typedef typename LT::T ET;
+  const int G = a.G, V = a.V;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const size_t row = (size_t)i * (G + 1) + j;
+  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + row * (size_t)V;
+  const bool draft_pos = j < rq.gamma;
+  const bool has_q = a.q != nullptr && draft_pos;
+  const float* qrow = has_q ? a.q + ((size_t)i * G + j) * (size_t)V : nullptr;
+  const float T = rq.T;
+  const float c = kLog2e / T;
+  const float invT = 1.f / T;
+  const bool temper = T != 1.f;
+  const bool filt = rq.kact || rq.pact;
+  const bool cand = rq.kact && rq.k <= kKFast;
+
+  StochState st;
+  st.m = -FLT_MAX;
+  st.z = 0.0;
+  st.r = 0.0;
+  st.qbad = 0u;
+  st.ps = ChunkState{0, 0u, false};
+  st.qs = ChunkState{0, 0u, false};
+  const int qm = has_q ? (temper ? 2 : 1) : 0;
+  if (cand) {
+    if (qm == 0) stream_stochastic<LT, VEC, 0, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
+    else if (qm == 1) stream_stochastic<LT, VEC, 1, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
+    else stream_stochastic<LT, VEC, 2, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
+  } else {
+    if (qm == 0) stream_stochastic<LT, VEC, 0, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
+    else if (qm == 1) stream_stochastic<LT, VEC, 1, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
+    else stream_stochastic<LT, VEC, 2, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
+  }
+
+  // ---- block totals ----
+  const float m = block_max_f(st.m, sh.red_f);
+  const double zpart = st.z * exp2(((double)st.m - (double)m) * (double)c);
+  const double Z = block_sum_d(zpart, sh.red_d);
+  const double R = has_q ? block_sum_d(st.r, sh.red_d) : 0.0;
+  const uint32_t qb = has_q ? block_max_u(st.qbad, sh.red_u) : 0u;
+  int fault = 0;
+  if (!(Z > 0.0) || isinf(Z)) fault |= kFaultTargetRow;
+  if (has_q && qb >= 0x7f800000u) fault |= kFaultDraftRow;
+
+  float cut_p = -INFINITY, cut_q = -INFINITY;
+  double Zk = Z, Rk = R;
+  int nlist = -1;
+  if (!fault && filt) {
+    if (cand && lane == 0) {
+      sh.ps[wave] = st.ps;
+      sh.qs[wave] = st.qs;
+    }
+    __syncthreads();
+    // target
+    bool done = false;
+    if (cand) {
+      KeptArgs ka;
+      ka.row = lrow;
+      ka.V = V;
+      ka.bf16 = sizeof(ET) == 2;
+      ka.draft = false;
+      ka.m = m;
+      ka.c = c;
+      ka.T = T;
+      ka.k = rq.k;
+      ka.top_p = rq.p;
+      ka.pact = rq.pact;
+      const Kept kp = kept_from_chunks(ka, (LDS_AS ChunkBuf*)sh.pb, (LDS_AS ChunkState*)sh.ps, (LDS_AS float*)sh.lval,
+                                       (LDS_AS int*)sh.lid, (LDS_AS double*)sh.lmass, (LDS_AS double*)sh.red_d,
+                                       (LDS_AS float*)sh.red_f, (LDS_AS int*)sh.misc);
+      if (kp.ok) {
+        done = true;
+        cut_p = kp.cut;
+        Zk = kp.mass;
+        nlist = kp.n;
+        ListEntry* L = a.lists + row * kLcap;
+        for (int t = tid; t < kp.n; t += kBlock) {
+          ListEntry e;
+          e.id = sh.lid[t];
+          e.val = sh.lval[t];
+          e.e = sh.lmass[t];
+          publish(L + t, e);
+        }
+      }
+      __syncthreads();
+    }
+    if (!done) {
+      GeneralArgs g;
+      g.row = lrow;
+      g.V = V;
+      g.bf16 = sizeof(ET) == 2;
+      g.draft = false;
+      g.m = m;
+      g.c = c;
+      g.invT = invT;
+      g.temper = temper;
+      g.k = rq.k;
+      g.kact = rq.kact;
+      g.top_p = rq.p;
+      g.pact = rq.pact;
+      g.total = Z;
+      const Filtered f = general_filter(g, (LDS_AS double*)sh.lmass, (LDS_AS double*)sh.sel_d,
+                                        (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d);
+      cut_p = f.cut;
+      Zk = f.mass;
+    }
+    // draft
+    if (has_q) {
+      bool qdone = false;
+      if (cand) {
+        KeptArgs ka;
+        ka.row = qrow;
+        ka.V = V;
+        ka.bf16 = false;
+        ka.draft = true;
+        ka.m = m;
+        ka.c = c;
+        ka.T = T;
+        ka.k = rq.k;
+        ka.top_p = rq.p;
+        ka.pact = rq.pact;
+        const Kept kq = kept_from_chunks(ka, (LDS_AS ChunkBuf*)sh.qb, (LDS_AS ChunkState*)sh.qs,
+                                         (LDS_AS float*)sh.lval, (LDS_AS int*)sh.lid, (LDS_AS double*)sh.lmass,
+                                         (LDS_AS double*)sh.red_d, (LDS_AS float*)sh.red_f, (LDS_AS int*)sh.misc);
+        if (kq.ok) {
+          qdone = true;
+          cut_q = kq.cut;
+          Rk = kq.mass;
+        }
+        __syncthreads();
+      }
+      if (!qdone) {
+        GeneralArgs g;
+        g.row = qrow;
+        g.V = V;
+        g.bf16 = false;
+        g.draft = true;
+        g.m = m;
+        g.c = c;
+        g.invT = invT;
+        g.temper = temper;
+        g.k = rq.k;
+        g.kact = rq.kact;
+        g.top_p = rq.p;
+        g.pact = rq.pact;
+        g.total = R;
+        const Filtered f = general_filter(g, (LDS_AS double*)sh.lmass, (LDS_AS double*)sh.sel_d,
+                                          (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d);
+        cut_q = f.cut;
+        Rk = f.mass;
+      }
+    }
+  }
+  if (!fault && has_q && !(Rk > 0.0)) fault |= kFaultDraftMass;
+
+  if (tid == 0) {
+    RowStats s;
+    s.m = m;
+    s.cut_p = cut_p;
+    s.cut_q = cut_q;
+    s.argmax = -1;
+    s.z = Zk;
+    s.r = Rk;
+    s.p_y = NAN;
+    s.q_y = NAN;
+    int acc = 0;
+    if (draft_pos && !fault) {
+      const int y = a.ids[(size_t)i * G + j];
+      const float ly = LT::at(lrow, (size_t)y);
+      const double e = (ly >= cut_p) ? mass_p(ly, m, c) : 0.0;
+      const double py = e / Zk;
+      double qy = 1.0;
+      if (a.q != nullptr) {
+        const float qv = qrow[y];
+        qy = (qv >= cut_q) ? temper_q(qv, T) / Rk : 0.0;
+      }
+      const double u = (double)a.u_accept[(size_t)i * G + j];
+      acc = (u * qy < py) ? 1 : 0;
+      s.p_y = py;
+      s.q_y = qy;
+    }
+    s.flags = acc | (fault << 8);
+    s.nlist = nlist;
+    s.pad[0] = s.pad[1] = 0;
+    publish(a.stats + row, s);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// kernels
+// ------------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void clear_kernel(unsigned int* done, int N) {
+  const int i = blockIdx.x * kBlock + threadIdx.x;
+  if (i < N) done[i] = 0u;
+}
+
+template <class LT, bool VEC>
+__global__ __launch_bounds__(kBlock, 3) void row_kernel(Args a) {
+  __shared__ KernelShared sh;
+  __shared__ int s_last;
+  const int G1 = a.G + 1;
+  const int i = blockIdx.x / G1, j = blockIdx.x - i * G1;
+  const Req rq = load_req(a, i);
+  if (!rq.fault && j <= rq.gamma) {
+    if (rq.greedy) greedy_row<LT, VEC>(a, rq, i, j, sh.row);
+    else stochastic_row<LT, VEC>(a, rq, i, j, sh.row);
+  }
+  // completion: every thread's published stores have completed before the
+  // barrier; the workgroup that brings the request's counter to G + 1 runs
+  // the finish
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned int prev = __hip_atomic_fetch_add(&a.done[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == (unsigned int)a.G);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // the kernel's only explicit argument sits at the start of its argument
+  // segment: the finish reads it from there instead of a private copy
+  finish_request<LT, VEC>((const CONST_AS Args*)__builtin_amdgcn_kernarg_segment_ptr(), i,
+                          (LDS_AS FinShared*)&sh.fin);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1198,6 +1587,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t stats_bytes(int N, int G) { return align_up((size_t)N * (G + 1) * sizeof(RowStats), 256); }
 size_t list_bytes(int N, int G) { return align_up((size_t)N * (G + 1) * kLcap * sizeof(ListEntry), 256); }
+size_t done_bytes(int N) { return align_up((size_t)N * sizeof(unsigned int), 256); }
 
 struct DeviceBuffer {
   void* ptr = nullptr;
@@ -1206,23 +1596,33 @@ struct DeviceBuffer {
 std::mutex g_ws_mutex;
 std::vector<DeviceBuffer> g_ws;  // one per device, grown on demand, kept until exit
 
+struct Events {
+  hipEvent_t start, mid, end;
+};
+
 template <class LT, bool VEC>
-hipError_t launch(const Args& a, hipStream_t stream) {
+hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
   const long rows = (long)a.N * (a.G + 1);
+  hipError_t e;
+  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((a.N + kBlock - 1) / kBlock)), dim3(kBlock), 0, stream, a.done,
+                     a.N);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((row_kernel<LT, VEC>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((finish_kernel<LT, VEC>), dim3((unsigned)a.N), dim3(kBlock), 0, stream, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev.mid && (e = hipEventRecord(ev.mid, stream)) != hipSuccess) return e;
+  if (ev.end && (e = hipEventRecord(ev.end, stream)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 int run(int N, int G, int V, const int32_t* ids, const float* q, const void* logits, int dtype,
         const float* temperature, const int32_t* top_k, const float* top_p, const float* u_accept,
         const float* u_sample, int32_t* out_tokens, int32_t* out_num, double* p_y, double* q_y, double* resid,
-        int32_t* fault, void* workspace, size_t workspace_bytes, void* stream) {
+        int32_t* fault, void* workspace, size_t workspace_bytes, void* stream, const Events& ev) {
   if (N < 0 || G < 0 || G > kMaxGamma || V < 1) return SPEC_VERIFY_ERR_SHAPE;
   if (dtype != SPEC_VERIFY_F32 && dtype != SPEC_VERIFY_BF16) return SPEC_VERIFY_ERR_DTYPE;
-  if ((long long)N * (G + 1) > 0x7fffffffLL || (long long)V * (G + 1) > (1LL << 40)) return SPEC_VERIFY_ERR_SHAPE;
+  if ((long long)N * (G + 1) > 0x7fffffffLL || (long long)V * (G + 1) > (1LL << 40) || V > 0x7fffffff - 2 * kStep)
+    return SPEC_VERIFY_ERR_SHAPE;
   if (N == 0) return SPEC_VERIFY_OK;
   if (!logits || !u_sample || !out_tokens || !out_num) return SPEC_VERIFY_ERR_NULL;
   if (G > 0 && (!ids || !u_accept)) return SPEC_VERIFY_ERR_NULL;
@@ -1235,7 +1635,7 @@ int run(int N, int G, int V, const int32_t* ids, const float* q, const void* log
     DeviceBuffer& b = g_ws[dev];
     if (b.bytes < need) {
       void* p = nullptr;
-      // the previous buffer may still be in use by queued work: keep it alive
+      // a smaller earlier buffer may still be read by queued work: it is kept
       if (hipMalloc(&p, need) != hipSuccess) return SPEC_VERIFY_ERR_HIP;
       b.ptr = p;
       b.bytes = need;
@@ -1263,8 +1663,10 @@ int run(int N, int G, int V, const int32_t* ids, const float* q, const void* log
   a.d_qy = q_y;
   a.d_resid = resid;
   a.d_fault = fault;
-  a.stats = reinterpret_cast<RowStats*>(workspace);
-  a.lists = reinterpret_cast<ListEntry*>(reinterpret_cast<char*>(workspace) + stats_bytes(N, G));
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.stats = reinterpret_cast<RowStats*>(ws);
+  a.lists = reinterpret_cast<ListEntry*>(ws + stats_bytes(N, G));
+  a.done = reinterpret_cast<unsigned int*>(ws + stats_bytes(N, G) + list_bytes(N, G));
 
   // 16-byte vector loads need every row start aligned: V a multiple of 8 and
   // 16-byte aligned base pointers
@@ -1272,9 +1674,9 @@ int run(int N, int G, int V, const int32_t* ids, const float* q, const void* log
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == SPEC_VERIFY_BF16)
-    e = vec ? launch<Bf16, true>(a, s) : launch<Bf16, false>(a, s);
+    e = vec ? launch<Bf16, true>(a, s, ev) : launch<Bf16, false>(a, s, ev);
   else
-    e = vec ? launch<F32, true>(a, s) : launch<F32, false>(a, s);
+    e = vec ? launch<F32, true>(a, s, ev) : launch<F32, false>(a, s, ev);
   return e == hipSuccess ? SPEC_VERIFY_OK : SPEC_VERIFY_ERR_HIP;
 }
 
@@ -1285,7 +1687,7 @@ extern "C" {
 size_t spec_verify_workspace_size(int N, int gmax, int V) {
   (void)V;
   if (N <= 0 || gmax < 0) return 256;
-  return stats_bytes(N, gmax) + list_bytes(N, gmax);
+  return stats_bytes(N, gmax) + list_bytes(N, gmax) + done_bytes(N);
 }
 
 int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* draft_probs, const void* target_logits,
@@ -1294,7 +1696,7 @@ int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* d
                 void* workspace, size_t workspace_bytes, void* stream) {
   return run(N, gmax, V, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes,
-             stream);
+             stream, Events{nullptr, nullptr, nullptr});
 }
 
 int spec_verify_diag(int N, int gmax, int V, const int32_t* draft_ids, const float* draft_probs,
@@ -1303,7 +1705,20 @@ int spec_verify_diag(int N, int gmax, int V, const int32_t* draft_ids, const flo
                      int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
                      void* workspace, size_t workspace_bytes, void* stream) {
   return run(N, gmax, V, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
-             u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream);
+             u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
+             Events{nullptr, nullptr, nullptr});
+}
+
+int spec_verify_timed(int N, int gmax, int V, const int32_t* draft_ids, const float* draft_probs,
+                      const void* target_logits, int logits_dtype, const float* temperature, const int32_t* top_k,
+                      const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
+                      int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
+                      void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_mid,
+                      void* ev_end) {
+  return run(N, gmax, V, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+             u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
+             Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
+                    reinterpret_cast<hipEvent_t>(ev_end)});
 }
 
 const char* spec_verify_status_string(int status) {

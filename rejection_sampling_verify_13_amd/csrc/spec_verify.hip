@@ -11,8 +11,9 @@
 //
 // Work per call, all on the caller's stream:
 //   clear_kernel  zeroes one completion counter per request.
-//   row_kernel    one 256-thread workgroup per (request, position) row, grid in
-//                 request-major order.  It streams the target-logit row and, at
+//   row_kernel    one 256-thread workgroup per (request, position) row: first
+//                 the draft positions in request-major order, then the bonus
+//                 positions.  It streams the target-logit row and, at
 //                 draft positions of sampled requests, the draft-probability
 //                 row once (16-byte nontemporal loads, the next step's loads in
 //                 flight while the current step is reduced) and computes: row
@@ -54,11 +55,11 @@ constexpr int kBlock = 256;             // threads per workgroup (4 waves)
 constexpr int kWaves = kBlock / 64;
 constexpr int kCh = 8;                  // tokens per thread per step
 constexpr int kStep = kBlock * kCh;     // tokens per workgroup step (2048)
-constexpr int kCap = 256;               // buffered chunks per wave and distribution
-constexpr int kKFast = 64;              // largest top_k served by the chunk buffers
-constexpr int kListMax = 512;           // merged candidate tokens (LDS)
-constexpr int kSegMax = kListMax / kWaves;
-constexpr int kLcap = kListMax;         // kept-list entries stored per row
+constexpr int kCap = 160;               // buffered candidate chunks per wave and distribution
+constexpr int kKFast = 64;              // largest top_k served by the candidate buffers
+constexpr int kSeg = 128;               // gathered candidate tokens per wave and distribution (LDS)
+constexpr int kMerge = kWaves * kSeg;   // gathered candidate tokens of one distribution
+constexpr int kLcap = kMerge;           // kept-list entries stored per row
 constexpr int kMaxChunks = 512;         // chunk sums held by the draw
 constexpr int kMaxGamma = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -283,8 +284,31 @@ __device__ inline T fetch(const T* src) {
 // ------------------------------------------------------------------------------------------
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
-__device__ inline uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
-__device__ inline int mbcnt(uint64_t m) { return __popcll(m & lanemask_lt()); }
+// Wave-uniform copies (s_readfirstlane): values that are the same in every
+// lane but reach a function through VGPR arguments or LDS, so that the
+// compiler keeps them in scalar registers and branches on them with scalar
+// branches instead of exec masks.
+__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline uint32_t uni(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ inline float uni(float x) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x))); }
+__device__ inline double uni(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+template <class T>
+__device__ inline T* uni(T* p) {
+  const uint64_t b = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
+// set bits of m below this lane (v_mbcnt: no mask register kept live)
+__device__ inline int mbcnt(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
 __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -321,6 +345,38 @@ __device__ inline int wave_or_i(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o);
   return v;
+}
+
+// Unsigned max / min over a full wave with DPP lane moves (no LDS round
+// trips): butterflies inside each row of 16 lanes, then the row broadcasts;
+// lane 63 ends with the result.
+template <int CTRL, int ROWS>
+__device__ inline uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
+}
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_mov<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_mov<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_mov<0x141, 0xF>(v));  // row_half_mirror
+  v = max(v, dpp_mov<0x140, 0xF>(v));  // row_mirror
+  v = max(v, dpp_mov<0x142, 0xA>(v));  // row_bcast:15
+  v = max(v, dpp_mov<0x143, 0xC>(v));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_mov<0xB1, 0xF>(v));
+  v = min(v, dpp_mov<0x4E, 0xF>(v));
+  v = min(v, dpp_mov<0x141, 0xF>(v));
+  v = min(v, dpp_mov<0x140, 0xF>(v));
+  v = min(v, dpp_mov<0x142, 0xA>(v));
+  v = min(v, dpp_mov<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ inline double readlane_d(double v, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // Block reductions: wave butterflies, then the four wave results combined in a
@@ -422,83 +478,123 @@ __device__ inline Req load_req(const Args& a, int i) {
 }
 
 // ------------------------------------------------------------------------------------------
-// chunk buffers for top-k (rising threshold, whole 8-token chunks)
+// candidate chunk buffers for top-k (rising threshold)
 // ------------------------------------------------------------------------------------------
 
-// A buffered chunk is 8 consecutive tokens of one lane: the order key of its
-// largest value and its first token id.  Values are re-read from the row only
-// for the few chunks that survive to the end of the pass.
+// Candidate chunks of one wave for one distribution.  A chunk is the 8
+// consecutive tokens one lane holds in one step: its largest order key, its
+// first token id and its raw values (R: the step's raw load), so that the
+// kept set is later found from LDS alone.  A chunk is appended when its key
+// reaches the wave's threshold; when the buffer fills, the threshold is raised
+// to the k-th largest buffered key and the buffer compacted.  The threshold
+// never exceeds the k-th largest value among the tokens the wave has seen, so
+// after the pass the buffer holds every one of the wave's tokens at or above
+// the row's k-th largest value.
+template <class R>
 struct ChunkBuf {
   uint32_t key[kCap];
   int base[kCap];
+  R val[kCap];
 };
 
 // Wave-uniform state of one buffer.
 struct ChunkState {
   int cnt;
-  uint32_t thr;   // order key; chunks whose maximum key is below it are not buffered
-  bool ovf;
+  uint32_t thr;   // chunks whose key is below it are not buffered
+  int ovf;        // ties kept the buffer too full: the radix select decides
 };
 
-// Key of the k-th largest of the buffered chunk maxima (1 <= k <= cnt).
-__device__ inline uint32_t wave_kth_chunk_key(const LDS_AS ChunkBuf* b, int cnt, int k) {
-  const int lane = lane_id();
-  uint32_t key[kCap / 64];
-#pragma unroll
-  for (int t = 0; t < kCap / 64; ++t) key[t] = lane + 64 * t < cnt ? b->key[lane + 64 * t] : 0u;
-  uint32_t P = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t T = P | (1u << bit);
-    int c = 0;
-#pragma unroll
-    for (int t = 0; t < kCap / 64; ++t) c += __popcll(__ballot(key[t] >= T));
-    if (c >= k) P = T;
-  }
-  return P;
-}
+constexpr int kCapLane = (kCap + 63) / 64;
+constexpr int kSlack = 16;             // refresh stops once at most k + kSlack chunks stay
 
-// Raise the threshold to the k-th largest buffered chunk maximum and keep only
-// the chunks at or above it (their count is >= k, ties included).  Plain
-// values in and out, so callers keep their state in registers.
-__device__ __noinline__ ChunkState chunk_refresh(LDS_AS ChunkBuf* b, ChunkState s, int k) {
+// member-wise copies of raw steps to and from LDS
+__device__ inline void raw_put(LDS_AS Bf16::Raw* d, const Bf16::Raw& r) { d->a = r.a; }
+__device__ inline void raw_put(LDS_AS F32::Raw* d, const F32::Raw& r) { d->a = r.a; d->b = r.b; }
+__device__ inline void raw_get(const LDS_AS Bf16::Raw* s, Bf16::Raw& r) { r.a = s->a; }
+__device__ inline void raw_get(const LDS_AS F32::Raw* s, F32::Raw& r) { r.a = s->a; r.b = s->b; }
+
+// Raise the threshold and keep only the chunks at or above it.  The new
+// threshold T has at least k buffered chunk keys >= T (so it does not exceed
+// the k-th largest chunk key, a lower bound of the wave's k-th largest value)
+// and, unless ties prevent it, at most k + kSlack: bisection on the key bits
+// below the common prefix of the smallest and largest key, stopping as soon
+// as the count is within that band.  Plain values in and out, so callers keep
+// their state in registers.
+template <class R>
+__device__ __noinline__ ChunkState chunk_refresh(LDS_AS ChunkBuf<R>* b, ChunkState s, int k) {
   const int lane = lane_id();
-  const uint32_t thr = wave_kth_chunk_key(b, s.cnt, k);
-  uint32_t key[kCap / 64];
-  int base[kCap / 64];
+  s.cnt = uni(s.cnt);
+  s.ovf = uni(s.ovf);
+  k = uni(k);
+  uint32_t key[kCapLane];
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
 #pragma unroll
-  for (int t = 0; t < kCap / 64; ++t) {
+  for (int t = 0; t < kCapLane; ++t) {
     const bool h = lane + 64 * t < s.cnt;
     key[t] = h ? b->key[lane + 64 * t] : 0u;
-    base[t] = h ? b->base[lane + 64 * t] : 0;
+    if (h) {
+      kmax = max(kmax, key[t]);
+      kmin = min(kmin, key[t]);
+    }
   }
-  wave_lds_sync();
-  int n = 0;
+  kmax = wave_max_u32(kmax);
+  kmin = wave_min_u32(kmin);
+  uint32_t thr = kmin;
+  if (kmin != kmax) {
+    const int top = 31 - __clz((int)(kmin ^ kmax));
+    thr = kmin & ~((2u << top) - 1u);
+    for (int bit = top; bit >= 0; --bit) {
+      const uint32_t T = thr | (1u << bit);
+      int c = 0;
 #pragma unroll
-  for (int t = 0; t < kCap / 64; ++t) {
-    const bool keep = lane + 64 * t < s.cnt && key[t] >= thr;
+      for (int t = 0; t < kCapLane; ++t) c += __popcll(__ballot(key[t] >= T));
+      if (c >= k) {
+        thr = T;
+        if (c <= k + kSlack) break;
+      }
+    }
+  }
+  int n = 0;
+  // compaction in slot order: an entry only moves to a lower slot, and slot
+  // group t is read completely before any of it is overwritten
+#pragma unroll
+  for (int t = 0; t < kCapLane; ++t) {
+    const int e = lane + 64 * t;
+    const bool h = e < s.cnt;
+    const int base = h ? b->base[e] : 0;
+    R val{};
+    if (h) raw_get(&b->val[e], val);
+    wave_lds_sync();
+    const bool keep = h && key[t] >= thr;
     const uint64_t m = __ballot(keep);
     if (keep) {
       const int p = n + mbcnt(m);
       b->key[p] = key[t];
-      b->base[p] = base[t];
+      b->base[p] = base;
+      raw_put(&b->val[p], val);
     }
     n += __popcll(m);
+    wave_lds_sync();
   }
-  wave_lds_sync();
   s.cnt = n;
   s.thr = thr;
-  if (s.cnt > kCap - 64) s.ovf = true;
+  if (s.cnt > kCap - 64) s.ovf = 1;
   return s;
 }
 
-// Offer this lane's chunk (maximum key `key`, first token `base`).
-__device__ inline void chunk_offer(LDS_AS ChunkBuf* b, ChunkState& s, int k, bool valid, uint32_t key, int base) {
+// Offer this lane's chunk (largest key `key`, first token `base`, raw values).
+template <class R>
+__device__ inline void chunk_offer(LDS_AS ChunkBuf<R>* b, ChunkState& s, int k, bool valid, uint32_t key, int base,
+                                   const R& raw) {
   bool ins = valid && key >= s.thr;
   uint64_t m = __ballot(ins);
   if (!m || s.ovf) return;
   int n = __popcll(m);
   if (s.cnt + n > kCap) {
     s = chunk_refresh(b, s, k);
+    s.cnt = uni(s.cnt);
+    s.thr = uni(s.thr);
+    s.ovf = uni(s.ovf);
     if (s.ovf) return;
     ins = valid && key >= s.thr;
     m = __ballot(ins);
@@ -508,6 +604,7 @@ __device__ inline void chunk_offer(LDS_AS ChunkBuf* b, ChunkState& s, int k, boo
     const int p = s.cnt + mbcnt(m);
     b->key[p] = key;
     b->base[p] = base;
+    raw_put(&b->val[p], raw);
   }
   s.cnt += n;
 }
@@ -613,20 +710,37 @@ __device__ double block_sum_above(KW kw, int V, uint32_t lo, double* red) {
 // shared memory
 // ------------------------------------------------------------------------------------------
 
+// Result of one distribution's top-k / top-p filter.
+struct MergeOut {
+  double mass;    // kept mass (target: sum of 2^((l - m) * c); draft: sum of q^(1/T))
+  float cut;      // keep iff value >= cut
+  int n;          // target: kept-list entries stored
+  int ok;         // 0: the buffers cannot decide (ties); the radix select does
+  int pad;
+};
+
+template <class LT>
 struct RowShared {
-  ChunkBuf pb[kWaves];
-  ChunkBuf qb[kWaves];
-  float lval[kListMax];
-  int lid[kListMax];
-  double lmass[kListMax];
+  // target and draft chunk buffers; once the gather has read them they hold
+  // the fp64 weights of the tie path and the radix-select histogram
+  ChunkBuf<typename LT::Raw> pb[kWaves];
+  ChunkBuf<F32::Raw> qb[kWaves];
+  uint32_t skey[2][kWaves * kSeg];   // gathered tokens, one segment per wave
+  int sid[2][kWaves * kSeg];
+  int scnt[2][kWaves];
   ChunkState ps[kWaves], qs[kWaves];
+  float xm[kWaves];
+  uint32_t xqb[kWaves];
+  uint32_t xlb[kWaves];
+  double xr[kWaves];
+  double xz[kWaves];
+  MergeOut mo[2];
   double red_d[kWaves];
   float red_f[kWaves];
   uint32_t red_u[kWaves];
   int red_i[kWaves];
   double sel_d[2];
   uint32_t sel_u[2];
-  int misc[8];
 };
 
 struct FinShared {
@@ -639,193 +753,255 @@ struct FinShared {
   double miscd[4];
 };
 
+template <class LT>
 union KernelShared {
-  RowShared row;
+  RowShared<LT> row;
   FinShared fin;
 };
 
 // ------------------------------------------------------------------------------------------
-// kept set from the chunk buffers
+// kept set from the candidate buffers (one wave per distribution)
 // ------------------------------------------------------------------------------------------
 
-struct Kept {
-  float cut;      // keep iff value >= cut
-  double mass;    // kept mass
-  int n;          // list entries (values >= the k-th largest)
-  bool ok;        // false: capacity exceeded, use the radix select
-};
-
-// After the stream: each wave prunes its buffer to its k-th largest chunk
-// maximum; every token of the buffered chunks at or above the best wave
-// threshold L (a lower bound of the true k-th largest value) is re-read from
-// the row into the LDS list; the exact k-th largest value is found there, the
-// tokens at or above it are weighed in fp64 (target: 2^((l - m) * c); draft:
-// q^(1/T)) and top-p is applied over whole tie groups.  `row` is the target
-// row (bf16 or fp32 per `bf16`) or the draft row (fp32); VEC rows are 16-byte
-// aligned with V a multiple of 8.
-struct KeptArgs {
-  const void* row;
-  int V;
-  bool bf16;      // row holds bfloat16 (else fp32)
-  bool draft;     // weights q^(1/T) (else 2^((l - m) * c))
-  float m, c, T;
+struct MergeIn {
   int k;
   float top_p;
-  bool pact;
+  int pact;
+  int draft;          // weights q^(1/T) (else 2^((l - m) * c))
+  float m, c, T;
+  ListEntry* list;    // the kept list is stored here (NULL: not stored)
 };
 
-__device__ inline float row_value(const KeptArgs& ka, int x) {
-  return ka.bf16 ? Bf16::at(reinterpret_cast<const uint16_t*>(ka.row), (size_t)x)
-                 : F32::at(reinterpret_cast<const float*>(ka.row), (size_t)x);
+__device__ inline double merge_weight(const MergeIn& in, float v) {
+  return in.draft ? temper_q(v, in.T) : mass_p(v, in.m, in.c);
 }
 
-__device__ __noinline__ Kept kept_from_chunks(KeptArgs ka, LDS_AS ChunkBuf* bufs, LDS_AS ChunkState* states,
-                                              LDS_AS float* lval, LDS_AS int* lid, LDS_AS double* lmass,
-                                              LDS_AS double* red_d, LDS_AS float* red_f, LDS_AS int* misc) {
-  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  const int k = ka.k;
-  Kept out;
-  LDS_AS ChunkBuf* b = bufs + w;
-  ChunkState s;
-  s.cnt = states[w].cnt;
-  s.thr = states[w].thr;
-  s.ovf = states[w].ovf;
-  if (s.cnt > k && !s.ovf) {
-    s = chunk_refresh(b, s, k);
-    s.ovf = false;  // no insertion follows: a full buffer is fine here
-  }
-  __syncthreads();
-  if (lane == 0) {
-    states[w].cnt = s.cnt;
-    states[w].thr = s.thr;
-    states[w].ovf = s.ovf;
-  }
-  __syncthreads();
-  bool ovf = false;
-  uint32_t L = 0u;
-  for (int v = 0; v < kWaves; ++v) {
-    ovf |= states[v].ovf;
-    L = max(L, states[v].thr);
-  }
-  if (ovf) {
-    out.ok = false;
-    return out;
-  }
-  const float Lf = okey_value(L);
-  // wave w re-reads the tokens of its chunks whose maximum reaches L
+__device__ inline void unpack_raw(const Bf16::Raw& r, float v[8]) { Bf16::unpack(r, v); }
+__device__ inline void unpack_raw(const F32::Raw& r, float v[8]) { F32::unpack(r, v); }
+
+// One wave copies the tokens of its own buffered chunks whose key reaches L
+// (tokens past the row end excluded) into its segment; returns their count
+// (more than kSeg: the segment overflowed).
+template <class R>
+__device__ inline int gather_tokens(const LDS_AS ChunkBuf<R>* b, int cnt, uint32_t L, int V, LDS_AS uint32_t* skey,
+                                    LDS_AS int* sid) {
+  const int lane = lane_id();
+  cnt = uni(cnt);
+  L = uni(L);
   int n = 0;
-  bool fits = true;
-  for (int e0 = 0; e0 < s.cnt; e0 += 64) {
+  for (int e0 = 0; e0 < cnt; e0 += 64) {
     const int e = e0 + lane;
-    const bool mine = e < s.cnt && b->key[e] >= L;
-    const int cb = mine ? b->base[e] : 0;
+    const bool h = e < cnt && b->key[e] >= L;
     float v[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = (mine && cb + t < ka.V) ? row_value(ka, cb + t) : -INFINITY;
+    int base = 0;
+    if (h) {
+      R raw;
+      raw_get(&b->val[e], raw);
+      unpack_raw(raw, v);
+      base = b->base[e];
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const bool take = mine && cb + t < ka.V && v[t] >= Lf;
-      const uint64_t m = __ballot(take);
-      if (n + __popcll(m) > kSegMax) fits = false;
-      if (take && fits) {
-        const int p = w * kSegMax + n + mbcnt(m);
-        lval[p] = v[t];
-        lid[p] = cb + t;
+      const uint32_t key = h ? okey(v[t]) : 0u;
+      const bool take = h && base + t < V && key >= L;
+      const uint64_t mb = __ballot(take);
+      const int p = n + mbcnt(mb);
+      if (take && p < kSeg) {
+        skey[p] = key;
+        sid[p] = base + t;
       }
-      n += __popcll(m);
+      n += __popcll(mb);
     }
   }
-  if (lane == 0) misc[w] = fits ? n : -1;
-  __syncthreads();
-  int off[kWaves + 1];
-  off[0] = 0;
-  bool ok = true;
-  for (int v = 0; v < kWaves; ++v) {
-    ok &= misc[v] >= 0;
-    off[v + 1] = off[v] + (misc[v] >= 0 ? misc[v] : 0);
+  return n;
+}
+
+// The gathered segments hold every token of the row whose key reaches L = the
+// largest wave threshold, a lower bound of the row's k-th largest key, so the
+// exact k-th largest key K is found among them by bisection (below the common
+// prefix of their smallest and largest key; bf16 keys end in 16 equal bits).
+// The tokens at or above K are weighed in fp64 and top-p keeps the smallest
+// run of whole tie groups, largest values first, whose mass reaches top_p of
+// the top-k mass.  Run by a single wave; `mmass` is scratch for the case of
+// more than 64 tokens tied at or above K.
+template <bool BF16KEYS>
+__device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, LDS_AS int* sid, const LDS_AS int* scnt,
+                                            LDS_AS double* mmass) {
+  const int lane = lane_id();
+  in.k = uni(in.k);
+  in.pact = uni(in.pact);
+  in.draft = uni(in.draft);
+  in.top_p = uni(in.top_p);
+  in.m = uni(in.m);
+  in.c = uni(in.c);
+  in.T = uni(in.T);
+  MergeOut out;
+  out.ok = 0;
+  out.n = 0;
+  out.cut = -INFINITY;
+  out.mass = 0.0;
+  out.pad = 0;
+  int segn[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    segn[w] = uni(scnt[w]);
+    if (segn[w] > kSeg) return out;
   }
-  if (!ok) {
-    __syncthreads();
-    out.ok = false;
-    return out;
-  }
-  // make the list contiguous (all reads before any write)
-  const int my = misc[w];
-  float tv0 = 0.f, tv1 = 0.f;
-  int ti0 = 0, ti1 = 0;
-  if (lane < my) { tv0 = lval[w * kSegMax + lane]; ti0 = lid[w * kSegMax + lane]; }
-  if (lane + 64 < my) { tv1 = lval[w * kSegMax + lane + 64]; ti1 = lid[w * kSegMax + lane + 64]; }
-  __syncthreads();
-  if (lane < my) { lval[off[w] + lane] = tv0; lid[off[w] + lane] = ti0; }
-  if (lane + 64 < my) { lval[off[w] + lane + 64] = tv1; lid[off[w] + lane + 64] = ti1; }
-  __syncthreads();
-  const int total = off[kWaves];
-  // exact k-th largest value of the list (which holds every value at or above it)
-  float kth = -INFINITY;
-  for (int t = tid; t < total; t += kBlock) {
-    const float v = lval[t];
-    int gt = 0, ge = 0;
-    for (int u = 0; u < total; ++u) {
-      gt += lval[u] > v;
-      ge += lval[u] >= v;
+  constexpr int G = kSeg / 64;
+  uint32_t kk[kWaves * G];
+  int ii[kWaves * G];
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int e = 64 * g + lane;
+      const bool h = e < segn[w];
+      kk[w * G + g] = h ? skey[w * kSeg + e] : 0u;
+      ii[w * G + g] = h ? sid[w * kSeg + e] : 0;
+      if (h) {
+        kmax = max(kmax, kk[w * G + g]);
+        kmin = min(kmin, kk[w * G + g]);
+      }
     }
-    if (gt < k && k <= ge) kth = v;
+  kmax = wave_max_u32(kmax);
+  kmin = wave_min_u32(kmin);
+  auto count_ge = [&](uint32_t T) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        if (64 * g < segn[w]) c += __popcll(__ballot(kk[w * G + g] >= T));
+    return c;
+  };
+  // exact k-th largest key (the gathered set holds the whole top-k set)
+  uint32_t K = kmin;
+  if (kmin != kmax) {
+    const int top = 31 - __clz((int)(kmin ^ kmax));
+    K = kmin & ~((2u << top) - 1u);
+    for (int bit = top; bit >= (BF16KEYS ? 16 : 0); --bit) {
+      const uint32_t T = K | (1u << bit);
+      if (count_ge(T) >= in.k) K = T;
+    }
+    if (BF16KEYS && count_ge(K | 0xffffu) >= in.k) K |= 0xffffu;
   }
-  kth = block_max_f(kth, (float*)red_f);
-  // tokens at or above the k-th largest, in list order
+  // the top-k set, compacted to the front of the segment area
+  wave_lds_sync();
   int nk = 0;
-  if (tid < 64) {
-    for (int base = 0; base < total; base += 64) {
-      const int e = base + lane;
-      float v = 0.f;
-      int id = 0;
-      bool take = false;
-      if (e < total) {
-        v = lval[e];
-        id = lid[e];
-        take = v >= kth;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (64 * g < segn[w]) {
+        const bool take = 64 * g + lane < segn[w] && kk[w * G + g] >= K;
+        const uint64_t mb = __ballot(take);
+        if (take) {
+          skey[nk + mbcnt(mb)] = kk[w * G + g];
+          sid[nk + mbcnt(mb)] = ii[w * G + g];
+        }
+        nk += __popcll(mb);
       }
-      wave_lds_sync();
-      const uint64_t m = __ballot(take);
-      if (take) {
-        lval[nk + mbcnt(m)] = v;
-        lid[nk + mbcnt(m)] = id;
-      }
-      nk += __popcll(m);
-      wave_lds_sync();
     }
-    if (lane == 0) misc[kWaves] = nk;
-  }
-  __syncthreads();
-  nk = misc[kWaves];
-  for (int t = tid; t < nk; t += kBlock) lmass[t] = ka.draft ? temper_q(lval[t], ka.T) : mass_p(lval[t], ka.m, ka.c);
-  __syncthreads();
-  double zk = 0.0;
-  for (int t = tid; t < nk; t += kBlock) zk += lmass[t];
-  zk = block_sum_d(zk, (double*)red_d);
-  float cut = kth;
-  if (ka.pact) {
-    const double target = (double)ka.top_p * zk;
-    float best = -INFINITY;
-    for (int t = tid; t < nk; t += kBlock) {
-      const float v = lval[t];
+  wave_lds_sync();
+  uint32_t cutkey = K;
+  if (nk <= 64) {
+    // one entry per lane
+    const bool h = lane < nk;
+    const uint32_t key = h ? skey[lane] : 0u;
+    const int id = h ? sid[lane] : -1;
+    const double e = h ? merge_weight(in, okey_value(key)) : 0.0;
+    const double zk = wave_sum_d(e);
+    double mass = zk;
+    bool keep = h;
+    if (in.pact) {
+      // cum = mass of the entries whose key is >= this lane's key
       double cum = 0.0;
-      for (int u = 0; u < nk; ++u) cum += (lval[u] >= v) ? lmass[u] : 0.0;
-      if (cum >= target) best = __builtin_fmaxf(best, v);
+      for (int u = 0; u < nk; ++u) {
+        const uint32_t ku = (uint32_t)__builtin_amdgcn_readlane((int)key, u);
+        const double eu = readlane_d(e, u);
+        cum += (ku >= key) ? eu : 0.0;
+      }
+      const double target = (double)in.top_p * zk;
+      const uint32_t best = wave_max_u32((h && cum >= target) ? key : 0u);
+      if (best != 0u) {  // else rounding kept the run below target: keep the whole top-k set
+        cutkey = best;
+        const uint64_t at = __ballot(h && key == best);
+        mass = readlane_d(cum, __ffsll((unsigned long long)at) - 1);
+        keep = h && key >= cutkey;
+      }
     }
-    best = block_max_f(best, (float*)red_f);
-    cut = (best == -INFINITY) ? kth : best;  // never reached by rounding: keep the whole top-k set
+    const uint64_t km = __ballot(keep);
+    if (in.list && keep) {
+      ListEntry le;
+      le.id = id;
+      le.val = okey_value(key);
+      le.e = e;
+      publish(in.list + mbcnt(km), le);
+    }
+    out.mass = mass;
+    out.n = __popcll(km);
+  } else {
+    // many values tied at the k-th largest: weights in LDS, quadratic top-p
+    double zp = 0.0;
+    for (int t = lane; t < nk; t += 64) {
+      const double e = merge_weight(in, okey_value(skey[t]));
+      mmass[t] = e;
+      zp += e;
+    }
+    const double zk = wave_sum_d(zp);
+    wave_lds_sync();
+    if (in.pact) {
+      const double target = (double)in.top_p * zk;
+      uint32_t best = 0u;
+      for (int t = lane; t < nk; t += 64) {
+        const uint32_t kt = skey[t];
+        double cum = 0.0;
+        for (int u = 0; u < nk; ++u) cum += (skey[u] >= kt) ? mmass[u] : 0.0;
+        if (cum >= target) best = max(best, kt);
+      }
+      best = wave_max_u32(best);
+      if (best != 0u) cutkey = best;
+    }
+    double zc = 0.0;
+    int n = 0;
+    for (int t0 = 0; t0 < nk; t0 += 64) {
+      const int t = t0 + lane;
+      const bool keep = t < nk && skey[t] >= cutkey;
+      const uint64_t mb = __ballot(keep);
+      if (keep) {
+        zc += mmass[t];
+        if (in.list) {
+          ListEntry le;
+          le.id = sid[t];
+          le.val = okey_value(skey[t]);
+          le.e = mmass[t];
+          publish(in.list + n + mbcnt(mb), le);
+        }
+      }
+      n += __popcll(mb);
+    }
+    out.mass = wave_sum_d(zc);
+    out.n = n;
   }
-  double zc = 0.0;
-  for (int t = tid; t < nk; t += kBlock) zc += (lval[t] >= cut) ? lmass[t] : 0.0;
-  out.mass = block_sum_d(zc, (double*)red_d);
-  out.cut = cut;
-  out.n = nk;
-  out.ok = true;
+  out.cut = okey_value(cutkey);
+  out.ok = 1;
   return out;
 }
 
-// Filters the chunk buffers do not serve: radix selects that re-read the row.
+// A row of target logits (bf16 or fp32) or draft probabilities (fp32).
+struct RowRef {
+  const void* row;
+  int V;
+  bool bf16;
+};
+
+__device__ inline float row_value(const RowRef& r, int x) {
+  return r.bf16 ? Bf16::at(reinterpret_cast<const uint16_t*>(r.row), (size_t)x)
+                : F32::at(reinterpret_cast<const float*>(r.row), (size_t)x);
+}
+
+// Filters the candidate buffers do not serve: radix selects that re-read the row.
 // Returns the cut value (-inf: keep all) and the kept mass in *mass.
 struct GeneralArgs {
   const void* row;
@@ -847,7 +1023,20 @@ struct Filtered {
 
 __device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hist, LDS_AS double* sel_d,
                                                 LDS_AS uint32_t* sel_u, LDS_AS double* red) {
-  KeptArgs ka;
+  g.row = uni(g.row);
+  g.V = uni(g.V);
+  g.bf16 = uni((int)g.bf16);
+  g.draft = uni((int)g.draft);
+  g.m = uni(g.m);
+  g.c = uni(g.c);
+  g.invT = uni(g.invT);
+  g.temper = uni((int)g.temper);
+  g.k = uni(g.k);
+  g.kact = uni((int)g.kact);
+  g.top_p = uni(g.top_p);
+  g.pact = uni((int)g.pact);
+  g.total = uni(g.total);
+  RowRef ka;
   ka.row = g.row;
   ka.V = g.V;
   ka.bf16 = g.bf16;
@@ -931,49 +1120,63 @@ struct StepRaw {
 
 struct StochState {
   float m;          // running max of this thread's logits
-  double z;         // sum of 2^((l - m) * c) over this thread's logits
-  double r;         // sum of q^(1/T)
+  double z;         // sum of 2^((l - m) * c) over this thread's logits (no top-k)
+  double r;         // sum of q^(1/T) (no top-k)
   uint32_t qbad;    // max raw bits of q (>= 0x7f800000: NaN, inf or sign bit)
+  uint32_t lbad;    // max bits of |l| (> 0x7f800000: NaN) (top-k)
   ChunkState ps, qs;
 };
 
 // QM: 0 no draft row, 1 draft row at T = 1, 2 draft row at T != 1.
 template <class LT, bool VEC, int QM, bool CAND>
 __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, const float* qrow, int V, float c, float invT, int k,
-                                  RowShared& sh, StochState& st) {
+                                  RowShared<LT>& sh, StochState& st) {
   typedef typename LT::Raw LR;
   const int tid = threadIdx.x, w = tid >> 6;
   const int nsteps = (V + kStep - 1) / kStep;
   auto process = [&](const LR& lr, const F32::Raw& qr, int base) {
-    const bool valid = base < V;
     float v[8];
     LT::unpack(lr, v);
     const float cm = max8(v);
-    if (cm > st.m) {
-      st.z *= (double)fast_exp2((st.m - cm) * c);
-      st.m = cm;
-    }
-    float e[8];
+    if (CAND) {
+      // with top-k the kept masses come from the candidates alone: only the
+      // max and a NaN check are needed from the full row
+      st.m = __builtin_fmaxf(st.m, cm);
+      uint32_t a[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) e[t] = fast_exp2((v[t] - st.m) * c);
-    st.z += (double)(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+      for (int t = 0; t < 8; ++t) a[t] = __float_as_uint(v[t]) & 0x7fffffffu;
+      st.lbad = max(st.lbad, max8u(a));
+    } else {
+      if (cm > st.m) {
+        st.z *= (double)fast_exp2((st.m - cm) * c);
+        st.m = cm;
+      }
+      float e[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) e[t] = fast_exp2((v[t] - st.m) * c);
+      st.z += (double)(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+    }
     uint32_t qmax = 0u;
     if (QM) {
       uint32_t u[8];
       F32::bits(qr, u);
       qmax = max8u(u);
       st.qbad = max(st.qbad, qmax);
-      float r[8];
+      if (!CAND) {
+        float r[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float qv = __uint_as_float(u[t]);
-        r[t] = (QM == 1) ? qv : fast_exp2(fast_log2(qv) * invT);
+        for (int t = 0; t < 8; ++t) {
+          const float qv = __uint_as_float(u[t]);
+          r[t] = (QM == 1) ? qv : fast_exp2(fast_log2(qv) * invT);
+        }
+        st.r += (double)(((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7])));
       }
-      st.r += (double)(((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7])));
     }
     if (CAND) {
-      chunk_offer((LDS_AS ChunkBuf*)&sh.pb[w], st.ps, k, valid, okey(cm), base);
-      if (QM) chunk_offer((LDS_AS ChunkBuf*)&sh.qb[w], st.qs, k, valid, qmax | 0x80000000u, base);  // okey of q >= 0
+      const bool valid = base < V;
+      chunk_offer((LDS_AS ChunkBuf<LR>*)&sh.pb[w], st.ps, k, valid, okey(cm), base, lr);
+      // okey of q >= 0 is its bits with the sign bit set
+      if (QM) chunk_offer((LDS_AS ChunkBuf<F32::Raw>*)&sh.qb[w], st.qs, k, valid, qmax | 0x80000000u, base, qr);
     }
   };
   // full steps (every lane's 8 tokens inside the row, vector loads only)
@@ -1061,6 +1264,26 @@ template <class LT, bool VEC>
 __device__ __noinline__ void finish_request(const CONST_AS Args* ap, int i, LDS_AS FinShared* sh) {
   Args a;
   __builtin_memcpy(&a, (const Args*)ap, sizeof(Args));
+  i = uni(i);
+  a.N = uni(a.N);
+  a.G = uni(a.G);
+  a.V = uni(a.V);
+  a.ids = uni(a.ids);
+  a.q = uni(a.q);
+  a.logits = uni(a.logits);
+  a.temperature = uni(a.temperature);
+  a.top_k = uni(a.top_k);
+  a.top_p = uni(a.top_p);
+  a.u_accept = uni(a.u_accept);
+  a.u_sample = uni(a.u_sample);
+  a.out_tokens = uni(a.out_tokens);
+  a.out_num = uni(a.out_num);
+  a.d_py = uni(a.d_py);
+  a.d_qy = uni(a.d_qy);
+  a.d_resid = uni(a.d_resid);
+  a.d_fault = uni(a.d_fault);
+  a.stats = uni(a.stats);
+  a.lists = uni(a.lists);
   typedef typename LT::T ET;
   typedef typename LT::Raw LR;
   const int G = a.G, V = a.V;
@@ -1312,7 +1535,7 @@ __device__ __noinline__ void finish_request(const CONST_AS Args* ap, int i, LDS_
 // ------------------------------------------------------------------------------------------
 
 template <class LT, bool VEC>
-__device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, int j, RowShared& sh) {
+__device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, int j, RowShared<LT>& sh) {
   typedef typename LT::T ET;
   const int G = a.G, V = a.V, tid = threadIdx.x;
   const size_t row = (size_t)i * (G + 1) + j;
@@ -1354,7 +1577,7 @@ __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, 
 }
 
 template <class LT, bool VEC>
-__device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int i, int j, RowShared& sh) {
+__device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int i, int j, RowShared<LT>& sh) {
   typedef typename LT::T ET;
   const int G = a.G, V = a.V;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -1370,77 +1593,140 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   const bool filt = rq.kact || rq.pact;
   const bool cand = rq.kact && rq.k <= kKFast;
 
+  // the draft token's logit and probability, loaded before the stream
+  int y = -1;
+  float ly = 0.f, qyv = 0.f;
+  if (tid == 0 && draft_pos) {
+    y = a.ids[(size_t)i * G + j];
+    ly = LT::at(lrow, (size_t)y);
+    if (a.q != nullptr) qyv = F32::at(qrow, (size_t)y);
+  }
+
   StochState st;
-  st.m = -FLT_MAX;
+  st.m = cand ? -INFINITY : -FLT_MAX;
   st.z = 0.0;
   st.r = 0.0;
   st.qbad = 0u;
-  st.ps = ChunkState{0, 0u, false};
-  st.qs = ChunkState{0, 0u, false};
+  st.lbad = 0u;
+  st.ps = ChunkState{0, 0u, 0};
+  st.qs = ChunkState{0, 0u, 0};
   const int qm = has_q ? (temper ? 2 : 1) : 0;
   if (cand) {
     if (qm == 0) stream_stochastic<LT, VEC, 0, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
     else if (qm == 1) stream_stochastic<LT, VEC, 1, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
     else stream_stochastic<LT, VEC, 2, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
+    // each wave cuts its own buffers down to its k-th largest key
+    if (st.ps.cnt > rq.k && !st.ps.ovf) st.ps = chunk_refresh((LDS_AS ChunkBuf<typename LT::Raw>*)&sh.pb[wave], st.ps, rq.k);
+    if (has_q && st.qs.cnt > rq.k && !st.qs.ovf)
+      st.qs = chunk_refresh((LDS_AS ChunkBuf<F32::Raw>*)&sh.qb[wave], st.qs, rq.k);
   } else {
     if (qm == 0) stream_stochastic<LT, VEC, 0, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
     else if (qm == 1) stream_stochastic<LT, VEC, 1, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
     else stream_stochastic<LT, VEC, 2, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
   }
 
-  // ---- block totals ----
-  const float m = block_max_f(st.m, sh.red_f);
-  const double zpart = st.z * exp2(((double)st.m - (double)m) * (double)c);
-  const double Z = block_sum_d(zpart, sh.red_d);
-  const double R = has_q ? block_sum_d(st.r, sh.red_d) : 0.0;
-  const uint32_t qb = has_q ? block_max_u(st.qbad, sh.red_u) : 0u;
+  // ---- block totals: two exchanges, combined in a fixed order ----
+  {
+    const float mw = wave_max_f(st.m);
+    const uint32_t qbw = has_q ? wave_max_u32(st.qbad) : 0u;
+    const uint32_t lbw = cand ? wave_max_u32(st.lbad) : 0u;
+    const double rw = (has_q && !cand) ? wave_sum_d(st.r) : 0.0;
+    if (lane == 0) {
+      sh.xm[wave] = mw;
+      sh.xqb[wave] = qbw;
+      sh.xlb[wave] = lbw;
+      sh.xr[wave] = rw;
+      sh.ps[wave] = st.ps;
+      sh.qs[wave] = st.qs;
+    }
+  }
+  __syncthreads();
+  const float m = __builtin_fmaxf(__builtin_fmaxf(sh.xm[0], sh.xm[1]), __builtin_fmaxf(sh.xm[2], sh.xm[3]));
+  const double R = (sh.xr[0] + sh.xr[1]) + (sh.xr[2] + sh.xr[3]);
+  const uint32_t qb = max(max(sh.xqb[0], sh.xqb[1]), max(sh.xqb[2], sh.xqb[3]));
+  const uint32_t lb = max(max(sh.xlb[0], sh.xlb[1]), max(sh.xlb[2], sh.xlb[3]));
+  if (cand) {
+    // each wave gathers the tokens of its own chunks that reach the largest
+    // wave threshold (an overflowed buffer marks the distribution undecided)
+    uint32_t L = 0u;
+    int ovf = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      L = max(L, sh.ps[w].thr);
+      ovf |= sh.ps[w].ovf;
+    }
+    int n = ovf ? kSeg + 1
+                : gather_tokens((const LDS_AS ChunkBuf<typename LT::Raw>*)&sh.pb[wave], st.ps.cnt, L, V,
+                                (LDS_AS uint32_t*)&sh.skey[0][wave * kSeg], (LDS_AS int*)&sh.sid[0][wave * kSeg]);
+    if (lane == 0) sh.scnt[0][wave] = n;
+    if (has_q) {
+      L = 0u;
+      ovf = 0;
+      for (int w = 0; w < kWaves; ++w) {
+        L = max(L, sh.qs[w].thr);
+        ovf |= sh.qs[w].ovf;
+      }
+      n = ovf ? kSeg + 1
+              : gather_tokens((const LDS_AS ChunkBuf<F32::Raw>*)&sh.qb[wave], st.qs.cnt, L, V,
+                              (LDS_AS uint32_t*)&sh.skey[1][wave * kSeg], (LDS_AS int*)&sh.sid[1][wave * kSeg]);
+      if (lane == 0) sh.scnt[1][wave] = n;
+    }
+  }
+  if (!cand) {
+    const double zw = wave_sum_d(st.z * exp2(((double)st.m - (double)m) * (double)c));
+    if (lane == 0) sh.xz[wave] = zw;
+  }
+  __syncthreads();
+  // without top-k: Z = sum over the row; with it the kept mass is found below
+  const double Z = cand ? 1.0 : (sh.xz[0] + sh.xz[1]) + (sh.xz[2] + sh.xz[3]);
   int fault = 0;
-  if (!(Z > 0.0) || isinf(Z)) fault |= kFaultTargetRow;
+  if (cand ? (lb > 0x7f800000u || !isfinite(m)) : (!(Z > 0.0) || isinf(Z))) fault |= kFaultTargetRow;
   if (has_q && qb >= 0x7f800000u) fault |= kFaultDraftRow;
 
   float cut_p = -INFINITY, cut_q = -INFINITY;
   double Zk = Z, Rk = R;
   int nlist = -1;
   if (!fault && filt) {
-    if (cand && lane == 0) {
-      sh.ps[wave] = st.ps;
-      sh.qs[wave] = st.qs;
-    }
-    __syncthreads();
-    // target
-    bool done = false;
+    bool pdone = false, qdone = !has_q;
     if (cand) {
-      KeptArgs ka;
-      ka.row = lrow;
-      ka.V = V;
-      ka.bf16 = sizeof(ET) == 2;
-      ka.draft = false;
-      ka.m = m;
-      ka.c = c;
-      ka.T = T;
-      ka.k = rq.k;
-      ka.top_p = rq.p;
-      ka.pact = rq.pact;
-      const Kept kp = kept_from_chunks(ka, (LDS_AS ChunkBuf*)sh.pb, (LDS_AS ChunkState*)sh.ps, (LDS_AS float*)sh.lval,
-                                       (LDS_AS int*)sh.lid, (LDS_AS double*)sh.lmass, (LDS_AS double*)sh.red_d,
-                                       (LDS_AS float*)sh.red_f, (LDS_AS int*)sh.misc);
-      if (kp.ok) {
-        done = true;
-        cut_p = kp.cut;
-        Zk = kp.mass;
-        nlist = kp.n;
-        ListEntry* L = a.lists + row * kLcap;
-        for (int t = tid; t < kp.n; t += kBlock) {
-          ListEntry e;
-          e.id = sh.lid[t];
-          e.val = sh.lval[t];
-          e.e = sh.lmass[t];
-          publish(L + t, e);
-        }
+      // wave 0 merges the target buffers, wave 1 the draft buffers
+      if (wave < (has_q ? 2 : 1)) {
+        const int d = wave;
+        MergeIn in;
+        in.k = rq.k;
+        in.top_p = rq.p;
+        in.pact = rq.pact;
+        in.draft = d;
+        in.m = m;
+        in.c = c;
+        in.T = T;
+        in.list = d == 0 ? a.lists + row * kLcap : nullptr;
+        MergeOut mo;
+        if (d == 0)
+          mo = wave_merge<sizeof(ET) == 2>(in, (LDS_AS uint32_t*)sh.skey[0], (LDS_AS int*)sh.sid[0],
+                                           (const LDS_AS int*)sh.scnt[0], (LDS_AS double*)sh.pb);
+        else
+          mo = wave_merge<false>(in, (LDS_AS uint32_t*)sh.skey[1], (LDS_AS int*)sh.sid[1],
+                                 (const LDS_AS int*)sh.scnt[1], (LDS_AS double*)sh.qb);
+        if (lane == 0) sh.mo[d] = mo;
       }
       __syncthreads();
+      const MergeOut mp = sh.mo[0];
+      if (mp.ok) {
+        pdone = true;
+        cut_p = mp.cut;
+        Zk = mp.mass;
+        nlist = mp.n;
+      }
+      if (has_q) {
+        const MergeOut mq = sh.mo[1];
+        if (mq.ok) {
+          qdone = true;
+          cut_q = mq.cut;
+          Rk = mq.mass;
+        }
+      }
     }
-    if (!done) {
+    if (!pdone) {
       GeneralArgs g;
       g.row = lrow;
       g.V = V;
@@ -1455,56 +1741,30 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       g.top_p = rq.p;
       g.pact = rq.pact;
       g.total = Z;
-      const Filtered f = general_filter(g, (LDS_AS double*)sh.lmass, (LDS_AS double*)sh.sel_d,
+      const Filtered f = general_filter(g, (LDS_AS double*)sh.pb, (LDS_AS double*)sh.sel_d,
                                         (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d);
       cut_p = f.cut;
       Zk = f.mass;
     }
-    // draft
-    if (has_q) {
-      bool qdone = false;
-      if (cand) {
-        KeptArgs ka;
-        ka.row = qrow;
-        ka.V = V;
-        ka.bf16 = false;
-        ka.draft = true;
-        ka.m = m;
-        ka.c = c;
-        ka.T = T;
-        ka.k = rq.k;
-        ka.top_p = rq.p;
-        ka.pact = rq.pact;
-        const Kept kq = kept_from_chunks(ka, (LDS_AS ChunkBuf*)sh.qb, (LDS_AS ChunkState*)sh.qs,
-                                         (LDS_AS float*)sh.lval, (LDS_AS int*)sh.lid, (LDS_AS double*)sh.lmass,
-                                         (LDS_AS double*)sh.red_d, (LDS_AS float*)sh.red_f, (LDS_AS int*)sh.misc);
-        if (kq.ok) {
-          qdone = true;
-          cut_q = kq.cut;
-          Rk = kq.mass;
-        }
-        __syncthreads();
-      }
-      if (!qdone) {
-        GeneralArgs g;
-        g.row = qrow;
-        g.V = V;
-        g.bf16 = false;
-        g.draft = true;
-        g.m = m;
-        g.c = c;
-        g.invT = invT;
-        g.temper = temper;
-        g.k = rq.k;
-        g.kact = rq.kact;
-        g.top_p = rq.p;
-        g.pact = rq.pact;
-        g.total = R;
-        const Filtered f = general_filter(g, (LDS_AS double*)sh.lmass, (LDS_AS double*)sh.sel_d,
-                                          (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d);
-        cut_q = f.cut;
-        Rk = f.mass;
-      }
+    if (!qdone) {
+      GeneralArgs g;
+      g.row = qrow;
+      g.V = V;
+      g.bf16 = false;
+      g.draft = true;
+      g.m = m;
+      g.c = c;
+      g.invT = invT;
+      g.temper = temper;
+      g.k = rq.k;
+      g.kact = rq.kact;
+      g.top_p = rq.p;
+      g.pact = rq.pact;
+      g.total = R;
+      const Filtered f = general_filter(g, (LDS_AS double*)sh.pb, (LDS_AS double*)sh.sel_d,
+                                        (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d);
+      cut_q = f.cut;
+      Rk = f.mass;
     }
   }
   if (!fault && has_q && !(Rk > 0.0)) fault |= kFaultDraftMass;
@@ -1521,15 +1781,10 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
     s.q_y = NAN;
     int acc = 0;
     if (draft_pos && !fault) {
-      const int y = a.ids[(size_t)i * G + j];
-      const float ly = LT::at(lrow, (size_t)y);
       const double e = (ly >= cut_p) ? mass_p(ly, m, c) : 0.0;
       const double py = e / Zk;
       double qy = 1.0;
-      if (a.q != nullptr) {
-        const float qv = qrow[y];
-        qy = (qv >= cut_q) ? temper_q(qv, T) / Rk : 0.0;
-      }
+      if (a.q != nullptr) qy = (qyv >= cut_q) ? temper_q(qyv, T) / Rk : 0.0;
       const double u = (double)a.u_accept[(size_t)i * G + j];
       acc = (u * qy < py) ? 1 : 0;
       s.p_y = py;
@@ -1553,10 +1808,14 @@ __global__ __launch_bounds__(kBlock) void clear_kernel(unsigned int* done, int N
 
 template <class LT, bool VEC>
 __global__ __launch_bounds__(kBlock, 3) void row_kernel(Args a) {
-  __shared__ KernelShared sh;
+  __shared__ KernelShared<LT> sh;
   __shared__ int s_last;
-  const int G1 = a.G + 1;
-  const int i = blockIdx.x / G1, j = blockIdx.x - i * G1;
+  // draft positions first (the larger rows), bonus positions last, so that
+  // the short rows fill the end of the launch
+  const int nd = a.N * a.G;
+  const int bx = (int)blockIdx.x;
+  const int i = bx < nd ? bx / a.G : bx - nd;
+  const int j = bx < nd ? bx - i * a.G : a.G;
   const Req rq = load_req(a, i);
   if (!rq.fault && j <= rq.gamma) {
     if (rq.greedy) greedy_row<LT, VEC>(a, rq, i, j, sh.row);

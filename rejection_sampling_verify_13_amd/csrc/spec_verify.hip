@@ -372,6 +372,37 @@ __device__ inline uint32_t wave_min_u32(uint32_t v) {
   v = min(v, dpp_mov<0x143, 0xC>(v));
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
+// Full-wave float max and fp64 sum with DPP (every lane must be active);
+// lanes of rows outside a row_bcast mask add the identity.
+__device__ inline float wave_max_f32(float v) {
+  v = __builtin_fmaxf(v, __uint_as_float(dpp_mov<0xB1, 0xF>(__float_as_uint(v))));
+  v = __builtin_fmaxf(v, __uint_as_float(dpp_mov<0x4E, 0xF>(__float_as_uint(v))));
+  v = __builtin_fmaxf(v, __uint_as_float(dpp_mov<0x141, 0xF>(__float_as_uint(v))));
+  v = __builtin_fmaxf(v, __uint_as_float(dpp_mov<0x140, 0xF>(__float_as_uint(v))));
+  v = __builtin_fmaxf(v, __uint_as_float(dpp_mov<0x142, 0xA>(__float_as_uint(v))));
+  v = __builtin_fmaxf(v, __uint_as_float(dpp_mov<0x143, 0xC>(__float_as_uint(v))));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+template <int CTRL, int ROWS>
+__device__ inline double dpp_add_src(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROWS, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROWS, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ inline double wave_sum_f64(double v) {
+  v += dpp_add_src<0xB1, 0xF>(v);
+  v += dpp_add_src<0x4E, 0xF>(v);
+  v += dpp_add_src<0x141, 0xF>(v);
+  v += dpp_add_src<0x140, 0xF>(v);
+  v += dpp_add_src<0x142, 0xA>(v);
+  v += dpp_add_src<0x143, 0xC>(v);
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 __device__ inline double readlane_d(double v, int l) {
   const uint64_t b = (uint64_t)__double_as_longlong(v);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
@@ -522,6 +553,8 @@ __device__ inline void raw_get(const LDS_AS F32::Raw* s, F32::Raw& r) { r.a = s-
 // their state in registers.
 template <class R>
 __device__ __noinline__ ChunkState chunk_refresh(LDS_AS ChunkBuf<R>* b, ChunkState s, int k) {
+  // the wave's next loads wait on this: issue ahead of the streaming waves
+  __builtin_amdgcn_s_setprio(2);
   const int lane = lane_id();
   s.cnt = uni(s.cnt);
   s.ovf = uni(s.ovf);
@@ -579,6 +612,7 @@ __device__ __noinline__ ChunkState chunk_refresh(LDS_AS ChunkBuf<R>* b, ChunkSta
   s.cnt = n;
   s.thr = thr;
   if (s.cnt > kCap - 64) s.ovf = 1;
+  __builtin_amdgcn_s_setprio(0);
   return s;
 }
 
@@ -866,25 +900,47 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
     }
   kmax = wave_max_u32(kmax);
   kmin = wave_min_u32(kmin);
+  // unused slots hold key 0 and every probe T is >= 1: no guards, and the
+  // group counts are independent (summed as a tree)
   auto count_ge = [&](uint32_t T) {
-    int c = 0;
+    int c[kWaves * G];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
+    for (int t = 0; t < kWaves * G; ++t) c[t] = __popcll(__ballot(kk[t] >= T));
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-        if (64 * g < segn[w]) c += __popcll(__ballot(kk[w * G + g] >= T));
-    return c;
+    for (int h = 1; h < kWaves * G; h <<= 1)
+#pragma unroll
+      for (int t = 0; t + h < kWaves * G; t += 2 * h) c[t] += c[t + h];
+    return c[0];
   };
-  // exact k-th largest key (the gathered set holds the whole top-k set)
+  // The top-k set is {key >= K} for the k-th largest key K (ties included).
+  // Bisection keeps count(>= K) >= k; once exactly k keys reach K the set is
+  // already that top-k set, and K is replaced by its smallest key below.
   uint32_t K = kmin;
   if (kmin != kmax) {
     const int top = 31 - __clz((int)(kmin ^ kmax));
     K = kmin & ~((2u << top) - 1u);
+    bool exact = false;
     for (int bit = top; bit >= (BF16KEYS ? 16 : 0); --bit) {
       const uint32_t T = K | (1u << bit);
-      if (count_ge(T) >= in.k) K = T;
+      const int c = count_ge(T);
+      if (c >= in.k) {
+        K = T;
+        if (c == in.k) {
+          exact = true;
+          break;
+        }
+      }
     }
-    if (BF16KEYS && count_ge(K | 0xffffu) >= in.k) K |= 0xffffu;
+    if (BF16KEYS && !exact && count_ge(K | 0xffffu) >= in.k) K |= 0xffffu;
+  }
+  {
+    uint32_t kmin2 = 0xffffffffu;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        if (64 * g + lane < segn[w] && kk[w * G + g] >= K) kmin2 = min(kmin2, kk[w * G + g]);
+    K = wave_min_u32(kmin2);
   }
   // the top-k set, compacted to the front of the segment area
   wave_lds_sync();
@@ -911,17 +967,30 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
     const uint32_t key = h ? skey[lane] : 0u;
     const int id = h ? sid[lane] : -1;
     const double e = h ? merge_weight(in, okey_value(key)) : 0.0;
-    const double zk = wave_sum_d(e);
+    const double zk = wave_sum_f64(e);
     double mass = zk;
     bool keep = h;
     if (in.pact) {
       // cum = mass of the entries whose key is >= this lane's key
-      double cum = 0.0;
-      for (int u = 0; u < nk; ++u) {
+      // (eight independent partial sums: the loop is latency-bound)
+      double part[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) part[t] = 0.0;
+      int u = 0;
+      for (; u + 8 <= nk; u += 8) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t ku = (uint32_t)__builtin_amdgcn_readlane((int)key, u + t);
+          const double eu = readlane_d(e, u + t);
+          part[t] += (ku >= key) ? eu : 0.0;
+        }
+      }
+      for (; u < nk; ++u) {
         const uint32_t ku = (uint32_t)__builtin_amdgcn_readlane((int)key, u);
         const double eu = readlane_d(e, u);
-        cum += (ku >= key) ? eu : 0.0;
+        part[0] += (ku >= key) ? eu : 0.0;
       }
+      const double cum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
       const double target = (double)in.top_p * zk;
       const uint32_t best = wave_max_u32((h && cum >= target) ? key : 0u);
       if (best != 0u) {  // else rounding kept the run below target: keep the whole top-k set
@@ -1543,6 +1612,7 @@ __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, 
   float best = -INFINITY, acc = 0.f;
   int bidx = -1;
   stream_greedy<LT, VEC>(lrow, V, best, bidx, acc);
+  __builtin_amdgcn_s_setprio(2);
   const float gbest = block_max_f(best, sh.red_f);
   int cand = (best == gbest && bidx >= 0) ? bidx : INT_MAX;
   cand = block_min_i(cand, sh.red_i);
@@ -1625,12 +1695,15 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
     else stream_stochastic<LT, VEC, 2, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
   }
 
+  // the rest of the row is short serial work that holds this workgroup's
+  // slot: issue it ahead of other workgroups' streaming waves
+  __builtin_amdgcn_s_setprio(2);
   // ---- block totals: two exchanges, combined in a fixed order ----
   {
-    const float mw = wave_max_f(st.m);
+    const float mw = wave_max_f32(st.m);
     const uint32_t qbw = has_q ? wave_max_u32(st.qbad) : 0u;
     const uint32_t lbw = cand ? wave_max_u32(st.lbad) : 0u;
-    const double rw = (has_q && !cand) ? wave_sum_d(st.r) : 0.0;
+    const double rw = (has_q && !cand) ? wave_sum_f64(st.r) : 0.0;
     if (lane == 0) {
       sh.xm[wave] = mw;
       sh.xqb[wave] = qbw;
@@ -1672,7 +1745,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
     }
   }
   if (!cand) {
-    const double zw = wave_sum_d(st.z * exp2(((double)st.m - (double)m) * (double)c));
+    const double zw = wave_sum_f64(st.z * exp2(((double)st.m - (double)m) * (double)c));
     if (lane == 0) sh.xz[wave] = zw;
   }
   __syncthreads();

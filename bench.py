@@ -65,20 +65,27 @@ def traffic_from_profile(digest, workload):
     return int(m.group(1))
 
 
-def cpu_baseline(spec, n_req, threads):
+def cpu_baseline(spec, n_req, threads, min_seconds=10.0):
+    """The fp64 C oracle timed on the host over the first n_req requests of
+    the same workload, repeated until about min_seconds have passed."""
     import numpy as np
     import oracle
     import workloads as W
     oracle.build(force=False)
     sub = W.generate(spec, requests=range(n_req), threads=threads)
-    t0 = time.perf_counter()
-    oracle.run(sub["draft_ids"], sub["draft_probs"], sub["target_logits"], sub["dtype"], sub["temperature"],
-               sub["top_k"], sub["top_p"], sub["u_accept"], sub["u_sample"], threads=threads)
-    dt = time.perf_counter() - t0
     pos = int(np.asarray(sub["gamma"]).sum())
-    return dict(value=pos / dt, unit="positions/s", cores=threads, kind="oracle",
-                sample="first %d of %d requests of the same workload (%d verified positions), fp64 C oracle, "
-                       "%d threads over requests, %.2f s wall" % (n_req, spec.N, pos, threads, dt))
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.run(sub["draft_ids"], sub["draft_probs"], sub["target_logits"], sub["dtype"], sub["temperature"],
+                   sub["top_k"], sub["top_p"], sub["u_accept"], sub["u_sample"], threads=threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return dict(value=pos * passes / dt, unit="positions/s", cores=threads, kind="oracle",
+                sample="first %d of %d requests of the same workload (%d verified positions) x %d passes, "
+                       "fp64 C oracle, %d threads over requests, %.1f s wall" % (n_req, spec.N, pos, passes, threads, dt))
 
 
 def main():
@@ -87,7 +94,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
-    ap.add_argument("--cpu-sample", type=int, default=96, help="requests timed on the CPU oracle (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=256, help="requests timed on the CPU oracle (0: skip)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -159,7 +166,6 @@ def main():
     wall = time.perf_counter() - t0
 
     row_ms = np.array([sum(e[0].elapsed_time(e[1]) for e in evs[k]) for k in range(K)])
-    fin_ms = np.array([sum(e[1].elapsed_time(e[2]) for e in evs[k]) for k in range(K)])
     ms_per_step = wall * 1e3 / K
     value = positions * K / wall
 
@@ -171,7 +177,6 @@ def main():
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel="row_kernel", kernel_avg_us=round(row_avg_s * 1e6, 2),
-                    finish_kernel_avg_us=round(float(fin_ms.mean()) * 1e3, 2),
                     algorithmic_bytes_per_launch=B_alg)
 
     if args.calib_copy_mb:

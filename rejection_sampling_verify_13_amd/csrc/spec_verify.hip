@@ -13,26 +13,28 @@
 //   clear_kernel  zeroes one completion counter per request.
 //   row_kernel    one 256-thread workgroup per (request, position) row: first
 //                 the draft positions in request-major order, then the bonus
-//                 positions.  It streams the target-logit row and, at
-//                 draft positions of sampled requests, the draft-probability
-//                 row once (16-byte nontemporal loads, the next step's loads in
-//                 flight while the current step is reduced) and computes: row
-//                 max, sum of exp over the row (fp32 terms, fp64 accumulation),
-//                 sum of q^(1/T), draft-row validity, greedy argmax.  With
-//                 top-k active (k <= kKFast) every lane whose 8-token chunk
-//                 holds a value at or above its wave's threshold appends the
-//                 whole chunk to an LDS buffer; the threshold is raised to the
-//                 k-th largest buffered chunk maximum whenever the buffer fills,
-//                 which never exceeds the true k-th largest value, so one pass
-//                 yields every token of the top-k set.  Other filter settings
-//                 use a radix select that re-reads the row.  p'(y) and q'(y)
-//                 are evaluated in fp64 and the flag u * q'(y) < p'(y) stored.
+//                 positions.  It streams the target-logit row and, at draft
+//                 positions of sampled requests, the draft-probability row
+//                 once (16-byte nontemporal loads, several steps of loads in
+//                 flight while the current step is reduced).
+//                 Without top-k: row max, sum of exp over the row (fp32 terms,
+//                 fp64 accumulation), sum of q^(1/T), draft-row validity.
+//                 With top-k (k <= kKFast): row max and validity only, plus
+//                 per wave an LDS buffer of the 8-token chunks whose largest
+//                 value reaches a rising threshold that never exceeds the row's
+//                 k-th largest value, so one pass yields every top-k token; one
+//                 wave per distribution then finds the exact k-th largest, the
+//                 fp64 kept masses and the top-p cut from LDS.  Other filter
+//                 settings use a radix select that re-reads the row.  Greedy
+//                 rows take the argmax.  p'(y) and q'(y) are evaluated in fp64
+//                 and the flag u * q'(y) < p'(y) stored; a row that may be the
+//                 one drawn from (the bonus row, or a rejected draft row) with
+//                 its top-k set in LDS also draws its token there.
 //                 The last workgroup of a request to finish (atomic counter)
-//                 then finds the first rejection A by ballot and draws the
-//                 replacement or bonus token by inverse CDF over ascending
-//                 token id: from the stored kept list of row A when filters are
-//                 active, otherwise by two passes over row A (chunk sums, then
-//                 the crossing chunk).  Outputs are written -1 padded.
+//                 finds the first rejection A by ballot and takes row A's
+//                 draw, or draws by inverse CDF over ascending token id with
+//                 two passes over row A (chunk sums, then the crossing chunk).
+//                 Outputs are written -1 padded.
 //
 // Compile: hipcc --offload-arch=gfx950 -O3 -shared -fPIC
 //          -Xclang -target-feature -Xclang -packed-fp32-ops
@@ -59,7 +61,6 @@ constexpr int kCap = 160;               // buffered candidate chunks per wave an
 constexpr int kKFast = 64;              // largest top_k served by the candidate buffers
 constexpr int kSeg = 128;               // gathered candidate tokens per wave and distribution (LDS)
 constexpr int kMerge = kWaves * kSeg;   // gathered candidate tokens of one distribution
-constexpr int kLcap = kMerge;           // kept-list entries stored per row
 constexpr int kMaxChunks = 512;         // chunk sums held by the draw
 constexpr int kMaxGamma = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -83,17 +84,11 @@ struct RowStats {
   double r;       // sum over the kept set of q^(1/T)
   double p_y;     // p'(y) at a draft position
   double q_y;     // q'(y) at a draft position
+  double s;       // mass S of the draw made in the row (when draw >= 0)
   int flags;      // bit 0: accepted; bits 8..15: fault bits
-  int nlist;      // entries of the stored kept list (-1: none stored)
-  int pad[2];
+  int draw;       // token drawn from this row's draw weights, -1: not drawn in the row pass
 };
 static_assert(sizeof(RowStats) == 64, "RowStats layout");
-
-struct ListEntry {
-  int id;
-  float val;      // the logit
-  double e;       // 2^((l - m) * c)
-};
 
 struct Args {
   int N, G, V;
@@ -112,7 +107,6 @@ struct Args {
   double* d_resid;
   int32_t* d_fault;
   RowStats* stats;
-  ListEntry* lists;
   unsigned int* done;   // completion counter per request
 };
 
@@ -251,7 +245,7 @@ __device__ inline double mass_p(float l, float m, float c) {
 // ------------------------------------------------------------------------------------------
 // hand-off of row results to the request's finishing workgroup
 //
-// Row statistics and kept lists are written with agent-scope atomic stores and
+// Row statistics are written with agent-scope atomic stores and
 // read back with agent-scope atomic loads: on gfx950 these are global stores /
 // loads with the device-coherence bit, which write through and read past the
 // per-XCD L2, so the finishing workgroup (possibly on another XCD) sees them
@@ -746,11 +740,11 @@ __device__ double block_sum_above(KW kw, int V, uint32_t lo, double* red) {
 
 // Result of one distribution's top-k / top-p filter.
 struct MergeOut {
-  double mass;    // kept mass (target: sum of 2^((l - m) * c); draft: sum of q^(1/T))
-  float cut;      // keep iff value >= cut
-  int n;          // target: kept-list entries stored
-  int ok;         // 0: the buffers cannot decide (ties); the radix select does
-  int pad;
+  double mass;      // kept mass (target: sum of 2^((l - m) * c); draft: sum of q^(1/T))
+  float cut;        // keep iff value >= cut
+  uint32_t cutkey;  // the same as an order key
+  int nk;           // top-k tokens left at the front of the key / id / weight arrays
+  int ok;           // 0: the buffers cannot decide (ties); the radix select does
 };
 
 template <class LT>
@@ -779,8 +773,7 @@ struct RowShared {
 
 struct FinShared {
   double wsum[kWaves][kMaxChunks];
-  double lw[kLcap];
-  int lwid[kLcap];
+  RowStats sa;
   double red_d[kWaves];
   int red_i[kWaves];
   int misc[8];
@@ -803,7 +796,6 @@ struct MergeIn {
   int pact;
   int draft;          // weights q^(1/T) (else 2^((l - m) * c))
   float m, c, T;
-  ListEntry* list;    // the kept list is stored here (NULL: not stored)
 };
 
 __device__ inline double merge_weight(const MergeIn& in, float v) {
@@ -856,8 +848,8 @@ __device__ inline int gather_tokens(const LDS_AS ChunkBuf<R>* b, int cnt, uint32
 // prefix of their smallest and largest key; bf16 keys end in 16 equal bits).
 // The tokens at or above K are weighed in fp64 and top-p keeps the smallest
 // run of whole tie groups, largest values first, whose mass reaches top_p of
-// the top-k mass.  Run by a single wave; `mmass` is scratch for the case of
-// more than 64 tokens tied at or above K.
+// the top-k mass.  Run by a single wave.  On return the top-k tokens are at
+// the front of skey / sid (nk of them) with their fp64 weights in mmass.
 template <bool BF16KEYS>
 __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, LDS_AS int* sid, const LDS_AS int* scnt,
                                             LDS_AS double* mmass) {
@@ -871,10 +863,10 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
   in.T = uni(in.T);
   MergeOut out;
   out.ok = 0;
-  out.n = 0;
+  out.nk = 0;
   out.cut = -INFINITY;
+  out.cutkey = 0u;
   out.mass = 0.0;
-  out.pad = 0;
   int segn[kWaves];
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
@@ -969,7 +961,6 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
     const double e = h ? merge_weight(in, okey_value(key)) : 0.0;
     const double zk = wave_sum_f64(e);
     double mass = zk;
-    bool keep = h;
     if (in.pact) {
       // cum = mass of the entries whose key is >= this lane's key
       // (eight independent partial sums: the loop is latency-bound)
@@ -997,19 +988,10 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
         cutkey = best;
         const uint64_t at = __ballot(h && key == best);
         mass = readlane_d(cum, __ffsll((unsigned long long)at) - 1);
-        keep = h && key >= cutkey;
       }
     }
-    const uint64_t km = __ballot(keep);
-    if (in.list && keep) {
-      ListEntry le;
-      le.id = id;
-      le.val = okey_value(key);
-      le.e = e;
-      publish(in.list + mbcnt(km), le);
-    }
+    if (h) mmass[lane] = e;
     out.mass = mass;
-    out.n = __popcll(km);
   } else {
     // many values tied at the k-th largest: weights in LDS, quadratic top-p
     double zp = 0.0;
@@ -1033,28 +1015,142 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
       if (best != 0u) cutkey = best;
     }
     double zc = 0.0;
-    int n = 0;
-    for (int t0 = 0; t0 < nk; t0 += 64) {
-      const int t = t0 + lane;
-      const bool keep = t < nk && skey[t] >= cutkey;
-      const uint64_t mb = __ballot(keep);
-      if (keep) {
-        zc += mmass[t];
-        if (in.list) {
-          ListEntry le;
-          le.id = sid[t];
-          le.val = okey_value(skey[t]);
-          le.e = mmass[t];
-          publish(in.list + n + mbcnt(mb), le);
-        }
-      }
-      n += __popcll(mb);
-    }
+    for (int t = lane; t < nk; t += 64)
+      if (skey[t] >= cutkey) zc += mmass[t];
     out.mass = wave_sum_d(zc);
-    out.n = n;
   }
   out.cut = okey_value(cutkey);
+  out.cutkey = cutkey;
+  out.nk = nk;
   out.ok = 1;
+  return out;
+}
+
+// ------------------------------------------------------------------------------------------
+// the draw from a row's kept list (rows with top-k)
+// ------------------------------------------------------------------------------------------
+
+struct DrawIn {
+  int nk;             // top-k tokens at the front of the key / id / weight arrays
+  uint32_t cutkey;    // a token is kept iff its key >= cutkey
+  double zk;          // kept target mass
+  int mode;           // 0: p'; 1: max(0, p' - q'); 2: p' with the draft token removed
+  const float* qrow;  // mode 1: the draft row
+  float cut_q, T;     // mode 1: draft cut and temperature
+  double rk;          // mode 1: kept draft mass
+  int y;              // mode 2: the draft token
+  float us;           // the request's draw uniform
+};
+
+struct DrawOut {
+  double s;           // mass S of the weights drawn from
+  int z;              // drawn token
+  int pad;
+};
+
+// Weights w over the kept tokens (every token with p' > 0 is among them, so
+// w is zero elsewhere); if they sum to zero, w = p'.  z = the smallest id
+// whose running sum of w in ascending id exceeds u * S, else the largest id
+// with w > 0.  Run by a single wave; wbuf is LDS scratch for more than 64
+// kept tokens.
+__device__ __noinline__ DrawOut wave_draw(DrawIn in, const LDS_AS uint32_t* skey, const LDS_AS int* sid,
+                                          const LDS_AS double* ke, LDS_AS double* wbuf) {
+  const int lane = lane_id();
+  in.nk = uni(in.nk);
+  in.cutkey = uni(in.cutkey);
+  in.zk = uni(in.zk);
+  in.mode = uni(in.mode);
+  in.qrow = uni(in.qrow);
+  in.cut_q = uni(in.cut_q);
+  in.T = uni(in.T);
+  in.rk = uni(in.rk);
+  in.y = uni(in.y);
+  in.us = uni(in.us);
+  auto weight = [&](bool keep, int id, double e, double& p) {
+    p = keep ? e / in.zk : 0.0;
+    double w = p;
+    if (in.mode == 1) {
+      double q = 0.0;
+      if (keep) {
+        const float qx = F32::at(in.qrow, (size_t)id);
+        q = (qx >= in.cut_q) ? temper_q(qx, in.T) / in.rk : 0.0;
+      }
+      w = p - q > 0.0 ? p - q : 0.0;
+    } else if (in.mode == 2) {
+      w = (id == in.y) ? 0.0 : p;
+    }
+    return w;
+  };
+  DrawOut out;
+  out.pad = 0;
+  uint32_t best = 0xffffffffu, last = 0u;  // last: largest id with w > 0, plus one
+  if (in.nk <= 64) {
+    const bool h = lane < in.nk;
+    const bool keep = h && skey[lane] >= in.cutkey;
+    const int id = h ? sid[lane] : 0;
+    double p;
+    double w = weight(keep, id, h ? ke[lane] : 0.0, p);
+    double S = wave_sum_f64(w);
+    if (S == 0.0) {
+      w = p;
+      S = wave_sum_f64(p);
+    }
+    const double tau = (double)in.us * S;
+    // running sum at this lane's id (eight independent partial sums)
+    double part[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) part[t] = 0.0;
+    int u = 0;
+    for (; u + 8 <= in.nk; u += 8) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int iu = __builtin_amdgcn_readlane(id, u + t);
+        const double wu = readlane_d(w, u + t);
+        part[t] += (iu <= id) ? wu : 0.0;
+      }
+    }
+    for (; u < in.nk; ++u) {
+      const int iu = __builtin_amdgcn_readlane(id, u);
+      const double wu = readlane_d(w, u);
+      part[0] += (iu <= id) ? wu : 0.0;
+    }
+    const double cum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+    if (w > 0.0) {
+      if (cum > tau) best = (uint32_t)id;
+      last = (uint32_t)id + 1u;
+    }
+    out.s = S;
+  } else {
+    // many tokens tied at the k-th largest value: weights in LDS, quadratic sums
+    double sp = 0.0, sw = 0.0;
+    for (int t = lane; t < in.nk; t += 64) {
+      double p;
+      const double w = weight(skey[t] >= in.cutkey, sid[t], ke[t], p);
+      wbuf[t] = w;
+      sw += w;
+      sp += p;
+    }
+    double S = wave_sum_d(sw);
+    wave_lds_sync();
+    if (S == 0.0) {
+      for (int t = lane; t < in.nk; t += 64) wbuf[t] = skey[t] >= in.cutkey ? ke[t] / in.zk : 0.0;
+      S = wave_sum_d(sp);
+      wave_lds_sync();
+    }
+    const double tau = (double)in.us * S;
+    for (int t = lane; t < in.nk; t += 64) {
+      if (!(wbuf[t] > 0.0)) continue;
+      const int id = sid[t];
+      double cum = 0.0;
+      for (int u = 0; u < in.nk; ++u) cum += (sid[u] <= id) ? wbuf[u] : 0.0;
+      if (cum > tau) best = min(best, (uint32_t)id);
+      last = max(last, (uint32_t)id + 1u);
+    }
+    out.s = S;
+  }
+  best = wave_min_u32(best);
+  last = wave_max_u32(last);
+  out.z = best != 0xffffffffu ? (int)best : (int)last - 1;
   return out;
 }
 
@@ -1329,8 +1425,13 @@ __device__ inline void step_weights(const float lv[8], const float qv[8], int ba
   }
 }
 
+// Draw from row A by two passes over it (rows without a top-k set in LDS):
+// chunk sums of the draw weights, then the crossing chunk.  Out of line: its
+// registers are not part of the common path.
 template <class LT, bool VEC>
-__device__ __noinline__ void finish_request(const CONST_AS Args* ap, int i, LDS_AS FinShared* sh) {
+__device__ __noinline__ DrawOut draw_two_pass(const CONST_AS Args* ap, int i, int A, int gamma, float T, float sa_m,
+                                              float sa_cut_p, float sa_cut_q, double sa_z, double sa_r,
+                                              LDS_AS FinShared* sh) {
   Args a;
   __builtin_memcpy(&a, (const Args*)ap, sizeof(Args));
   i = uni(i);
@@ -1352,7 +1453,157 @@ __device__ __noinline__ void finish_request(const CONST_AS Args* ap, int i, LDS_
   a.d_resid = uni(a.d_resid);
   a.d_fault = uni(a.d_fault);
   a.stats = uni(a.stats);
-  a.lists = uni(a.lists);
+  A = uni(A);
+  gamma = uni(gamma);
+  T = uni(T);
+  typedef typename LT::T ET;
+  typedef typename LT::Raw LR;
+  const int G = a.G, V = a.V;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  struct {
+    float m, cut_p, cut_q;
+    double z, r;
+  } sa = {uni(sa_m), uni(sa_cut_p), uni(sa_cut_q), uni(sa_z), uni(sa_r)};
+  int z = -1;
+  double S_out = NAN;
+  const bool resid = A < gamma;
+  const int yA = resid ? a.ids[(size_t)i * G + A] : -1;
+  int mode = resid ? (a.q ? 1 : 2) : 0;
+  const size_t row = (size_t)i * (G + 1) + A;
+  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + row * (size_t)V;
+  const float* qrow = (mode == 1) ? a.q + ((size_t)i * G + A) * (size_t)V : nullptr;
+  const double us = (double)a.u_sample[i];
+  {
+    // ---- two passes over row A ----
+    const float m = sa.m, c = kLog2e / T, invT = 1.f / T;
+    const bool temper = T != 1.f;
+    const float invZ = (float)(1.0 / sa.z);
+    const float invR = (mode == 1) ? (float)(1.0 / sa.r) : 0.f;
+    const int nsteps = (V + kStep - 1) / kStep;
+    const int spc = (nsteps + kMaxChunks - 1) / kMaxChunks;  // steps per chunk
+    const int nch = (nsteps + spc - 1) / spc;
+    double S = 0.0;
+    int last = -1;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+      last = -1;
+      double csum = 0.0;
+      auto step = [&](const LR& lr, const F32::Raw& qr, int base, int s) {
+        float lv[8], qv[8], w[8];
+        LT::unpack(lr, lv);
+        F32::unpack(qr, qv);
+        step_weights(lv, qv, base, mode, m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w);
+        double ts = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ts += (double)w[e];
+          if (w[e] > 0.f) last = base + e;
+        }
+        csum += wave_sum_d(ts);
+        if ((s + 1) % spc == 0 || s + 1 == nsteps) {
+          if (lane == 0) sh->wsum[wave][s / spc] = csum;
+          csum = 0.0;
+        }
+      };
+      const int nfull = VEC ? V / kStep : 0;
+      const int base0 = tid * kCh;
+      ring_stream<4, StepRaw<LR>>(
+          nfull,
+          [&](int s) {
+            StepRaw<LR> r;
+            r.l = LT::load(lrow + base0 + s * kStep);
+            r.q = F32::Raw{};
+            if (mode == 1) r.q = F32::load(qrow + base0 + s * kStep);
+            return r;
+          },
+          [&](const StepRaw<LR>& r, int s) { step(r.l, r.q, base0 + s * kStep, s); });
+      int base = base0 + nfull * kStep;
+      for (int s = nfull; s < nsteps; ++s) {
+        step(load_logits<LT, VEC>(lrow, base, V), mode == 1 ? load_probs<VEC>(qrow, base, V) : F32::Raw{}, base, s);
+        base += kStep;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        double tot = 0.0;
+        for (int ch = 0; ch < nch; ++ch) tot += ((sh->wsum[0][ch] + sh->wsum[1][ch]) + (sh->wsum[2][ch] + sh->wsum[3][ch]));
+        sh->miscd[0] = tot;
+      }
+      __syncthreads();
+      S = sh->miscd[0];
+      __syncthreads();
+      if (S > 0.0 || mode == 0) break;
+      mode = 0;  // zero residual: draw from p'
+    }
+    last = block_max_i(last, (int*)sh->red_i);
+    const double tau = us * S;
+    // the chunk holding the crossing (serial over at most kMaxChunks totals)
+    if (tid == 0) {
+      double pre = 0.0;
+      int found = -1;
+      for (int ch = 0; ch < nch; ++ch) {
+        const double cs = (sh->wsum[0][ch] + sh->wsum[1][ch]) + (sh->wsum[2][ch] + sh->wsum[3][ch]);
+        if (pre + cs > tau && cs > 0.0) {
+          found = ch;
+          break;
+        }
+        pre += cs;
+      }
+      sh->misc[2] = found;
+      sh->miscd[1] = pre;
+    }
+    __syncthreads();
+    const int found = sh->misc[2];
+    double pre = sh->miscd[1];
+    __syncthreads();
+    if (found < 0) {
+      z = last;
+    } else {
+      // walk the steps of the chunk in token order; the crossing is in the
+      // last run (thread, step) whose starting prefix is <= tau
+      int bestkey = -1, bestz = -1;
+      for (int s = found * spc; s < min(nsteps, (found + 1) * spc); ++s) {
+        const int base = s * kStep + tid * kCh;
+        float lv[8], qv[8], w[8];
+        LT::unpack(load_logits<LT, VEC>(lrow, min(base, V), V), lv);
+        F32::unpack(mode == 1 ? load_probs<VEC>(qrow, min(base, V), V) : F32::Raw{}, qv);
+        step_weights(lv, qv, base, mode, m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w);
+        double ts = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ts += (double)w[e];
+        double total;
+        const double ex = pre + block_exscan_d(ts, (double*)sh->red_d, &total);
+        if (ts > 0.0 && ex <= tau) {
+          double acc = ex;
+          int zz = -1, lastpos = -1;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (w[e] > 0.f) lastpos = base + e;
+            acc += (double)w[e];
+            if (zz < 0 && w[e] > 0.f && acc > tau) zz = base + e;
+          }
+          bestkey = (s - found * spc) * kBlock + tid;
+          bestz = zz >= 0 ? zz : lastpos;
+        }
+        pre += total;
+      }
+      const int win = block_max_i(bestkey, (int*)sh->red_i);
+      if (tid == 0) sh->misc[3] = -1;
+      __syncthreads();
+      if (win >= 0 && bestkey == win) sh->misc[3] = bestz;
+      __syncthreads();
+      z = sh->misc[3];
+      if (z < 0) z = last;
+    }
+    S_out = S;
+  }
+  DrawOut d;
+  d.z = z;
+  d.s = S_out;
+  d.pad = 0;
+  return d;
+}
+
+template <class LT, bool VEC>
+__device__ __forceinline__ void finish_request(const Args& a, int i, LDS_AS FinShared* sh) {
   typedef typename LT::T ET;
   typedef typename LT::Raw LR;
   const int G = a.G, V = a.V;
@@ -1361,25 +1612,40 @@ __device__ __noinline__ void finish_request(const CONST_AS Args* ap, int i, LDS_
   int32_t* out = a.out_tokens + (size_t)i * (G + 1);
   const RowStats* st = a.stats + (size_t)i * (G + 1);
 
+  // wave 0 loads the row records of rows 0..gamma in one round (lane j: row j;
+  // a 65th row, gamma = 64, is loaded by every lane), finds the fault bits and
+  // the first rejection A, and leaves row A's record in LDS
   int fault = rq.fault, A = 0;
   if (!fault) {
     if (wave == 0) {
-      int f = 0;
-      for (int jj = lane; jj <= rq.gamma; jj += 64) f |= fetch(st + jj).flags >> 8;
-      f = wave_or_i(f);
-      const bool acc = lane < rq.gamma && (fetch(st + lane).flags & 1);
-      const uint64_t accm = __ballot(acc);
+      const bool mine = lane <= rq.gamma;
+      RowStats r{};
+      if (mine) r = fetch(st + lane);
+      RowStats r64{};
+      if (rq.gamma == 64) r64 = fetch(st + 64);
+      int f = mine ? (r.flags >> 8) : 0;
+      f = wave_or_i(f) | ((rq.gamma == 64) ? (r64.flags >> 8) : 0);
+      const uint64_t accm = __ballot(lane < rq.gamma && (r.flags & 1));
       const uint64_t within = rq.gamma >= 64 ? ~0ull : ((1ull << rq.gamma) - 1ull);
       const uint64_t rej = ~accm & within;
+      const int Aw = rej ? (__ffsll((unsigned long long)rej) - 1) : rq.gamma;
       if (lane == 0) {
         sh->misc[0] = f;
-        sh->misc[1] = rej ? (__ffsll((unsigned long long)rej) - 1) : rq.gamma;
+        sh->misc[1] = Aw;
+      }
+      if (Aw == 64) {
+        if (lane == 0) __builtin_memcpy((RowStats*)&sh->sa, &r64, sizeof(RowStats));
+      } else if (lane == Aw) {
+        __builtin_memcpy((RowStats*)&sh->sa, &r, sizeof(RowStats));
+      }
+      if (!f) {
+        if (a.d_py && lane < G) a.d_py[(size_t)i * G + lane] = (lane < rq.gamma && !rq.greedy) ? r.p_y : NAN;
+        if (a.d_qy && lane < G) a.d_qy[(size_t)i * G + lane] = (lane < rq.gamma && !rq.greedy) ? r.q_y : NAN;
       }
     }
     __syncthreads();
     fault = sh->misc[0];
     A = sh->misc[1];
-    __syncthreads();
   }
 
   if (fault) {
@@ -1396,188 +1662,22 @@ __device__ __noinline__ void finish_request(const CONST_AS Args* ap, int i, LDS_
     return;
   }
 
+  RowStats sa;
+  __builtin_memcpy(&sa, (const RowStats*)&sh->sa, sizeof(RowStats));
   int z;
   double S_out = NAN;
   if (rq.greedy) {
-    z = fetch(st + A).argmax;
+    z = sa.argmax;
+  } else if (sa.draw >= 0) {
+    // drawn by row A's own workgroup from its kept list
+    z = sa.draw;
+    S_out = sa.s;
   } else {
-    const RowStats sa = fetch(st + A);
-    const bool resid = A < rq.gamma;
-    const int yA = resid ? a.ids[(size_t)i * G + A] : -1;
-    int mode = resid ? (a.q ? 1 : 2) : 0;
-    const size_t row = (size_t)i * (G + 1) + A;
-    const ET* lrow = reinterpret_cast<const ET*>(a.logits) + row * (size_t)V;
-    const float* qrow = (mode == 1) ? a.q + ((size_t)i * G + A) * (size_t)V : nullptr;
-    const float T = rq.T;
-    const double us = (double)a.u_sample[i];
-
-    if (sa.nlist >= 0) {
-      // ---- kept list of row A: every token with p' > 0 is in it ----
-      const ListEntry* L = a.lists + row * kLcap;
-      const int n = sa.nlist;
-      double part = 0.0;
-      for (int t = tid; t < n; t += kBlock) {
-        const ListEntry e = fetch(L + t);
-        const double p = (e.val >= sa.cut_p) ? e.e / sa.z : 0.0;
-        double w = p;
-        if (mode == 1) {
-          const float qx = qrow[e.id];
-          const double q = (qx >= sa.cut_q) ? temper_q(qx, T) / sa.r : 0.0;
-          w = p - q > 0.0 ? p - q : 0.0;
-        } else if (mode == 2) {
-          w = (e.id == yA) ? 0.0 : p;
-        }
-        sh->lw[t] = w;
-        sh->lwid[t] = e.id;
-        part += w;
-      }
-      double S = block_sum_d(part, (double*)sh->red_d);
-      if (S == 0.0) {
-        part = 0.0;
-        for (int t = tid; t < n; t += kBlock) {
-          const ListEntry e = fetch(L + t);
-          const double p = (e.val >= sa.cut_p) ? e.e / sa.z : 0.0;
-          sh->lw[t] = p;
-          part += p;
-        }
-        S = block_sum_d(part, (double*)sh->red_d);
-      }
-      const double tau = us * S;
-      int best = INT_MAX, last = -1;
-      for (int t = tid; t < n; t += kBlock) {
-        if (!(sh->lw[t] > 0.0)) continue;
-        const int id = sh->lwid[t];
-        double cum = 0.0;
-        for (int u = 0; u < n; ++u) cum += (sh->lwid[u] <= id) ? sh->lw[u] : 0.0;
-        if (cum > tau) best = min(best, id);
-        last = max(last, id);
-      }
-      best = block_min_i(best, (int*)sh->red_i);
-      last = block_max_i(last, (int*)sh->red_i);
-      z = (best != INT_MAX) ? best : last;
-      S_out = S;
-    } else {
-      // ---- two passes over row A ----
-      const float m = sa.m, c = kLog2e / T, invT = 1.f / T;
-      const bool temper = T != 1.f;
-      const float invZ = (float)(1.0 / sa.z);
-      const float invR = (mode == 1) ? (float)(1.0 / sa.r) : 0.f;
-      const int nsteps = (V + kStep - 1) / kStep;
-      const int spc = (nsteps + kMaxChunks - 1) / kMaxChunks;  // steps per chunk
-      const int nch = (nsteps + spc - 1) / spc;
-      double S = 0.0;
-      int last = -1;
-      for (int attempt = 0; attempt < 2; ++attempt) {
-        last = -1;
-        double csum = 0.0;
-        auto step = [&](const LR& lr, const F32::Raw& qr, int base, int s) {
-          float lv[8], qv[8], w[8];
-          LT::unpack(lr, lv);
-          F32::unpack(qr, qv);
-          step_weights(lv, qv, base, mode, m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w);
-          double ts = 0.0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ts += (double)w[e];
-            if (w[e] > 0.f) last = base + e;
-          }
-          csum += wave_sum_d(ts);
-          if ((s + 1) % spc == 0 || s + 1 == nsteps) {
-            if (lane == 0) sh->wsum[wave][s / spc] = csum;
-            csum = 0.0;
-          }
-        };
-        const int nfull = VEC ? V / kStep : 0;
-        const int base0 = tid * kCh;
-        ring_stream<4, StepRaw<LR>>(
-            nfull,
-            [&](int s) {
-              StepRaw<LR> r;
-              r.l = LT::load(lrow + base0 + s * kStep);
-              r.q = F32::Raw{};
-              if (mode == 1) r.q = F32::load(qrow + base0 + s * kStep);
-              return r;
-            },
-            [&](const StepRaw<LR>& r, int s) { step(r.l, r.q, base0 + s * kStep, s); });
-        int base = base0 + nfull * kStep;
-        for (int s = nfull; s < nsteps; ++s) {
-          step(load_logits<LT, VEC>(lrow, base, V), mode == 1 ? load_probs<VEC>(qrow, base, V) : F32::Raw{}, base, s);
-          base += kStep;
-        }
-        __syncthreads();
-        if (tid == 0) {
-          double tot = 0.0;
-          for (int ch = 0; ch < nch; ++ch) tot += ((sh->wsum[0][ch] + sh->wsum[1][ch]) + (sh->wsum[2][ch] + sh->wsum[3][ch]));
-          sh->miscd[0] = tot;
-        }
-        __syncthreads();
-        S = sh->miscd[0];
-        __syncthreads();
-        if (S > 0.0 || mode == 0) break;
-        mode = 0;  // zero residual: draw from p'
-      }
-      last = block_max_i(last, (int*)sh->red_i);
-      const double tau = us * S;
-      // the chunk holding the crossing (serial over at most kMaxChunks totals)
-      if (tid == 0) {
-        double pre = 0.0;
-        int found = -1;
-        for (int ch = 0; ch < nch; ++ch) {
-          const double cs = (sh->wsum[0][ch] + sh->wsum[1][ch]) + (sh->wsum[2][ch] + sh->wsum[3][ch]);
-          if (pre + cs > tau && cs > 0.0) {
-            found = ch;
-            break;
-          }
-          pre += cs;
-        }
-        sh->misc[2] = found;
-        sh->miscd[1] = pre;
-      }
-      __syncthreads();
-      const int found = sh->misc[2];
-      double pre = sh->miscd[1];
-      __syncthreads();
-      if (found < 0) {
-        z = last;
-      } else {
-        // walk the steps of the chunk in token order; the crossing is in the
-        // last run (thread, step) whose starting prefix is <= tau
-        int bestkey = -1, bestz = -1;
-        for (int s = found * spc; s < min(nsteps, (found + 1) * spc); ++s) {
-          const int base = s * kStep + tid * kCh;
-          float lv[8], qv[8], w[8];
-          LT::unpack(load_logits<LT, VEC>(lrow, min(base, V), V), lv);
-          F32::unpack(mode == 1 ? load_probs<VEC>(qrow, min(base, V), V) : F32::Raw{}, qv);
-          step_weights(lv, qv, base, mode, m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w);
-          double ts = 0.0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ts += (double)w[e];
-          double total;
-          const double ex = pre + block_exscan_d(ts, (double*)sh->red_d, &total);
-          if (ts > 0.0 && ex <= tau) {
-            double acc = ex;
-            int zz = -1, lastpos = -1;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              if (w[e] > 0.f) lastpos = base + e;
-              acc += (double)w[e];
-              if (zz < 0 && w[e] > 0.f && acc > tau) zz = base + e;
-            }
-            bestkey = (s - found * spc) * kBlock + tid;
-            bestz = zz >= 0 ? zz : lastpos;
-          }
-          pre += total;
-        }
-        const int win = block_max_i(bestkey, (int*)sh->red_i);
-        if (tid == 0) sh->misc[3] = -1;
-        __syncthreads();
-        if (win >= 0 && bestkey == win) sh->misc[3] = bestz;
-        __syncthreads();
-        z = sh->misc[3];
-        if (z < 0) z = last;
-      }
-      S_out = S;
-    }
+    // row A had no top-k set in LDS: two passes over it here
+    const DrawOut d = draw_two_pass<LT, VEC>((const CONST_AS Args*)__builtin_amdgcn_kernarg_segment_ptr(), i, A,
+                                             rq.gamma, rq.T, sa.m, sa.cut_p, sa.cut_q, sa.z, sa.r, sh);
+    z = d.z;
+    S_out = d.s;
   }
 
   for (int t = tid; t <= G; t += kBlock) {
@@ -1591,12 +1691,6 @@ __device__ __noinline__ void finish_request(const CONST_AS Args* ap, int i, LDS_
     if (a.d_fault) a.d_fault[i] = 0;
     if (a.d_resid) a.d_resid[i] = S_out;
   }
-  if (a.d_py)
-    for (int t = tid; t < G; t += kBlock)
-      a.d_py[(size_t)i * G + t] = (t < rq.gamma && !rq.greedy) ? fetch(st + t).p_y : NAN;
-  if (a.d_qy)
-    for (int t = tid; t < G; t += kBlock)
-      a.d_qy[(size_t)i * G + t] = (t < rq.gamma && !rq.greedy) ? fetch(st + t).q_y : NAN;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1639,9 +1733,9 @@ __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, 
     s.r = 0.0;
     s.p_y = NAN;
     s.q_y = NAN;
+    s.s = NAN;
     s.flags = ((j < rq.gamma && y == cand) ? 1 : 0) | (fault << 8);
-    s.nlist = -1;
-    s.pad[0] = s.pad[1] = 0;
+    s.draw = -1;
     publish(a.stats + row, s);
   }
 }
@@ -1757,7 +1851,8 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
 
   float cut_p = -INFINITY, cut_q = -INFINITY;
   double Zk = Z, Rk = R;
-  int nlist = -1;
+  MergeOut mp;  // target top-k set left in LDS by the merge (mp.ok)
+  mp.ok = 0;
   if (!fault && filt) {
     bool pdone = false, qdone = !has_q;
     if (cand) {
@@ -1772,7 +1867,6 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
         in.m = m;
         in.c = c;
         in.T = T;
-        in.list = d == 0 ? a.lists + row * kLcap : nullptr;
         MergeOut mo;
         if (d == 0)
           mo = wave_merge<sizeof(ET) == 2>(in, (LDS_AS uint32_t*)sh.skey[0], (LDS_AS int*)sh.sid[0],
@@ -1783,12 +1877,11 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
         if (lane == 0) sh.mo[d] = mo;
       }
       __syncthreads();
-      const MergeOut mp = sh.mo[0];
+      mp = sh.mo[0];
       if (mp.ok) {
         pdone = true;
         cut_p = mp.cut;
         Zk = mp.mass;
-        nlist = mp.n;
       }
       if (has_q) {
         const MergeOut mq = sh.mo[1];
@@ -1834,7 +1927,8 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       g.top_p = rq.p;
       g.pact = rq.pact;
       g.total = R;
-      const Filtered f = general_filter(g, (LDS_AS double*)sh.pb, (LDS_AS double*)sh.sel_d,
+      // (histogram in the draft buffers: the target weights stay for the draw)
+      const Filtered f = general_filter(g, (LDS_AS double*)sh.qb, (LDS_AS double*)sh.sel_d,
                                         (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d);
       cut_q = f.cut;
       Rk = f.mass;
@@ -1842,7 +1936,10 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   }
   if (!fault && has_q && !(Rk > 0.0)) fault |= kFaultDraftMass;
 
-  if (tid == 0) {
+  if (wave == 0) {
+    // accept flag (thread 0 holds the draft token's values), then, if this row
+    // can be the one the request draws from (the bonus row, or a rejected
+    // draft row), the draw itself from the kept list still in LDS
     RowStats s;
     s.m = m;
     s.cut_p = cut_p;
@@ -1853,7 +1950,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
     s.p_y = NAN;
     s.q_y = NAN;
     int acc = 0;
-    if (draft_pos && !fault) {
+    if (lane == 0 && draft_pos && !fault) {
       const double e = (ly >= cut_p) ? mass_p(ly, m, c) : 0.0;
       const double py = e / Zk;
       double qy = 1.0;
@@ -1863,10 +1960,31 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       s.p_y = py;
       s.q_y = qy;
     }
-    s.flags = acc | (fault << 8);
-    s.nlist = nlist;
-    s.pad[0] = s.pad[1] = 0;
-    publish(a.stats + row, s);
+    acc = __builtin_amdgcn_readlane(acc, 0);
+    DrawOut d;
+    d.z = -1;
+    d.s = NAN;
+    if (!fault && mp.ok && !(draft_pos && acc)) {
+      DrawIn din;
+      din.nk = mp.nk;
+      din.cutkey = mp.cutkey;
+      din.zk = Zk;
+      din.mode = draft_pos ? (has_q ? 1 : 2) : 0;
+      din.qrow = qrow;
+      din.cut_q = cut_q;
+      din.T = T;
+      din.rk = Rk;
+      din.y = __builtin_amdgcn_readlane(y, 0);
+      din.us = a.u_sample[i];
+      d = wave_draw(din, (const LDS_AS uint32_t*)sh.skey[0], (const LDS_AS int*)sh.sid[0],
+                    (const LDS_AS double*)sh.pb, (LDS_AS double*)sh.qb);
+    }
+    if (lane == 0) {
+      s.s = d.s;
+      s.flags = acc | (fault << 8);
+      s.draw = d.z;
+      publish(a.stats + row, s);
+    }
   }
 }
 
@@ -1907,8 +2025,7 @@ __global__ __launch_bounds__(kBlock, 3) void row_kernel(Args a) {
   if (!s_last) return;
   // the kernel's only explicit argument sits at the start of its argument
   // segment: the finish reads it from there instead of a private copy
-  finish_request<LT, VEC>((const CONST_AS Args*)__builtin_amdgcn_kernarg_segment_ptr(), i,
-                          (LDS_AS FinShared*)&sh.fin);
+  finish_request<LT, VEC>(a, i, (LDS_AS FinShared*)&sh.fin);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1918,7 +2035,6 @@ __global__ __launch_bounds__(kBlock, 3) void row_kernel(Args a) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t stats_bytes(int N, int G) { return align_up((size_t)N * (G + 1) * sizeof(RowStats), 256); }
-size_t list_bytes(int N, int G) { return align_up((size_t)N * (G + 1) * kLcap * sizeof(ListEntry), 256); }
 size_t done_bytes(int N) { return align_up((size_t)N * sizeof(unsigned int), 256); }
 
 struct DeviceBuffer {
@@ -1997,8 +2113,7 @@ int run(int N, int G, int V, const int32_t* ids, const float* q, const void* log
   a.d_fault = fault;
   char* ws = reinterpret_cast<char*>(workspace);
   a.stats = reinterpret_cast<RowStats*>(ws);
-  a.lists = reinterpret_cast<ListEntry*>(ws + stats_bytes(N, G));
-  a.done = reinterpret_cast<unsigned int*>(ws + stats_bytes(N, G) + list_bytes(N, G));
+  a.done = reinterpret_cast<unsigned int*>(ws + stats_bytes(N, G));
 
   // 16-byte vector loads need every row start aligned: V a multiple of 8 and
   // 16-byte aligned base pointers
@@ -2019,7 +2134,7 @@ extern "C" {
 size_t spec_verify_workspace_size(int N, int gmax, int V) {
   (void)V;
   if (N <= 0 || gmax < 0) return 256;
-  return stats_bytes(N, gmax) + list_bytes(N, gmax) + done_bytes(N);
+  return stats_bytes(N, gmax) + done_bytes(N);
 }
 
 int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* draft_probs, const void* target_logits,

@@ -541,18 +541,19 @@ __device__ inline void raw_get(const LDS_AS F32::Raw* s, F32::Raw& r) { r.a = s-
 // Raise the threshold and keep only the chunks at or above it.  The new
 // threshold T has at least k buffered chunk keys >= T (so it does not exceed
 // the k-th largest chunk key, a lower bound of the wave's k-th largest value)
-// and, unless ties prevent it, at most k + kSlack: bisection on the key bits
+// and, unless ties prevent it, at most k + slack: bisection on the key bits
 // below the common prefix of the smallest and largest key, stopping as soon
 // as the count is within that band.  Plain values in and out, so callers keep
 // their state in registers.
 template <class R>
-__device__ __noinline__ ChunkState chunk_refresh(LDS_AS ChunkBuf<R>* b, ChunkState s, int k) {
+__device__ __noinline__ ChunkState chunk_refresh(LDS_AS ChunkBuf<R>* b, ChunkState s, int k, int slack) {
   // the wave's next loads wait on this: issue ahead of the streaming waves
   __builtin_amdgcn_s_setprio(2);
   const int lane = lane_id();
   s.cnt = uni(s.cnt);
   s.ovf = uni(s.ovf);
   k = uni(k);
+  slack = uni(slack);
   uint32_t key[kCapLane];
   uint32_t kmax = 0u, kmin = 0xffffffffu;
 #pragma unroll
@@ -577,7 +578,7 @@ __device__ __noinline__ ChunkState chunk_refresh(LDS_AS ChunkBuf<R>* b, ChunkSta
       for (int t = 0; t < kCapLane; ++t) c += __popcll(__ballot(key[t] >= T));
       if (c >= k) {
         thr = T;
-        if (c <= k + kSlack) break;
+        if (c <= k + slack) break;
       }
     }
   }
@@ -619,7 +620,7 @@ __device__ inline void chunk_offer(LDS_AS ChunkBuf<R>* b, ChunkState& s, int k, 
   if (!m || s.ovf) return;
   int n = __popcll(m);
   if (s.cnt + n > kCap) {
-    s = chunk_refresh(b, s, k);
+    s = chunk_refresh(b, s, k, kSlack);
     s.cnt = uni(s.cnt);
     s.thr = uni(s.thr);
     s.ovf = uni(s.ovf);
@@ -753,8 +754,8 @@ struct RowShared {
   // the fp64 weights of the tie path and the radix-select histogram
   ChunkBuf<typename LT::Raw> pb[kWaves];
   ChunkBuf<F32::Raw> qb[kWaves];
-  uint32_t skey[2][kWaves * kSeg];   // gathered tokens, one segment per wave
-  int sid[2][kWaves * kSeg];
+  alignas(16) uint32_t skey[2][kWaves * kSeg];   // gathered tokens, one segment per wave
+  alignas(16) int sid[2][kWaves * kSeg];
   int scnt[2][kWaves];
   ChunkState ps[kWaves], qs[kWaves];
   float xm[kWaves];
@@ -790,7 +791,43 @@ union KernelShared {
 // kept set from the candidate buffers (one wave per distribution)
 // ------------------------------------------------------------------------------------------
 
+// Sums over u < n (n a multiple of 8, at most 64) of e[u] where keys[u] >= key
+// (ids[u] <= id for the draw), read from LDS with broadcast vector loads and
+// accumulated in eight independent partial sums; unused slots hold key 0 (id
+// INT_MAX) and weight 0.
+__device__ inline double tree8(const double p[8]) {
+  return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+}
+__device__ inline double lds_sum_key_ge(const LDS_AS uint32_t* keys, const LDS_AS double* e, int n, uint32_t key) {
+  double part[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) part[t] = 0.0;
+  for (int u = 0; u < n; u += 8) {
+    const u32x4 k0 = *(const LDS_AS u32x4*)(keys + u);
+    const u32x4 k1 = *(const LDS_AS u32x4*)(keys + u + 4);
+    const uint32_t kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) part[t] += (kv[t] >= key) ? e[u + t] : 0.0;
+  }
+  return tree8(part);
+}
+__device__ inline double lds_sum_id_le(const LDS_AS int* ids, const LDS_AS double* w, int n, int id) {
+  double part[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) part[t] = 0.0;
+  for (int u = 0; u < n; u += 8) {
+    const u32x4 i0 = *(const LDS_AS u32x4*)(ids + u);
+    const u32x4 i1 = *(const LDS_AS u32x4*)(ids + u + 4);
+    const int iv[8] = {(int)i0.x, (int)i0.y, (int)i0.z, (int)i0.w, (int)i1.x, (int)i1.y, (int)i1.z, (int)i1.w};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) part[t] += (iv[t] <= id) ? w[u + t] : 0.0;
+  }
+  return tree8(part);
+}
+
 struct MergeIn {
+  uint32_t L;         // largest wave threshold: gathered tokens below it are dropped
+  int ovf;            // a wave's buffer overflowed
   int k;
   float top_p;
   int pact;
@@ -854,6 +891,8 @@ template <bool BF16KEYS>
 __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, LDS_AS int* sid, const LDS_AS int* scnt,
                                             LDS_AS double* mmass) {
   const int lane = lane_id();
+  in.L = uni(in.L);
+  in.ovf = uni(in.ovf);
   in.k = uni(in.k);
   in.pact = uni(in.pact);
   in.draft = uni(in.draft);
@@ -867,6 +906,7 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
   out.cut = -INFINITY;
   out.cutkey = 0u;
   out.mass = 0.0;
+  if (in.ovf) return out;
   int segn[kWaves];
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
@@ -882,8 +922,12 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int e = 64 * g + lane;
-      const bool h = e < segn[w];
+      bool h = e < segn[w];
       kk[w * G + g] = h ? skey[w * kSeg + e] : 0u;
+      if (kk[w * G + g] < in.L) {
+        kk[w * G + g] = 0u;
+        h = false;
+      }
       ii[w * G + g] = h ? sid[w * kSeg + e] : 0;
       if (h) {
         kmax = max(kmax, kk[w * G + g]);
@@ -957,31 +1001,20 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
     // one entry per lane
     const bool h = lane < nk;
     const uint32_t key = h ? skey[lane] : 0u;
-    const int id = h ? sid[lane] : -1;
+    const int id = h ? sid[lane] : INT_MAX;
     const double e = h ? merge_weight(in, okey_value(key)) : 0.0;
+    // the 64 slots padded (key 0, id INT_MAX, weight 0) for the LDS sums here
+    // and in the draw
+    wave_lds_sync();
+    skey[lane] = key;
+    sid[lane] = id;
+    mmass[lane] = e;
+    wave_lds_sync();
     const double zk = wave_sum_f64(e);
     double mass = zk;
     if (in.pact) {
       // cum = mass of the entries whose key is >= this lane's key
-      // (eight independent partial sums: the loop is latency-bound)
-      double part[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) part[t] = 0.0;
-      int u = 0;
-      for (; u + 8 <= nk; u += 8) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const uint32_t ku = (uint32_t)__builtin_amdgcn_readlane((int)key, u + t);
-          const double eu = readlane_d(e, u + t);
-          part[t] += (ku >= key) ? eu : 0.0;
-        }
-      }
-      for (; u < nk; ++u) {
-        const uint32_t ku = (uint32_t)__builtin_amdgcn_readlane((int)key, u);
-        const double eu = readlane_d(e, u);
-        part[0] += (ku >= key) ? eu : 0.0;
-      }
-      const double cum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+      const double cum = lds_sum_key_ge(skey, mmass, (nk + 7) & ~7, key);
       const double target = (double)in.top_p * zk;
       const uint32_t best = wave_max_u32((h && cum >= target) ? key : 0u);
       if (best != 0u) {  // else rounding kept the run below target: keep the whole top-k set
@@ -990,7 +1023,6 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
         mass = readlane_d(cum, __ffsll((unsigned long long)at) - 1);
       }
     }
-    if (h) mmass[lane] = e;
     out.mass = mass;
   } else {
     // many values tied at the k-th largest: weights in LDS, quadratic top-p
@@ -1087,7 +1119,7 @@ __device__ __noinline__ DrawOut wave_draw(DrawIn in, const LDS_AS uint32_t* skey
   if (in.nk <= 64) {
     const bool h = lane < in.nk;
     const bool keep = h && skey[lane] >= in.cutkey;
-    const int id = h ? sid[lane] : 0;
+    const int id = sid[lane];
     double p;
     double w = weight(keep, id, h ? ke[lane] : 0.0, p);
     double S = wave_sum_f64(w);
@@ -1096,25 +1128,10 @@ __device__ __noinline__ DrawOut wave_draw(DrawIn in, const LDS_AS uint32_t* skey
       S = wave_sum_f64(p);
     }
     const double tau = (double)in.us * S;
-    // running sum at this lane's id (eight independent partial sums)
-    double part[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) part[t] = 0.0;
-    int u = 0;
-    for (; u + 8 <= in.nk; u += 8) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int iu = __builtin_amdgcn_readlane(id, u + t);
-        const double wu = readlane_d(w, u + t);
-        part[t] += (iu <= id) ? wu : 0.0;
-      }
-    }
-    for (; u < in.nk; ++u) {
-      const int iu = __builtin_amdgcn_readlane(id, u);
-      const double wu = readlane_d(w, u);
-      part[0] += (iu <= id) ? wu : 0.0;
-    }
-    const double cum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+    // running sum at this lane's id (the 64 id slots are padded with INT_MAX)
+    wbuf[lane] = w;
+    wave_lds_sync();
+    const double cum = lds_sum_id_le(sid, wbuf, (in.nk + 7) & ~7, id);
     if (w > 0.0) {
       if (cum > tau) best = (uint32_t)id;
       last = (uint32_t)id + 1u;
@@ -1779,10 +1796,24 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
     if (qm == 0) stream_stochastic<LT, VEC, 0, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
     else if (qm == 1) stream_stochastic<LT, VEC, 1, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
     else stream_stochastic<LT, VEC, 2, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
-    // each wave cuts its own buffers down to its k-th largest key
-    if (st.ps.cnt > rq.k && !st.ps.ovf) st.ps = chunk_refresh((LDS_AS ChunkBuf<typename LT::Raw>*)&sh.pb[wave], st.ps, rq.k);
+    // each wave cuts its own buffers down to its k-th largest chunk key and
+    // copies the tokens at or above that threshold into its segment
+    __builtin_amdgcn_s_setprio(2);
+    if (st.ps.cnt > rq.k && !st.ps.ovf)
+      st.ps = chunk_refresh((LDS_AS ChunkBuf<typename LT::Raw>*)&sh.pb[wave], st.ps, rq.k, 0);
     if (has_q && st.qs.cnt > rq.k && !st.qs.ovf)
-      st.qs = chunk_refresh((LDS_AS ChunkBuf<F32::Raw>*)&sh.qb[wave], st.qs, rq.k);
+      st.qs = chunk_refresh((LDS_AS ChunkBuf<F32::Raw>*)&sh.qb[wave], st.qs, rq.k, 0);
+    __builtin_amdgcn_s_setprio(2);
+    int n = st.ps.ovf ? kSeg + 1
+                      : gather_tokens((const LDS_AS ChunkBuf<typename LT::Raw>*)&sh.pb[wave], st.ps.cnt, st.ps.thr, V,
+                                      (LDS_AS uint32_t*)&sh.skey[0][wave * kSeg], (LDS_AS int*)&sh.sid[0][wave * kSeg]);
+    if (lane == 0) sh.scnt[0][wave] = n;
+    if (has_q) {
+      n = st.qs.ovf ? kSeg + 1
+                    : gather_tokens((const LDS_AS ChunkBuf<F32::Raw>*)&sh.qb[wave], st.qs.cnt, st.qs.thr, V,
+                                    (LDS_AS uint32_t*)&sh.skey[1][wave * kSeg], (LDS_AS int*)&sh.sid[1][wave * kSeg]);
+      if (lane == 0) sh.scnt[1][wave] = n;
+    }
   } else {
     if (qm == 0) stream_stochastic<LT, VEC, 0, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
     else if (qm == 1) stream_stochastic<LT, VEC, 1, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
@@ -1813,38 +1844,49 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   const uint32_t qb = max(max(sh.xqb[0], sh.xqb[1]), max(sh.xqb[2], sh.xqb[3]));
   const uint32_t lb = max(max(sh.xlb[0], sh.xlb[1]), max(sh.xlb[2], sh.xlb[3]));
   if (cand) {
-    // each wave gathers the tokens of its own chunks that reach the largest
-    // wave threshold (an overflowed buffer marks the distribution undecided)
-    uint32_t L = 0u;
-    int ovf = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      L = max(L, sh.ps[w].thr);
-      ovf |= sh.ps[w].ovf;
-    }
-    int n = ovf ? kSeg + 1
-                : gather_tokens((const LDS_AS ChunkBuf<typename LT::Raw>*)&sh.pb[wave], st.ps.cnt, L, V,
-                                (LDS_AS uint32_t*)&sh.skey[0][wave * kSeg], (LDS_AS int*)&sh.sid[0][wave * kSeg]);
-    if (lane == 0) sh.scnt[0][wave] = n;
-    if (has_q) {
-      L = 0u;
-      ovf = 0;
-      for (int w = 0; w < kWaves; ++w) {
-        L = max(L, sh.qs[w].thr);
-        ovf |= sh.qs[w].ovf;
+    // a segment that overflowed is gathered again with the largest wave
+    // threshold, which keeps far fewer tokens
+    const bool p_over = (sh.scnt[0][0] > kSeg) | (sh.scnt[0][1] > kSeg) | (sh.scnt[0][2] > kSeg) | (sh.scnt[0][3] > kSeg);
+    const bool q_over = has_q && ((sh.scnt[1][0] > kSeg) | (sh.scnt[1][1] > kSeg) | (sh.scnt[1][2] > kSeg) |
+                                  (sh.scnt[1][3] > kSeg));
+    if (p_over || q_over) {
+      const int np = sh.scnt[0][wave], nq = has_q ? sh.scnt[1][wave] : 0;
+      __syncthreads();
+      if (np > kSeg) {
+        uint32_t L = 0u;
+        int ovf = 0;
+        for (int w = 0; w < kWaves; ++w) {
+          L = max(L, sh.ps[w].thr);
+          ovf |= sh.ps[w].ovf;
+        }
+        const int n = ovf ? kSeg + 1
+                          : gather_tokens((const LDS_AS ChunkBuf<typename LT::Raw>*)&sh.pb[wave], st.ps.cnt, L, V,
+                                          (LDS_AS uint32_t*)&sh.skey[0][wave * kSeg], (LDS_AS int*)&sh.sid[0][wave * kSeg]);
+        if (lane == 0) sh.scnt[0][wave] = n;
       }
-      n = ovf ? kSeg + 1
-              : gather_tokens((const LDS_AS ChunkBuf<F32::Raw>*)&sh.qb[wave], st.qs.cnt, L, V,
-                              (LDS_AS uint32_t*)&sh.skey[1][wave * kSeg], (LDS_AS int*)&sh.sid[1][wave * kSeg]);
-      if (lane == 0) sh.scnt[1][wave] = n;
+      if (nq > kSeg) {
+        uint32_t L = 0u;
+        int ovf = 0;
+        for (int w = 0; w < kWaves; ++w) {
+          L = max(L, sh.qs[w].thr);
+          ovf |= sh.qs[w].ovf;
+        }
+        const int n = ovf ? kSeg + 1
+                          : gather_tokens((const LDS_AS ChunkBuf<F32::Raw>*)&sh.qb[wave], st.qs.cnt, L, V,
+                                          (LDS_AS uint32_t*)&sh.skey[1][wave * kSeg], (LDS_AS int*)&sh.sid[1][wave * kSeg]);
+        if (lane == 0) sh.scnt[1][wave] = n;
+      }
+      __syncthreads();
     }
   }
+  // without top-k: Z = sum over the row; with it the kept mass is found below
+  double Z = 1.0;
   if (!cand) {
     const double zw = wave_sum_f64(st.z * exp2(((double)st.m - (double)m) * (double)c));
     if (lane == 0) sh.xz[wave] = zw;
+    __syncthreads();
+    Z = (sh.xz[0] + sh.xz[1]) + (sh.xz[2] + sh.xz[3]);
   }
-  __syncthreads();
-  // without top-k: Z = sum over the row; with it the kept mass is found below
-  const double Z = cand ? 1.0 : (sh.xz[0] + sh.xz[1]) + (sh.xz[2] + sh.xz[3]);
   int fault = 0;
   if (cand ? (lb > 0x7f800000u || !isfinite(m)) : (!(Z > 0.0) || isinf(Z))) fault |= kFaultTargetRow;
   if (has_q && qb >= 0x7f800000u) fault |= kFaultDraftRow;
@@ -1860,6 +1902,13 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       if (wave < (has_q ? 2 : 1)) {
         const int d = wave;
         MergeIn in;
+        in.L = 0u;
+        in.ovf = 0;
+        for (int w = 0; w < kWaves; ++w) {
+          const ChunkState cs = d == 0 ? sh.ps[w] : sh.qs[w];
+          in.L = max(in.L, cs.thr);
+          in.ovf |= cs.ovf;
+        }
         in.k = rq.k;
         in.top_p = rq.p;
         in.pact = rq.pact;

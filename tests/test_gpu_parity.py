@@ -250,6 +250,33 @@ def test_special_rows():
     parity(b, "special rows")
 
 
+def test_top_k_candidates_clustered_in_one_wave():
+    """Rows whose values rise smoothly across the tokens one wave of the
+    workgroup streams (so nearly every token of that wave's best chunks passes
+    its own threshold), while the true top-k values sit in another wave's
+    tokens: the kept set must still be exact."""
+    V = 32000
+    rng = np.random.default_rng(21)
+    ids = np.arange(V)
+    wave = (ids % 2048) // 512
+    reqs = []
+    for r in range(3):
+        rows_l, rows_q = [], []
+        for j in range(3):
+            l = rng.standard_normal(V) * 0.5
+            l[wave == 0] = 3.0 + 1e-4 * ids[wave == 0]
+            spikes = rng.choice(np.flatnonzero(wave == 1), 80, replace=False)
+            l[spikes] = 10.0 + rng.standard_normal(80)
+            rows_l.append(l.astype(np.float32))
+            d = l + 0.3 * rng.standard_normal(V)
+            e = np.exp(d - d.max())
+            rows_q.append((e / e.sum()).astype(np.float32))
+        y = [int(np.argmax(rows_q[0])), int(rng.choice(np.flatnonzero(wave == 0)))]
+        reqs.append(one_request(y, np.stack(rows_q[:2]), np.stack(rows_l), k=50, p=0.9,
+                                ua=rng.uniform(size=2), us=float(rng.uniform())))
+    parity(stack(reqs), "top-k candidates clustered in one wave")
+
+
 # ------------------------------------------------------------------------------------------
 # full workloads, launched exactly as the benchmark does, sampled requests checked
 # ------------------------------------------------------------------------------------------

@@ -798,6 +798,19 @@ union KernelShared {
 __device__ inline double tree8(const double p[8]) {
   return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
+// Eight weights of one group, loaded unconditionally (an empty asm pins the
+// loads, which the compiler would otherwise turn into masked per-lane loads
+// under the select).
+__device__ inline void lds_load8_f64(const LDS_AS double* e, double ev[8]) {
+  typedef double f64x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    f64x2 x = *(const LDS_AS f64x2*)(e + 2 * h);
+    asm volatile("" : "+v"(x));
+    ev[2 * h] = x.x;
+    ev[2 * h + 1] = x.y;
+  }
+}
 __device__ inline double lds_sum_key_ge(const LDS_AS uint32_t* keys, const LDS_AS double* e, int n, uint32_t key) {
   double part[8];
 #pragma unroll
@@ -805,9 +818,11 @@ __device__ inline double lds_sum_key_ge(const LDS_AS uint32_t* keys, const LDS_A
   for (int u = 0; u < n; u += 8) {
     const u32x4 k0 = *(const LDS_AS u32x4*)(keys + u);
     const u32x4 k1 = *(const LDS_AS u32x4*)(keys + u + 4);
+    double ev[8];
+    lds_load8_f64(e + u, ev);
     const uint32_t kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) part[t] += (kv[t] >= key) ? e[u + t] : 0.0;
+    for (int t = 0; t < 8; ++t) part[t] += (kv[t] >= key) ? ev[t] : 0.0;
   }
   return tree8(part);
 }
@@ -818,9 +833,11 @@ __device__ inline double lds_sum_id_le(const LDS_AS int* ids, const LDS_AS doubl
   for (int u = 0; u < n; u += 8) {
     const u32x4 i0 = *(const LDS_AS u32x4*)(ids + u);
     const u32x4 i1 = *(const LDS_AS u32x4*)(ids + u + 4);
+    double wv[8];
+    lds_load8_f64(w + u, wv);
     const int iv[8] = {(int)i0.x, (int)i0.y, (int)i0.z, (int)i0.w, (int)i1.x, (int)i1.y, (int)i1.z, (int)i1.w};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) part[t] += (iv[t] <= id) ? w[u + t] : 0.0;
+    for (int t = 0; t < 8; ++t) part[t] += (iv[t] <= id) ? wv[t] : 0.0;
   }
   return tree8(part);
 }
@@ -1364,7 +1381,7 @@ __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, co
   // full steps (every lane's 8 tokens inside the row, vector loads only)
   const int nfull = VEC ? V / kStep : 0;
   const int base0 = tid * kCh;
-  ring_stream<QM ? 4 : 8, StepRaw<LR>>(
+  ring_stream<QM ? 5 : 10, StepRaw<LR>>(
       nfull,
       [&](int s) {
         StepRaw<LR> r;

@@ -397,6 +397,21 @@ __device__ inline double wave_sum_f64(double v) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// Inclusive prefix sum over a full wave (row shifts, then row broadcasts).
+template <int CTRL, int ROWS>
+__device__ inline int dpp_src0(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+__device__ inline int wave_incl_scan_i32(int v) {
+  v += dpp_src0<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_src0<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_src0<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_src0<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_src0<0x142, 0xA>(v);  // row_bcast:15
+  v += dpp_src0<0x143, 0xC>(v);  // row_bcast:31
+  return v;
+}
+
 __device__ inline double readlane_d(double v, int l) {
   const uint64_t b = (uint64_t)__double_as_longlong(v);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
@@ -966,25 +981,55 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
     return c[0];
   };
   // The top-k set is {key >= K} for the k-th largest key K (ties included).
-  // Bisection keeps count(>= K) >= k; once exactly k keys reach K the set is
-  // already that top-k set, and K is replaced by its smallest key below.
+  // K is decided 8 bits at a time below the common prefix of the gathered
+  // keys: an LDS histogram of the next digit over the keys that share the
+  // decided prefix, then the largest digit whose keys, with all larger ones,
+  // number at least k.  Once exactly k keys reach the decided prefix they are
+  // the top-k set, and K is replaced by their smallest key below.
   uint32_t K = kmin;
   if (kmin != kmax) {
+    LDS_AS int* hist = (LDS_AS int*)mmass;  // 256 bins; the weights come later
     const int top = 31 - __clz((int)(kmin ^ kmax));
-    K = kmin & ~((2u << top) - 1u);
+    uint32_t P = kmin & ~((2u << top) - 1u);
+    int above = 0;  // keys whose decided bits exceed P's
+    int hi = top;
+    constexpr int lo = BF16KEYS ? 16 : 0;  // bf16 keys end in 16 equal bits
     bool exact = false;
-    for (int bit = top; bit >= (BF16KEYS ? 16 : 0); --bit) {
-      const uint32_t T = K | (1u << bit);
-      const int c = count_ge(T);
-      if (c >= in.k) {
-        K = T;
-        if (c == in.k) {
-          exact = true;
-          break;
-        }
+    while (hi >= lo) {
+      const int d = min(8, hi - lo + 1);
+      const int sh = hi - d + 1;
+      const uint32_t dmask = (1u << d) - 1u;
+      *(LDS_AS u32x4*)(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+      wave_lds_sync();
+#pragma unroll
+      for (int t = 0; t < kWaves * G; ++t) {
+        const uint32_t x = kk[t];
+        const bool match = x != 0u && (hi == 31 || ((x ^ P) >> (hi + 1)) == 0u);
+        if (match) __hip_atomic_fetch_add(hist + ((x >> sh) & dmask), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      wave_lds_sync();
+      const u32x4 b = *(const LDS_AS u32x4*)(hist + 4 * lane);
+      const int S = wave_incl_scan_i32((int)(b.x + b.y + b.z + b.w));
+      const int T = __builtin_amdgcn_readlane(S, 63);
+      // keys with digit >= 4 * lane + i
+      const int s3 = T - S + (int)b.w, s2 = s3 + (int)b.z, s1 = s2 + (int)b.y, s0 = s1 + (int)b.x;
+      const int Ls = 63 - __clzll((long long)__ballot(above + s0 >= in.k));  // lane 0 always qualifies
+      const int pick = (above + s3 >= in.k) ? 3 : (above + s2 >= in.k) ? 2 : (above + s1 >= in.k) ? 1 : 0;
+      const int sp = pick == 3 ? s3 : pick == 2 ? s2 : pick == 1 ? s1 : s0;
+      const int bp = (int)(pick == 3 ? b.w : pick == 2 ? b.z : pick == 1 ? b.y : b.x);
+      const int D = 4 * Ls + __builtin_amdgcn_readlane(pick, Ls);
+      const int cge = above + __builtin_amdgcn_readlane(sp, Ls);  // keys >= the new prefix
+      P |= (uint32_t)D << sh;
+      above = cge - __builtin_amdgcn_readlane(bp, Ls);
+      hi = sh - 1;
+      wave_lds_sync();
+      if (cge == in.k) {
+        exact = true;
+        break;
       }
     }
-    if (BF16KEYS && !exact && count_ge(K | 0xffffu) >= in.k) K |= 0xffffu;
+    if (BF16KEYS && !exact && count_ge(P | 0xffffu) >= in.k) P |= 0xffffu;
+    K = P;
   }
   {
     uint32_t kmin2 = 0xffffffffu;

@@ -124,9 +124,10 @@ int spec_verify_diag(int N, int gmax, int V, const int32_t *draft_ids, const flo
 /*
  * spec_verify_diag plus three optional hipEvent_t handles (created by the
  * caller, may be NULL) that are recorded on `stream`: ev_start before the
- * row pass, ev_mid between the row pass and the per-request finish, ev_end
- * after it.  For timing the two phases; results are identical to
- * spec_verify_diag.
+ * row pass (which ends with each request's accept scan and, where the draw
+ * row kept a top-k set, the draw), ev_mid after it, ev_end after the draw
+ * pass that re-reads the draw row of the remaining sampled requests.  For
+ * timing the two phases; results are identical to spec_verify_diag.
  */
 int spec_verify_timed(int N, int gmax, int V, const int32_t *draft_ids, const float *draft_probs,
                       const void *target_logits, int logits_dtype, const float *temperature,

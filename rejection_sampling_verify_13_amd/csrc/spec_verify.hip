@@ -61,7 +61,7 @@ constexpr int kCap = 160;               // buffered candidate chunks per wave an
 constexpr int kKFast = 64;              // largest top_k served by the candidate buffers
 constexpr int kSeg = 128;               // gathered candidate tokens per wave and distribution (LDS)
 constexpr int kMerge = kWaves * kSeg;   // gathered candidate tokens of one distribution
-constexpr int kMaxChunks = 512;         // chunk sums held by the draw
+constexpr int kDrawSteps = 4;           // draw pass: 2048-token steps per workgroup
 constexpr int kMaxGamma = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -90,6 +90,24 @@ struct RowStats {
 };
 static_assert(sizeof(RowStats) == 64, "RowStats layout");
 
+// A request whose draw is left to draw_kernel (row A had no kept list in LDS).
+struct DrawRec {
+  int need;       // 1: draw_kernel draws out_tokens[i, A]
+  int A;          // the draw row
+  int mode;       // 0: p'; 1: max(0, p' - q'); 2: p' with the draft token removed
+  int yA;         // mode 2: the draft token at row A
+};
+
+// Sums of one 512-token block (one wave's tokens of one step) of row A.
+struct DrawSum {
+  double sw;      // sum of the draw weights w
+  double sp;      // sum of p' (the weights if w sums to zero)
+  int lastw;      // largest id with w > 0, plus one (0: none)
+  int lastp;      // largest id with p' > 0, plus one
+  int pad[2];
+};
+static_assert(sizeof(DrawSum) == 32, "DrawSum layout");
+
 struct Args {
   int N, G, V;
   const int32_t* ids;
@@ -107,7 +125,12 @@ struct Args {
   double* d_resid;
   int32_t* d_fault;
   RowStats* stats;
-  unsigned int* done;   // completion counter per request
+  unsigned int* done;   // completion counter per request (row pass)
+  DrawRec* drec;        // per request
+  DrawSum* dsum;        // [N][steps][kWaves]
+  unsigned int* ddone;  // completion counter per request (draw pass)
+  int dspw;             // draw pass: steps per workgroup
+  int dparts;           // draw pass: workgroups per request
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -788,7 +811,6 @@ struct RowShared {
 };
 
 struct FinShared {
-  double wsum[kWaves][kMaxChunks];
   RowStats sa;
   double red_d[kWaves];
   int red_i[kWaves];
@@ -1504,183 +1526,6 @@ __device__ inline void step_weights(const float lv[8], const float qv[8], int ba
   }
 }
 
-// Draw from row A by two passes over it (rows without a top-k set in LDS):
-// chunk sums of the draw weights, then the crossing chunk.  Out of line: its
-// registers are not part of the common path.
-template <class LT, bool VEC>
-__device__ __noinline__ DrawOut draw_two_pass(const CONST_AS Args* ap, int i, int A, int gamma, float T, float sa_m,
-                                              float sa_cut_p, float sa_cut_q, double sa_z, double sa_r,
-                                              LDS_AS FinShared* sh) {
-  Args a;
-  __builtin_memcpy(&a, (const Args*)ap, sizeof(Args));
-  i = uni(i);
-  a.N = uni(a.N);
-  a.G = uni(a.G);
-  a.V = uni(a.V);
-  a.ids = uni(a.ids);
-  a.q = uni(a.q);
-  a.logits = uni(a.logits);
-  a.temperature = uni(a.temperature);
-  a.top_k = uni(a.top_k);
-  a.top_p = uni(a.top_p);
-  a.u_accept = uni(a.u_accept);
-  a.u_sample = uni(a.u_sample);
-  a.out_tokens = uni(a.out_tokens);
-  a.out_num = uni(a.out_num);
-  a.d_py = uni(a.d_py);
-  a.d_qy = uni(a.d_qy);
-  a.d_resid = uni(a.d_resid);
-  a.d_fault = uni(a.d_fault);
-  a.stats = uni(a.stats);
-  A = uni(A);
-  gamma = uni(gamma);
-  T = uni(T);
-  typedef typename LT::T ET;
-  typedef typename LT::Raw LR;
-  const int G = a.G, V = a.V;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  struct {
-    float m, cut_p, cut_q;
-    double z, r;
-  } sa = {uni(sa_m), uni(sa_cut_p), uni(sa_cut_q), uni(sa_z), uni(sa_r)};
-  int z = -1;
-  double S_out = NAN;
-  const bool resid = A < gamma;
-  const int yA = resid ? a.ids[(size_t)i * G + A] : -1;
-  int mode = resid ? (a.q ? 1 : 2) : 0;
-  const size_t row = (size_t)i * (G + 1) + A;
-  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + row * (size_t)V;
-  const float* qrow = (mode == 1) ? a.q + ((size_t)i * G + A) * (size_t)V : nullptr;
-  const double us = (double)a.u_sample[i];
-  {
-    // ---- two passes over row A ----
-    const float m = sa.m, c = kLog2e / T, invT = 1.f / T;
-    const bool temper = T != 1.f;
-    const float invZ = (float)(1.0 / sa.z);
-    const float invR = (mode == 1) ? (float)(1.0 / sa.r) : 0.f;
-    const int nsteps = (V + kStep - 1) / kStep;
-    const int spc = (nsteps + kMaxChunks - 1) / kMaxChunks;  // steps per chunk
-    const int nch = (nsteps + spc - 1) / spc;
-    double S = 0.0;
-    int last = -1;
-    for (int attempt = 0; attempt < 2; ++attempt) {
-      last = -1;
-      double csum = 0.0;
-      auto step = [&](const LR& lr, const F32::Raw& qr, int base, int s) {
-        float lv[8], qv[8], w[8];
-        LT::unpack(lr, lv);
-        F32::unpack(qr, qv);
-        step_weights(lv, qv, base, mode, m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w);
-        double ts = 0.0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          ts += (double)w[e];
-          if (w[e] > 0.f) last = base + e;
-        }
-        csum += wave_sum_d(ts);
-        if ((s + 1) % spc == 0 || s + 1 == nsteps) {
-          if (lane == 0) sh->wsum[wave][s / spc] = csum;
-          csum = 0.0;
-        }
-      };
-      const int nfull = VEC ? V / kStep : 0;
-      const int base0 = tid * kCh;
-      ring_stream<4, StepRaw<LR>>(
-          nfull,
-          [&](int s) {
-            StepRaw<LR> r;
-            r.l = LT::load(lrow + base0 + s * kStep);
-            r.q = F32::Raw{};
-            if (mode == 1) r.q = F32::load(qrow + base0 + s * kStep);
-            return r;
-          },
-          [&](const StepRaw<LR>& r, int s) { step(r.l, r.q, base0 + s * kStep, s); });
-      int base = base0 + nfull * kStep;
-      for (int s = nfull; s < nsteps; ++s) {
-        step(load_logits<LT, VEC>(lrow, base, V), mode == 1 ? load_probs<VEC>(qrow, base, V) : F32::Raw{}, base, s);
-        base += kStep;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        double tot = 0.0;
-        for (int ch = 0; ch < nch; ++ch) tot += ((sh->wsum[0][ch] + sh->wsum[1][ch]) + (sh->wsum[2][ch] + sh->wsum[3][ch]));
-        sh->miscd[0] = tot;
-      }
-      __syncthreads();
-      S = sh->miscd[0];
-      __syncthreads();
-      if (S > 0.0 || mode == 0) break;
-      mode = 0;  // zero residual: draw from p'
-    }
-    last = block_max_i(last, (int*)sh->red_i);
-    const double tau = us * S;
-    // the chunk holding the crossing (serial over at most kMaxChunks totals)
-    if (tid == 0) {
-      double pre = 0.0;
-      int found = -1;
-      for (int ch = 0; ch < nch; ++ch) {
-        const double cs = (sh->wsum[0][ch] + sh->wsum[1][ch]) + (sh->wsum[2][ch] + sh->wsum[3][ch]);
-        if (pre + cs > tau && cs > 0.0) {
-          found = ch;
-          break;
-        }
-        pre += cs;
-      }
-      sh->misc[2] = found;
-      sh->miscd[1] = pre;
-    }
-    __syncthreads();
-    const int found = sh->misc[2];
-    double pre = sh->miscd[1];
-    __syncthreads();
-    if (found < 0) {
-      z = last;
-    } else {
-      // walk the steps of the chunk in token order; the crossing is in the
-      // last run (thread, step) whose starting prefix is <= tau
-      int bestkey = -1, bestz = -1;
-      for (int s = found * spc; s < min(nsteps, (found + 1) * spc); ++s) {
-        const int base = s * kStep + tid * kCh;
-        float lv[8], qv[8], w[8];
-        LT::unpack(load_logits<LT, VEC>(lrow, min(base, V), V), lv);
-        F32::unpack(mode == 1 ? load_probs<VEC>(qrow, min(base, V), V) : F32::Raw{}, qv);
-        step_weights(lv, qv, base, mode, m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w);
-        double ts = 0.0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ts += (double)w[e];
-        double total;
-        const double ex = pre + block_exscan_d(ts, (double*)sh->red_d, &total);
-        if (ts > 0.0 && ex <= tau) {
-          double acc = ex;
-          int zz = -1, lastpos = -1;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (w[e] > 0.f) lastpos = base + e;
-            acc += (double)w[e];
-            if (zz < 0 && w[e] > 0.f && acc > tau) zz = base + e;
-          }
-          bestkey = (s - found * spc) * kBlock + tid;
-          bestz = zz >= 0 ? zz : lastpos;
-        }
-        pre += total;
-      }
-      const int win = block_max_i(bestkey, (int*)sh->red_i);
-      if (tid == 0) sh->misc[3] = -1;
-      __syncthreads();
-      if (win >= 0 && bestkey == win) sh->misc[3] = bestz;
-      __syncthreads();
-      z = sh->misc[3];
-      if (z < 0) z = last;
-    }
-    S_out = S;
-  }
-  DrawOut d;
-  d.z = z;
-  d.s = S_out;
-  d.pad = 0;
-  return d;
-}
-
 template <class LT, bool VEC>
 __device__ __forceinline__ void finish_request(const Args& a, int i, LDS_AS FinShared* sh) {
   typedef typename LT::T ET;
@@ -1730,6 +1575,7 @@ __device__ __forceinline__ void finish_request(const Args& a, int i, LDS_AS FinS
   if (fault) {
     for (int t = tid; t <= G; t += kBlock) out[t] = -1;
     if (tid == 0) {
+      a.drec[i] = DrawRec{0, 0, 0, -1};
       a.out_num[i] = -1;
       if (a.d_fault) a.d_fault[i] = fault;
       if (a.d_resid) a.d_resid[i] = NAN;
@@ -1743,8 +1589,9 @@ __device__ __forceinline__ void finish_request(const Args& a, int i, LDS_AS FinS
 
   RowStats sa;
   __builtin_memcpy(&sa, (const RowStats*)&sh->sa, sizeof(RowStats));
-  int z;
+  int z = -1;
   double S_out = NAN;
+  bool defer = false;
   if (rq.greedy) {
     z = sa.argmax;
   } else if (sa.draw >= 0) {
@@ -1752,23 +1599,22 @@ __device__ __forceinline__ void finish_request(const Args& a, int i, LDS_AS FinS
     z = sa.draw;
     S_out = sa.s;
   } else {
-    // row A had no top-k set in LDS: two passes over it here
-    const DrawOut d = draw_two_pass<LT, VEC>((const CONST_AS Args*)__builtin_amdgcn_kernarg_segment_ptr(), i, A,
-                                             rq.gamma, rq.T, sa.m, sa.cut_p, sa.cut_q, sa.z, sa.r, sh);
-    z = d.z;
-    S_out = d.s;
+    // row A had no top-k set in LDS: draw_kernel re-reads it
+    defer = true;
   }
 
   for (int t = tid; t <= G; t += kBlock) {
     int v = -1;
     if (t < A) v = a.ids[(size_t)i * G + t];
     else if (t == A) v = z;
-    out[t] = v;
+    if (!(defer && t == A)) out[t] = v;
   }
   if (tid == 0) {
+    const bool resid = A < rq.gamma;
+    a.drec[i] = DrawRec{defer ? 1 : 0, A, resid ? (a.q ? 1 : 2) : 0, resid ? a.ids[(size_t)i * G + A] : -1};
     a.out_num[i] = A;
     if (a.d_fault) a.d_fault[i] = 0;
-    if (a.d_resid) a.d_resid[i] = S_out;
+    if (a.d_resid && !defer) a.d_resid[i] = S_out;
   }
 }
 
@@ -2103,9 +1949,12 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
 // kernels
 // ------------------------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kBlock) void clear_kernel(unsigned int* done, int N) {
+__global__ __launch_bounds__(kBlock) void clear_kernel(unsigned int* done, unsigned int* ddone, int N) {
   const int i = blockIdx.x * kBlock + threadIdx.x;
-  if (i < N) done[i] = 0u;
+  if (i < N) {
+    done[i] = 0u;
+    ddone[i] = 0u;
+  }
 }
 
 template <class LT, bool VEC>
@@ -2140,6 +1989,175 @@ __global__ __launch_bounds__(kBlock, 3) void row_kernel(Args a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// draw pass: requests whose draw row had no kept list in LDS
+// ------------------------------------------------------------------------------------------
+
+// Inclusive prefix sum of doubles over a full wave.
+__device__ inline double wave_incl_scan_f64(double v) {
+  v += dpp_add_src<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_add_src<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_add_src<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_add_src<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_add_src<0x142, 0xA>(v);  // row_bcast:15
+  v += dpp_add_src<0x143, 0xC>(v);  // row_bcast:31
+  return v;
+}
+
+// Draw weights w (mode 0: p'; 1: max(0, p' - q'); 2: p' with the draft
+// token removed) and p' of one lane's 8 tokens; tokens past the row end read
+// as -inf logits and zero probabilities, so both are zero there.
+__device__ inline void draw_weights(const float lv[8], const float qv[8], int base, int mode, float m, float c,
+                                    float invZ, float cut_p, float cut_q, float invR, float invT, bool temper, int yA,
+                                    float w[8], float p[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = (lv[e] >= cut_p) ? fast_exp2((lv[e] - m) * c) * invZ : 0.f;
+    float x = p[e];
+    if (mode == 1) {
+      const float r = temper ? fast_exp2(fast_log2(qv[e]) * invT) : qv[e];
+      const float q = (qv[e] >= cut_q) ? r * invR : 0.f;
+      x = __builtin_fmaxf(p[e] - q, 0.f);
+    } else if (mode == 2) {
+      x = (base + e == yA) ? 0.f : p[e];
+    }
+    w[e] = x;
+  }
+}
+
+// Grid: dparts workgroups per request, each summing the draw weights of
+// kDrawSteps steps of row A per 512-token block (one wave's tokens of one
+// step); the last workgroup of the request scans the block sums in token
+// order, re-reads the block where the running sum first exceeds u * S and
+// finds the token there (inverse CDF over ascending id; if the weights sum to
+// zero, over p'; if rounding leaves no crossing, the largest id with w > 0).
+template <class LT, bool VEC>
+__global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
+  typedef typename LT::T ET;
+  __shared__ int s_last;
+  const int i = blockIdx.x / a.dparts, part = blockIdx.x - i * a.dparts;
+  const DrawRec dr = a.drec[i];
+  if (!dr.need) return;
+  const int G = a.G, V = a.V;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int A = dr.A, mode = dr.mode, yA = dr.yA;
+  const size_t row = (size_t)i * (G + 1) + A;
+  const RowStats sa = a.stats[row];
+  const float T = a.temperature ? a.temperature[i] : 1.f;
+  const float c = kLog2e / T, invT = 1.f / T;
+  const bool temper = T != 1.f;
+  const float invZ = (float)(1.0 / sa.z);
+  const float invR = (mode == 1) ? (float)(1.0 / sa.r) : 0.f;
+  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + row * (size_t)V;
+  const float* qrow = (mode == 1) ? a.q + ((size_t)i * G + A) * (size_t)V : nullptr;
+  const int nsteps = (V + kStep - 1) / kStep;
+  DrawSum* ds = a.dsum + (size_t)i * nsteps * kWaves;
+  const int s0 = part * a.dspw, s1 = min(nsteps, s0 + a.dspw);
+  for (int s = s0; s < s1; ++s) {
+    const int base = s * kStep + tid * kCh;
+    float lv[8], qv[8], w[8], pw[8];
+    LT::unpack(load_logits<LT, VEC>(lrow, base, V), lv);
+    if (mode == 1) F32::unpack(load_probs<VEC>(qrow, base, V), qv);
+    else
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = 0.f;
+    draw_weights(lv, qv, base, mode, sa.m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w, pw);
+    double sw = 0.0, sp = 0.0;
+    uint32_t lw = 0u, lp = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sw += (double)w[e];
+      sp += (double)pw[e];
+      if (w[e] > 0.f) lw = (uint32_t)(base + e + 1);
+      if (pw[e] > 0.f) lp = (uint32_t)(base + e + 1);
+    }
+    DrawSum d;
+    d.sw = wave_sum_f64(sw);
+    d.sp = wave_sum_f64(sp);
+    d.lastw = (int)wave_max_u32(lw);
+    d.lastp = (int)wave_max_u32(lp);
+    d.pad[0] = d.pad[1] = 0;
+    if (lane == 0) publish(ds + (size_t)s * kWaves + wave, d);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = (__hip_atomic_fetch_add(&a.ddone[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (unsigned int)(a.dparts - 1));
+  __syncthreads();
+  if (!s_last || wave != 0) return;
+
+  const int nrec = nsteps * kWaves;
+  double tw = 0.0, tp = 0.0;
+  uint32_t lastw = 0u, lastp = 0u;
+  for (int r0 = 0; r0 < nrec; r0 += 64) {
+    DrawSum d{};
+    if (r0 + lane < nrec) d = fetch(ds + r0 + lane);
+    tw += d.sw;
+    tp += d.sp;
+    lastw = max(lastw, (uint32_t)d.lastw);
+    lastp = max(lastp, (uint32_t)d.lastp);
+  }
+  tw = wave_sum_f64(tw);
+  tp = wave_sum_f64(tp);
+  lastw = wave_max_u32(lastw);
+  lastp = wave_max_u32(lastp);
+  const bool usep = !(tw > 0.0);  // zero residual: draw from p'
+  const double S = usep ? tp : tw;
+  const int dmode = usep ? 0 : mode;
+  const double tau = (double)a.u_sample[i] * S;
+  // the first block whose running sum exceeds tau
+  double pre = 0.0, pstar = 0.0;
+  int rstar = -1;
+  for (int r0 = 0; r0 < nrec; r0 += 64) {
+    double x = 0.0;
+    if (r0 + lane < nrec) {
+      const DrawSum d = fetch(ds + r0 + lane);
+      x = usep ? d.sp : d.sw;
+    }
+    const double incl = wave_incl_scan_f64(x);
+    const uint64_t hit = __ballot(r0 + lane < nrec && x > 0.0 && pre + incl > tau);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      rstar = r0 + l;
+      pstar = pre + (l > 0 ? readlane_d(incl, l - 1) : 0.0);
+      break;
+    }
+    pre += readlane_d(incl, 63);
+  }
+  int z;
+  if (rstar < 0) {
+    z = (int)(usep ? lastp : lastw) - 1;
+  } else {
+    const int base = (rstar / kWaves) * kStep + (rstar % kWaves) * 512 + lane * kCh;
+    float lv[8], qv[8], w[8], pw[8];
+    LT::unpack(load_logits<LT, VEC>(lrow, base, V), lv);
+    if (dmode == 1) F32::unpack(load_probs<VEC>(qrow, base, V), qv);
+    else
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = 0.f;
+    draw_weights(lv, qv, base, dmode, sa.m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w, pw);
+    double ls = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ls += (double)w[e];
+    double acc = pstar + (wave_incl_scan_f64(ls) - ls);
+    int zz = INT_MAX, lastpos = -1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (w[e] > 0.f) lastpos = base + e;
+      acc += (double)w[e];
+      if (zz == INT_MAX && w[e] > 0.f && acc > tau) zz = base + e;
+    }
+    const int best = -wave_max_i(-zz);
+    const int lastb = wave_max_i(lastpos);
+    z = best != INT_MAX ? best : lastb;
+  }
+  if (lane == 0) {
+    a.out_tokens[(size_t)i * (G + 1) + A] = z;
+    if (a.d_resid) a.d_resid[i] = S;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------------------
 
@@ -2147,6 +2165,10 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t stats_bytes(int N, int G) { return align_up((size_t)N * (G + 1) * sizeof(RowStats), 256); }
 size_t done_bytes(int N) { return align_up((size_t)N * sizeof(unsigned int), 256); }
+size_t drec_bytes(int N) { return align_up((size_t)N * sizeof(DrawRec), 256); }
+size_t dsum_bytes(int N, int V) {
+  return align_up((size_t)N * ((V + kStep - 1) / kStep) * kWaves * sizeof(DrawSum), 256);
+}
 
 struct DeviceBuffer {
   void* ptr = nullptr;
@@ -2164,12 +2186,14 @@ hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
   const long rows = (long)a.N * (a.G + 1);
   hipError_t e;
   hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((a.N + kBlock - 1) / kBlock)), dim3(kBlock), 0, stream, a.done,
-                     a.N);
+                     a.ddone, a.N);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((row_kernel<LT, VEC>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.mid && (e = hipEventRecord(ev.mid, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((draw_kernel<LT, VEC>), dim3((unsigned)((long)a.N * a.dparts)), dim3(kBlock), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.end && (e = hipEventRecord(ev.end, stream)) != hipSuccess) return e;
   return hipSuccess;
 }
@@ -2224,7 +2248,16 @@ int run(int N, int G, int V, const int32_t* ids, const float* q, const void* log
   a.d_fault = fault;
   char* ws = reinterpret_cast<char*>(workspace);
   a.stats = reinterpret_cast<RowStats*>(ws);
-  a.done = reinterpret_cast<unsigned int*>(ws + stats_bytes(N, G));
+  size_t off = stats_bytes(N, G);
+  a.done = reinterpret_cast<unsigned int*>(ws + off);
+  off += done_bytes(N);
+  a.ddone = reinterpret_cast<unsigned int*>(ws + off);
+  off += done_bytes(N);
+  a.drec = reinterpret_cast<DrawRec*>(ws + off);
+  off += drec_bytes(N);
+  a.dsum = reinterpret_cast<DrawSum*>(ws + off);
+  a.dspw = kDrawSteps;
+  a.dparts = ((V + kStep - 1) / kStep + kDrawSteps - 1) / kDrawSteps;
 
   // 16-byte vector loads need every row start aligned: V a multiple of 8 and
   // 16-byte aligned base pointers
@@ -2243,9 +2276,8 @@ int run(int N, int G, int V, const int32_t* ids, const float* q, const void* log
 extern "C" {
 
 size_t spec_verify_workspace_size(int N, int gmax, int V) {
-  (void)V;
-  if (N <= 0 || gmax < 0) return 256;
-  return stats_bytes(N, gmax) + done_bytes(N);
+  if (N <= 0 || gmax < 0 || V <= 0) return 256;
+  return stats_bytes(N, gmax) + 2 * done_bytes(N) + drec_bytes(N) + dsum_bytes(N, V);
 }
 
 int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* draft_probs, const void* target_logits,

@@ -10,9 +10,10 @@
 // token's cell removed).  The exact contract is stated in include/spec_verify.h.
 //
 // Work per call, all on the caller's stream:
-//   clear_kernel  zeroes one completion counter per request.
+//   plan_kernel   zeroes the per-request completion counters and lists the
+//                 draft rows (request, position < gamma_i) request-major.
 //   row_kernel    one 256-thread workgroup per (request, position) row: first
-//                 the draft positions in request-major order, then the bonus
+//                 the draft positions in position-major order, then the bonus
 //                 positions.  It streams the target-logit row and, at draft
 //                 positions of sampled requests, the draft-probability row
 //                 once (16-byte nontemporal loads, several steps of loads in
@@ -129,8 +130,8 @@ struct Args {
   DrawRec* drec;        // per request
   DrawSum* dsum;        // [N][steps][kWaves]
   unsigned int* ddone;  // completion counter per request (draw pass)
-  int dspw;             // draw pass: steps per workgroup
-  int dparts;           // draw pass: workgroups per request
+  int* plan;            // [0]: number of draft rows D; then D entries i * 64 + j, request-major
+  int dparts;           // draw pass: workgroups per request (kDrawSteps steps each)
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -1949,42 +1950,88 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
 // kernels
 // ------------------------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kBlock) void clear_kernel(unsigned int* done, unsigned int* ddone, int N) {
-  const int i = blockIdx.x * kBlock + threadIdx.x;
-  if (i < N) {
-    done[i] = 0u;
-    ddone[i] = 0u;
+// One workgroup: zeroes the completion counters and lists the draft rows
+// (request i, position j < gamma_i) request-major, so that the row pass
+// launches no workgroup for a padding position.  gamma_i is the index of the
+// first negative draft id, as in load_req.
+__global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
+  __shared__ int s_scan[kBlock];
+  __shared__ int s_base;
+  const int tid = threadIdx.x;
+  constexpr int kPer = 4;  // requests per thread and round
+  if (tid == 0) s_base = 0;
+  __syncthreads();
+  for (int r0 = 0; r0 < a.N; r0 += kBlock * kPer) {
+    int g[kPer];
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = r0 + tid * kPer + u;
+      g[u] = 0;
+      if (i < a.N) {
+        a.done[i] = 0u;
+        a.ddone[i] = 0u;
+        int gam = a.G;
+        for (int jj = a.G - 1; jj >= 0; --jj)
+          if (a.ids[(size_t)i * a.G + jj] < 0) gam = jj;
+        g[u] = gam;
+      }
+      cnt += g[u];
+    }
+    s_scan[tid] = cnt;
+    __syncthreads();
+    // inclusive scan over the workgroup (Hillis-Steele in LDS)
+    for (int o = 1; o < kBlock; o <<= 1) {
+      const int v = tid >= o ? s_scan[tid - o] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    int off = s_base + s_scan[tid] - cnt;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = r0 + tid * kPer + u;
+      for (int jj = 0; jj < g[u]; ++jj) a.plan[1 + off + jj] = i * 64 + jj;
+      off += g[u];
+    }
+    __syncthreads();
+    if (tid == kBlock - 1) s_base += s_scan[tid];
+    __syncthreads();
   }
+  if (tid == 0) a.plan[0] = s_base;
 }
 
 template <class LT, bool VEC>
 __global__ __launch_bounds__(kBlock, 3) void row_kernel(Args a) {
   __shared__ KernelShared<LT> sh;
   __shared__ int s_last;
-  // draft positions first (the larger rows), bonus positions last, so that
-  // the short rows fill the end of the launch
-  const int nd = a.N * a.G;
+  // the draft rows first (the larger rows; the plan lists them request-major,
+  // so consecutive blocks, which dispatch round-robin over the XCDs, read
+  // neighbouring rows), then one bonus row per request; the launch covers
+  // N * (gmax + 1) blocks and the ones past the real rows exit at once
+  const int nd = a.plan[0];
   const int bx = (int)blockIdx.x;
-  const int i = bx < nd ? bx / a.G : bx - nd;
-  const int j = bx < nd ? bx - i * a.G : a.G;
+  if (bx >= nd + a.N) return;
+  const bool bonus = bx >= nd;
+  const int m = bonus ? 0 : a.plan[1 + bx];
+  const int i = bonus ? bx - nd : (m >> 6);
   const Req rq = load_req(a, i);
-  if (!rq.fault && j <= rq.gamma) {
+  const int j = bonus ? rq.gamma : (m & 63);
+  if (!rq.fault) {
     if (rq.greedy) greedy_row<LT, VEC>(a, rq, i, j, sh.row);
     else stochastic_row<LT, VEC>(a, rq, i, j, sh.row);
   }
   // completion: every thread's published stores have completed before the
-  // barrier; the workgroup that brings the request's counter to G + 1 runs
-  // the finish
+  // barrier; the workgroup that brings the request's counter to gamma + 1
+  // runs the finish
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned int prev = __hip_atomic_fetch_add(&a.done[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (unsigned int)a.G);
+    s_last = (prev == (unsigned int)rq.gamma);
   }
   __syncthreads();
   if (!s_last) return;
-  // the kernel's only explicit argument sits at the start of its argument
-  // segment: the finish reads it from there instead of a private copy
   finish_request<LT, VEC>(a, i, (LDS_AS FinShared*)&sh.fin);
 }
 
@@ -2051,15 +2098,26 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   const float* qrow = (mode == 1) ? a.q + ((size_t)i * G + A) * (size_t)V : nullptr;
   const int nsteps = (V + kStep - 1) / kStep;
   DrawSum* ds = a.dsum + (size_t)i * nsteps * kWaves;
-  const int s0 = part * a.dspw, s1 = min(nsteps, s0 + a.dspw);
-  for (int s = s0; s < s1; ++s) {
+  const int s0 = part * kDrawSteps;
+  // all of this workgroup's loads first, then the sums
+  typename LT::Raw lr[kDrawSteps];
+  F32::Raw qr[kDrawSteps];
+#pragma unroll
+  for (int u = 0; u < kDrawSteps; ++u) {
+    const int base = (s0 + u) * kStep + tid * kCh;
+    if (s0 + u < nsteps) {
+      lr[u] = load_logits<LT, VEC>(lrow, base, V);
+      qr[u] = (mode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kDrawSteps; ++u) {
+    const int s = s0 + u;
+    if (s >= nsteps) break;
     const int base = s * kStep + tid * kCh;
     float lv[8], qv[8], w[8], pw[8];
-    LT::unpack(load_logits<LT, VEC>(lrow, base, V), lv);
-    if (mode == 1) F32::unpack(load_probs<VEC>(qrow, base, V), qv);
-    else
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[e] = 0.f;
+    LT::unpack(lr[u], lv);
+    F32::unpack(qr[u], qv);
     draw_weights(lv, qv, base, mode, sa.m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w, pw);
     double sw = 0.0, sp = 0.0;
     uint32_t lw = 0u, lp = 0u;
@@ -2166,6 +2224,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 size_t stats_bytes(int N, int G) { return align_up((size_t)N * (G + 1) * sizeof(RowStats), 256); }
 size_t done_bytes(int N) { return align_up((size_t)N * sizeof(unsigned int), 256); }
 size_t drec_bytes(int N) { return align_up((size_t)N * sizeof(DrawRec), 256); }
+size_t plan_bytes(int N, int G) { return align_up(((size_t)N * G + 1) * sizeof(int), 256); }
 size_t dsum_bytes(int N, int V) {
   return align_up((size_t)N * ((V + kStep - 1) / kStep) * kWaves * sizeof(DrawSum), 256);
 }
@@ -2185,8 +2244,7 @@ template <class LT, bool VEC>
 hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
   const long rows = (long)a.N * (a.G + 1);
   hipError_t e;
-  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((a.N + kBlock - 1) / kBlock)), dim3(kBlock), 0, stream, a.done,
-                     a.ddone, a.N);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((row_kernel<LT, VEC>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
@@ -2256,7 +2314,8 @@ int run(int N, int G, int V, const int32_t* ids, const float* q, const void* log
   a.drec = reinterpret_cast<DrawRec*>(ws + off);
   off += drec_bytes(N);
   a.dsum = reinterpret_cast<DrawSum*>(ws + off);
-  a.dspw = kDrawSteps;
+  off += dsum_bytes(N, V);
+  a.plan = reinterpret_cast<int*>(ws + off);
   a.dparts = ((V + kStep - 1) / kStep + kDrawSteps - 1) / kDrawSteps;
 
   // 16-byte vector loads need every row start aligned: V a multiple of 8 and
@@ -2277,7 +2336,7 @@ extern "C" {
 
 size_t spec_verify_workspace_size(int N, int gmax, int V) {
   if (N <= 0 || gmax < 0 || V <= 0) return 256;
-  return stats_bytes(N, gmax) + 2 * done_bytes(N) + drec_bytes(N) + dsum_bytes(N, V);
+  return stats_bytes(N, gmax) + 2 * done_bytes(N) + drec_bytes(N) + dsum_bytes(N, V) + plan_bytes(N, gmax);
 }
 
 int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* draft_probs, const void* target_logits,

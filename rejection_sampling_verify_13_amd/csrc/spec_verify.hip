@@ -585,7 +585,7 @@ __device__ inline void raw_get(const LDS_AS F32::Raw* s, F32::Raw& r) { r.a = s-
 // as the count is within that band.  Plain values in and out, so callers keep
 // their state in registers.
 template <class R>
-__device__ __noinline__ ChunkState chunk_refresh(LDS_AS ChunkBuf<R>* b, ChunkState s, int k, int slack) {
+__device__ __forceinline__ ChunkState chunk_refresh(LDS_AS ChunkBuf<R>* b, ChunkState s, int k, int slack) {
   // the wave's next loads wait on this: issue ahead of the streaming waves
   __builtin_amdgcn_s_setprio(2);
   const int lane = lane_id();

@@ -133,6 +133,8 @@ SMALL = {
     "gamma_max_64": W.config(2, N=3, gmax=64, V=2048),
     "tiny_vocab": W.config(1, N=20, V=3),
     "vocab_one": W.config(1, N=6, V=1),
+    # more requests than the row planner lists per round, ragged drafts
+    "many_requests_ragged": W.config(5, N=1500, gmax=3, V=1024, q_mode="dense"),
 }
 
 
@@ -248,6 +250,23 @@ def test_special_rows():
     reqs.append(one_request([1, 2], q, big, ua=[0.5, 0.5], us=0.5))
     b = stack(reqs)
     parity(b, "special rows")
+
+
+def test_all_64_drafts_accepted():
+    """gmax = 64 with q' = p' at every position: every draft is accepted and the
+    bonus token is drawn from the 65th row."""
+    V = 3000
+    rng = np.random.default_rng(33)
+    reqs = []
+    for r in range(2):
+        l = (rng.standard_normal((65, V)) * 2).astype(np.float32)
+        e = np.exp(l[:64].astype(np.float64) - l[:64].max(axis=1, keepdims=True))
+        q = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+        y = [int(np.argmax(l[j])) for j in range(64)]
+        reqs.append(one_request(y, q, l, k=0 if r == 0 else 20, ua=rng.uniform(0, 0.5, 64), us=float(rng.uniform())))
+    b = stack(reqs)
+    g, o, res = parity(b, "all 64 drafts accepted")
+    assert list(g["num_accepted"]) == [64, 64]
 
 
 def test_top_k_candidates_clustered_in_one_wave():

@@ -1955,7 +1955,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
 // launches no workgroup for a padding position.  gamma_i is the index of the
 // first negative draft id, as in load_req.
 __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
-  __shared__ int s_scan[kBlock];
+  __shared__ int s_scan[kWaves];
   __shared__ int s_base;
   const int tid = threadIdx.x;
   constexpr int kPer = 4;  // requests per thread and round
@@ -1978,16 +1978,14 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
       }
       cnt += g[u];
     }
-    s_scan[tid] = cnt;
+    // exclusive offsets: wave scans, then the four wave totals
+    const int incl = wave_incl_scan_i32(cnt);
+    if (lane_id() == 63) s_scan[tid >> 6] = incl;
     __syncthreads();
-    // inclusive scan over the workgroup (Hillis-Steele in LDS)
-    for (int o = 1; o < kBlock; o <<= 1) {
-      const int v = tid >= o ? s_scan[tid - o] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
-    }
-    int off = s_base + s_scan[tid] - cnt;
+    int before = s_base;
+    for (int w = 0; w < (tid >> 6); ++w) before += s_scan[w];
+    const int round_total = s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
+    int off = before + incl - cnt;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = r0 + tid * kPer + u;
@@ -1995,7 +1993,7 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
       off += g[u];
     }
     __syncthreads();
-    if (tid == kBlock - 1) s_base += s_scan[tid];
+    if (tid == 0) s_base += round_total;
     __syncthreads();
   }
   if (tid == 0) a.plan[0] = s_base;

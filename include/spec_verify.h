@@ -59,6 +59,9 @@ extern "C" {
 #define SPEC_VERIFY_OK 0
 #define SPEC_VERIFY_ERR_NULL 1      /* a required pointer is NULL                        */
 #define SPEC_VERIFY_ERR_SHAPE 2     /* N < 0, gmax outside [0, 64], V < 1, or too large  */
+/* "Too large": V * (gmax + 1) above 2^40, V above 2^31 - 4097, or either
+ * launch grid reaching 2^32 work-items: 256 * N * (gmax + 1) (row pass) or
+ * 256 * N * (ceil(ceil(V / 2048) / 4) + 1) (draw pass). */
 #define SPEC_VERIFY_ERR_DTYPE 3     /* unknown logits_dtype                              */
 #define SPEC_VERIFY_ERR_WORKSPACE 4 /* workspace_bytes below spec_verify_workspace_size  */
 #define SPEC_VERIFY_ERR_HIP 5       /* a HIP runtime call failed (launch, allocation)     */
@@ -124,10 +127,11 @@ int spec_verify_diag(int N, int gmax, int V, const int32_t *draft_ids, const flo
 /*
  * spec_verify_diag plus three optional hipEvent_t handles (created by the
  * caller, may be NULL) that are recorded on `stream`: ev_start before the
- * row pass (which ends with each request's accept scan and, where the draw
- * row kept a top-k set, the draw), ev_mid after it, ev_end after the draw
- * pass that re-reads the draw row of the remaining sampled requests.  For
- * timing the two phases; results are identical to spec_verify_diag.
+ * row pass (every row's statistics and accept flag, and the draw of a row
+ * that may be drawn from and kept its top-k set on chip), ev_mid after it,
+ * ev_end after the draw pass (each request's first rejection and outputs,
+ * and the draw for requests whose draw row made none).  For timing the two
+ * phases; results are identical to spec_verify_diag.
  */
 int spec_verify_timed(int N, int gmax, int V, const int32_t *draft_ids, const float *draft_probs,
                       const void *target_logits, int logits_dtype, const float *temperature,

@@ -10,14 +10,15 @@
 // token's cell removed).  The exact contract is stated in include/spec_verify.h.
 //
 // Work per call, all on the caller's stream:
-//   plan_kernel   zeroes the per-request completion counters and lists the
-//                 draft rows (request, position < gamma_i) request-major.
-//   row_kernel    one 256-thread workgroup per (request, position) row: first
-//                 the draft positions in position-major order, then the bonus
-//                 positions.  It streams the target-logit row and, at draft
-//                 positions of sampled requests, the draft-probability row
-//                 once (16-byte nontemporal loads, several steps of loads in
-//                 flight while the current step is reduced).
+//   plan_kernel   stores gamma_i and clears the outcome bits of each request's
+//                 record, and lists the draft rows (request, position <
+//                 gamma_i) request-major.
+//   row_kernel    one 256-thread workgroup per real row: the listed draft rows,
+//                 then one bonus row per request.  It streams the target-logit
+//                 row and, at draft positions of sampled requests, the
+//                 draft-probability row once (16-byte nontemporal loads,
+//                 several steps of loads in flight while the current step is
+//                 reduced).
 //                 Without top-k: row max, sum of exp over the row (fp32 terms,
 //                 fp64 accumulation), sum of q^(1/T), draft-row validity.
 //                 With top-k (k <= kKFast): row max and validity only, plus
@@ -30,13 +31,14 @@
 //                 rows take the argmax.  p'(y) and q'(y) are evaluated in fp64
 //                 and the flag u * q'(y) < p'(y) stored; a row that may be the
 //                 one drawn from (the bonus row, or a rejected draft row) with
-//                 its top-k set in LDS also draws its token there.
-//                 The last workgroup of a request to finish (atomic counter)
-//                 finds the first rejection A by ballot and takes row A's
-//                 draw, or draws by inverse CDF over ascending token id with
-//                 two passes over row A (chunk sums, then the crossing chunk).
-//                 Outputs are written -1 padded.
-//
+//                 its top-k set in LDS also draws its token there.  Each row
+//                 ORs its accept bit, fault bits and whether it drew into the
+//                 request's record.
+//   draw_kernel   per request: the first rejection A from the record, the
+//                 outputs (-1 padded), and, where row A made no draw of its
+//                 own, the draw by inverse CDF over ascending token id with
+//                 two passes over row A (block sums, then the crossing block).
+
 // Compile: hipcc --offload-arch=gfx950 -O3 -shared -fPIC
 //          -Xclang -target-feature -Xclang -packed-fp32-ops
 
@@ -91,13 +93,18 @@ struct RowStats {
 };
 static_assert(sizeof(RowStats) == 64, "RowStats layout");
 
-// A request whose draw is left to draw_kernel (row A had no kept list in LDS).
-struct DrawRec {
-  int need;       // 1: draw_kernel draws out_tokens[i, A]
-  int A;          // the draw row
-  int mode;       // 0: p'; 1: max(0, p' - q'); 2: p' with the draft token removed
-  int yA;         // mode 2: the draft token at row A
+// Outcome of one request's rows, gathered with atomic ORs: the plan kernel
+// stores gamma_i and clears the bits, each row workgroup adds its own, and the
+// draw pass reads the record once to find the first rejection A.
+struct ReqRec {
+  unsigned long long acc;     // bit j: the draft token at position j was accepted
+  unsigned long long nodraw;  // bit j: row j (j < 64) made no draw of its own
+  unsigned int nodraw64;      // 1: row 64 (gamma_i = 64) made no draw of its own
+  unsigned int fault;         // fault bits of the request and of its rows
+  int gamma;                  // gamma_i
+  int pad;
 };
+static_assert(sizeof(ReqRec) == 32, "ReqRec layout");
 
 // Sums of one 512-token block (one wave's tokens of one step) of row A.
 struct DrawSum {
@@ -126,8 +133,7 @@ struct Args {
   double* d_resid;
   int32_t* d_fault;
   RowStats* stats;
-  unsigned int* done;   // completion counter per request (row pass)
-  DrawRec* drec;        // per request
+  ReqRec* rec;          // per request
   DrawSum* dsum;        // [N][steps][kWaves]
   unsigned int* ddone;  // completion counter per request (draw pass)
   int* plan;            // [0]: number of draft rows D; then D entries i * 64 + j, request-major
@@ -267,15 +273,14 @@ __device__ inline double mass_p(float l, float m, float c) {
 }
 
 // ------------------------------------------------------------------------------------------
-// hand-off of row results to the request's finishing workgroup
+// hand-off of partial results between workgroups of one launch
 //
-// Row statistics are written with agent-scope atomic stores and
-// read back with agent-scope atomic loads: on gfx950 these are global stores /
-// loads with the device-coherence bit, which write through and read past the
-// per-XCD L2, so the finishing workgroup (possibly on another XCD) sees them
-// without a cache-wide write-back or invalidate.  Each writer waits for its
-// stores to complete before the workgroup barrier that precedes the counter
-// increment.
+// Records are written with agent-scope atomic stores and read back with
+// agent-scope atomic loads: on gfx950 these are global stores / loads with
+// the device-coherence bit, which write through and read past the per-XCD L2,
+// so the consuming workgroup (possibly on another XCD) sees them without a
+// cache-wide write-back or invalidate.  Each writer waits for its stores to
+// complete before the workgroup barrier that precedes the counter increment.
 // ------------------------------------------------------------------------------------------
 
 template <class T>
@@ -295,6 +300,19 @@ __device__ inline T fetch(const T* src) {
 #pragma unroll
   for (int t = 0; t < (int)(sizeof(T) / 8); ++t) d[t] = __hip_atomic_load(s + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return v;
+}
+
+// Adds row j's outcome to request i's record (one thread).  The ORs return
+// nothing, so the workgroup does not wait for them; the draw pass, a later
+// launch, reads the record.
+__device__ inline void note_row(const Args& a, int i, int j, int acc, int fault, bool nodraw) {
+  ReqRec* r = a.rec + i;
+  if (acc) __hip_atomic_fetch_or(&r->acc, 1ull << j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (fault) __hip_atomic_fetch_or(&r->fault, (unsigned int)fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (nodraw) {
+    if (j < 64) __hip_atomic_fetch_or(&r->nodraw, 1ull << j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else __hip_atomic_fetch_or(&r->nodraw64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -811,19 +829,6 @@ struct RowShared {
   uint32_t sel_u[2];
 };
 
-struct FinShared {
-  RowStats sa;
-  double red_d[kWaves];
-  int red_i[kWaves];
-  int misc[8];
-  double miscd[4];
-};
-
-template <class LT>
-union KernelShared {
-  RowShared<LT> row;
-  FinShared fin;
-};
 
 // ------------------------------------------------------------------------------------------
 // kept set from the candidate buffers (one wave per distribution)
@@ -1505,121 +1510,6 @@ __device__ void stream_greedy(const typename LT::T* lrow, int V, float& best, in
 }
 
 // ------------------------------------------------------------------------------------------
-// per-request finish (run by the last workgroup of the request)
-// ------------------------------------------------------------------------------------------
-
-// Draw weights of one step (mode 0: p'; 1: max(0, p' - q'); 2: p' with y removed).
-__device__ inline void step_weights(const float lv[8], const float qv[8], int base, int mode, float m, float c,
-                                    float invZ, float cut_p, float cut_q, float invR, float invT, bool temper, int yA,
-                                    float w[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float p = (lv[e] >= cut_p) ? fast_exp2((lv[e] - m) * c) * invZ : 0.f;
-    float x = p;
-    if (mode == 1) {
-      const float r = temper ? fast_exp2(fast_log2(qv[e]) * invT) : qv[e];
-      const float q = (qv[e] >= cut_q) ? r * invR : 0.f;
-      x = __builtin_fmaxf(p - q, 0.f);
-    } else if (mode == 2) {
-      x = (base + e == yA) ? 0.f : p;
-    }
-    w[e] = x;
-  }
-}
-
-template <class LT, bool VEC>
-__device__ __forceinline__ void finish_request(const Args& a, int i, LDS_AS FinShared* sh) {
-  typedef typename LT::T ET;
-  typedef typename LT::Raw LR;
-  const int G = a.G, V = a.V;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const Req rq = load_req(a, i);
-  int32_t* out = a.out_tokens + (size_t)i * (G + 1);
-  const RowStats* st = a.stats + (size_t)i * (G + 1);
-
-  // wave 0 loads the row records of rows 0..gamma in one round (lane j: row j;
-  // a 65th row, gamma = 64, is loaded by every lane), finds the fault bits and
-  // the first rejection A, and leaves row A's record in LDS
-  int fault = rq.fault, A = 0;
-  if (!fault) {
-    if (wave == 0) {
-      const bool mine = lane <= rq.gamma;
-      RowStats r{};
-      if (mine) r = fetch(st + lane);
-      RowStats r64{};
-      if (rq.gamma == 64) r64 = fetch(st + 64);
-      int f = mine ? (r.flags >> 8) : 0;
-      f = wave_or_i(f) | ((rq.gamma == 64) ? (r64.flags >> 8) : 0);
-      const uint64_t accm = __ballot(lane < rq.gamma && (r.flags & 1));
-      const uint64_t within = rq.gamma >= 64 ? ~0ull : ((1ull << rq.gamma) - 1ull);
-      const uint64_t rej = ~accm & within;
-      const int Aw = rej ? (__ffsll((unsigned long long)rej) - 1) : rq.gamma;
-      if (lane == 0) {
-        sh->misc[0] = f;
-        sh->misc[1] = Aw;
-      }
-      if (Aw == 64) {
-        if (lane == 0) __builtin_memcpy((RowStats*)&sh->sa, &r64, sizeof(RowStats));
-      } else if (lane == Aw) {
-        __builtin_memcpy((RowStats*)&sh->sa, &r, sizeof(RowStats));
-      }
-      if (!f) {
-        if (a.d_py && lane < G) a.d_py[(size_t)i * G + lane] = (lane < rq.gamma && !rq.greedy) ? r.p_y : NAN;
-        if (a.d_qy && lane < G) a.d_qy[(size_t)i * G + lane] = (lane < rq.gamma && !rq.greedy) ? r.q_y : NAN;
-      }
-    }
-    __syncthreads();
-    fault = sh->misc[0];
-    A = sh->misc[1];
-  }
-
-  if (fault) {
-    for (int t = tid; t <= G; t += kBlock) out[t] = -1;
-    if (tid == 0) {
-      a.drec[i] = DrawRec{0, 0, 0, -1};
-      a.out_num[i] = -1;
-      if (a.d_fault) a.d_fault[i] = fault;
-      if (a.d_resid) a.d_resid[i] = NAN;
-    }
-    if (a.d_py)
-      for (int t = tid; t < G; t += kBlock) a.d_py[(size_t)i * G + t] = NAN;
-    if (a.d_qy)
-      for (int t = tid; t < G; t += kBlock) a.d_qy[(size_t)i * G + t] = NAN;
-    return;
-  }
-
-  RowStats sa;
-  __builtin_memcpy(&sa, (const RowStats*)&sh->sa, sizeof(RowStats));
-  int z = -1;
-  double S_out = NAN;
-  bool defer = false;
-  if (rq.greedy) {
-    z = sa.argmax;
-  } else if (sa.draw >= 0) {
-    // drawn by row A's own workgroup from its kept list
-    z = sa.draw;
-    S_out = sa.s;
-  } else {
-    // row A had no top-k set in LDS: draw_kernel re-reads it
-    defer = true;
-  }
-
-  for (int t = tid; t <= G; t += kBlock) {
-    int v = -1;
-    if (t < A) v = a.ids[(size_t)i * G + t];
-    else if (t == A) v = z;
-    if (!(defer && t == A)) out[t] = v;
-  }
-  if (tid == 0) {
-    const bool resid = A < rq.gamma;
-    a.drec[i] = DrawRec{defer ? 1 : 0, A, resid ? (a.q ? 1 : 2) : 0, resid ? a.ids[(size_t)i * G + A] : -1};
-    a.out_num[i] = A;
-    if (a.d_fault) a.d_fault[i] = 0;
-    if (a.d_resid && !defer) a.d_resid[i] = S_out;
-  }
-}
-
-// ------------------------------------------------------------------------------------------
 // row processing
 // ------------------------------------------------------------------------------------------
 
@@ -1661,8 +1551,9 @@ __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, 
     s.q_y = NAN;
     s.s = NAN;
     s.flags = ((j < rq.gamma && y == cand) ? 1 : 0) | (fault << 8);
-    s.draw = -1;
+    s.draw = s.argmax;  // a greedy row's token is its argmax
     publish(a.stats + row, s);
+    note_row(a, i, j, s.flags & 1, fault, false);
   }
 }
 
@@ -1942,6 +1833,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       s.flags = acc | (fault << 8);
       s.draw = d.z;
       publish(a.stats + row, s);
+      note_row(a, i, j, acc, fault, d.z < 0);
     }
   }
 }
@@ -1950,7 +1842,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
 // kernels
 // ------------------------------------------------------------------------------------------
 
-// One workgroup: zeroes the completion counters and lists the draft rows
+// One workgroup: clears the per-request records and lists the draft rows
 // (request i, position j < gamma_i) request-major, so that the row pass
 // launches no workgroup for a padding position.  gamma_i is the index of the
 // first negative draft id, as in load_req.
@@ -1969,12 +1861,12 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
       const int i = r0 + tid * kPer + u;
       g[u] = 0;
       if (i < a.N) {
-        a.done[i] = 0u;
         a.ddone[i] = 0u;
         int gam = a.G;
         for (int jj = a.G - 1; jj >= 0; --jj)
           if (a.ids[(size_t)i * a.G + jj] < 0) gam = jj;
         g[u] = gam;
+        a.rec[i] = ReqRec{0ull, 0ull, 0u, 0u, gam, 0};
       }
       cnt += g[u];
     }
@@ -2001,8 +1893,7 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
 
 template <class LT, bool VEC>
 __global__ __launch_bounds__(kBlock, 3) void row_kernel(Args a) {
-  __shared__ KernelShared<LT> sh;
-  __shared__ int s_last;
+  __shared__ RowShared<LT> sh;
   // the draft rows first (the larger rows; the plan lists them request-major,
   // so consecutive blocks, which dispatch round-robin over the XCDs, read
   // neighbouring rows), then one bonus row per request; the launch covers
@@ -2015,22 +1906,12 @@ __global__ __launch_bounds__(kBlock, 3) void row_kernel(Args a) {
   const int i = bonus ? bx - nd : (m >> 6);
   const Req rq = load_req(a, i);
   const int j = bonus ? rq.gamma : (m & 63);
-  if (!rq.fault) {
-    if (rq.greedy) greedy_row<LT, VEC>(a, rq, i, j, sh.row);
-    else stochastic_row<LT, VEC>(a, rq, i, j, sh.row);
+  if (rq.fault) {
+    if (threadIdx.x == 0) note_row(a, i, j, 0, rq.fault, false);
+    return;
   }
-  // completion: every thread's published stores have completed before the
-  // barrier; the workgroup that brings the request's counter to gamma + 1
-  // runs the finish
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned int prev = __hip_atomic_fetch_add(&a.done[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (unsigned int)rq.gamma);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  finish_request<LT, VEC>(a, i, (LDS_AS FinShared*)&sh.fin);
+  if (rq.greedy) greedy_row<LT, VEC>(a, rq, i, j, sh);
+  else stochastic_row<LT, VEC>(a, rq, i, j, sh);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -2069,22 +1950,80 @@ __device__ inline void draw_weights(const float lv[8], const float qv[8], int ba
   }
 }
 
-// Grid: dparts workgroups per request, each summing the draw weights of
-// kDrawSteps steps of row A per 512-token block (one wave's tokens of one
-// step); the last workgroup of the request scans the block sums in token
-// order, re-reads the block where the running sum first exceeds u * S and
-// finds the token there (inverse CDF over ascending id; if the weights sum to
-// zero, over p'; if rounding leaves no crossing, the largest id with w > 0).
+// Request i's outputs from its record: the accepted drafts before the first
+// rejection A, the token at A (drawn in the row pass, or a greedy row's
+// argmax; left to the draw below when `defer`), -1 after it, and the
+// diagnostics.  Run by one workgroup per request.
+__device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, int A, bool defer) {
+  const int G = a.G, tid = threadIdx.x;
+  int32_t* out = a.out_tokens + (size_t)i * (G + 1);
+  const RowStats* st = a.stats + (size_t)i * (G + 1);
+  if (rr.fault) {
+    for (int t = tid; t <= G; t += kBlock) out[t] = -1;
+    if (tid == 0) {
+      a.out_num[i] = -1;
+      if (a.d_fault) a.d_fault[i] = (int)rr.fault;
+      if (a.d_resid) a.d_resid[i] = NAN;
+    }
+    if (a.d_py)
+      for (int t = tid; t < G; t += kBlock) a.d_py[(size_t)i * G + t] = NAN;
+    if (a.d_qy)
+      for (int t = tid; t < G; t += kBlock) a.d_qy[(size_t)i * G + t] = NAN;
+    return;
+  }
+  int z = -1;
+  double S = NAN;
+  if (!defer) {
+    z = st[A].draw;
+    S = st[A].s;
+  }
+  for (int t = tid; t <= G; t += kBlock) {
+    if (defer && t == A) continue;
+    out[t] = t < A ? a.ids[(size_t)i * G + t] : (t == A ? z : -1);
+  }
+  if (tid == 0) {
+    a.out_num[i] = A;
+    if (a.d_fault) a.d_fault[i] = 0;
+    if (a.d_resid && !defer) a.d_resid[i] = S;
+  }
+  if (a.d_py || a.d_qy) {
+    for (int t = tid; t < G; t += kBlock) {
+      const bool real = t < rr.gamma;
+      if (a.d_py) a.d_py[(size_t)i * G + t] = real ? st[t].p_y : NAN;
+      if (a.d_qy) a.d_qy[(size_t)i * G + t] = real ? st[t].q_y : NAN;
+    }
+  }
+}
+
+// Grid: dparts + 1 workgroups per request.  Each reads the request's record
+// and finds the first rejection A; the last one writes the outputs.  If row
+// A made no draw of its own (no kept list in LDS), each of the other dparts
+// workgroups sums the draw weights of kDrawSteps steps of row A per 512-token
+// block (one wave's tokens of one step); the last of them to finish scans the
+// block sums in token order, re-reads the block where the running sum first
+// exceeds u * S and finds the token there (inverse CDF over ascending id; if
+// the weights sum to zero, over p'; if rounding leaves no crossing, the
+// largest id with w > 0).
 template <class LT, bool VEC>
 __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   typedef typename LT::T ET;
   __shared__ int s_last;
-  const int i = blockIdx.x / a.dparts, part = blockIdx.x - i * a.dparts;
-  const DrawRec dr = a.drec[i];
-  if (!dr.need) return;
+  const int i = blockIdx.x / (a.dparts + 1), part = blockIdx.x - i * (a.dparts + 1);
+  const ReqRec rr = a.rec[i];
+  const int gamma = rr.gamma;
+  const uint64_t within = gamma >= 64 ? ~0ull : ((1ull << gamma) - 1ull);
+  const uint64_t rej = ~rr.acc & within;
+  const int A = rej ? (__ffsll((unsigned long long)rej) - 1) : gamma;
+  const bool defer = !rr.fault && (A >= 64 ? rr.nodraw64 != 0u : ((rr.nodraw >> A) & 1ull) != 0ull);
+  if (part == a.dparts) {
+    request_outputs(a, i, rr, A, defer);
+    return;
+  }
+  if (!defer) return;
   const int G = a.G, V = a.V;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int A = dr.A, mode = dr.mode, yA = dr.yA;
+  const int mode = A < gamma ? (a.q ? 1 : 2) : 0;
+  const int yA = mode == 2 ? a.ids[(size_t)i * G + A] : -1;
   const size_t row = (size_t)i * (G + 1) + A;
   const RowStats sa = a.stats[row];
   const float T = a.temperature ? a.temperature[i] : 1.f;
@@ -2221,7 +2160,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t stats_bytes(int N, int G) { return align_up((size_t)N * (G + 1) * sizeof(RowStats), 256); }
 size_t done_bytes(int N) { return align_up((size_t)N * sizeof(unsigned int), 256); }
-size_t drec_bytes(int N) { return align_up((size_t)N * sizeof(DrawRec), 256); }
+size_t rec_bytes(int N) { return align_up((size_t)N * sizeof(ReqRec), 256); }
 size_t plan_bytes(int N, int G) { return align_up(((size_t)N * G + 1) * sizeof(int), 256); }
 size_t dsum_bytes(int N, int V) {
   return align_up((size_t)N * ((V + kStep - 1) / kStep) * kWaves * sizeof(DrawSum), 256);
@@ -2248,7 +2187,7 @@ hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
   hipLaunchKernelGGL((row_kernel<LT, VEC>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.mid && (e = hipEventRecord(ev.mid, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((draw_kernel<LT, VEC>), dim3((unsigned)((long)a.N * a.dparts)), dim3(kBlock), 0, stream, a);
+  hipLaunchKernelGGL((draw_kernel<LT, VEC>), dim3((unsigned)((long)a.N * (a.dparts + 1))), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.end && (e = hipEventRecord(ev.end, stream)) != hipSuccess) return e;
   return hipSuccess;
@@ -2260,7 +2199,10 @@ int run(int N, int G, int V, const int32_t* ids, const float* q, const void* log
         int32_t* fault, void* workspace, size_t workspace_bytes, void* stream, const Events& ev) {
   if (N < 0 || G < 0 || G > kMaxGamma || V < 1) return SPEC_VERIFY_ERR_SHAPE;
   if (dtype != SPEC_VERIFY_F32 && dtype != SPEC_VERIFY_BF16) return SPEC_VERIFY_ERR_DTYPE;
-  if ((long long)N * (G + 1) > 0x7fffffffLL || (long long)V * (G + 1) > (1LL << 40) || V > 0x7fffffff - 2 * kStep)
+  if ((long long)V * (G + 1) > (1LL << 40) || V > 0x7fffffff - 2 * kStep) return SPEC_VERIFY_ERR_SHAPE;
+  // a dispatch holds its grid size in work-items as a 32-bit number
+  const long long dparts = ((long long)(V + kStep - 1) / kStep + kDrawSteps - 1) / kDrawSteps;
+  if ((long long)N * (G + 1) * kBlock > 0xffffffffLL || (long long)N * (dparts + 1) * kBlock > 0xffffffffLL)
     return SPEC_VERIFY_ERR_SHAPE;
   if (N == 0) return SPEC_VERIFY_OK;
   if (!logits || !u_sample || !out_tokens || !out_num) return SPEC_VERIFY_ERR_NULL;
@@ -2305,16 +2247,14 @@ int run(int N, int G, int V, const int32_t* ids, const float* q, const void* log
   char* ws = reinterpret_cast<char*>(workspace);
   a.stats = reinterpret_cast<RowStats*>(ws);
   size_t off = stats_bytes(N, G);
-  a.done = reinterpret_cast<unsigned int*>(ws + off);
-  off += done_bytes(N);
+  a.rec = reinterpret_cast<ReqRec*>(ws + off);
+  off += rec_bytes(N);
   a.ddone = reinterpret_cast<unsigned int*>(ws + off);
   off += done_bytes(N);
-  a.drec = reinterpret_cast<DrawRec*>(ws + off);
-  off += drec_bytes(N);
   a.dsum = reinterpret_cast<DrawSum*>(ws + off);
   off += dsum_bytes(N, V);
   a.plan = reinterpret_cast<int*>(ws + off);
-  a.dparts = ((V + kStep - 1) / kStep + kDrawSteps - 1) / kDrawSteps;
+  a.dparts = (int)dparts;
 
   // 16-byte vector loads need every row start aligned: V a multiple of 8 and
   // 16-byte aligned base pointers
@@ -2334,7 +2274,7 @@ extern "C" {
 
 size_t spec_verify_workspace_size(int N, int gmax, int V) {
   if (N <= 0 || gmax < 0 || V <= 0) return 256;
-  return stats_bytes(N, gmax) + 2 * done_bytes(N) + drec_bytes(N) + dsum_bytes(N, V) + plan_bytes(N, gmax);
+  return stats_bytes(N, gmax) + rec_bytes(N) + done_bytes(N) + dsum_bytes(N, V) + plan_bytes(N, gmax);
 }
 
 int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* draft_probs, const void* target_logits,

@@ -67,6 +67,10 @@ def test_host_validation(lib):
     assert _call(lib, ids=0) == 1
     assert _call(lib, ua=0) == 1
     assert _call(lib, N=0) == 0  # empty batch: nothing to do
+    # grids whose size in work-items (256 per workgroup) needs more than 32 bits
+    assert _call(lib, N=(1 << 24) // 65 + 1, G=64) == 2     # row pass: N * (gmax + 1) workgroups
+    assert _call(lib, N=(1 << 24) // 2, G=0, V=16) == 2      # draw pass: N * 2 workgroups at V <= 8192
+    assert _call(lib, N=(1 << 24) // 2 - 1, G=0, V=16, logits=0) == 1  # just inside: the next check fires
     small = ctypes.c_void_p(0x1000)
     assert _call(lib, ws=small, wsb=16) == 4
 

@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
     ap.add_argument("--cpu-sample", type=int, default=256, help="requests timed on the CPU oracle (0: skip)")
+    ap.add_argument("--layout", choices=("auto", "padded", "flat"), default="auto",
+                    help="input layout: padded [N, gmax] calls, or one flattened (ragged) call; auto: flattened "
+                         "for a batch that mixes requests with and without draft rows (config 5), else padded")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -118,7 +121,12 @@ def main():
     print("[bench] generating workload %d (N=%d gmax=%d V=%d)" % (args.config, spec.N, spec.gmax, spec.V),
           file=sys.stderr, flush=True)
     batch = W.generate(spec, threads=threads)
-    parts = W.split_by_q(batch) if (batch["draft_probs"] is not None and not batch["has_q"].all()) else [batch]
+    mixed = batch["draft_probs"] is not None and not batch["has_q"].all()
+    flat = args.layout == "flat" or (args.layout == "auto" and mixed)
+    if flat:
+        parts = [W.flatten(batch)]
+    else:
+        parts = W.split_by_q(batch) if mixed else [batch]
     B_alg, B_target, B_draft = workload_bytes(batch)
     positions = int(batch["gamma"].sum())
     rows = int((batch["gamma"] + 1).sum())
@@ -128,8 +136,12 @@ def main():
     for _ in range(2):
         ps = []
         for p in parts:
-            d = sv.to_device(p, dev)
-            Np, Gp = p["draft_ids"].shape
+            if flat:
+                d = sv.to_device_flat(p, dev)
+                Np, Gp = p["cu_num_draft_tokens"].shape[0], p["gmax"]
+            else:
+                d = sv.to_device(p, dev)
+                Np, Gp = p["draft_ids"].shape
             Vp = p["target_logits"].shape[-1]
             d["ws"] = torch.empty((sv.workspace_size(Np, Gp, Vp),), dtype=torch.uint8, device=dev)
             d["out_t"] = torch.empty((Np, Gp + 1), dtype=torch.int32, device=dev)
@@ -144,9 +156,11 @@ def main():
             ev = None
             if events is not None:
                 ev = events[pi]
-            sv.verify(d["draft_ids"], d["draft_probs"], d["target_logits"], d["temperature"], d["top_k"], d["top_p"],
-                      d["u_accept"], d["u_sample"], out_tokens=d["out_t"], out_num_accepted=d["out_n"],
-                      workspace=d["ws"], stream=stream, events=ev)
+            kw = dict(out_tokens=d["out_t"], out_num_accepted=d["out_n"], workspace=d["ws"], stream=stream, events=ev)
+            if flat:
+                sv.verify_flat_batch(d, **kw)
+            else:
+                sv.verify_batch(d, **kw)
 
     for k in range(args.warmup):
         step(k)
@@ -212,6 +226,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": desc, "requests": spec.N, "gamma": spec.gmax, "vocab": spec.V,
+                   "layout": "flattened, one call" if flat else "padded, %d call(s)" % len(parts),
                    "target_logits": spec.dtype, "draft_probs": "f32" if spec.q_mode != "null" else None,
                    "verified_positions_per_step": positions, "rows_per_step": rows,
                    "algorithmic_bytes_per_step": B_alg, "target_bytes": B_target, "draft_bytes": B_draft},

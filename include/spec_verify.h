@@ -73,6 +73,7 @@ extern "C" {
 #define SPEC_VERIFY_FAULT_TARGET_ROW 8
 #define SPEC_VERIFY_FAULT_DRAFT_ROW 16
 #define SPEC_VERIFY_FAULT_DRAFT_MASS 32
+#define SPEC_VERIFY_FAULT_DRAFT_COUNT 64 /* flattened layout: gamma_i outside [0, gmax] or past num_drafts */
 
 /*
  * Bytes of device workspace one call with these sizes needs.  The layout is
@@ -140,6 +141,57 @@ int spec_verify_timed(int N, int gmax, int V, const int32_t *draft_ids, const fl
                       double *p_y, double *q_y, double *resid_mass, int32_t *fault,
                       void *workspace, size_t workspace_bytes, void *stream,
                       void *ev_start, void *ev_mid, void *ev_end);
+
+/*
+ * Verify a batch in the flattened (ragged) layout, with no padding rows.
+ * vLLM page, section "SpecDecodeMetadata：验证阶段的「索引地图」": the drafts of
+ * all requests are concatenated in request order and a prefix sum of the
+ * draft counts locates each request's span.  Request i has gamma_i =
+ * cu_num_draft_tokens[i] - cu_num_draft_tokens[i-1] drafts (the term for
+ * i = 0 is 0), 0 <= gamma_i <= gmax, and num_drafts = cu_num_draft_tokens[N-1].
+ * All array arguments are DEVICE pointers owned by the caller:
+ *   cu_num_draft_tokens  int32    [N]                inclusive prefix sums of gamma_i
+ *   draft_ids            int32    [num_drafts]       request i's at cu[i-1] .. cu[i]-1
+ *   draft_probs          float32  [Q, V] or NULL     the draft rows of the requests that carry
+ *                                                    them, in request order (Q = sum of their gamma_i)
+ *   has_draft_probs      uint8    [N] or NULL        request i carries draft rows iff nonzero
+ *                                                    (NULL: all do; ignored when draft_probs is NULL);
+ *                                                    the others are draft-free (n-gram) requests
+ *   target_logits        f32/bf16 [num_drafts + N, V] request i's gamma_i draft positions, then its
+ *                                                    bonus position: rows cu[i-1] + i .. cu[i] + i
+ *   temperature, top_k, top_p, u_sample  [N]  as for spec_verify
+ *   u_accept             float32  [num_drafts]       aligned with draft_ids
+ *   out_tokens           int32    [N, gmax+1]        written, -1 padded as for spec_verify
+ *   out_num_accepted     int32    [N]                written
+ * The method, the outputs, the faults, the workspace (spec_verify_workspace_size
+ * with the same N, gmax, V) and the stream behave as for spec_verify; a
+ * request whose count is out of range gets SPEC_VERIFY_FAULT_DRAFT_COUNT and
+ * its inputs are not read.  Returns SPEC_VERIFY_ERR_NULL for a NULL
+ * cu_num_draft_tokens (N > 0), or NULL draft_ids / u_accept when num_drafts
+ * > 0; SPEC_VERIFY_ERR_SHAPE for num_drafts outside [0, N * gmax].
+ */
+int spec_verify_flat(int N, int gmax, int V, int num_drafts, const int32_t *cu_num_draft_tokens,
+                     const int32_t *draft_ids, const float *draft_probs,
+                     const uint8_t *has_draft_probs, const void *target_logits, int logits_dtype,
+                     const float *temperature, const int32_t *top_k, const float *top_p,
+                     const float *u_accept, const float *u_sample, int32_t *out_tokens,
+                     int32_t *out_num_accepted, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/*
+ * spec_verify_flat with the diagnostic outputs of spec_verify_diag (p_y and
+ * q_y are [N, gmax], position j of request i at [i, j]) and the three
+ * optional events of spec_verify_timed.
+ */
+int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t *cu_num_draft_tokens,
+                           const int32_t *draft_ids, const float *draft_probs,
+                           const uint8_t *has_draft_probs, const void *target_logits,
+                           int logits_dtype, const float *temperature, const int32_t *top_k,
+                           const float *top_p, const float *u_accept, const float *u_sample,
+                           int32_t *out_tokens, int32_t *out_num_accepted, double *p_y,
+                           double *q_y, double *resid_mass, int32_t *fault, void *workspace,
+                           size_t workspace_bytes, void *stream, void *ev_start, void *ev_mid,
+                           void *ev_end);
 
 /* Human-readable text of a return code (static storage). */
 const char *spec_verify_status_string(int status);

@@ -24,9 +24,10 @@ FAULT_TOP_P = 4
 FAULT_TARGET_ROW = 8
 FAULT_DRAFT_ROW = 16
 FAULT_DRAFT_MASS = 32
+FAULT_DRAFT_COUNT = 64
 
-EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_timed", "spec_verify_workspace_size",
-           "spec_verify_status_string", "spec_verify_version")
+EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_timed", "spec_verify_flat", "spec_verify_flat_timed",
+           "spec_verify_workspace_size", "spec_verify_status_string", "spec_verify_version")
 
 
 class SpecVerifyError(RuntimeError):
@@ -46,6 +47,11 @@ def _load():
     lib.spec_verify_diag.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
     lib.spec_verify_timed.restype = I
     lib.spec_verify_timed.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P, Z, P, P, P, P]
+    lib.spec_verify_flat.restype = I
+    lib.spec_verify_flat.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P, P, P, P, P, P, P, Z, P]
+    lib.spec_verify_flat_timed.restype = I
+    lib.spec_verify_flat_timed.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P, Z, P,
+                                           P, P, P]
     lib.spec_verify_workspace_size.restype = Z
     lib.spec_verify_workspace_size.argtypes = [I, I, I]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
@@ -154,6 +160,87 @@ def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, 
     return out_tokens, out_num_accepted
 
 
+def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, target_logits, gmax,
+                temperature=None, top_k=None, top_p=None, u_accept=None, u_sample=None, *, out_tokens=None,
+                out_num_accepted=None, workspace=None, stream=None, diag=False, events=None):
+    """Verify a batch in the flattened layout (spec_verify_flat in include/spec_verify.h).
+
+    cu_num_draft_tokens int32 [N] (inclusive prefix sums of the draft counts),
+    draft_ids int32 [T], draft_probs float32 [Q, V] or None (the draft rows of
+    the requests that carry them, in request order), has_draft_probs uint8 [N]
+    or None, target_logits bfloat16/float32 [T + N, V] (each request's draft
+    positions, then its bonus position), gmax (the output width is gmax + 1),
+    temperature / top_k / top_p / u_sample [N] as for verify(), u_accept
+    float32 [T].  Returns what verify() returns; with diag=True p_y and q_y
+    are [N, gmax].  ``events`` as for verify().
+    """
+    if target_logits.dim() != 2:
+        raise ValueError("target_logits must be [T + N, V]")
+    N = cu_num_draft_tokens.shape[0]
+    G = int(gmax)
+    R, V = target_logits.shape
+    T = R - N
+    if T < 0:
+        raise ValueError("target_logits has fewer rows than requests")
+    dev = target_logits.device
+    if target_logits.dtype == torch.bfloat16:
+        dt = BF16
+    elif target_logits.dtype == torch.float32:
+        dt = F32
+    else:
+        raise TypeError("target_logits must be bfloat16 or float32")
+    if not target_logits.is_contiguous():
+        raise ValueError("target_logits must be contiguous")
+    _check(cu_num_draft_tokens, "cu_num_draft_tokens", torch.int32, (N,), dev)
+    _check(draft_ids, "draft_ids", torch.int32, (T,), dev)
+    if draft_probs is not None:
+        if draft_probs.dim() != 2 or draft_probs.shape[1] != V:
+            raise ValueError("draft_probs must be [Q, V]")
+        _check(draft_probs, "draft_probs", torch.float32, tuple(draft_probs.shape), dev)
+    _check(has_draft_probs, "has_draft_probs", torch.uint8, (N,), dev)
+    _check(temperature, "temperature", torch.float32, (N,), dev)
+    _check(top_k, "top_k", torch.int32, (N,), dev)
+    _check(top_p, "top_p", torch.float32, (N,), dev)
+    _check(u_accept, "u_accept", torch.float32, (T,), dev)
+    _check(u_sample, "u_sample", torch.float32, (N,), dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((N, G + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((N,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", torch.int32, (N, G + 1), dev)
+    _check(out_num_accepted, "out_num_accepted", torch.int32, (N,), dev)
+    if workspace is None:
+        workspace = torch.empty((workspace_size(N, G, V),), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    head = (N, G, V, T, _ptr(cu_num_draft_tokens), _ptr(draft_ids), _ptr(draft_probs), _ptr(has_draft_probs),
+            _ptr(target_logits), dt, _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(u_accept), _ptr(u_sample),
+            _ptr(out_tokens), _ptr(out_num_accepted))
+    d = None
+    with torch.cuda.device(dev):
+        if diag or events is not None:
+            if diag:
+                d = dict(p_y=torch.empty((N, G), dtype=torch.float64, device=dev),
+                         q_y=torch.empty((N, G), dtype=torch.float64, device=dev),
+                         resid_mass=torch.empty((N,), dtype=torch.float64, device=dev),
+                         fault=torch.empty((N,), dtype=torch.int32, device=dev))
+                dp = (_ptr(d["p_y"]), _ptr(d["q_y"]), _ptr(d["resid_mass"]), _ptr(d["fault"]))
+            else:
+                dp = (None, None, None, None)
+            evp = (None, None, None) if events is None else tuple(
+                None if e is None else ctypes.c_void_p(e.cuda_event) for e in events)
+            rc = lib.spec_verify_flat_timed(*head, *dp, _ptr(workspace), ws_bytes, sptr, *evp)
+        else:
+            rc = lib.spec_verify_flat(*head, _ptr(workspace), ws_bytes, sptr)
+    if rc != 0:
+        raise SpecVerifyError("spec_verify_flat failed: %s" % lib.spec_verify_status_string(rc).decode())
+    if diag:
+        return out_tokens, out_num_accepted, d
+    return out_tokens, out_num_accepted
+
+
 def to_device(batch: dict, device="cuda"):
     """Move a numpy batch (the layout of the workloads module) to torch tensors."""
     import numpy as np
@@ -174,3 +261,27 @@ def verify_batch(dev_batch: dict, **kw):
     return verify(dev_batch["draft_ids"], dev_batch["draft_probs"], dev_batch["target_logits"],
                   dev_batch["temperature"], dev_batch["top_k"], dev_batch["top_p"], dev_batch["u_accept"],
                   dev_batch["u_sample"], **kw)
+
+
+def to_device_flat(flat: dict, device="cuda"):
+    """Move a flattened numpy batch (workloads.flatten) to torch tensors."""
+    import numpy as np
+    out = {"gmax": flat["gmax"]}
+    for k in ("cu_num_draft_tokens", "draft_ids", "draft_probs", "has_draft_probs", "temperature", "top_k",
+              "top_p", "u_accept", "u_sample"):
+        v = flat.get(k)
+        out[k] = None if v is None else torch.from_numpy(np.ascontiguousarray(v)).to(device)
+    tl = flat["target_logits"]
+    if flat["dtype"] == "bf16":
+        out["target_logits"] = torch.from_numpy(np.ascontiguousarray(tl).view(np.int16)).to(device).view(torch.bfloat16)
+    else:
+        out["target_logits"] = torch.from_numpy(np.ascontiguousarray(tl)).to(device)
+    return out
+
+
+def verify_flat_batch(dev_flat: dict, **kw):
+    """verify_flat() with the arguments taken from a to_device_flat() dict."""
+    return verify_flat(dev_flat["cu_num_draft_tokens"], dev_flat["draft_ids"], dev_flat["draft_probs"],
+                       dev_flat["has_draft_probs"], dev_flat["target_logits"], dev_flat["gmax"],
+                       dev_flat["temperature"], dev_flat["top_k"], dev_flat["top_p"], dev_flat["u_accept"],
+                       dev_flat["u_sample"], **kw)

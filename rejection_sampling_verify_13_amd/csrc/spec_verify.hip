@@ -75,6 +75,7 @@ enum {
   kFaultTargetRow = SPEC_VERIFY_FAULT_TARGET_ROW,
   kFaultDraftRow = SPEC_VERIFY_FAULT_DRAFT_ROW,
   kFaultDraftMass = SPEC_VERIFY_FAULT_DRAFT_MASS,
+  kFaultDraftCount = SPEC_VERIFY_FAULT_DRAFT_COUNT,
 };
 
 // Per-row results (64 bytes).
@@ -93,18 +94,23 @@ struct RowStats {
 };
 static_assert(sizeof(RowStats) == 64, "RowStats layout");
 
-// Outcome of one request's rows, gathered with atomic ORs: the plan kernel
-// stores gamma_i and clears the bits, each row workgroup adds its own, and the
-// draw pass reads the record once to find the first rejection A.
+// One request's place in the inputs and the outcome of its rows.  The plan
+// kernel writes the layout fields and clears the bits; each row workgroup ORs
+// its own bits in; the draw pass reads the record once to find the first
+// rejection A.
 struct ReqRec {
   unsigned long long acc;     // bit j: the draft token at position j was accepted
   unsigned long long nodraw;  // bit j: row j (j < 64) made no draw of its own
   unsigned int nodraw64;      // 1: row 64 (gamma_i = 64) made no draw of its own
-  unsigned int fault;         // fault bits of the request and of its rows
+  unsigned int fault;         // fault bits of the request's rows (row pass)
   int gamma;                  // gamma_i
+  int tgt0;                   // target_logits row of position 0
+  int id0;                    // index of draft 0 in draft_ids and u_accept
+  int q0;                     // draft_probs row of position 0; -1: no draft rows
+  unsigned int lfault;        // layout fault found by the plan kernel
   int pad;
 };
-static_assert(sizeof(ReqRec) == 32, "ReqRec layout");
+static_assert(sizeof(ReqRec) == 48, "ReqRec layout");
 
 // Sums of one 512-token block (one wave's tokens of one step) of row A.
 struct DrawSum {
@@ -138,6 +144,10 @@ struct Args {
   unsigned int* ddone;  // completion counter per request (draw pass)
   int* plan;            // [0]: number of draft rows D; then D entries i * 64 + j, request-major
   int dparts;           // draw pass: workgroups per request (kDrawSteps steps each)
+  // flattened layout (cu == nullptr: the padded [N, G] layout)
+  const int32_t* cu;    // [N] inclusive prefix sums of gamma_i
+  const uint8_t* has_q; // [N] request i has draft rows iff nonzero; nullptr: all do (when q != nullptr)
+  int T;                // number of drafts, cu[N - 1]
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -528,6 +538,9 @@ __device__ inline double block_exscan_d(double v, double* red, double* total) {
 
 struct Req {
   int gamma;      // number of draft tokens
+  int tgt0;       // target_logits row of position 0
+  int id0;        // index of draft 0 in draft_ids and u_accept
+  int q0;         // draft_probs row of position 0; -1: no draft rows
   float T;        // temperature
   int k;          // top_k (raw)
   float p;        // top_p (raw)
@@ -537,16 +550,20 @@ struct Req {
   bool pact;      // top-p filter active
 };
 
-// Every wave of the block evaluates this redundantly (gmax <= 64 ids).
+// The request's layout (from the plan kernel's record) and parameters, and
+// the draft-id check; every wave of the block evaluates this redundantly
+// (gamma_i <= 64 ids).
 __device__ inline Req load_req(const Args& a, int i) {
   Req r;
   const int lane = lane_id();
-  const int32_t* ids = a.ids + (size_t)i * a.G;
-  int id = (lane < a.G) ? ids[lane] : -1;
-  uint64_t neg = __ballot(lane < a.G && id < 0);
-  r.gamma = neg ? (__ffsll((unsigned long long)neg) - 1) : a.G;
-  uint64_t bad = __ballot(lane < r.gamma && id >= a.V);
-  r.fault = bad ? kFaultDraftId : 0;
+  const ReqRec* rr = a.rec + i;
+  r.gamma = rr->gamma;
+  r.tgt0 = rr->tgt0;
+  r.id0 = rr->id0;
+  r.q0 = rr->q0;
+  r.fault = (int)rr->lfault;
+  const int id = lane < r.gamma ? a.ids[(size_t)r.id0 + lane] : 0;
+  if (__ballot(lane < r.gamma && (id < 0 || id >= a.V))) r.fault |= kFaultDraftId;
   r.T = a.temperature ? a.temperature[i] : 1.f;
   r.k = a.top_k ? a.top_k[i] : 0;
   r.p = a.top_p ? a.top_p[i] : 1.f;
@@ -1517,8 +1534,8 @@ template <class LT, bool VEC>
 __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, int j, RowShared<LT>& sh) {
   typedef typename LT::T ET;
   const int G = a.G, V = a.V, tid = threadIdx.x;
-  const size_t row = (size_t)i * (G + 1) + j;
-  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + row * (size_t)V;
+  const size_t row = (size_t)i * (G + 1) + j;  // the row record
+  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + ((size_t)rq.tgt0 + j) * (size_t)V;
   float best = -INFINITY, acc = 0.f;
   int bidx = -1;
   stream_greedy<LT, VEC>(lrow, V, best, bidx, acc);
@@ -1539,7 +1556,7 @@ __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, 
   }
   if (tid == 0) {
     const int fault = (bad || gbest == INFINITY || cand == INT_MAX) ? kFaultTargetRow : 0;
-    const int y = j < rq.gamma ? a.ids[(size_t)i * G + j] : -1;
+    const int y = j < rq.gamma ? a.ids[(size_t)rq.id0 + j] : -1;
     RowStats s;
     s.m = gbest;
     s.cut_p = -INFINITY;
@@ -1562,11 +1579,12 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   typedef typename LT::T ET;
   const int G = a.G, V = a.V;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const size_t row = (size_t)i * (G + 1) + j;
-  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + row * (size_t)V;
+  const size_t row = (size_t)i * (G + 1) + j;  // the row record
+  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + ((size_t)rq.tgt0 + j) * (size_t)V;
   const bool draft_pos = j < rq.gamma;
-  const bool has_q = a.q != nullptr && draft_pos;
-  const float* qrow = has_q ? a.q + ((size_t)i * G + j) * (size_t)V : nullptr;
+  const bool req_q = rq.q0 >= 0;  // the request carries draft rows
+  const bool has_q = req_q && draft_pos;
+  const float* qrow = has_q ? a.q + ((size_t)rq.q0 + j) * (size_t)V : nullptr;
   const float T = rq.T;
   const float c = kLog2e / T;
   const float invT = 1.f / T;
@@ -1578,9 +1596,9 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   int y = -1;
   float ly = 0.f, qyv = 0.f;
   if (tid == 0 && draft_pos) {
-    y = a.ids[(size_t)i * G + j];
+    y = a.ids[(size_t)rq.id0 + j];
     ly = LT::at(lrow, (size_t)y);
-    if (a.q != nullptr) qyv = F32::at(qrow, (size_t)y);
+    if (req_q) qyv = F32::at(qrow, (size_t)y);
   }
 
   StochState st;
@@ -1803,8 +1821,8 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       const double e = (ly >= cut_p) ? mass_p(ly, m, c) : 0.0;
       const double py = e / Zk;
       double qy = 1.0;
-      if (a.q != nullptr) qy = (qyv >= cut_q) ? temper_q(qyv, T) / Rk : 0.0;
-      const double u = (double)a.u_accept[(size_t)i * G + j];
+      if (req_q) qy = (qyv >= cut_q) ? temper_q(qyv, T) / Rk : 0.0;
+      const double u = (double)a.u_accept[(size_t)rq.id0 + j];
       acc = (u * qy < py) ? 1 : 0;
       s.p_y = py;
       s.q_y = qy;
@@ -1842,53 +1860,100 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
 // kernels
 // ------------------------------------------------------------------------------------------
 
-// One workgroup: clears the per-request records and lists the draft rows
+// One workgroup: writes each request's record (gamma_i, where its rows and
+// drafts sit in the inputs, cleared outcome bits) and lists the draft rows
 // (request i, position j < gamma_i) request-major, so that the row pass
-// launches no workgroup for a padding position.  gamma_i is the index of the
-// first negative draft id, as in load_req.
+// launches no workgroup for a padding position.  Padded layout: gamma_i is
+// the index of the first negative draft id.  Flattened layout: gamma_i =
+// cu[i] - cu[i-1]; a count outside [0, G] (or past T) faults the request,
+// which then lists no draft rows; the draft-probability rows of the requests
+// that carry them are consecutive, so request i's first one is the sum of
+// gamma_r over the earlier such requests (a second prefix sum).
 __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
-  __shared__ int s_scan[kWaves];
-  __shared__ int s_base;
-  const int tid = threadIdx.x;
+  __shared__ int s_scan[2][kWaves];
+  __shared__ int s_base[2];
+  const int tid = threadIdx.x, wave = tid >> 6;
   constexpr int kPer = 4;  // requests per thread and round
-  if (tid == 0) s_base = 0;
+  if (tid < 2) s_base[tid] = 0;
   __syncthreads();
   for (int r0 = 0; r0 < a.N; r0 += kBlock * kPer) {
-    int g[kPer];
-    int cnt = 0;
+    int g[kPer], gq[kPer], id0[kPer];
+    unsigned int lf[kPer];
+    bool hq[kPer];
+    int cnt = 0, qcnt = 0;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = r0 + tid * kPer + u;
-      g[u] = 0;
+      g[u] = gq[u] = id0[u] = 0;
+      lf[u] = 0u;
+      hq[u] = false;
       if (i < a.N) {
         a.ddone[i] = 0u;
-        int gam = a.G;
-        for (int jj = a.G - 1; jj >= 0; --jj)
-          if (a.ids[(size_t)i * a.G + jj] < 0) gam = jj;
-        g[u] = gam;
-        a.rec[i] = ReqRec{0ull, 0ull, 0u, 0u, gam, 0};
+        if (a.cu) {
+          const int prev = i ? a.cu[i - 1] : 0, cur = a.cu[i];
+          const long long gam = (long long)cur - prev;
+          id0[u] = prev;
+          hq[u] = a.q && (!a.has_q || a.has_q[i]);
+          if (prev < 0 || gam < 0 || gam > a.G || cur > a.T) lf[u] = kFaultDraftCount;
+          else g[u] = (int)gam;
+          // later requests' draft-probability rows sit after this one's, whatever its count
+          gq[u] = (hq[u] && gam > 0) ? (int)min(gam, (long long)a.T) : 0;
+        } else {
+          int gam = a.G;
+          for (int jj = a.G - 1; jj >= 0; --jj)
+            if (a.ids[(size_t)i * a.G + jj] < 0) gam = jj;
+          g[u] = gam;
+          id0[u] = i * a.G;
+          hq[u] = a.q != nullptr;
+        }
       }
       cnt += g[u];
+      qcnt += gq[u];
     }
     // exclusive offsets: wave scans, then the four wave totals
     const int incl = wave_incl_scan_i32(cnt);
-    if (lane_id() == 63) s_scan[tid >> 6] = incl;
+    const int qincl = wave_incl_scan_i32(qcnt);
+    if (lane_id() == 63) {
+      s_scan[0][wave] = incl;
+      s_scan[1][wave] = qincl;
+    }
     __syncthreads();
-    int before = s_base;
-    for (int w = 0; w < (tid >> 6); ++w) before += s_scan[w];
-    const int round_total = s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
-    int off = before + incl - cnt;
+    int off = s_base[0] + incl - cnt, qoff = s_base[1] + qincl - qcnt;
+    for (int w = 0; w < wave; ++w) {
+      off += s_scan[0][w];
+      qoff += s_scan[1][w];
+    }
+    const int round_total = s_scan[0][0] + s_scan[0][1] + s_scan[0][2] + s_scan[0][3];
+    const int qround_total = s_scan[1][0] + s_scan[1][1] + s_scan[1][2] + s_scan[1][3];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = r0 + tid * kPer + u;
+      if (i < a.N) {
+        ReqRec r;
+        r.acc = 0ull;
+        r.nodraw = 0ull;
+        r.nodraw64 = 0u;
+        r.fault = 0u;
+        r.gamma = g[u];
+        r.tgt0 = a.cu ? id0[u] + i : i * (a.G + 1);
+        r.id0 = id0[u];
+        r.q0 = !hq[u] ? -1 : (a.cu ? qoff : i * a.G);
+        r.lfault = lf[u];
+        r.pad = 0;
+        a.rec[i] = r;
+      }
       for (int jj = 0; jj < g[u]; ++jj) a.plan[1 + off + jj] = i * 64 + jj;
       off += g[u];
+      qoff += gq[u];
     }
     __syncthreads();
-    if (tid == 0) s_base += round_total;
+    if (tid == 0) {
+      s_base[0] += round_total;
+      s_base[1] += qround_total;
+    }
     __syncthreads();
   }
-  if (tid == 0) a.plan[0] = s_base;
+  if (tid == 0) a.plan[0] = s_base[0];
 }
 
 template <class LT, bool VEC>
@@ -1958,11 +2023,12 @@ __device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, i
   const int G = a.G, tid = threadIdx.x;
   int32_t* out = a.out_tokens + (size_t)i * (G + 1);
   const RowStats* st = a.stats + (size_t)i * (G + 1);
-  if (rr.fault) {
+  const unsigned int fault = rr.fault | rr.lfault;
+  if (fault) {
     for (int t = tid; t <= G; t += kBlock) out[t] = -1;
     if (tid == 0) {
       a.out_num[i] = -1;
-      if (a.d_fault) a.d_fault[i] = (int)rr.fault;
+      if (a.d_fault) a.d_fault[i] = (int)fault;
       if (a.d_resid) a.d_resid[i] = NAN;
     }
     if (a.d_py)
@@ -1979,7 +2045,7 @@ __device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, i
   }
   for (int t = tid; t <= G; t += kBlock) {
     if (defer && t == A) continue;
-    out[t] = t < A ? a.ids[(size_t)i * G + t] : (t == A ? z : -1);
+    out[t] = t < A ? a.ids[(size_t)rr.id0 + t] : (t == A ? z : -1);
   }
   if (tid == 0) {
     a.out_num[i] = A;
@@ -2014,7 +2080,7 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   const uint64_t within = gamma >= 64 ? ~0ull : ((1ull << gamma) - 1ull);
   const uint64_t rej = ~rr.acc & within;
   const int A = rej ? (__ffsll((unsigned long long)rej) - 1) : gamma;
-  const bool defer = !rr.fault && (A >= 64 ? rr.nodraw64 != 0u : ((rr.nodraw >> A) & 1ull) != 0ull);
+  const bool defer = !(rr.fault | rr.lfault) && (A >= 64 ? rr.nodraw64 != 0u : ((rr.nodraw >> A) & 1ull) != 0ull);
   if (part == a.dparts) {
     request_outputs(a, i, rr, A, defer);
     return;
@@ -2022,17 +2088,17 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   if (!defer) return;
   const int G = a.G, V = a.V;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int mode = A < gamma ? (a.q ? 1 : 2) : 0;
-  const int yA = mode == 2 ? a.ids[(size_t)i * G + A] : -1;
-  const size_t row = (size_t)i * (G + 1) + A;
+  const int mode = A < gamma ? (rr.q0 >= 0 ? 1 : 2) : 0;
+  const int yA = mode == 2 ? a.ids[(size_t)rr.id0 + A] : -1;
+  const size_t row = (size_t)i * (G + 1) + A;  // the row record
   const RowStats sa = a.stats[row];
   const float T = a.temperature ? a.temperature[i] : 1.f;
   const float c = kLog2e / T, invT = 1.f / T;
   const bool temper = T != 1.f;
   const float invZ = (float)(1.0 / sa.z);
   const float invR = (mode == 1) ? (float)(1.0 / sa.r) : 0.f;
-  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + row * (size_t)V;
-  const float* qrow = (mode == 1) ? a.q + ((size_t)i * G + A) * (size_t)V : nullptr;
+  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + ((size_t)rr.tgt0 + A) * (size_t)V;
+  const float* qrow = (mode == 1) ? a.q + ((size_t)rr.q0 + A) * (size_t)V : nullptr;
   const int nsteps = (V + kStep - 1) / kStep;
   DrawSum* ds = a.dsum + (size_t)i * nsteps * kWaves;
   const int s0 = part * kDrawSteps;
@@ -2193,11 +2259,20 @@ hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
   return hipSuccess;
 }
 
-int run(int N, int G, int V, const int32_t* ids, const float* q, const void* logits, int dtype,
+// Where the drafts sit: the padded layout (cu == nullptr) or the flattened one.
+struct Layout {
+  const int32_t* cu;
+  const uint8_t* has_q;
+  int T;
+};
+
+int run(int N, int G, int V, const Layout& lay, const int32_t* ids, const float* q, const void* logits, int dtype,
         const float* temperature, const int32_t* top_k, const float* top_p, const float* u_accept,
         const float* u_sample, int32_t* out_tokens, int32_t* out_num, double* p_y, double* q_y, double* resid,
         int32_t* fault, void* workspace, size_t workspace_bytes, void* stream, const Events& ev) {
   if (N < 0 || G < 0 || G > kMaxGamma || V < 1) return SPEC_VERIFY_ERR_SHAPE;
+  const bool flat = lay.cu != nullptr;
+  if (flat && (lay.T < 0 || (long long)lay.T > (long long)N * G)) return SPEC_VERIFY_ERR_SHAPE;
   if (dtype != SPEC_VERIFY_F32 && dtype != SPEC_VERIFY_BF16) return SPEC_VERIFY_ERR_DTYPE;
   if ((long long)V * (G + 1) > (1LL << 40) || V > 0x7fffffff - 2 * kStep) return SPEC_VERIFY_ERR_SHAPE;
   // a dispatch holds its grid size in work-items as a 32-bit number
@@ -2206,7 +2281,7 @@ int run(int N, int G, int V, const int32_t* ids, const float* q, const void* log
     return SPEC_VERIFY_ERR_SHAPE;
   if (N == 0) return SPEC_VERIFY_OK;
   if (!logits || !u_sample || !out_tokens || !out_num) return SPEC_VERIFY_ERR_NULL;
-  if (G > 0 && (!ids || !u_accept)) return SPEC_VERIFY_ERR_NULL;
+  if ((flat ? lay.T : G) > 0 && (!ids || !u_accept)) return SPEC_VERIFY_ERR_NULL;
   const size_t need = spec_verify_workspace_size(N, G, V);
   if (!workspace) {
     int dev = 0;
@@ -2255,6 +2330,9 @@ int run(int N, int G, int V, const int32_t* ids, const float* q, const void* log
   off += dsum_bytes(N, V);
   a.plan = reinterpret_cast<int*>(ws + off);
   a.dparts = (int)dparts;
+  a.cu = lay.cu;
+  a.has_q = lay.has_q;
+  a.T = lay.T;
 
   // 16-byte vector loads need every row start aligned: V a multiple of 8 and
   // 16-byte aligned base pointers
@@ -2281,7 +2359,7 @@ int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* d
                 int logits_dtype, const float* temperature, const int32_t* top_k, const float* top_p,
                 const float* u_accept, const float* u_sample, int32_t* out_tokens, int32_t* out_num_accepted,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  return run(N, gmax, V, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes,
              stream, Events{nullptr, nullptr, nullptr});
 }
@@ -2291,7 +2369,7 @@ int spec_verify_diag(int N, int gmax, int V, const int32_t* draft_ids, const flo
                      const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
                      int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return run(N, gmax, V, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{nullptr, nullptr, nullptr});
 }
@@ -2302,8 +2380,35 @@ int spec_verify_timed(int N, int gmax, int V, const int32_t* draft_ids, const fl
                       int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
                       void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_mid,
                       void* ev_end) {
-  return run(N, gmax, V, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
+             Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
+                    reinterpret_cast<hipEvent_t>(ev_end)});
+}
+
+int spec_verify_flat(int N, int gmax, int V, int num_drafts, const int32_t* cu_num_draft_tokens,
+                     const int32_t* draft_ids, const float* draft_probs, const uint8_t* has_draft_probs,
+                     const void* target_logits, int logits_dtype, const float* temperature, const int32_t* top_k,
+                     const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
+                     int32_t* out_num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
+  if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, draft_ids, draft_probs,
+             target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens,
+             out_num_accepted, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
+             Events{nullptr, nullptr, nullptr});
+}
+
+int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t* cu_num_draft_tokens,
+                           const int32_t* draft_ids, const float* draft_probs, const uint8_t* has_draft_probs,
+                           const void* target_logits, int logits_dtype, const float* temperature,
+                           const int32_t* top_k, const float* top_p, const float* u_accept, const float* u_sample,
+                           int32_t* out_tokens, int32_t* out_num_accepted, double* p_y, double* q_y,
+                           double* resid_mass, int32_t* fault, void* workspace, size_t workspace_bytes, void* stream,
+                           void* ev_start, void* ev_mid, void* ev_end) {
+  if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, draft_ids, draft_probs,
+             target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens,
+             out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
                     reinterpret_cast<hipEvent_t>(ev_end)});
 }

@@ -48,6 +48,23 @@ def gpu_run(batch, diag=True, stream=None):
     return res
 
 
+def gpu_run_flat(batch, diag=True, stream=None):
+    """Run a numpy batch on cuda:0 as one call in the flattened layout (a mixed
+    dense / draft-free batch included: the draft-row mask selects per request)."""
+    import torch
+    import rejection_sampling_verify_13_amd as sv
+    import workloads as W
+    d = sv.to_device_flat(W.flatten(batch))
+    if diag:
+        t, n, dg = sv.verify_flat_batch(d, diag=True, stream=stream)
+        out = dict(tokens=t, num_accepted=n, **dg)
+    else:
+        t, n = sv.verify_flat_batch(d, stream=stream)
+        out = dict(tokens=t, num_accepted=n)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
 def oracle_run(batch, threads=8):
     import oracle
     import workloads as W

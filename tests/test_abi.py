@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_verify_diag", "spec_verify_workspace_size", "spec_verify_status_string",
-              "spec_verify_version"):
+              "spec_verify_version", "spec_verify_flat", "spec_verify_flat_timed"):
         assert n in names
 
 
@@ -73,6 +73,23 @@ def test_host_validation(lib):
     assert _call(lib, N=(1 << 24) // 2 - 1, G=0, V=16, logits=0) == 1  # just inside: the next check fires
     small = ctypes.c_void_p(0x1000)
     assert _call(lib, ws=small, wsb=16) == 4
+
+
+def _flat(lib, N=2, G=3, V=16, T=4, cu=1, ids=1, logits=1, ua=1, us=1, out=1, num=1):
+    P = lambda flag: ctypes.c_void_p(0x1000) if flag else None
+    return lib.spec_verify_flat(N, G, V, T, P(cu), P(ids), None, None, P(logits), 1, None, None, None, P(ua), P(us),
+                                P(out), P(num), None, 0, None)
+
+
+def test_flat_host_validation(lib):
+    assert _flat(lib, cu=0) == 1
+    assert _flat(lib, T=-1) == 2
+    assert _flat(lib, T=7) == 2          # more drafts than N * gmax
+    assert _flat(lib, ids=0) == 1
+    assert _flat(lib, ua=0) == 1
+    assert _flat(lib, T=0, ids=0, ua=0, logits=0) == 1   # ids may be NULL without drafts; logits may not
+    assert _flat(lib, N=0, cu=0) == 0    # empty batch
+    assert _flat(lib, G=65) == 2
 
 
 def test_workspace_size_grows_with_rows(lib):

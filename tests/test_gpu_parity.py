@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from conftest import floats, ints, read_golden
-from parity import check_layout, compare, gpu_run, log, oracle_run
+from parity import check_layout, compare, gpu_run, gpu_run_flat, log, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -309,7 +309,8 @@ def test_full_size_sampled(cfg):
     log("[parity] full config %d: N=%d gmax=%d V=%d (generating)" % (cfg, spec.N, spec.gmax, spec.V))
     b = W.generate(spec, threads=16)
     log("[parity] full config %d: running on the GPU" % cfg)
-    g = gpu_run(b)
+    # config 5 (ragged, half draft-free) goes as one flattened call, as the benchmark runs it
+    g = gpu_run_flat(b) if cfg == 5 else gpu_run(b)
     check_layout(b, g)
     rng = np.random.default_rng(77 + cfg)
     if cfg == 5:  # both halves: dense q first, then draft-free
@@ -339,3 +340,96 @@ def test_full_size_sampled(cfg):
         assert g["num_accepted"][i] == A and g["tokens"][i, A] == am[A]
     assert (g["fault"] == 0).all()
     log("[parity] full config %d ok %s, greedy checked %d" % (cfg, res, len(greedy)))
+
+
+# ------------------------------------------------------------------------------------------
+# flattened (ragged) layout: one call, a per-request draft-row mask
+# ------------------------------------------------------------------------------------------
+
+FLAT = {
+    "flat_cfg5_small_mixed": W.config(5, N=48, V=6144),
+    "flat_cfg3_small": W.config(3, N=16, V=12000),
+    "flat_cfg4_small_greedy": W.config(4, N=40, V=7000, greedy_count=10),
+    "flat_null_q": W.config(3, N=12, V=8000, q_mode="null"),
+    "flat_unaligned_f32": W.config(5, N=20, V=3001, dtype="f32"),
+    "flat_gamma_max_64": W.config(2, N=3, gmax=64, V=2048),
+    "flat_gamma_zero": W.config(2, N=12, gmax=0, V=3000),
+    "flat_many_requests_mixed": W.config(5, N=1500, gmax=3, V=1024),
+}
+
+
+@pytest.mark.parametrize("name", list(FLAT))
+def test_flat_layout_parity(name):
+    b = W.generate(FLAT[name])
+    log("[parity] %s: N=%d gmax=%d V=%d (flattened, one call)" % (name, b["draft_ids"].shape[0],
+                                                                   b["draft_ids"].shape[1],
+                                                                   b["target_logits"].shape[-1]))
+    g = gpu_run_flat(b)
+    res = compare(g, oracle_run(b), label=name)
+    check_layout(b, g)
+    log("[parity] %s ok %s" % (name, res))
+
+
+def test_flat_equals_padded_bit_for_bit():
+    # the two layouts run the same arithmetic: identical tokens, masses and faults
+    b = W.generate(W.config(5, N=40, V=5000))
+    log("[parity] flat vs padded: N=40 V=5000")
+    f, p = gpu_run_flat(b), gpu_run(b)
+    for k in ("tokens", "num_accepted", "fault"):
+        np.testing.assert_array_equal(f[k], p[k])
+    for k in ("p_y", "q_y", "resid_mass"):
+        np.testing.assert_array_equal(f[k].view(np.uint64), p[k].view(np.uint64))
+
+
+def _flat_call(flat, gmax, T):
+    """verify_flat with num_drafts = T, which may stop short of the prefix sums:
+    the arrays sized by num_drafts are cut to it (a faulted request reads none
+    of its rows)."""
+    import torch
+    import rejection_sampling_verify_13_amd as sv
+    d = sv.to_device_flat(flat)
+    N = d["cu_num_draft_tokens"].shape[0]
+    t, n, dg = sv.verify_flat(d["cu_num_draft_tokens"], d["draft_ids"][:T].contiguous(), d["draft_probs"],
+                              d["has_draft_probs"], d["target_logits"][: T + N].contiguous(), gmax,
+                              d["temperature"], d["top_k"], d["top_p"], d["u_accept"][:T].contiguous(),
+                              d["u_sample"], diag=True)
+    torch.cuda.synchronize()
+    return dict(tokens=t.cpu().numpy(), num_accepted=n.cpu().numpy(), **{k: v.cpu().numpy() for k, v in dg.items()})
+
+
+def test_flat_count_above_gmax_faults_only_that_request():
+    import rejection_sampling_verify_13_amd as sv
+    b = W.generate(W.config(5, N=24, V=3000, q_mode="dense"))
+    gam = b["gamma"]
+    gcall = int(gam.max()) - 1
+    assert gcall >= 1 and (gam > gcall).any() and (gam <= gcall).any()
+    log("[parity] flat counts above gmax=%d" % gcall)
+    g = _flat_call(W.flatten(b), gcall, int(gam.sum()))
+    o = oracle_run(b)
+    bad = gam > gcall
+    assert (g["fault"][bad] == sv.FAULT_DRAFT_COUNT).all()
+    assert (g["tokens"][bad] == -1).all() and (g["num_accepted"][bad] == -1).all()
+    ok = ~bad
+    np.testing.assert_array_equal(g["fault"][ok], o["fault"][ok])
+    amb = o["margin"][ok] < 1e-6
+    tok_g, tok_o = g["tokens"][ok], o["tokens"][ok][:, : gcall + 1]
+    same = (tok_g == tok_o).all(axis=1) & (g["num_accepted"][ok] == o["num_accepted"][ok])
+    assert (same | amb).all()
+    assert (o["tokens"][ok][:, gcall + 1:] == -1).all()
+
+
+def test_flat_prefix_past_num_drafts_faults_the_tail():
+    import rejection_sampling_verify_13_amd as sv
+    b = W.generate(W.config(3, N=10, V=4000))
+    gam = b["gamma"]
+    T = int(gam.sum())
+    log("[parity] flat prefix sums past num_drafts = %d" % (T - 1))
+    g = _flat_call(W.flatten(b), int(b["draft_ids"].shape[1]), T - 1)
+    o = oracle_run(b)
+    cu = np.cumsum(gam)
+    bad = cu > T - 1
+    assert bad[-1] and (g["fault"][bad] == sv.FAULT_DRAFT_COUNT).all()
+    ok = ~bad
+    amb = o["margin"][ok] < 1e-6
+    same = (g["tokens"][ok] == o["tokens"][ok]).all(axis=1) & (g["num_accepted"][ok] == o["num_accepted"][ok])
+    assert (same | amb).all()

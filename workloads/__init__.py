@@ -235,3 +235,44 @@ def split_by_q(batch: dict):
         p["draft_probs"] = batch["draft_probs"][lo:hi] if (dense and batch["draft_probs"] is not None) else None
         parts.append(p)
     return parts
+
+
+def flatten(batch: dict) -> dict:
+    """The same batch in the flattened (ragged) layout: no padding rows.
+
+    Request i's drafts occupy draft_ids[cu[i-1]:cu[i]] (cu = inclusive prefix
+    sums of gamma_i), its target rows are its gamma_i draft positions followed
+    by its bonus position, and draft_probs holds only the draft rows of the
+    requests that carry them, in request order (has_draft_probs marks those
+    requests).  Pure data movement: nothing of the verifier is computed."""
+    ids = batch["draft_ids"]
+    N, G = ids.shape
+    if "gamma" in batch:
+        gam = np.asarray(batch["gamma"], np.int64)
+    elif G == 0:
+        gam = np.zeros(N, np.int64)
+    else:
+        gam = np.where((ids < 0).any(axis=1), np.argmax(ids < 0, axis=1), G).astype(np.int64)
+    cu = np.cumsum(gam).astype(np.int32)
+    T = int(cu[-1]) if N else 0
+    V = batch["target_logits"].shape[-1]
+    flat_ids = np.concatenate([ids[i, :gam[i]] for i in range(N)] + [np.zeros(0, np.int32)]).astype(np.int32)
+    ua = np.concatenate([batch["u_accept"][i, :gam[i]] for i in range(N)] + [np.zeros(0, np.float32)])
+    tl = batch["target_logits"]
+    logits = np.empty((T + N, V), tl.dtype)
+    r = 0
+    for i in range(N):
+        logits[r:r + gam[i] + 1] = tl[i, :gam[i] + 1]
+        r += gam[i] + 1
+    q = batch.get("draft_probs")
+    has_q = None
+    flat_q = None
+    if q is not None:
+        hq = np.asarray(batch.get("has_q", np.ones(N, bool)), bool)
+        has_q = hq.astype(np.uint8)
+        rows = [q[i, :gam[i]] for i in range(N) if hq[i]]
+        flat_q = np.concatenate(rows + [np.zeros((0, V), np.float32)]).astype(np.float32)
+    return dict(cu_num_draft_tokens=cu, draft_ids=flat_ids, draft_probs=flat_q, has_draft_probs=has_q,
+                target_logits=logits, dtype=batch["dtype"], gmax=G, temperature=batch["temperature"],
+                top_k=batch["top_k"], top_p=batch["top_p"], u_accept=ua.astype(np.float32),
+                u_sample=batch["u_sample"])

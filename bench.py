@@ -98,6 +98,9 @@ def main():
     ap.add_argument("--layout", choices=("auto", "padded", "flat"), default="auto",
                     help="input layout: padded [N, gmax] calls, or one flattened (ragged) call; auto: flattened "
                          "for a batch that mixes requests with and without draft rows (config 5), else padded")
+    ap.add_argument("--rollback", action="store_true",
+                    help="also enqueue the KV bookkeeping (spec_verify_rollback) after every verify call, "
+                         "inside the timed step")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -146,6 +149,10 @@ def main():
             d["ws"] = torch.empty((sv.workspace_size(Np, Gp, Vp),), dtype=torch.uint8, device=dev)
             d["out_t"] = torch.empty((Np, Gp + 1), dtype=torch.int32, device=dev)
             d["out_n"] = torch.empty((Np,), dtype=torch.int32, device=dev)
+            if args.rollback:
+                d["nct"] = torch.full((Np,), 1 << 20, dtype=torch.int32, device=dev)
+                d["slots"] = torch.arange(d["draft_ids"].numel(), dtype=torch.int32, device=dev).view(
+                    d["draft_ids"].shape)
             ps.append(d)
         sets.append(ps)
     del batch["target_logits"], batch["draft_probs"]
@@ -161,6 +168,10 @@ def main():
                 sv.verify_flat_batch(d, **kw)
             else:
                 sv.verify_batch(d, **kw)
+            if args.rollback:
+                lay = dict(cu_num_draft_tokens=d["cu_num_draft_tokens"], gmax=d["gmax"]) if flat else \
+                    dict(draft_ids=d["draft_ids"])
+                sv.rollback(d["out_n"], num_computed_tokens=d["nct"], slot_mapping=d["slots"], stream=stream, **lay)
 
     for k in range(args.warmup):
         step(k)
@@ -227,6 +238,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "requests": spec.N, "gamma": spec.gmax, "vocab": spec.V,
                    "layout": "flattened, one call" if flat else "padded, %d call(s)" % len(parts),
+                   "kv_rollback_in_step": bool(args.rollback),
                    "target_logits": spec.dtype, "draft_probs": "f32" if spec.q_mode != "null" else None,
                    "verified_positions_per_step": positions, "rows_per_step": rows,
                    "algorithmic_bytes_per_step": B_alg, "target_bytes": B_target, "draft_bytes": B_draft},

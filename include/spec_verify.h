@@ -193,6 +193,30 @@ int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t
                            size_t workspace_bytes, void *stream, void *ev_start, void *ev_mid,
                            void *ev_end);
 
+/*
+ * KV bookkeeping after a verify call, enqueued on `stream` after it (KV page
+ * "投机解码如何与 KV Cache 交互：Placeholder、回滚与草稿 KV", sections 3.1 and 3.2;
+ * vLLM page, the padded drafter batch paragraph: rejected draft slots become
+ * PADDING_SLOT_ID).  For request i with A_i = num_accepted[i] accepted of its
+ * gamma_i drafts, the gamma_i - A_i rejected ones are rolled back:
+ *   num_computed_tokens[i]      -= gamma_i - A_i   if it is positive
+ *   num_output_placeholders[i]  -= gamma_i - A_i   if it is positive
+ *   slot_mapping at draft positions A_i .. gamma_i - 1 = -1
+ * gamma_i comes from exactly one of cu_num_draft_tokens [N] (flattened
+ * layout; slot_mapping [num_drafts] aligned with the flattened drafts) or
+ * draft_ids [N, gmax] (padded layout, gamma_i = index of the first negative
+ * id; slot_mapping [N, gmax]).  All arrays are DEVICE int32 arrays; the three
+ * updated ones may each be NULL (not updated).  A request whose A_i is outside
+ * [0, gamma_i] (num_accepted = -1 after a fault) or whose count exceeds gmax
+ * is left unchanged.  Returns SPEC_VERIFY_ERR_SHAPE for N < 0 or gmax outside
+ * [0, 64]; SPEC_VERIFY_ERR_NULL for a NULL num_accepted (N > 0) or unless
+ * exactly one of cu_num_draft_tokens / draft_ids is given (gmax > 0).
+ */
+int spec_verify_rollback(int N, int gmax, const int32_t *cu_num_draft_tokens,
+                         const int32_t *draft_ids, const int32_t *num_accepted,
+                         int32_t *num_computed_tokens, int32_t *num_output_placeholders,
+                         int32_t *slot_mapping, void *stream);
+
 /* Human-readable text of a return code (static storage). */
 const char *spec_verify_status_string(int status);
 

@@ -5,7 +5,9 @@ the CPU-baseline leg of ``bench.py`` may import this package.  The product
 library never loads it, and it imports nothing from the product package.
 
 The arithmetic lives in ``spec_verify_oracle.c`` (plain C, fp64, single
-threaded); this module only compiles it with gcc and marshals numpy arrays.
+threaded); this module only compiles it with gcc and marshals numpy arrays,
+except for ``rollback``, the integer KV bookkeeping after a verify call,
+which is written out here in plain Python.
 ``run(..., threads=n)`` splits the batch into contiguous request ranges and
 calls the C routine on each range from a thread pool: requests are independent,
 so the result does not depend on ``n``.
@@ -184,3 +186,32 @@ def build_variant(source_text: str, out_dir: str) -> "Variant":
 def source_text() -> str:
     with open(_SRC) as f:
         return f.read()
+
+
+def rollback(num_accepted, gamma, num_computed_tokens=None, num_output_placeholders=None, slot_rows=None):
+    """KV bookkeeping after verification, one request at a time.
+
+    KV page "投机解码如何与 KV Cache 交互：Placeholder、回滚与草稿 KV", section 3.1:
+    the rejected drafts are gamma_i - A_i; num_computed_tokens steps back by
+    that many when it is positive, and so does num_output_placeholders.
+    vLLM page, the padded drafter batch paragraph: a rejected draft's KV slot
+    becomes PADDING_SLOT_ID (-1).  slot_rows[i] is request i's slot array
+    (one entry per draft position).  A request whose A_i is outside
+    [0, gamma_i] (a faulted verify) is left unchanged.  Returns new copies."""
+    n = len(num_accepted)
+    nct = None if num_computed_tokens is None else [int(x) for x in num_computed_tokens]
+    nop = None if num_output_placeholders is None else [int(x) for x in num_output_placeholders]
+    slots = None if slot_rows is None else [list(int(x) for x in r) for r in slot_rows]
+    for i in range(n):
+        A, g = int(num_accepted[i]), int(gamma[i])
+        if A < 0 or A > g:
+            continue
+        rejected = g - A
+        if nct is not None and nct[i] > 0:
+            nct[i] -= rejected
+        if nop is not None and nop[i] > 0:
+            nop[i] -= rejected
+        if slots is not None:
+            for j in range(A, g):
+                slots[i][j] = -1
+    return nct, nop, slots

@@ -27,7 +27,7 @@ FAULT_DRAFT_MASS = 32
 FAULT_DRAFT_COUNT = 64
 
 EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_timed", "spec_verify_flat", "spec_verify_flat_timed",
-           "spec_verify_workspace_size", "spec_verify_status_string", "spec_verify_version")
+           "spec_verify_rollback", "spec_verify_workspace_size", "spec_verify_status_string", "spec_verify_version")
 
 
 class SpecVerifyError(RuntimeError):
@@ -52,6 +52,8 @@ def _load():
     lib.spec_verify_flat_timed.restype = I
     lib.spec_verify_flat_timed.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P, Z, P,
                                            P, P, P]
+    lib.spec_verify_rollback.restype = I
+    lib.spec_verify_rollback.argtypes = [I, I, P, P, P, P, P, P, P]
     lib.spec_verify_workspace_size.restype = Z
     lib.spec_verify_workspace_size.argtypes = [I, I, I]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
@@ -285,3 +287,42 @@ def verify_flat_batch(dev_flat: dict, **kw):
                        dev_flat["has_draft_probs"], dev_flat["target_logits"], dev_flat["gmax"],
                        dev_flat["temperature"], dev_flat["top_k"], dev_flat["top_p"], dev_flat["u_accept"],
                        dev_flat["u_sample"], **kw)
+
+
+def rollback(num_accepted, *, cu_num_draft_tokens=None, draft_ids=None, gmax=None, num_computed_tokens=None,
+             num_output_placeholders=None, slot_mapping=None, stream=None):
+    """KV bookkeeping after a verify call (spec_verify_rollback in include/spec_verify.h).
+
+    Give the draft counts as cu_num_draft_tokens int32 [N] (flattened layout,
+    slot_mapping [T]) or draft_ids int32 [N, gmax] (padded, slot_mapping
+    [N, gmax]).  num_computed_tokens, num_output_placeholders (int32 [N]) and
+    slot_mapping are updated in place on ``stream``; each may be None."""
+    N = num_accepted.shape[0]
+    dev = num_accepted.device
+    _check(num_accepted, "num_accepted", torch.int32, (N,), dev)
+    if (cu_num_draft_tokens is None) == (draft_ids is None):
+        raise ValueError("give exactly one of cu_num_draft_tokens and draft_ids")
+    if draft_ids is not None:
+        G = draft_ids.shape[1]
+        _check(draft_ids, "draft_ids", torch.int32, (N, G), dev)
+        if slot_mapping is not None:
+            _check(slot_mapping, "slot_mapping", torch.int32, (N, G), dev)
+    else:
+        if gmax is None:
+            raise ValueError("gmax is required with cu_num_draft_tokens")
+        G = int(gmax)
+        _check(cu_num_draft_tokens, "cu_num_draft_tokens", torch.int32, (N,), dev)
+        if slot_mapping is not None:
+            _check(slot_mapping, "slot_mapping", torch.int32, tuple(slot_mapping.shape), dev)
+            if slot_mapping.dim() != 1:
+                raise ValueError("slot_mapping must be [T] in the flattened layout")
+    _check(num_computed_tokens, "num_computed_tokens", torch.int32, (N,), dev)
+    _check(num_output_placeholders, "num_output_placeholders", torch.int32, (N,), dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_rollback(N, G, _ptr(cu_num_draft_tokens), _ptr(draft_ids), _ptr(num_accepted),
+                                      _ptr(num_computed_tokens), _ptr(num_output_placeholders), _ptr(slot_mapping),
+                                      ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise SpecVerifyError("spec_verify_rollback failed: %s" % lib.spec_verify_status_string(rc).decode())

@@ -2219,6 +2219,49 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// KV bookkeeping after a verify call
+// ------------------------------------------------------------------------------------------
+
+struct RollbackArgs {
+  int N, G;
+  const int32_t* cu;         // [N] flattened layout, or nullptr
+  const int32_t* ids;        // [N, G] padded layout (gamma_i = first negative id), or nullptr
+  const int32_t* num_accepted;
+  int32_t* num_computed;     // [N] or nullptr
+  int32_t* num_placeholders; // [N] or nullptr
+  int32_t* slots;            // aligned with the drafts ([T] or [N, G]), or nullptr
+};
+
+// One thread per request (KV page "投机解码如何与 KV Cache 交互", sections
+// 3.1 and 3.2; vLLM page, the padded drafter batch paragraph): the gamma_i - A_i
+// rejected drafts are taken back from num_computed_tokens and from the
+// placeholder count when those are positive, and their KV slots become
+// PADDING_SLOT_ID (-1).  A request with A_i outside [0, gamma_i] (a faulted
+// verify) or an invalid count is left as it is.
+__global__ __launch_bounds__(kBlock) void rollback_kernel(RollbackArgs r) {
+  const int i = (int)(blockIdx.x * kBlock + threadIdx.x);
+  if (i >= r.N) return;
+  int gamma, id0;
+  if (r.cu) {
+    const int prev = i ? r.cu[i - 1] : 0;
+    gamma = r.cu[i] - prev;
+    id0 = prev;
+  } else {
+    gamma = r.G;
+    for (int jj = r.G - 1; jj >= 0; --jj)
+      if (r.ids[(size_t)i * r.G + jj] < 0) gamma = jj;
+    id0 = i * r.G;
+  }
+  const int A = r.num_accepted[i];
+  if (A < 0 || A > gamma || gamma > r.G) return;
+  const int rejected = gamma - A;
+  if (r.num_computed && r.num_computed[i] > 0) r.num_computed[i] -= rejected;
+  if (r.num_placeholders && r.num_placeholders[i] > 0) r.num_placeholders[i] -= rejected;
+  if (r.slots)
+    for (int j = A; j < gamma; ++j) r.slots[(size_t)id0 + j] = -1;
+}
+
+// ------------------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------------------
 
@@ -2411,6 +2454,27 @@ int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t
              out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
                     reinterpret_cast<hipEvent_t>(ev_end)});
+}
+
+int spec_verify_rollback(int N, int gmax, const int32_t* cu_num_draft_tokens, const int32_t* draft_ids,
+                         const int32_t* num_accepted, int32_t* num_computed_tokens, int32_t* num_output_placeholders,
+                         int32_t* slot_mapping, void* stream) {
+  if (N < 0 || gmax < 0 || gmax > kMaxGamma) return SPEC_VERIFY_ERR_SHAPE;
+  if (N == 0) return SPEC_VERIFY_OK;
+  if (!num_accepted) return SPEC_VERIFY_ERR_NULL;
+  if ((cu_num_draft_tokens != nullptr) == (draft_ids != nullptr) && gmax > 0) return SPEC_VERIFY_ERR_NULL;
+  RollbackArgs r;
+  r.N = N;
+  r.G = gmax;
+  r.cu = cu_num_draft_tokens;
+  r.ids = cu_num_draft_tokens ? nullptr : draft_ids;
+  r.num_accepted = num_accepted;
+  r.num_computed = num_computed_tokens;
+  r.num_placeholders = num_output_placeholders;
+  r.slots = slot_mapping;
+  hipLaunchKernelGGL(rollback_kernel, dim3((unsigned)((N + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                     reinterpret_cast<hipStream_t>(stream), r);
+  return hipGetLastError() == hipSuccess ? SPEC_VERIFY_OK : SPEC_VERIFY_ERR_HIP;
 }
 
 const char* spec_verify_status_string(int status) {

@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_verify_diag", "spec_verify_workspace_size", "spec_verify_status_string",
-              "spec_verify_version", "spec_verify_flat", "spec_verify_flat_timed"):
+              "spec_verify_version", "spec_verify_flat", "spec_verify_flat_timed", "spec_verify_rollback"):
         assert n in names
 
 
@@ -90,6 +90,16 @@ def test_flat_host_validation(lib):
     assert _flat(lib, T=0, ids=0, ua=0, logits=0) == 1   # ids may be NULL without drafts; logits may not
     assert _flat(lib, N=0, cu=0) == 0    # empty batch
     assert _flat(lib, G=65) == 2
+
+
+def test_rollback_host_validation(lib):
+    P = ctypes.c_void_p(0x1000)
+    assert lib.spec_verify_rollback(-1, 4, P, None, P, None, None, None, None) == 2
+    assert lib.spec_verify_rollback(3, 65, P, None, P, None, None, None, None) == 2
+    assert lib.spec_verify_rollback(3, 4, P, None, None, None, None, None, None) == 1   # num_accepted
+    assert lib.spec_verify_rollback(3, 4, None, None, P, None, None, None, None) == 1   # no counts
+    assert lib.spec_verify_rollback(3, 4, P, P, P, None, None, None, None) == 1        # both layouts
+    assert lib.spec_verify_rollback(0, 4, None, None, None, None, None, None, None) == 0
 
 
 def test_workspace_size_grows_with_rows(lib):

@@ -433,3 +433,82 @@ def test_flat_prefix_past_num_drafts_faults_the_tail():
     amb = o["margin"][ok] < 1e-6
     same = (g["tokens"][ok] == o["tokens"][ok]).all(axis=1) & (g["num_accepted"][ok] == o["num_accepted"][ok])
     assert (same | amb).all()
+
+
+# ------------------------------------------------------------------------------------------
+# KV bookkeeping after verification
+# ------------------------------------------------------------------------------------------
+
+def _rollback_case(rng, N, G, flat):
+    gam = rng.integers(0, G + 1, N)
+    A = np.array([rng.integers(-1, g + 1) for g in gam], np.int32)
+    nct = rng.integers(-3, 5000, N).astype(np.int32)
+    nop = rng.integers(0, 10, N).astype(np.int32)
+    slots = [rng.integers(0, 1 << 30, g).astype(np.int32) for g in gam]
+    return gam, A, nct, nop, slots
+
+
+@pytest.mark.parametrize("flat", [False, True])
+def test_rollback_matches_oracle(flat):
+    import torch
+    import oracle
+    import rejection_sampling_verify_13_amd as sv
+    rng = np.random.default_rng(11 + flat)
+    N, G = 700, 8
+    gam, A, nct, nop, slots = _rollback_case(rng, N, G, flat)
+    log("[parity] rollback %s N=%d" % ("flattened" if flat else "padded", N))
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    nct_d, nop_d = t(nct), t(nop)
+    if flat:
+        cu = np.cumsum(gam).astype(np.int32)
+        sl_d = t(np.concatenate(slots + [np.zeros(0, np.int32)]))
+        sv.rollback(t(A), cu_num_draft_tokens=t(cu), gmax=G, num_computed_tokens=nct_d,
+                    num_output_placeholders=nop_d, slot_mapping=sl_d)
+    else:
+        ids = np.full((N, G), -1, np.int32)
+        sl = np.full((N, G), 7, np.int32)
+        for i in range(N):
+            ids[i, : gam[i]] = rng.integers(0, 100, gam[i])
+            sl[i, : gam[i]] = slots[i]
+        sl_d = t(sl)
+        sv.rollback(t(A), draft_ids=t(ids), num_computed_tokens=nct_d, num_output_placeholders=nop_d,
+                    slot_mapping=sl_d)
+    torch.cuda.synchronize()
+    c, p, s = oracle.rollback(A, gam, nct, nop, slots)
+    np.testing.assert_array_equal(nct_d.cpu().numpy(), np.array(c, np.int32))
+    np.testing.assert_array_equal(nop_d.cpu().numpy(), np.array(p, np.int32))
+    got = sl_d.cpu().numpy()
+    if flat:
+        np.testing.assert_array_equal(got, np.concatenate([np.array(r, np.int32) for r in s] + [np.zeros(0, np.int32)]))
+    else:
+        for i in range(N):
+            np.testing.assert_array_equal(got[i, : gam[i]], np.array(s[i], np.int32))
+            assert (got[i, gam[i]:] == 7).all()  # padding positions are not touched
+
+
+def test_verify_then_rollback_on_one_stream():
+    import torch
+    import oracle
+    import rejection_sampling_verify_13_amd as sv
+    b = W.generate(W.config(5, N=64, V=4096))
+    f = W.flatten(b)
+    log("[parity] verify then rollback: N=64 flattened, one stream")
+    d = sv.to_device_flat(f)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        nct = torch.full((64,), 1000, dtype=torch.int32, device="cuda")
+        sl = torch.arange(d["draft_ids"].shape[0], dtype=torch.int32, device="cuda")
+        _, n = sv.verify_flat_batch(d, stream=s)
+        sv.rollback(n, cu_num_draft_tokens=d["cu_num_draft_tokens"], gmax=f["gmax"], num_computed_tokens=nct,
+                    slot_mapping=sl, stream=s)
+    torch.cuda.synchronize()
+    A = n.cpu().numpy()
+    o = oracle_run(b)
+    amb = o["margin"] < 1e-6
+    assert ((A == o["num_accepted"]) | amb).all()
+    gam = b["gamma"]
+    slots = [list(range(a, b_)) for a, b_ in zip(np.r_[0, np.cumsum(gam)[:-1]], np.cumsum(gam))]
+    c, _, ss = oracle.rollback(A, gam, np.full(64, 1000), None, slots)
+    np.testing.assert_array_equal(nct.cpu().numpy(), np.array(c))
+    np.testing.assert_array_equal(sl.cpu().numpy(), np.array([x for r in ss for x in r], np.int32))

@@ -64,7 +64,7 @@ constexpr int kCap = 160;               // buffered candidate chunks per wave an
 constexpr int kKFast = 64;              // largest top_k served by the candidate buffers
 constexpr int kSeg = 128;               // gathered candidate tokens per wave and distribution (LDS)
 constexpr int kMerge = kWaves * kSeg;   // gathered candidate tokens of one distribution
-constexpr int kDrawSteps = 4;           // draw pass: 2048-token steps per workgroup
+constexpr int kDrawSpan = 4;            // draw pass: 2048-token steps per workgroup, all loads in flight
 constexpr int kMaxGamma = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -143,7 +143,8 @@ struct Args {
   DrawSum* dsum;        // [N][steps][kWaves]
   unsigned int* ddone;  // completion counter per request (draw pass)
   int* plan;            // [0]: number of draft rows D; then D entries i * 64 + j, request-major
-  int dparts;           // draw pass: workgroups per request (kDrawSteps steps each)
+  DrawSum* dtot;        // [N][dparts] sums of each draw workgroup's blocks
+  int dparts;           // draw pass: workgroups per request (kDrawSpan steps each)
   // flattened layout (cu == nullptr: the padded [N, G] layout)
   const int32_t* cu;    // [N] inclusive prefix sums of gamma_i
   const uint8_t* has_q; // [N] request i has draft rows iff nonzero; nullptr: all do (when q != nullptr)
@@ -2064,16 +2065,21 @@ __device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, i
 // Grid: dparts + 1 workgroups per request.  Each reads the request's record
 // and finds the first rejection A; the last one writes the outputs.  If row
 // A made no draw of its own (no kept list in LDS), each of the other dparts
-// workgroups sums the draw weights of kDrawSteps steps of row A per 512-token
-// block (one wave's tokens of one step); the last of them to finish scans the
-// block sums in token order, re-reads the block where the running sum first
-// exceeds u * S and finds the token there (inverse CDF over ascending id; if
-// the weights sum to zero, over p'; if rounding leaves no crossing, the
-// largest id with w > 0).
+// workgroups loads kDrawSpan steps of row A (all of them in flight at once)
+// and stores the sums of the draw weights and of p' per 512-token block (one
+// wave's tokens of one step), then its own total: the last lane of
+// a wave prefix scan over its blocks in token order.  The last of them to
+// finish scans the part totals in token order, repeats the scan of the part
+// where the running sum first exceeds u * S (the same arithmetic, so the two
+// levels agree), re-reads the block where it is crossed and finds the token
+// (inverse CDF over ascending id; if the weights sum to zero, over p'; if
+// rounding leaves no crossing, the largest id with w > 0).
 template <class LT, bool VEC>
 __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   typedef typename LT::T ET;
+  typedef typename LT::Raw LR;
   __shared__ int s_last;
+  __shared__ DrawSum s_blk[kDrawSpan * kWaves];
   const int i = blockIdx.x / (a.dparts + 1), part = blockIdx.x - i * (a.dparts + 1);
   const ReqRec rr = a.rec[i];
   const int gamma = rr.gamma;
@@ -2101,23 +2107,24 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   const float* qrow = (mode == 1) ? a.q + ((size_t)rr.q0 + A) * (size_t)V : nullptr;
   const int nsteps = (V + kStep - 1) / kStep;
   DrawSum* ds = a.dsum + (size_t)i * nsteps * kWaves;
-  const int s0 = part * kDrawSteps;
-  // all of this workgroup's loads first, then the sums
-  typename LT::Raw lr[kDrawSteps];
-  F32::Raw qr[kDrawSteps];
+  DrawSum* dt = a.dtot + (size_t)i * a.dparts;
+  const int s0 = part * kDrawSpan, cnt = min(kDrawSpan, nsteps - s0);
+  // all of this workgroup's loads first, then the sums (block sums go to LDS:
+  // a global store here would count against the counter the loads wait on)
+  LR lr[kDrawSpan];
+  F32::Raw qr[kDrawSpan];
 #pragma unroll
-  for (int u = 0; u < kDrawSteps; ++u) {
+  for (int u = 0; u < kDrawSpan; ++u) {
     const int base = (s0 + u) * kStep + tid * kCh;
-    if (s0 + u < nsteps) {
+    if (u < cnt) {
       lr[u] = load_logits<LT, VEC>(lrow, base, V);
       qr[u] = (mode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
     }
   }
 #pragma unroll
-  for (int u = 0; u < kDrawSteps; ++u) {
-    const int s = s0 + u;
-    if (s >= nsteps) break;
-    const int base = s * kStep + tid * kCh;
+  for (int u = 0; u < kDrawSpan; ++u) {
+    if (u >= cnt) break;
+    const int base = (s0 + u) * kStep + tid * kCh;
     float lv[8], qv[8], w[8], pw[8];
     LT::unpack(lr[u], lv);
     F32::unpack(qr[u], qv);
@@ -2137,7 +2144,25 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
     d.lastw = (int)wave_max_u32(lw);
     d.lastp = (int)wave_max_u32(lp);
     d.pad[0] = d.pad[1] = 0;
-    if (lane == 0) publish(ds + (size_t)s * kWaves + wave, d);
+    if (lane == 0) __builtin_memcpy((DrawSum*)&s_blk[u * kWaves + wave], &d, sizeof(DrawSum));
+  }
+  __syncthreads();
+  if (tid < cnt * kWaves) {
+    DrawSum d;
+    __builtin_memcpy(&d, (const DrawSum*)&s_blk[tid], sizeof(DrawSum));
+    publish(ds + (size_t)s0 * kWaves + tid, d);
+  }
+  if (wave == 0) {
+    // this part's total: the last lane of the scan over its blocks in order
+    DrawSum b{};
+    if (lane < cnt * kWaves) __builtin_memcpy(&b, (const DrawSum*)&s_blk[lane], sizeof(DrawSum));
+    DrawSum t;
+    t.sw = readlane_d(wave_incl_scan_f64(b.sw), 63);
+    t.sp = readlane_d(wave_incl_scan_f64(b.sp), 63);
+    t.lastw = (int)wave_max_u32((uint32_t)b.lastw);
+    t.lastp = (int)wave_max_u32((uint32_t)b.lastp);
+    t.pad[0] = t.pad[1] = 0;
+    if (lane == 0) publish(dt + part, t);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -2147,43 +2172,55 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   __syncthreads();
   if (!s_last || wave != 0) return;
 
-  const int nrec = nsteps * kWaves;
+  // the totals over the parts, in part order
   double tw = 0.0, tp = 0.0;
   uint32_t lastw = 0u, lastp = 0u;
-  for (int r0 = 0; r0 < nrec; r0 += 64) {
+  for (int p0 = 0; p0 < a.dparts; p0 += 64) {
     DrawSum d{};
-    if (r0 + lane < nrec) d = fetch(ds + r0 + lane);
-    tw += d.sw;
-    tp += d.sp;
-    lastw = max(lastw, (uint32_t)d.lastw);
-    lastp = max(lastp, (uint32_t)d.lastp);
+    if (p0 + lane < a.dparts) d = fetch(dt + p0 + lane);
+    tw += readlane_d(wave_incl_scan_f64(d.sw), 63);
+    tp += readlane_d(wave_incl_scan_f64(d.sp), 63);
+    lastw = max(lastw, wave_max_u32((uint32_t)d.lastw));
+    lastp = max(lastp, wave_max_u32((uint32_t)d.lastp));
   }
-  tw = wave_sum_f64(tw);
-  tp = wave_sum_f64(tp);
-  lastw = wave_max_u32(lastw);
-  lastp = wave_max_u32(lastp);
   const bool usep = !(tw > 0.0);  // zero residual: draw from p'
   const double S = usep ? tp : tw;
   const int dmode = usep ? 0 : mode;
   const double tau = (double)a.u_sample[i] * S;
-  // the first block whose running sum exceeds tau
+  // the part, then the block within it, where the running sum first exceeds tau
   double pre = 0.0, pstar = 0.0;
-  int rstar = -1;
-  for (int r0 = 0; r0 < nrec; r0 += 64) {
+  int kstar = -1;
+  for (int p0 = 0; p0 < a.dparts && kstar < 0; p0 += 64) {
     double x = 0.0;
-    if (r0 + lane < nrec) {
-      const DrawSum d = fetch(ds + r0 + lane);
+    if (p0 + lane < a.dparts) {
+      const DrawSum d = fetch(dt + p0 + lane);
       x = usep ? d.sp : d.sw;
     }
     const double incl = wave_incl_scan_f64(x);
-    const uint64_t hit = __ballot(r0 + lane < nrec && x > 0.0 && pre + incl > tau);
+    const uint64_t hit = __ballot(p0 + lane < a.dparts && x > 0.0 && pre + incl > tau);
     if (hit) {
       const int l = __ffsll((unsigned long long)hit) - 1;
-      rstar = r0 + l;
+      kstar = p0 + l;
       pstar = pre + (l > 0 ? readlane_d(incl, l - 1) : 0.0);
-      break;
+    } else {
+      pre += readlane_d(incl, 63);
     }
-    pre += readlane_d(incl, 63);
+  }
+  int rstar = -1;
+  if (kstar >= 0) {
+    const int k0 = kstar * kDrawSpan, kc = min(kDrawSpan, nsteps - k0);
+    double x = 0.0;
+    if (lane < kc * kWaves) {
+      const DrawSum d = fetch(ds + (size_t)k0 * kWaves + lane);
+      x = usep ? d.sp : d.sw;
+    }
+    const double incl = wave_incl_scan_f64(x);
+    const uint64_t hit = __ballot(lane < kc * kWaves && x > 0.0 && pstar + incl > tau);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      rstar = k0 * kWaves + l;
+      pstar += (l > 0 ? readlane_d(incl, l - 1) : 0.0);
+    }
   }
   int z;
   if (rstar < 0) {
@@ -2274,6 +2311,8 @@ size_t plan_bytes(int N, int G) { return align_up(((size_t)N * G + 1) * sizeof(i
 size_t dsum_bytes(int N, int V) {
   return align_up((size_t)N * ((V + kStep - 1) / kStep) * kWaves * sizeof(DrawSum), 256);
 }
+size_t draw_parts(int V) { return ((size_t)(V + kStep - 1) / kStep + kDrawSpan - 1) / kDrawSpan; }
+size_t dtot_bytes(int N, int V) { return align_up((size_t)N * draw_parts(V) * sizeof(DrawSum), 256); }
 
 struct DeviceBuffer {
   void* ptr = nullptr;
@@ -2319,7 +2358,7 @@ int run(int N, int G, int V, const Layout& lay, const int32_t* ids, const float*
   if (dtype != SPEC_VERIFY_F32 && dtype != SPEC_VERIFY_BF16) return SPEC_VERIFY_ERR_DTYPE;
   if ((long long)V * (G + 1) > (1LL << 40) || V > 0x7fffffff - 2 * kStep) return SPEC_VERIFY_ERR_SHAPE;
   // a dispatch holds its grid size in work-items as a 32-bit number
-  const long long dparts = ((long long)(V + kStep - 1) / kStep + kDrawSteps - 1) / kDrawSteps;
+  const long long dparts = (long long)draw_parts(V);
   if ((long long)N * (G + 1) * kBlock > 0xffffffffLL || (long long)N * (dparts + 1) * kBlock > 0xffffffffLL)
     return SPEC_VERIFY_ERR_SHAPE;
   if (N == 0) return SPEC_VERIFY_OK;
@@ -2371,6 +2410,8 @@ int run(int N, int G, int V, const Layout& lay, const int32_t* ids, const float*
   off += done_bytes(N);
   a.dsum = reinterpret_cast<DrawSum*>(ws + off);
   off += dsum_bytes(N, V);
+  a.dtot = reinterpret_cast<DrawSum*>(ws + off);
+  off += dtot_bytes(N, V);
   a.plan = reinterpret_cast<int*>(ws + off);
   a.dparts = (int)dparts;
   a.cu = lay.cu;
@@ -2395,7 +2436,8 @@ extern "C" {
 
 size_t spec_verify_workspace_size(int N, int gmax, int V) {
   if (N <= 0 || gmax < 0 || V <= 0) return 256;
-  return stats_bytes(N, gmax) + rec_bytes(N) + done_bytes(N) + dsum_bytes(N, V) + plan_bytes(N, gmax);
+  return stats_bytes(N, gmax) + rec_bytes(N) + done_bytes(N) + dsum_bytes(N, V) + dtot_bytes(N, V) +
+         plan_bytes(N, gmax);
 }
 
 int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* draft_probs, const void* target_logits,

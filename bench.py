@@ -53,6 +53,23 @@ def workload_bytes(batch):
     return target + draft + small, target, draft
 
 
+def synthetic_bytes(batch, rates):
+    """Algorithmic bytes of the synthetic acceptance mode: only row A_i of each
+    request is read (A_i = the first j with u_j >= rate_j, else gamma_i), its
+    draft row too when A_i < gamma_i and the request carries draft rows."""
+    import numpy as np
+    V = batch["target_logits"].shape[-1]
+    s_l = 2 if batch["dtype"] == "bf16" else 4
+    N, G = batch["draft_ids"].shape
+    gam = batch["gamma"].astype(np.int64)
+    hq = batch["has_q"] if batch["draft_probs"] is not None else np.zeros(N, bool)
+    total = 0
+    for i in range(N):
+        A = next((j for j in range(gam[i]) if not batch["u_accept"][i, j] < rates[j]), gam[i])
+        total += V * s_l + (V * 4 if (A < gam[i] and hq[i]) else 0)
+    return total + N * G * 4 * 2 + N * 4 * 4 + N * (G + 1) * 4 + N * 4
+
+
 def traffic_from_profile(digest, workload):
     """HBM bytes per row-kernel launch from the committed counter summary, if
     it was taken on this exact kernel source and workload; else None."""
@@ -101,6 +118,9 @@ def main():
     ap.add_argument("--rollback", action="store_true",
                     help="also enqueue the KV bookkeeping (spec_verify_rollback) after every verify call, "
                          "inside the timed step")
+    ap.add_argument("--synthetic-rates", default=None,
+                    help="comma-separated per-position acceptance rates: run the synthetic acceptance mode "
+                         "(flattened layout; only row A of each request is read)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -125,12 +145,19 @@ def main():
           file=sys.stderr, flush=True)
     batch = W.generate(spec, threads=threads)
     mixed = batch["draft_probs"] is not None and not batch["has_q"].all()
-    flat = args.layout == "flat" or (args.layout == "auto" and mixed)
+    rates = None if args.synthetic_rates is None else np.array(
+        [float(x) for x in args.synthetic_rates.split(",")], np.float32)
+    if rates is not None and len(rates) != spec.gmax:
+        sys.exit("--synthetic-rates needs %d rates" % spec.gmax)
+    flat = args.layout == "flat" or (args.layout == "auto" and mixed) or rates is not None
     if flat:
         parts = [W.flatten(batch)]
     else:
         parts = W.split_by_q(batch) if mixed else [batch]
     B_alg, B_target, B_draft = workload_bytes(batch)
+    if rates is not None:
+        B_alg = synthetic_bytes(batch, rates)
+        B_target = B_draft = None
     positions = int(batch["gamma"].sum())
     rows = int((batch["gamma"] + 1).sum())
 
@@ -153,6 +180,8 @@ def main():
                 d["nct"] = torch.full((Np,), 1 << 20, dtype=torch.int32, device=dev)
                 d["slots"] = torch.arange(d["draft_ids"].numel(), dtype=torch.int32, device=dev).view(
                     d["draft_ids"].shape)
+            if rates is not None:
+                d["rates"] = torch.from_numpy(rates).to(dev)
             ps.append(d)
         sets.append(ps)
     del batch["target_logits"], batch["draft_probs"]
@@ -164,6 +193,8 @@ def main():
             if events is not None:
                 ev = events[pi]
             kw = dict(out_tokens=d["out_t"], out_num_accepted=d["out_n"], workspace=d["ws"], stream=stream, events=ev)
+            if rates is not None:
+                kw.update(synthetic_rates=d["rates"])
             if flat:
                 sv.verify_flat_batch(d, **kw)
             else:
@@ -239,6 +270,7 @@ def main():
         "config": {"workload": desc, "requests": spec.N, "gamma": spec.gmax, "vocab": spec.V,
                    "layout": "flattened, one call" if flat else "padded, %d call(s)" % len(parts),
                    "kv_rollback_in_step": bool(args.rollback),
+                   "synthetic_rates": None if rates is None else [float(x) for x in rates],
                    "target_logits": spec.dtype, "draft_probs": "f32" if spec.q_mode != "null" else None,
                    "verified_positions_per_step": positions, "rows_per_step": rows,
                    "algorithmic_bytes_per_step": B_alg, "target_bytes": B_target, "draft_bytes": B_draft},

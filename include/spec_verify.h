@@ -194,6 +194,32 @@ int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t
                            void *ev_end);
 
 /*
+ * The synthetic acceptance mode (vLLM page, section "关于 synthetic / block
+ * 验证模式"), for exercising a drafter without real target probabilities:
+ * draft j of every request is accepted iff u_accept < synthetic_rates[j]
+ * (DEVICE float32 [gmax], expected non-increasing in j; the rule is applied
+ * as given), so the first rejection A_i is known before any row is read and
+ * the row pass streams only row A_i of each request.  The token at A_i is
+ * drawn as in spec_verify: the argmax of row A_i for a greedy request, else
+ * the replacement from max(0, p' - q') (p' if that is zero) at a rejection, or
+ * the bonus from p' when every draft was accepted.  Faults come from the
+ * request's parameters and from row A_i (the other rows are not read).
+ * Arguments as for spec_verify_flat, plus `fault` (DEVICE int32 [N] or NULL)
+ * and the three optional events of spec_verify_timed.  Returns
+ * SPEC_VERIFY_ERR_NULL for a NULL synthetic_rates when N > 0 and gmax > 0.
+ */
+int spec_verify_flat_synthetic(int N, int gmax, int V, int num_drafts,
+                               const int32_t *cu_num_draft_tokens, const int32_t *draft_ids,
+                               const float *draft_probs, const uint8_t *has_draft_probs,
+                               const void *target_logits, int logits_dtype,
+                               const float *temperature, const int32_t *top_k, const float *top_p,
+                               const float *synthetic_rates, const float *u_accept,
+                               const float *u_sample, int32_t *out_tokens,
+                               int32_t *out_num_accepted, int32_t *fault, void *workspace,
+                               size_t workspace_bytes, void *stream, void *ev_start, void *ev_mid,
+                               void *ev_end);
+
+/*
  * KV bookkeeping after a verify call, enqueued on `stream` after it (KV page
  * "投机解码如何与 KV Cache 交互：Placeholder、回滚与草稿 KV", sections 3.1 and 3.2;
  * vLLM page, the padded drafter batch paragraph: rejected draft slots become

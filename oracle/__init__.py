@@ -52,6 +52,9 @@ def _bind(path):
     lib.oracle_spec_verify.restype = ctypes.c_int
     lib.oracle_spec_verify.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int] + [P] * 2 + \
         [P, ctypes.c_int] + [P] * 12
+    lib.oracle_spec_verify_synthetic.restype = ctypes.c_int
+    lib.oracle_spec_verify_synthetic.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int] + [P] * 2 + \
+        [P, ctypes.c_int] + [P] * 11
     lib.oracle_target_probs.restype = ctypes.c_int
     lib.oracle_target_probs.argtypes = [ctypes.c_int, P, ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                         ctypes.c_double, P, P]
@@ -80,13 +83,14 @@ def _c(a, dtype):
 
 
 def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=None, top_p=None,
-        u_accept=None, u_sample=None, threads: int = 1, _lib_override=None) -> dict:
+        u_accept=None, u_sample=None, threads: int = 1, _lib_override=None, synthetic_rates=None) -> dict:
     """Verify a batch on the CPU.
 
     ``dtype`` is "f32" (``target_logits`` float32) or "bf16" (``target_logits``
     uint16 bit patterns).  Returns a dict with tokens [N,gmax+1], num_accepted
     [N], p_y / q_y [N,gmax] (NaN where not computed), resid_mass [N], margin [N]
-    and fault [N].
+    and fault [N].  With ``synthetic_rates`` (float32 [gmax]) the synthetic
+    acceptance mode runs instead: draft j is accepted iff u_j < rate_j.
     """
     lib = _lib_override or _load()
     ids = _c(draft_ids, np.int32)
@@ -111,10 +115,21 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
     def sl(a, lo):
         return None if a is None else a[lo:].ctypes.data
 
+    rates = None if synthetic_rates is None else _c(synthetic_rates, np.float32)
+    if rates is not None:
+        assert rates.shape == (gmax,), rates.shape
+        out["p_y"][:] = np.nan
+        out["q_y"][:] = np.nan
+
     def one(lo, hi):
         n = hi - lo
         if n <= 0:
             return 0
+        if rates is not None:
+            return lib.oracle_spec_verify_synthetic(
+                n, gmax, V, sl(ids, lo), sl(q, lo), sl(tl, lo), dt, sl(T, lo), sl(k, lo), sl(p, lo),
+                rates.ctypes.data, sl(ua, lo), sl(us, lo), sl(out["tokens"], lo), sl(out["num_accepted"], lo),
+                sl(out["resid_mass"], lo), sl(out["margin"], lo), sl(out["fault"], lo))
         return lib.oracle_spec_verify(n, gmax, V, sl(ids, lo), sl(q, lo), sl(tl, lo), dt, sl(T, lo), sl(k, lo),
                                       sl(p, lo), sl(ua, lo), sl(us, lo), sl(out["tokens"], lo),
                                       sl(out["num_accepted"], lo), sl(out["p_y"], lo), sl(out["q_y"], lo),

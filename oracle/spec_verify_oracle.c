@@ -20,7 +20,9 @@
  *          两个分支" (bonus token, temperature/top-k/top-p preprocessing, -1
  *          placeholder output), "Greedy kernel：逐 token 比较" and
  *          "Random kernel：无偏接受 + 重采样" (draft-free residual: the draft
- *          token's cell removed).
+ *          token's cell removed), "关于 synthetic / block 验证模式" (synthetic
+ *          acceptance: draft j accepted iff u_j < rate_j, no target
+ *          probabilities).
  *
  * Readings taken where the sources are silent or disagree (each is restated in
  * the design notes of the repository):
@@ -283,6 +285,55 @@ static void write_fault(request_t *r, int fault) {
 }
 
 /*
+ * The token at the first rejection A (or the bonus position A = g): the
+ * replacement weights max(0, p' - q') at a rejection [SD §04], with q' the
+ * one-hot of the draft token when there are no draft probabilities [VLLM,
+ * "Random kernel"], or p' of the bonus row when every draft was accepted
+ * [SD §03, §06]; zero residual mass falls back to p'_A.  P[A] (and Q[A] with
+ * draft probabilities, P[g] for the bonus) must be filled.
+ */
+static int32_t draw_token(const request_t *r, double *const *P, double *const *Q, int A, int g, double *S_out,
+                          double *cmargin) {
+    const long V = r->V;
+    double *w = (double *)malloc(sizeof(double) * V);
+    double S = 0.0;
+    long x;
+    if (A < g) {
+        for (x = 0; x < V; x++) {
+            double qx = r->q ? Q[A][x] : (x == r->ids[A] ? 1.0 : 0.0);
+            double d = P[A][x] - qx;
+            w[x] = d > 0.0 ? d : 0.0;
+            S += w[x];
+        }
+        if (S == 0.0) {
+            for (x = 0; x < V; x++) {
+                w[x] = P[A][x];
+                S += w[x];
+            }
+        }
+    } else {
+        for (x = 0; x < V; x++) {
+            w[x] = P[g][x];
+            S += w[x];
+        }
+    }
+    int32_t z = inverse_cdf(V, w, S, r->u_sample, cmargin);
+    *S_out = S;
+    free(w);
+    return z;
+}
+
+/* output row: accepted drafts, then the replacement or bonus, then -1
+ * [VLLM, "拒绝采样…两个分支", output buffer of max_spec_len + 1] */
+static void write_output(request_t *r, int A, int32_t z) {
+    int j;
+    for (j = 0; j <= r->gmax; j++) r->tokens[j] = -1;
+    for (j = 0; j < A; j++) r->tokens[j] = r->ids[j];
+    r->tokens[A] = z;
+    *r->num_accepted = A;
+}
+
+/*
  * One request: the round of [SD §06] in the batched form of [VLLM,
  * "拒绝采样…两个分支"].
  */
@@ -399,36 +450,11 @@ static void verify_request(request_t *r) {
         }
         if (A == g && topp_m[2 * g] < mg) mg = topp_m[2 * g];
 
-        /* replacement weights max(0, p' - q') at the first rejection [SD §04],
-         * or p' of the bonus row when every draft was accepted [SD §03, §06] */
-        double *w = (double *)malloc(sizeof(double) * V);
-        double S = 0.0;
-        long x;
-        if (A < g) {
-            for (x = 0; x < V; x++) {
-                double qx = r->q ? Q[A][x] : (x == r->ids[A] ? 1.0 : 0.0);
-                double d = P[A][x] - qx;
-                w[x] = d > 0.0 ? d : 0.0;
-                S += w[x];
-            }
-            if (S == 0.0) {
-                for (x = 0; x < V; x++) {
-                    w[x] = P[A][x];
-                    S += w[x];
-                }
-            }
-        } else {
-            for (x = 0; x < V; x++) {
-                w[x] = P[g][x];
-                S += w[x];
-            }
-        }
-        double cm;
-        z = inverse_cdf(V, w, S, r->u_sample, &cm);
+        double cm, S;
+        z = draw_token(r, P, Q, A, g, &S, &cm);
         if (cm < mg) mg = cm;
         if (r->resid_mass) *r->resid_mass = S;
         if (r->margin) *r->margin = mg;
-        free(w);
         for (j = 0; j <= g; j++) {
             free(P[j]);
             free(Q[j]);
@@ -438,12 +464,7 @@ static void verify_request(request_t *r) {
         free(topp_m);
     }
 
-    /* output row: accepted drafts, then the replacement or bonus, then -1
-     * [VLLM, "拒绝采样…两个分支", output buffer of max_spec_len + 1] */
-    for (j = 0; j <= r->gmax; j++) r->tokens[j] = -1;
-    for (j = 0; j < A; j++) r->tokens[j] = r->ids[j];
-    r->tokens[A] = z;
-    *r->num_accepted = A;
+    write_output(r, A, z);
 }
 
 /*
@@ -485,6 +506,126 @@ int oracle_spec_verify(int N, int gmax, int V, const int32_t *draft_ids, const f
         r.margin = margin ? margin + i : NULL;
         r.fault_out = fault ? fault + i : NULL;
         verify_request(&r);
+    }
+    return 0;
+}
+
+/*
+ * One request in the synthetic acceptance mode [VLLM, "关于 synthetic / block
+ * 验证模式"]: draft j is accepted iff u_j < rate_j, without the target
+ * probabilities, so A (the first rejection, or gamma) is known before any row
+ * is read.  Readings: only row A is read (faults come from it and from the
+ * request's parameters), and its token is drawn as in the standard method:
+ * the argmax of row A for a greedy request, else the replacement
+ * max(0, p'_A - q'_A) (p'_A if that is zero) at a rejection, or p' of the
+ * bonus row.  p_y and q_y are not computed (NaN).
+ */
+static void verify_request_synthetic(request_t *r, const float *rates) {
+    const long V = r->V;
+    int j, g = r->gmax, fault = 0;
+
+    if (r->p_y)
+        for (j = 0; j < r->gmax; j++) r->p_y[j] = NAN;
+    if (r->q_y)
+        for (j = 0; j < r->gmax; j++) r->q_y[j] = NAN;
+    if (r->resid_mass) *r->resid_mass = NAN;
+    if (r->margin) *r->margin = INFINITY;
+    if (r->fault_out) *r->fault_out = 0;
+
+    for (j = 0; j < r->gmax; j++)
+        if (r->ids[j] < 0) {
+            g = j;
+            break;
+        }
+    for (j = 0; j < g; j++)
+        if (r->ids[j] >= V) fault |= OF_DRAFT_ID;
+    const double T = r->T;
+    if (isnan(T) || T < 0.0 || isinf(T) || (T > 0.0 && T < (double)FLT_MIN)) fault |= OF_TEMPERATURE;
+    const int greedy = (T == 0.0);
+    if (!greedy && !(fault & OF_TEMPERATURE) && (isnan(r->top_p) || r->top_p <= 0.0)) fault |= OF_TOP_P;
+    if (fault) {
+        write_fault(r, fault);
+        return;
+    }
+
+    /* the synthetic accept test, position by position until the first rejection */
+    double mg = INFINITY;
+    int A = g;
+    for (j = 0; j < g; j++) {
+        double u = (double)r->u_accept[j], rate = (double)rates[j];
+        double d = fabs(u - rate);
+        if (d < mg) mg = d;
+        if (!(u < rate)) {
+            A = j;
+            break;
+        }
+    }
+
+    int32_t z = -1;
+    if (greedy) {
+        fault |= greedy_row(V, logit_row(r, A), r->dtype, &z);
+    } else {
+        /* only row A's distributions: P[A] (also P[g] when A = g), Q[A] */
+        double **P = (double **)calloc((size_t)g + 1, sizeof(double *));
+        double **Q = (double **)calloc((size_t)g + 1, sizeof(double *));
+        double tm;
+        P[A] = (double *)malloc(sizeof(double) * V);
+        fault |= target_probs_row(V, logit_row(r, A), r->dtype, T, r->top_k, r->top_p, P[A], &tm);
+        if (tm < mg) mg = tm;
+        if (!fault && A < g && r->q) {
+            Q[A] = (double *)malloc(sizeof(double) * V);
+            fault |= draft_probs_row(V, r->q + (size_t)A * V, T, r->top_k, r->top_p, Q[A], &tm);
+            if (tm < mg) mg = tm;
+        }
+        if (!fault) {
+            double cm, S;
+            z = draw_token(r, P, Q, A, g, &S, &cm);
+            if (cm < mg) mg = cm;
+            if (r->resid_mass) *r->resid_mass = S;
+        }
+        free(P[A]);
+        free(Q[A]);
+        free(P);
+        free(Q);
+    }
+    if (fault) {
+        write_fault(r, fault);
+        return;
+    }
+    if (r->margin) *r->margin = mg;
+    write_output(r, A, z);
+}
+
+/* The batched entry of the synthetic acceptance mode; rates [gmax]. */
+int oracle_spec_verify_synthetic(int N, int gmax, int V, const int32_t *draft_ids, const float *draft_probs,
+                                 const void *target_logits, int dtype, const float *temperature,
+                                 const int32_t *top_k, const float *top_p, const float *rates,
+                                 const float *u_accept, const float *u_sample, int32_t *out_tokens,
+                                 int32_t *out_num_accepted, double *resid_mass, double *margin, int32_t *fault) {
+    int i;
+    if (N < 0 || gmax < 0 || V < 1 || (dtype != 0 && dtype != 1) || (gmax > 0 && !rates)) return 1;
+    size_t esz = dtype == 1 ? 2 : 4;
+    for (i = 0; i < N; i++) {
+        request_t r;
+        r.V = V;
+        r.gmax = gmax;
+        r.ids = draft_ids + (size_t)i * gmax;
+        r.q = draft_probs ? draft_probs + (size_t)i * gmax * V : NULL;
+        r.logits = (const char *)target_logits + (size_t)i * (gmax + 1) * (size_t)V * esz;
+        r.dtype = dtype;
+        r.T = temperature ? (double)temperature[i] : 1.0;
+        r.top_k = top_k ? top_k[i] : 0;
+        r.top_p = top_p ? (double)top_p[i] : 1.0;
+        r.u_accept = u_accept + (size_t)i * gmax;
+        r.u_sample = (double)u_sample[i];
+        r.tokens = out_tokens + (size_t)i * (gmax + 1);
+        r.num_accepted = out_num_accepted + i;
+        r.p_y = NULL;
+        r.q_y = NULL;
+        r.resid_mass = resid_mass ? resid_mass + i : NULL;
+        r.margin = margin ? margin + i : NULL;
+        r.fault_out = fault ? fault + i : NULL;
+        verify_request_synthetic(&r, rates);
     }
     return 0;
 }

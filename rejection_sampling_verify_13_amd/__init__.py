@@ -27,7 +27,8 @@ FAULT_DRAFT_MASS = 32
 FAULT_DRAFT_COUNT = 64
 
 EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_timed", "spec_verify_flat", "spec_verify_flat_timed",
-           "spec_verify_rollback", "spec_verify_workspace_size", "spec_verify_status_string", "spec_verify_version")
+           "spec_verify_flat_synthetic", "spec_verify_rollback", "spec_verify_workspace_size",
+           "spec_verify_status_string", "spec_verify_version")
 
 
 class SpecVerifyError(RuntimeError):
@@ -52,6 +53,9 @@ def _load():
     lib.spec_verify_flat_timed.restype = I
     lib.spec_verify_flat_timed.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P, Z, P,
                                            P, P, P]
+    lib.spec_verify_flat_synthetic.restype = I
+    lib.spec_verify_flat_synthetic.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, Z, P,
+                                               P, P, P]
     lib.spec_verify_rollback.restype = I
     lib.spec_verify_rollback.argtypes = [I, I, P, P, P, P, P, P, P]
     lib.spec_verify_workspace_size.restype = Z
@@ -164,7 +168,7 @@ def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, 
 
 def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, target_logits, gmax,
                 temperature=None, top_k=None, top_p=None, u_accept=None, u_sample=None, *, out_tokens=None,
-                out_num_accepted=None, workspace=None, stream=None, diag=False, events=None):
+                out_num_accepted=None, workspace=None, stream=None, diag=False, events=None, synthetic_rates=None):
     """Verify a batch in the flattened layout (spec_verify_flat in include/spec_verify.h).
 
     cu_num_draft_tokens int32 [N] (inclusive prefix sums of the draft counts),
@@ -174,7 +178,9 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
     positions, then its bonus position), gmax (the output width is gmax + 1),
     temperature / top_k / top_p / u_sample [N] as for verify(), u_accept
     float32 [T].  Returns what verify() returns; with diag=True p_y and q_y
-    are [N, gmax].  ``events`` as for verify().
+    are [N, gmax].  ``events`` as for verify().  With ``synthetic_rates``
+    (float32 [gmax]) the synthetic acceptance mode runs (spec_verify_flat_synthetic):
+    draft j is accepted iff u_accept < rate_j; diag then returns only ``fault``.
     """
     if target_logits.dim() != 2:
         raise ValueError("target_logits must be [T + N, V]")
@@ -221,6 +227,19 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
             _ptr(target_logits), dt, _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(u_accept), _ptr(u_sample),
             _ptr(out_tokens), _ptr(out_num_accepted))
     d = None
+    if synthetic_rates is not None:
+        _check(synthetic_rates, "synthetic_rates", torch.float32, (G,), dev)
+        if diag:
+            d = dict(fault=torch.empty((N,), dtype=torch.int32, device=dev))
+        evp = (None, None, None) if events is None else tuple(
+            None if e is None else ctypes.c_void_p(e.cuda_event) for e in events)
+        with torch.cuda.device(dev):
+            rc = lib.spec_verify_flat_synthetic(*head[:13], _ptr(synthetic_rates), *head[13:],
+                                                _ptr(d["fault"]) if diag else None, _ptr(workspace), ws_bytes, sptr,
+                                                *evp)
+        if rc != 0:
+            raise SpecVerifyError("spec_verify_flat_synthetic failed: %s" % lib.spec_verify_status_string(rc).decode())
+        return (out_tokens, out_num_accepted, d) if diag else (out_tokens, out_num_accepted)
     with torch.cuda.device(dev):
         if diag or events is not None:
             if diag:

@@ -142,13 +142,15 @@ struct Args {
   ReqRec* rec;          // per request
   DrawSum* dsum;        // [N][steps][kWaves]
   unsigned int* ddone;  // completion counter per request (draw pass)
-  int* plan;            // [0]: number of draft rows D; then D entries i * 64 + j, request-major
+  int* plan;            // [0]: number of listed rows D; then D entries i * 128 + j, request-major
   DrawSum* dtot;        // [N][dparts] sums of each draw workgroup's blocks
   int dparts;           // draw pass: workgroups per request (kDrawSpan steps each)
   // flattened layout (cu == nullptr: the padded [N, G] layout)
   const int32_t* cu;    // [N] inclusive prefix sums of gamma_i
   const uint8_t* has_q; // [N] request i has draft rows iff nonzero; nullptr: all do (when q != nullptr)
   int T;                // number of drafts, cu[N - 1]
+  int synthetic;        // 1: the synthetic acceptance mode (draft j accepted iff u_j < srates[j])
+  const float* srates;  // synthetic acceptance rates [G]
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -1568,7 +1570,7 @@ __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, 
     s.p_y = NAN;
     s.q_y = NAN;
     s.s = NAN;
-    s.flags = ((j < rq.gamma && y == cand) ? 1 : 0) | (fault << 8);
+    s.flags = ((!a.synthetic && j < rq.gamma && y == cand) ? 1 : 0) | (fault << 8);
     s.draw = s.argmax;  // a greedy row's token is its argmax
     publish(a.stats + row, s);
     note_row(a, i, j, s.flags & 1, fault, false);
@@ -1824,7 +1826,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       double qy = 1.0;
       if (req_q) qy = (qyv >= cut_q) ? temper_q(qyv, T) / Rk : 0.0;
       const double u = (double)a.u_accept[(size_t)rq.id0 + j];
-      acc = (u * qy < py) ? 1 : 0;
+      acc = (!a.synthetic && u * qy < py) ? 1 : 0;  // synthetic mode: the listed draft row is A
       s.p_y = py;
       s.q_y = qy;
     }
@@ -1878,37 +1880,40 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
   if (tid < 2) s_base[tid] = 0;
   __syncthreads();
   for (int r0 = 0; r0 < a.N; r0 += kBlock * kPer) {
-    int g[kPer], gq[kPer], id0[kPer];
+    int gam[kPer], nl[kPer], gq[kPer], id0[kPer];
     unsigned int lf[kPer];
     bool hq[kPer];
     int cnt = 0, qcnt = 0;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = r0 + tid * kPer + u;
-      g[u] = gq[u] = id0[u] = 0;
+      gam[u] = nl[u] = gq[u] = id0[u] = 0;
       lf[u] = 0u;
       hq[u] = false;
       if (i < a.N) {
         a.ddone[i] = 0u;
         if (a.cu) {
           const int prev = i ? a.cu[i - 1] : 0, cur = a.cu[i];
-          const long long gam = (long long)cur - prev;
+          const long long g = (long long)cur - prev;
           id0[u] = prev;
           hq[u] = a.q && (!a.has_q || a.has_q[i]);
-          if (prev < 0 || gam < 0 || gam > a.G || cur > a.T) lf[u] = kFaultDraftCount;
-          else g[u] = (int)gam;
+          if (prev < 0 || g < 0 || g > a.G || cur > a.T) lf[u] = kFaultDraftCount;
+          else gam[u] = (int)g;
           // later requests' draft-probability rows sit after this one's, whatever its count
-          gq[u] = (hq[u] && gam > 0) ? (int)min(gam, (long long)a.T) : 0;
+          gq[u] = (hq[u] && g > 0) ? (int)min(g, (long long)a.T) : 0;
         } else {
-          int gam = a.G;
+          int g = a.G;
           for (int jj = a.G - 1; jj >= 0; --jj)
-            if (a.ids[(size_t)i * a.G + jj] < 0) gam = jj;
-          g[u] = gam;
+            if (a.ids[(size_t)i * a.G + jj] < 0) g = jj;
+          gam[u] = g;
           id0[u] = i * a.G;
           hq[u] = a.q != nullptr;
         }
+        // rows listed: the draft rows; in the synthetic mode only row A (the bonus
+        // rows of the standard mode are launched after the listed ones)
+        nl[u] = a.synthetic ? 1 : gam[u];
       }
-      cnt += g[u];
+      cnt += nl[u];
       qcnt += gq[u];
     }
     // exclusive offsets: wave scans, then the four wave totals
@@ -1930,21 +1935,32 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
     for (int u = 0; u < kPer; ++u) {
       const int i = r0 + tid * kPer + u;
       if (i < a.N) {
+        // synthetic mode: draft j is accepted iff u_j < rate_j, so the first
+        // rejection A is known before any row is read
+        int As = gam[u];
+        if (a.synthetic)
+          for (int jj = 0; jj < gam[u]; ++jj)
+            if (!(a.u_accept[(size_t)id0[u] + jj] < a.srates[jj])) {
+              As = jj;
+              break;
+            }
         ReqRec r;
-        r.acc = 0ull;
+        r.acc = !a.synthetic ? 0ull : (As >= 64 ? ~0ull : ((1ull << As) - 1ull));
         r.nodraw = 0ull;
         r.nodraw64 = 0u;
         r.fault = 0u;
-        r.gamma = g[u];
+        r.gamma = gam[u];
         r.tgt0 = a.cu ? id0[u] + i : i * (a.G + 1);
         r.id0 = id0[u];
         r.q0 = !hq[u] ? -1 : (a.cu ? qoff : i * a.G);
         r.lfault = lf[u];
         r.pad = 0;
         a.rec[i] = r;
+        if (a.synthetic) a.plan[1 + off] = i * 128 + As;
+        else
+          for (int jj = 0; jj < gam[u]; ++jj) a.plan[1 + off + jj] = i * 128 + jj;
       }
-      for (int jj = 0; jj < g[u]; ++jj) a.plan[1 + off + jj] = i * 64 + jj;
-      off += g[u];
+      off += nl[u];
       qoff += gq[u];
     }
     __syncthreads();
@@ -1966,12 +1982,12 @@ __global__ __launch_bounds__(kBlock, 3) void row_kernel(Args a) {
   // N * (gmax + 1) blocks and the ones past the real rows exit at once
   const int nd = a.plan[0];
   const int bx = (int)blockIdx.x;
-  if (bx >= nd + a.N) return;
+  if (bx >= nd + (a.synthetic ? 0 : a.N)) return;
   const bool bonus = bx >= nd;
   const int m = bonus ? 0 : a.plan[1 + bx];
-  const int i = bonus ? bx - nd : (m >> 6);
+  const int i = bonus ? bx - nd : (m >> 7);
   const Req rq = load_req(a, i);
-  const int j = bonus ? rq.gamma : (m & 63);
+  const int j = bonus ? rq.gamma : (m & 127);
   if (rq.fault) {
     if (threadIdx.x == 0) note_row(a, i, j, 0, rq.fault, false);
     return;
@@ -2055,7 +2071,7 @@ __device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, i
   }
   if (a.d_py || a.d_qy) {
     for (int t = tid; t < G; t += kBlock) {
-      const bool real = t < rr.gamma;
+      const bool real = t < rr.gamma && !a.synthetic;
       if (a.d_py) a.d_py[(size_t)i * G + t] = real ? st[t].p_y : NAN;
       if (a.d_qy) a.d_qy[(size_t)i * G + t] = real ? st[t].q_y : NAN;
     }
@@ -2327,7 +2343,7 @@ struct Events {
 
 template <class LT, bool VEC>
 hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
-  const long rows = (long)a.N * (a.G + 1);
+  const long rows = a.synthetic ? (long)a.N : (long)a.N * (a.G + 1);  // synthetic mode: row A only
   hipError_t e;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2348,7 +2364,7 @@ struct Layout {
   int T;
 };
 
-int run(int N, int G, int V, const Layout& lay, const int32_t* ids, const float* q, const void* logits, int dtype,
+int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* srates, const int32_t* ids, const float* q, const void* logits, int dtype,
         const float* temperature, const int32_t* top_k, const float* top_p, const float* u_accept,
         const float* u_sample, int32_t* out_tokens, int32_t* out_num, double* p_y, double* q_y, double* resid,
         int32_t* fault, void* workspace, size_t workspace_bytes, void* stream, const Events& ev) {
@@ -2417,6 +2433,8 @@ int run(int N, int G, int V, const Layout& lay, const int32_t* ids, const float*
   a.cu = lay.cu;
   a.has_q = lay.has_q;
   a.T = lay.T;
+  a.synthetic = synthetic ? 1 : 0;
+  a.srates = srates;
 
   // 16-byte vector loads need every row start aligned: V a multiple of 8 and
   // 16-byte aligned base pointers
@@ -2444,7 +2462,7 @@ int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* d
                 int logits_dtype, const float* temperature, const int32_t* top_k, const float* top_p,
                 const float* u_accept, const float* u_sample, int32_t* out_tokens, int32_t* out_num_accepted,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes,
              stream, Events{nullptr, nullptr, nullptr});
 }
@@ -2454,7 +2472,7 @@ int spec_verify_diag(int N, int gmax, int V, const int32_t* draft_ids, const flo
                      const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
                      int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{nullptr, nullptr, nullptr});
 }
@@ -2465,7 +2483,7 @@ int spec_verify_timed(int N, int gmax, int V, const int32_t* draft_ids, const fl
                       int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
                       void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_mid,
                       void* ev_end) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
                     reinterpret_cast<hipEvent_t>(ev_end)});
@@ -2477,7 +2495,7 @@ int spec_verify_flat(int N, int gmax, int V, int num_drafts, const int32_t* cu_n
                      const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
                      int32_t* out_num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
-  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, draft_ids, draft_probs,
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, draft_ids, draft_probs,
              target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens,
              out_num_accepted, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
              Events{nullptr, nullptr, nullptr});
@@ -2491,9 +2509,25 @@ int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t
                            double* resid_mass, int32_t* fault, void* workspace, size_t workspace_bytes, void* stream,
                            void* ev_start, void* ev_mid, void* ev_end) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
-  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, draft_ids, draft_probs,
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, draft_ids, draft_probs,
              target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens,
              out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
+             Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
+                    reinterpret_cast<hipEvent_t>(ev_end)});
+}
+
+int spec_verify_flat_synthetic(int N, int gmax, int V, int num_drafts, const int32_t* cu_num_draft_tokens,
+                               const int32_t* draft_ids, const float* draft_probs, const uint8_t* has_draft_probs,
+                               const void* target_logits, int logits_dtype, const float* temperature,
+                               const int32_t* top_k, const float* top_p, const float* synthetic_rates,
+                               const float* u_accept, const float* u_sample, int32_t* out_tokens,
+                               int32_t* out_num_accepted, int32_t* fault, void* workspace, size_t workspace_bytes,
+                               void* stream, void* ev_start, void* ev_mid, void* ev_end) {
+  if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
+  if (N > 0 && gmax > 0 && !synthetic_rates) return SPEC_VERIFY_ERR_NULL;
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, true, synthetic_rates, draft_ids, draft_probs, target_logits, logits_dtype,
+             temperature, top_k, top_p, u_accept, u_sample, out_tokens, out_num_accepted, nullptr, nullptr, nullptr,
+             fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
                     reinterpret_cast<hipEvent_t>(ev_end)});
 }

@@ -48,31 +48,36 @@ def gpu_run(batch, diag=True, stream=None):
     return res
 
 
-def gpu_run_flat(batch, diag=True, stream=None):
+def gpu_run_flat(batch, diag=True, stream=None, synthetic_rates=None):
     """Run a numpy batch on cuda:0 as one call in the flattened layout (a mixed
-    dense / draft-free batch included: the draft-row mask selects per request)."""
+    dense / draft-free batch included: the draft-row mask selects per request);
+    with synthetic_rates, in the synthetic acceptance mode."""
     import torch
     import rejection_sampling_verify_13_amd as sv
     import workloads as W
     d = sv.to_device_flat(W.flatten(batch))
+    kw = {}
+    if synthetic_rates is not None:
+        kw["synthetic_rates"] = torch.from_numpy(np.ascontiguousarray(synthetic_rates, np.float32)).cuda()
     if diag:
-        t, n, dg = sv.verify_flat_batch(d, diag=True, stream=stream)
+        t, n, dg = sv.verify_flat_batch(d, diag=True, stream=stream, **kw)
         out = dict(tokens=t, num_accepted=n, **dg)
     else:
-        t, n = sv.verify_flat_batch(d, stream=stream)
+        t, n = sv.verify_flat_batch(d, stream=stream, **kw)
         out = dict(tokens=t, num_accepted=n)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-def oracle_run(batch, threads=8):
+def oracle_run(batch, threads=8, synthetic_rates=None):
     import oracle
     import workloads as W
     parts = [batch]
     if batch["draft_probs"] is not None and "has_q" in batch and not batch["has_q"].all():
         parts = W.split_by_q(batch)
     outs = [oracle.run(p["draft_ids"], p["draft_probs"], p["target_logits"], p["dtype"], p["temperature"],
-                       p["top_k"], p["top_p"], p["u_accept"], p["u_sample"], threads=threads) for p in parts]
+                       p["top_k"], p["top_p"], p["u_accept"], p["u_sample"], threads=threads,
+                       synthetic_rates=synthetic_rates) for p in parts]
     return {k: np.concatenate([o[k] for o in outs], axis=0) for k in outs[0]}
 
 

@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_verify_diag", "spec_verify_workspace_size", "spec_verify_status_string",
-              "spec_verify_version", "spec_verify_flat", "spec_verify_flat_timed", "spec_verify_rollback"):
+              "spec_verify_version", "spec_verify_flat", "spec_verify_flat_timed", "spec_verify_rollback",
+              "spec_verify_flat_synthetic"):
         assert n in names
 
 
@@ -90,6 +91,16 @@ def test_flat_host_validation(lib):
     assert _flat(lib, T=0, ids=0, ua=0, logits=0) == 1   # ids may be NULL without drafts; logits may not
     assert _flat(lib, N=0, cu=0) == 0    # empty batch
     assert _flat(lib, G=65) == 2
+
+
+def test_synthetic_host_validation(lib):
+    P = lambda: ctypes.c_void_p(0x1000)
+    call = lambda N, G, rates: lib.spec_verify_flat_synthetic(N, G, 16, N * G, P(), P(), None, None, P(), 1, None,
+                                                               None, None, rates, P(), P(), P(), P(), None, None,
+                                                               0, None, None, None, None)
+    assert call(2, 3, None) == 1          # rates required with drafts
+    assert call(0, 3, None) == 0          # empty batch
+    assert call(2, 65, P()) == 2
 
 
 def test_rollback_host_validation(lib):

@@ -512,3 +512,30 @@ def test_verify_then_rollback_on_one_stream():
     c, _, ss = oracle.rollback(A, gam, np.full(64, 1000), None, slots)
     np.testing.assert_array_equal(nct.cpu().numpy(), np.array(c))
     np.testing.assert_array_equal(sl.cpu().numpy(), np.array([x for r in ss for x in r], np.int32))
+
+
+# ------------------------------------------------------------------------------------------
+# synthetic acceptance mode (u_j < rate_j; only row A is read)
+# ------------------------------------------------------------------------------------------
+
+SYN_RATES = np.array([0.9, 0.8, 0.7, 0.55, 0.4, 0.3, 0.2, 0.1], np.float32)
+SYN = {
+    "syn_cfg3_small": W.config(3, N=16, V=12000),
+    "syn_cfg5_small_mixed": W.config(5, N=48, V=6144),
+    "syn_cfg4_small_greedy": W.config(4, N=40, V=7000, greedy_count=10),
+    "syn_cfg2_unaligned": W.config(2, N=16, V=4999),
+    "syn_gamma_zero": W.config(2, N=8, gmax=0, V=3000),
+}
+
+
+@pytest.mark.parametrize("name", list(SYN))
+def test_synthetic_parity(name):
+    b = W.generate(SYN[name])
+    G = b["draft_ids"].shape[1]
+    rates = SYN_RATES[:G]
+    log("[parity] %s: synthetic acceptance, N=%d gmax=%d V=%d" % (name, b["draft_ids"].shape[0], G,
+                                                                  b["target_logits"].shape[-1]))
+    g = gpu_run_flat(b, synthetic_rates=rates)
+    res = compare(g, oracle_run(b, synthetic_rates=rates), label=name)
+    check_layout(b, g)
+    log("[parity] %s ok %s" % (name, res))

@@ -15,8 +15,8 @@ MUTANTS = {
     "accept_not_strict": ("if (!(u * qy < py))", "if (!(u * qy <= py))"),
     "residual_sign": ("double d = P[A][x] - qx;", "double d = qx - P[A][x];"),
     "residual_wrong_row": ("double d = P[A][x] - qx;", "double d = P[g][x] - qx;"),
-    "bonus_wrong_row": ("                w[x] = P[g][x];", "                w[x] = P[0][x];"),
-    "zero_residual_fallback_row": ("                    w[x] = P[A][x];", "                    w[x] = P[g][x];"),
+    "bonus_wrong_row": ("            w[x] = P[g][x];", "            w[x] = P[0][x];"),
+    "zero_residual_fallback_row": ("                w[x] = P[A][x];", "                w[x] = P[g][x];"),
     "null_q_keeps_draft_cell": ("(x == r->ids[A] ? 1.0 : 0.0)", "0.0"),
     "draft_not_renormalised": ("q_out[x] = keep[x] ? r[x] / z : 0.0;", "q_out[x] = keep[x] ? r[x] : 0.0;"),
     "temperature_multiplies": ("s[x] = l / T;", "s[x] = l * T;"),

@@ -10,11 +10,14 @@
 // token's cell removed).  The exact contract is stated in include/spec_verify.h.
 //
 // Work per call, all on the caller's stream:
-//   plan_kernel   stores gamma_i and clears the outcome bits of each request's
-//                 record, and lists the draft rows (request, position <
-//                 gamma_i) request-major.
-//   row_kernel    one 256-thread workgroup per real row: the listed draft rows,
-//                 then one bonus row per request.  It streams the target-logit
+//   plan_kernel   stores gamma_i and where the request's rows and drafts sit
+//                 (padded or flattened layout), clears the outcome bits of each
+//                 request's record, and lists the draft rows (request,
+//                 position < gamma_i) request-major; in the synthetic
+//                 acceptance mode it finds the first rejection A from the
+//                 uniforms and lists row A alone.
+//   row_kernel    one 256-thread workgroup per real row: the listed rows, then
+//                 (standard mode) one bonus row per request.  It streams the target-logit
 //                 row and, at draft positions of sampled requests, the
 //                 draft-probability row once (16-byte nontemporal loads,
 //                 several steps of loads in flight while the current step is
@@ -37,7 +40,10 @@
 //   draw_kernel   per request: the first rejection A from the record, the
 //                 outputs (-1 padded), and, where row A made no draw of its
 //                 own, the draw by inverse CDF over ascending token id with
-//                 two passes over row A (block sums, then the crossing block).
+//                 two passes over row A (block sums and part totals, then the
+//                 crossing block).
+//   rollback_kernel  (own entry point, after a verify call) the KV bookkeeping
+//                 of the rejected drafts.
 
 // Compile: hipcc --offload-arch=gfx950 -O3 -shared -fPIC
 //          -Xclang -target-feature -Xclang -packed-fp32-ops

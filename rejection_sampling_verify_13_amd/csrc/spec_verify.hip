@@ -69,7 +69,6 @@ constexpr int kStep = kBlock * kCh;     // tokens per workgroup step (2048)
 constexpr int kCap = 160;               // buffered candidate chunks per wave and distribution
 constexpr int kKFast = 64;              // largest top_k served by the candidate buffers
 constexpr int kSeg = 128;               // gathered candidate tokens per wave and distribution (LDS)
-constexpr int kMerge = kWaves * kSeg;   // gathered candidate tokens of one distribution
 constexpr int kDrawSpan = 4;            // draw pass: 2048-token steps per workgroup, all loads in flight
 constexpr int kMaxGamma = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -381,11 +380,6 @@ __device__ inline float wave_max_f(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
   return v;
 }
-__device__ inline uint32_t wave_max_u(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
 __device__ inline int wave_max_i(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
@@ -394,11 +388,6 @@ __device__ inline int wave_max_i(int v) {
 __device__ inline int wave_min_i(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ inline int wave_or_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o);
   return v;
 }
 
@@ -498,14 +487,6 @@ __device__ inline float block_max_f(float v, float* red) {
   __syncthreads();
   return r;
 }
-__device__ inline uint32_t block_max_u(uint32_t v, uint32_t* red) {
-  v = wave_max_u(v);
-  if (lane_id() == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint32_t r = max(max(red[0], red[1]), max(red[2], red[3]));
-  __syncthreads();
-  return r;
-}
 __device__ inline int block_max_i(int v, int* red) {
   v = wave_max_i(v);
   if (lane_id() == 0) red[threadIdx.x >> 6] = v;
@@ -521,24 +502,6 @@ __device__ inline int block_min_i(int v, int* red) {
   int r = min(min(red[0], red[1]), min(red[2], red[3]));
   __syncthreads();
   return r;
-}
-
-// Exclusive prefix sum over the block in thread order (fp64); *total gets the sum.
-__device__ inline double block_exscan_d(double v, double* red, double* total) {
-  const int lane = lane_id(), w = threadIdx.x >> 6;
-  double inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    double t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
-  if (lane == 63) red[w] = inc;
-  __syncthreads();
-  double before = 0.0;
-  for (int k = 0; k < w; ++k) before += red[k];
-  *total = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
-  return before + inc - v;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1980,7 +1943,7 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
 }
 
 template <class LT, bool VEC>
-__global__ __launch_bounds__(kBlock, 3) void row_kernel(Args a) {
+__global__ __launch_bounds__(kBlock, sizeof(typename LT::T) == 2 ? 3 : 2) void row_kernel(Args a) {
   __shared__ RowShared<LT> sh;
   // the draft rows first (the larger rows; the plan lists them request-major,
   // so consecutive blocks, which dispatch round-robin over the XCDs, read

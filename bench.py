@@ -121,6 +121,8 @@ def main():
     ap.add_argument("--synthetic-rates", default=None,
                     help="comma-separated per-position acceptance rates: run the synthetic acceptance mode "
                          "(flattened layout; only row A of each request is read)")
+    ap.add_argument("--banned", type=int, default=0,
+                    help="ban this many seeded random token ids per request (flattened layout, identical in p and q)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -149,7 +151,13 @@ def main():
         [float(x) for x in args.synthetic_rates.split(",")], np.float32)
     if rates is not None and len(rates) != spec.gmax:
         sys.exit("--synthetic-rates needs %d rates" % spec.gmax)
-    flat = args.layout == "flat" or (args.layout == "auto" and mixed) or rates is not None
+    flat = args.layout == "flat" or (args.layout == "auto" and mixed) or rates is not None or args.banned > 0
+    ban = None
+    if args.banned > 0:
+        brng = np.random.default_rng(7)
+        lists = [np.sort(brng.choice(spec.V, size=args.banned, replace=False)) for _ in range(spec.N)]
+        ban = (np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32),
+               np.concatenate(lists).astype(np.int32))
     if flat:
         parts = [W.flatten(batch)]
     else:
@@ -182,6 +190,9 @@ def main():
                     d["draft_ids"].shape)
             if rates is not None:
                 d["rates"] = torch.from_numpy(rates).to(dev)
+            if ban is not None:
+                d["ban_off"] = torch.from_numpy(ban[0]).to(dev)
+                d["ban_ids"] = torch.from_numpy(ban[1]).to(dev)
             ps.append(d)
         sets.append(ps)
     del batch["target_logits"], batch["draft_probs"]
@@ -195,6 +206,8 @@ def main():
             kw = dict(out_tokens=d["out_t"], out_num_accepted=d["out_n"], workspace=d["ws"], stream=stream, events=ev)
             if rates is not None:
                 kw.update(synthetic_rates=d["rates"])
+            if ban is not None:
+                kw.update(banned_offsets=d["ban_off"], banned_ids=d["ban_ids"])
             if flat:
                 sv.verify_flat_batch(d, **kw)
             else:
@@ -271,6 +284,7 @@ def main():
                    "layout": "flattened, one call" if flat else "padded, %d call(s)" % len(parts),
                    "kv_rollback_in_step": bool(args.rollback),
                    "synthetic_rates": None if rates is None else [float(x) for x in rates],
+                   "banned_per_request": args.banned,
                    "target_logits": spec.dtype, "draft_probs": "f32" if spec.q_mode != "null" else None,
                    "verified_positions_per_step": positions, "rows_per_step": rows,
                    "algorithmic_bytes_per_step": B_alg, "target_bytes": B_target, "draft_bytes": B_draft},

@@ -74,6 +74,7 @@ extern "C" {
 #define SPEC_VERIFY_FAULT_DRAFT_ROW 16
 #define SPEC_VERIFY_FAULT_DRAFT_MASS 32
 #define SPEC_VERIFY_FAULT_DRAFT_COUNT 64 /* flattened layout: gamma_i outside [0, gmax] or past num_drafts */
+#define SPEC_VERIFY_FAULT_BAN_LIST 128   /* banned-token list longer than 512, not ascending, or an id outside [0, V) */
 
 /*
  * Bytes of device workspace one call with these sizes needs.  The layout is
@@ -192,6 +193,29 @@ int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t
                            double *q_y, double *resid_mass, int32_t *fault, void *workspace,
                            size_t workspace_bytes, void *stream, void *ev_start, void *ev_mid,
                            void *ev_end);
+
+/*
+ * spec_verify_flat_timed with banned tokens (zwjcode.cn page, section 06: p and
+ * q must go through identical transforms, banned tokens among them): a banned
+ * token of request i has logit -inf in every target row of the request and
+ * probability 0 in every draft row, before temperature, top-k and top-p.  It
+ * can therefore never be committed, and a draft of it is always rejected.
+ *   banned_offsets  int32 [N + 1]   request i's list is banned_ids[off[i] .. off[i+1]-1]
+ *   banned_ids      int32           strictly ascending per request, each in [0, V),
+ *                                   at most 512 per request
+ * A request whose list breaks those rules gets SPEC_VERIFY_FAULT_BAN_LIST.
+ * Returns SPEC_VERIFY_ERR_NULL if either list pointer is NULL (N > 0).
+ */
+int spec_verify_flat_banned(int N, int gmax, int V, int num_drafts, const int32_t *cu_num_draft_tokens,
+                            const int32_t *draft_ids, const float *draft_probs,
+                            const uint8_t *has_draft_probs, const void *target_logits,
+                            int logits_dtype, const float *temperature, const int32_t *top_k,
+                            const float *top_p, const int32_t *banned_offsets,
+                            const int32_t *banned_ids, const float *u_accept, const float *u_sample,
+                            int32_t *out_tokens, int32_t *out_num_accepted, double *p_y,
+                            double *q_y, double *resid_mass, int32_t *fault, void *workspace,
+                            size_t workspace_bytes, void *stream, void *ev_start, void *ev_mid,
+                            void *ev_end);
 
 /*
  * The synthetic acceptance mode (vLLM page, section "关于 synthetic / block

@@ -33,6 +33,8 @@ FAULT_TOP_P = 4
 FAULT_TARGET_ROW = 8
 FAULT_DRAFT_ROW = 16
 FAULT_DRAFT_MASS = 32
+FAULT_BAN_LIST = 128
+BAN_MAX = 512
 
 
 def build(force: bool = True) -> str:
@@ -83,7 +85,8 @@ def _c(a, dtype):
 
 
 def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=None, top_p=None,
-        u_accept=None, u_sample=None, threads: int = 1, _lib_override=None, synthetic_rates=None) -> dict:
+        u_accept=None, u_sample=None, threads: int = 1, _lib_override=None, synthetic_rates=None,
+        banned=None) -> dict:
     """Verify a batch on the CPU.
 
     ``dtype`` is "f32" (``target_logits`` float32) or "bf16" (``target_logits``
@@ -91,6 +94,15 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
     [N], p_y / q_y [N,gmax] (NaN where not computed), resid_mass [N], margin [N]
     and fault [N].  With ``synthetic_rates`` (float32 [gmax]) the synthetic
     acceptance mode runs instead: draft j is accepted iff u_j < rate_j.
+
+    ``banned`` = (offsets [N + 1], ids): request i's banned tokens are
+    ids[offsets[i]:offsets[i+1]].  Following the zwjcode.cn page, section 06
+    (p and q go through identical transforms, banned tokens among them), a
+    banned token is a token whose logit is -inf in every target row of the
+    request and whose probability is 0 in every draft row; the batch is run on
+    inputs changed that way.  A list longer than BAN_MAX, not strictly
+    ascending, or with an id outside [0, V) faults its request (FAULT_BAN_LIST,
+    with the request's parameter faults and no row read).
     """
     lib = _lib_override or _load()
     ids = _c(draft_ids, np.int32)
@@ -102,6 +114,20 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
     q = _c(draft_probs, np.float32)
     if q is not None:
         assert q.shape == (N, gmax, V), q.shape
+    bad_list = np.zeros(N, bool)
+    if banned is not None:
+        off, bid = np.asarray(banned[0], np.int64), np.asarray(banned[1], np.int64)
+        tl = tl.copy()
+        q = None if q is None else q.copy()
+        for i in range(N):
+            n = off[i + 1] - off[i]
+            lst = bid[off[i]:off[i + 1]] if n >= 0 else bid[:0]
+            if n < 0 or n > BAN_MAX or (lst < 0).any() or (lst >= V).any() or (np.diff(lst) <= 0).any():
+                bad_list[i] = True
+                continue
+            tl[i][:, lst] = 0xFF80 if dt == 1 else -np.inf
+            if q is not None:
+                q[i][:, lst] = 0.0
     T = _c(temperature, np.float32)
     k = _c(top_k, np.int32)
     p = _c(top_p, np.float32)
@@ -144,6 +170,14 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
             rc = list(ex.map(lambda t: one(bounds[t], bounds[t + 1]), range(threads)))
     if any(rc):
         raise ValueError("oracle rejected the shapes or dtype")
+    for i in np.nonzero(bad_list)[0]:
+        out["fault"][i] = (out["fault"][i] & (FAULT_DRAFT_ID | FAULT_TEMPERATURE | FAULT_TOP_P)) | FAULT_BAN_LIST
+        out["tokens"][i] = -1
+        out["num_accepted"][i] = -1
+        out["p_y"][i] = np.nan
+        out["q_y"][i] = np.nan
+        out["resid_mass"][i] = np.nan
+        out["margin"][i] = np.inf
     return out
 
 

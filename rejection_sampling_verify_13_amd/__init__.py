@@ -25,9 +25,10 @@ FAULT_TARGET_ROW = 8
 FAULT_DRAFT_ROW = 16
 FAULT_DRAFT_MASS = 32
 FAULT_DRAFT_COUNT = 64
+FAULT_BAN_LIST = 128
 
 EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_timed", "spec_verify_flat", "spec_verify_flat_timed",
-           "spec_verify_flat_synthetic", "spec_verify_rollback", "spec_verify_workspace_size",
+           "spec_verify_flat_synthetic", "spec_verify_flat_banned", "spec_verify_rollback", "spec_verify_workspace_size",
            "spec_verify_status_string", "spec_verify_version")
 
 
@@ -56,6 +57,9 @@ def _load():
     lib.spec_verify_flat_synthetic.restype = I
     lib.spec_verify_flat_synthetic.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, Z, P,
                                                P, P, P]
+    lib.spec_verify_flat_banned.restype = I
+    lib.spec_verify_flat_banned.argtypes = ([I, I, I, I] + [P] * 5 + [I] + [P] * 3 + [P, P] + [P] * 4 + [P] * 4 +
+                                            [P, Z, P] + [P] * 3)
     lib.spec_verify_rollback.restype = I
     lib.spec_verify_rollback.argtypes = [I, I, P, P, P, P, P, P, P]
     lib.spec_verify_workspace_size.restype = Z
@@ -168,7 +172,8 @@ def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, 
 
 def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, target_logits, gmax,
                 temperature=None, top_k=None, top_p=None, u_accept=None, u_sample=None, *, out_tokens=None,
-                out_num_accepted=None, workspace=None, stream=None, diag=False, events=None, synthetic_rates=None):
+                out_num_accepted=None, workspace=None, stream=None, diag=False, events=None, synthetic_rates=None,
+                banned_offsets=None, banned_ids=None):
     """Verify a batch in the flattened layout (spec_verify_flat in include/spec_verify.h).
 
     cu_num_draft_tokens int32 [N] (inclusive prefix sums of the draft counts),
@@ -181,6 +186,8 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
     are [N, gmax].  ``events`` as for verify().  With ``synthetic_rates``
     (float32 [gmax]) the synthetic acceptance mode runs (spec_verify_flat_synthetic):
     draft j is accepted iff u_accept < rate_j; diag then returns only ``fault``.
+    With ``banned_offsets`` (int32 [N + 1]) and ``banned_ids`` (int32, ascending
+    per request) those tokens are banned in p and q alike (spec_verify_flat_banned).
     """
     if target_logits.dim() != 2:
         raise ValueError("target_logits must be [T + N, V]")
@@ -239,6 +246,29 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
                                                 *evp)
         if rc != 0:
             raise SpecVerifyError("spec_verify_flat_synthetic failed: %s" % lib.spec_verify_status_string(rc).decode())
+        return (out_tokens, out_num_accepted, d) if diag else (out_tokens, out_num_accepted)
+    if banned_offsets is not None or banned_ids is not None:
+        if synthetic_rates is not None:
+            raise ValueError("banned tokens are not supported together with the synthetic mode")
+        _check(banned_offsets, "banned_offsets", torch.int32, (N + 1,), dev)
+        if banned_ids is None or banned_ids.dim() != 1:
+            raise ValueError("banned_ids must be a 1-d int32 tensor")
+        _check(banned_ids, "banned_ids", torch.int32, tuple(banned_ids.shape), dev)
+        if diag:
+            d = dict(p_y=torch.empty((N, G), dtype=torch.float64, device=dev),
+                     q_y=torch.empty((N, G), dtype=torch.float64, device=dev),
+                     resid_mass=torch.empty((N,), dtype=torch.float64, device=dev),
+                     fault=torch.empty((N,), dtype=torch.int32, device=dev))
+            dp = (_ptr(d["p_y"]), _ptr(d["q_y"]), _ptr(d["resid_mass"]), _ptr(d["fault"]))
+        else:
+            dp = (None, None, None, None)
+        evp = (None, None, None) if events is None else tuple(
+            None if e is None else ctypes.c_void_p(e.cuda_event) for e in events)
+        with torch.cuda.device(dev):
+            rc = lib.spec_verify_flat_banned(*head[:13], _ptr(banned_offsets), _ptr(banned_ids), *head[13:], *dp,
+                                             _ptr(workspace), ws_bytes, sptr, *evp)
+        if rc != 0:
+            raise SpecVerifyError("spec_verify_flat_banned failed: %s" % lib.spec_verify_status_string(rc).decode())
         return (out_tokens, out_num_accepted, d) if diag else (out_tokens, out_num_accepted)
     with torch.cuda.device(dev):
         if diag or events is not None:

@@ -81,7 +81,9 @@ enum {
   kFaultDraftRow = SPEC_VERIFY_FAULT_DRAFT_ROW,
   kFaultDraftMass = SPEC_VERIFY_FAULT_DRAFT_MASS,
   kFaultDraftCount = SPEC_VERIFY_FAULT_DRAFT_COUNT,
+  kFaultBanList = SPEC_VERIFY_FAULT_BAN_LIST,
 };
+constexpr int kBanMax = 512;            // banned tokens per request (ascending list kept in LDS)
 
 // Per-row results (64 bytes).
 struct RowStats {
@@ -154,6 +156,8 @@ struct Args {
   const int32_t* cu;    // [N] inclusive prefix sums of gamma_i
   const uint8_t* has_q; // [N] request i has draft rows iff nonzero; nullptr: all do (when q != nullptr)
   int T;                // number of drafts, cu[N - 1]
+  const int32_t* ban_off;  // [N + 1] banned-token list offsets, or nullptr
+  const int32_t* ban_ids;  // ascending ids per request
   int synthetic;        // 1: the synthetic acceptance mode (draft j accepted iff u_j < srates[j])
   const float* srates;  // synthetic acceptance rates [G]
 };
@@ -820,6 +824,70 @@ struct RowShared {
 
 
 // ------------------------------------------------------------------------------------------
+// banned tokens: a request's ascending list in LDS; a banned token reads as a
+// -inf logit and a zero draft probability wherever a row is read
+// ------------------------------------------------------------------------------------------
+
+// Walks the list along consecutive 512-token wave ranges: ban_mask(lo) gives
+// this lane the mask of its 8 tokens lo + 8 * lane .. + 7 and consumes the ids
+// below lo + 512, 64 at a time (the list is ascending, so those ids are a
+// prefix of the 64 read).  Wave-uniform state.
+struct BanWalk {
+  int ptr, n;
+};
+__device__ inline BanWalk ban_start(const LDS_AS int* ban, int n) {
+  BanWalk b;
+  b.ptr = 0;
+  b.n = uni(n);
+  return b;
+}
+__device__ inline uint32_t ban_mask(BanWalk& b, const LDS_AS int* ban, int lo) {
+  uint32_t m = 0u;
+  const int lane = lane_id();
+  while (b.ptr < b.n) {
+    const int id = b.ptr + lane < b.n ? ban[b.ptr + lane] : INT_MAX;
+    const uint64_t below = __ballot(id < lo + 512);
+    uint64_t in = __ballot(id >= lo && id < lo + 512);
+    while (in) {
+      const int t = __builtin_amdgcn_readlane(id, __ffsll((unsigned long long)in) - 1) - lo;
+      if ((t >> 3) == lane) m |= 1u << (t & 7);
+      in &= in - 1;
+    }
+    const int c = __popcll(below);
+    b.ptr += c;
+    if (c < 64) break;
+  }
+  return m;
+}
+__device__ inline bool ban_has(const LDS_AS int* ban, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (ban[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo < n && ban[lo] == x;
+}
+// masked tokens of one lane's raw step: -inf logits, zero probabilities
+__device__ inline void ban_apply(Bf16::Raw& r, uint32_t m) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    if ((m >> t) & 1u) {
+      const uint32_t w = r.a[t >> 1];
+      r.a[t >> 1] = (t & 1) ? ((w & 0x0000ffffu) | 0xff800000u) : ((w & 0xffff0000u) | 0x0000ff80u);
+    }
+}
+__device__ inline void ban_apply(F32::Raw& r, uint32_t m, uint32_t fill) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if ((m >> t) & 1u) r.a[t] = fill;
+    if ((m >> (t + 4)) & 1u) r.b[t] = fill;
+  }
+}
+__device__ inline void ban_logits(Bf16::Raw& r, uint32_t m) { ban_apply(r, m); }
+__device__ inline void ban_logits(F32::Raw& r, uint32_t m) { ban_apply(r, m, 0xff800000u); }
+
+// ------------------------------------------------------------------------------------------
 // kept set from the candidate buffers (one wave per distribution)
 // ------------------------------------------------------------------------------------------
 
@@ -1165,7 +1233,8 @@ struct DrawOut {
 // with w > 0.  Run by a single wave; wbuf is LDS scratch for more than 64
 // kept tokens.
 __device__ __noinline__ DrawOut wave_draw(DrawIn in, const LDS_AS uint32_t* skey, const LDS_AS int* sid,
-                                          const LDS_AS double* ke, LDS_AS double* wbuf) {
+                                          const LDS_AS double* ke, LDS_AS double* wbuf, const LDS_AS int* ban,
+                                          int nban) {
   const int lane = lane_id();
   in.nk = uni(in.nk);
   in.cutkey = uni(in.cutkey);
@@ -1177,13 +1246,14 @@ __device__ __noinline__ DrawOut wave_draw(DrawIn in, const LDS_AS uint32_t* skey
   in.rk = uni(in.rk);
   in.y = uni(in.y);
   in.us = uni(in.us);
+  nban = uni(nban);
   auto weight = [&](bool keep, int id, double e, double& p) {
     p = keep ? e / in.zk : 0.0;
     double w = p;
     if (in.mode == 1) {
       double q = 0.0;
       if (keep) {
-        const float qx = F32::at(in.qrow, (size_t)id);
+        const float qx = (nban && ban_has(ban, nban, id)) ? 0.f : F32::at(in.qrow, (size_t)id);
         q = (qx >= in.cut_q) ? temper_q(qx, in.T) / in.rk : 0.0;
       }
       w = p - q > 0.0 ? p - q : 0.0;
@@ -1283,7 +1353,8 @@ struct Filtered {
 };
 
 __device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hist, LDS_AS double* sel_d,
-                                                LDS_AS uint32_t* sel_u, LDS_AS double* red) {
+                                                LDS_AS uint32_t* sel_u, LDS_AS double* red, const LDS_AS int* ban,
+                                                int nban) {
   g.row = uni(g.row);
   g.V = uni(g.V);
   g.bf16 = uni((int)g.bf16);
@@ -1297,6 +1368,7 @@ __device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hi
   g.top_p = uni(g.top_p);
   g.pact = uni((int)g.pact);
   g.total = uni(g.total);
+  nban = uni(nban);
   RowRef ka;
   ka.row = g.row;
   ka.V = g.V;
@@ -1305,13 +1377,17 @@ __device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hi
     return g.draft ? (g.temper ? (double)fast_exp2(fast_log2(v) * g.invT) : (double)v)
                    : (double)fast_exp2((v - g.m) * g.c);
   };
+  auto value = [&](int x) -> float {
+    if (nban && ban_has(ban, nban, x)) return g.draft ? 0.f : -INFINITY;
+    return row_value(ka, x);
+  };
   auto kw = [&](int x, uint32_t& key, double& w) {
-    const float v = row_value(ka, x);
+    const float v = value(x);
     key = okey(v);
     w = weight(v);
   };
   auto kc = [&](int x, uint32_t& key, double& w) {
-    key = okey(row_value(ka, x));
+    key = okey(value(x));
     w = 1.0;
   };
   uint32_t lo = 0u;
@@ -1389,9 +1465,9 @@ struct StochState {
 };
 
 // QM: 0 no draft row, 1 draft row at T = 1, 2 draft row at T != 1.
-template <class LT, bool VEC, int QM, bool CAND>
+template <class LT, bool VEC, int QM, bool CAND, bool BAN>
 __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, const float* qrow, int V, float c, float invT, int k,
-                                  RowShared<LT>& sh, StochState& st) {
+                                  RowShared<LT>& sh, StochState& st, const LDS_AS int* ban, int nban) {
   typedef typename LT::Raw LR;
   const int tid = threadIdx.x, w = tid >> 6;
   const int nsteps = (V + kStep - 1) / kStep;
@@ -1443,6 +1519,8 @@ __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, co
   // full steps (every lane's 8 tokens inside the row, vector loads only)
   const int nfull = VEC ? V / kStep : 0;
   const int base0 = tid * kCh;
+  BanWalk bw;
+  if (BAN) bw = ban_start(ban, nban);
   ring_stream<QM ? 5 : 10, StepRaw<LR>>(
       nfull,
       [&](int s) {
@@ -1451,13 +1529,32 @@ __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, co
         if (QM) r.q = F32::load(qrow + base0 + s * kStep);
         return r;
       },
-      [&](const StepRaw<LR>& r, int s) { process(r.l, r.q, base0 + s * kStep); });
+      [&](const StepRaw<LR>& r, int s) {
+        if (BAN) {
+          StepRaw<LR> b = r;
+          const uint32_t m = ban_mask(bw, ban, s * kStep + w * 512);
+          if (m) {
+            ban_logits(b.l, m);
+            if (QM) ban_apply(b.q, m, 0u);
+          }
+          process(b.l, b.q, base0 + s * kStep);
+        } else {
+          process(r.l, r.q, base0 + s * kStep);
+        }
+      });
   int base = base0 + nfull * kStep;
   // the ragged tail (and every step of rows that are not 16-byte aligned)
   for (int s = nfull; s < nsteps; ++s) {
-    const LR lr = load_logits<LT, VEC>(lrow, base, V);
+    LR lr = load_logits<LT, VEC>(lrow, base, V);
     F32::Raw qr{};
     if (QM) qr = load_probs<VEC>(qrow, base, V);
+    if (BAN) {
+      const uint32_t m = ban_mask(bw, ban, s * kStep + w * 512);
+      if (m) {
+        ban_logits(lr, m);
+        if (QM) ban_apply(qr, m, 0u);
+      }
+    }
     process(lr, qr, base);
     base += kStep;
   }
@@ -1465,16 +1562,21 @@ __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, co
 
 // Greedy rows: argmax (lowest id among equal maxima) and a running sum that
 // flags NaN / +inf for an exact re-check.
-template <class LT, bool VEC>
-__device__ void stream_greedy(const typename LT::T* lrow, int V, float& best, int& bidx, float& acc) {
+template <class LT, bool VEC, bool BAN>
+__device__ void stream_greedy(const typename LT::T* lrow, int V, float& best, int& bidx, float& acc,
+                              const LDS_AS int* ban, int nban) {
   typedef typename LT::Raw LR;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6;
   const int nsteps = (V + kStep - 1) / kStep;
-  auto process = [&](const LR& lr, int base) {
+  // m: banned tokens of the step (read as -inf, left out of the running sum)
+  auto process = [&](const LR& lr, int base, uint32_t m) {
     float v[8];
     LT::unpack(lr, v);
     if (base < V) {
-      acc += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+      float a[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) a[t] = ((m >> t) & 1u) ? 0.f : v[t];
+      acc += ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
       const float cm = max8(v);
       if (cm > best) {
         int f = 7;
@@ -1488,12 +1590,24 @@ __device__ void stream_greedy(const typename LT::T* lrow, int V, float& best, in
   };
   const int nfull = VEC ? V / kStep : 0;
   const int base0 = tid * kCh;
+  BanWalk bw;
+  if (BAN) bw = ban_start(ban, nban);
+  auto masked = [&](const LR& r, int s, int base) {
+    if (BAN) {
+      LR b = r;
+      const uint32_t m = ban_mask(bw, ban, s * kStep + w * 512);
+      if (m) ban_logits(b, m);
+      process(b, base, m);
+    } else {
+      process(r, base, 0u);
+    }
+  };
   ring_stream<8, LR>(
       nfull, [&](int s) { return LT::load(lrow + base0 + s * kStep); },
-      [&](const LR& r, int s) { process(r, base0 + s * kStep); });
+      [&](const LR& r, int s) { masked(r, s, base0 + s * kStep); });
   int base = base0 + nfull * kStep;
   for (int s = nfull; s < nsteps; ++s) {
-    process(load_logits<LT, VEC>(lrow, base, V), base);
+    masked(load_logits<LT, VEC>(lrow, base, V), s, base);
     base += kStep;
   }
 }
@@ -1502,15 +1616,16 @@ __device__ void stream_greedy(const typename LT::T* lrow, int V, float& best, in
 // row processing
 // ------------------------------------------------------------------------------------------
 
-template <class LT, bool VEC>
-__device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, int j, RowShared<LT>& sh) {
+template <class LT, bool VEC, bool BAN>
+__device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, int j, RowShared<LT>& sh,
+                                           const LDS_AS int* ban, int nban) {
   typedef typename LT::T ET;
   const int G = a.G, V = a.V, tid = threadIdx.x;
   const size_t row = (size_t)i * (G + 1) + j;  // the row record
   const ET* lrow = reinterpret_cast<const ET*>(a.logits) + ((size_t)rq.tgt0 + j) * (size_t)V;
   float best = -INFINITY, acc = 0.f;
   int bidx = -1;
-  stream_greedy<LT, VEC>(lrow, V, best, bidx, acc);
+  stream_greedy<LT, VEC, BAN>(lrow, V, best, bidx, acc, ban, nban);
   __builtin_amdgcn_s_setprio(2);
   const float gbest = block_max_f(best, sh.red_f);
   int cand = (best == gbest && bidx >= 0) ? bidx : INT_MAX;
@@ -1521,6 +1636,7 @@ __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, 
   int bad = 0;
   if (suspicious) {
     for (int x = tid; x < V; x += kBlock) {
+      if (BAN && ban_has(ban, nban, x)) continue;  // a banned token reads as -inf
       const float l = LT::at(lrow, (size_t)x);
       bad |= (l != l) || (l == INFINITY);
     }
@@ -1546,8 +1662,9 @@ __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, 
   }
 }
 
-template <class LT, bool VEC>
-__device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int i, int j, RowShared<LT>& sh) {
+template <class LT, bool VEC, bool BAN>
+__device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int i, int j, RowShared<LT>& sh,
+                                               const LDS_AS int* ban, int nban) {
   typedef typename LT::T ET;
   const int G = a.G, V = a.V;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -1571,6 +1688,10 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
     y = a.ids[(size_t)rq.id0 + j];
     ly = LT::at(lrow, (size_t)y);
     if (req_q) qyv = F32::at(qrow, (size_t)y);
+    if (BAN && ban_has(ban, nban, y)) {
+      ly = -INFINITY;
+      qyv = 0.f;
+    }
   }
 
   StochState st;
@@ -1583,9 +1704,9 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   st.qs = ChunkState{0, 0u, 0};
   const int qm = has_q ? (temper ? 2 : 1) : 0;
   if (cand) {
-    if (qm == 0) stream_stochastic<LT, VEC, 0, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
-    else if (qm == 1) stream_stochastic<LT, VEC, 1, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
-    else stream_stochastic<LT, VEC, 2, true>(lrow, qrow, V, c, invT, rq.k, sh, st);
+    if (qm == 0) stream_stochastic<LT, VEC, 0, true, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
+    else if (qm == 1) stream_stochastic<LT, VEC, 1, true, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
+    else stream_stochastic<LT, VEC, 2, true, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
     // each wave cuts its own buffers down to its k-th largest chunk key and
     // copies the tokens at or above that threshold into its segment
     __builtin_amdgcn_s_setprio(2);
@@ -1605,9 +1726,9 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       if (lane == 0) sh.scnt[1][wave] = n;
     }
   } else {
-    if (qm == 0) stream_stochastic<LT, VEC, 0, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
-    else if (qm == 1) stream_stochastic<LT, VEC, 1, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
-    else stream_stochastic<LT, VEC, 2, false>(lrow, qrow, V, c, invT, rq.k, sh, st);
+    if (qm == 0) stream_stochastic<LT, VEC, 0, false, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
+    else if (qm == 1) stream_stochastic<LT, VEC, 1, false, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
+    else stream_stochastic<LT, VEC, 2, false, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
   }
 
   // the rest of the row is short serial work that holds this workgroup's
@@ -1747,7 +1868,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       g.pact = rq.pact;
       g.total = Z;
       const Filtered f = general_filter(g, (LDS_AS double*)sh.pb, (LDS_AS double*)sh.sel_d,
-                                        (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d);
+                                        (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d, ban, BAN ? nban : 0);
       cut_p = f.cut;
       Zk = f.mass;
     }
@@ -1768,7 +1889,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       g.total = R;
       // (histogram in the draft buffers: the target weights stay for the draw)
       const Filtered f = general_filter(g, (LDS_AS double*)sh.qb, (LDS_AS double*)sh.sel_d,
-                                        (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d);
+                                        (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d, ban, BAN ? nban : 0);
       cut_q = f.cut;
       Rk = f.mass;
     }
@@ -1816,7 +1937,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       din.y = __builtin_amdgcn_readlane(y, 0);
       din.us = a.u_sample[i];
       d = wave_draw(din, (const LDS_AS uint32_t*)sh.skey[0], (const LDS_AS int*)sh.sid[0],
-                    (const LDS_AS double*)sh.pb, (LDS_AS double*)sh.qb);
+                    (const LDS_AS double*)sh.pb, (LDS_AS double*)sh.qb, ban, BAN ? nban : 0);
     }
     if (lane == 0) {
       s.s = d.s;
@@ -1942,9 +2063,10 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
   if (tid == 0) a.plan[0] = s_base[0];
 }
 
-template <class LT, bool VEC>
+template <class LT, bool VEC, bool BAN>
 __global__ __launch_bounds__(kBlock, sizeof(typename LT::T) == 2 ? 3 : 2) void row_kernel(Args a) {
   __shared__ RowShared<LT> sh;
+  __shared__ int s_ban[BAN ? kBanMax : 1];
   // the draft rows first (the larger rows; the plan lists them request-major,
   // so consecutive blocks, which dispatch round-robin over the XCDs, read
   // neighbouring rows), then one bonus row per request; the launch covers
@@ -1955,14 +2077,30 @@ __global__ __launch_bounds__(kBlock, sizeof(typename LT::T) == 2 ? 3 : 2) void r
   const bool bonus = bx >= nd;
   const int m = bonus ? 0 : a.plan[1 + bx];
   const int i = bonus ? bx - nd : (m >> 7);
-  const Req rq = load_req(a, i);
+  Req rq = load_req(a, i);
   const int j = bonus ? rq.gamma : (m & 127);
+  int nban = 0;
+  if (BAN) {
+    // the request's banned tokens into LDS: at most kBanMax, strictly
+    // ascending, each in [0, V); otherwise the request faults
+    const int b0 = a.ban_off[i], n = a.ban_off[i + 1] - b0;
+    int bad = (n < 0 || n > kBanMax) ? 1 : 0;
+    if (!bad)
+      for (int t = threadIdx.x; t < n; t += kBlock) {
+        const int id = a.ban_ids[(size_t)b0 + t];
+        s_ban[t] = id;
+        bad |= (id < 0 || id >= a.V || (t > 0 && a.ban_ids[(size_t)b0 + t - 1] >= id)) ? 1 : 0;
+      }
+    bad = __syncthreads_or(bad);
+    if (bad) rq.fault |= kFaultBanList;
+    else nban = n;
+  }
   if (rq.fault) {
     if (threadIdx.x == 0) note_row(a, i, j, 0, rq.fault, false);
     return;
   }
-  if (rq.greedy) greedy_row<LT, VEC>(a, rq, i, j, sh);
-  else stochastic_row<LT, VEC>(a, rq, i, j, sh);
+  if (rq.greedy) greedy_row<LT, VEC, BAN>(a, rq, i, j, sh, (const LDS_AS int*)s_ban, nban);
+  else stochastic_row<LT, VEC, BAN>(a, rq, i, j, sh, (const LDS_AS int*)s_ban, nban);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -2059,12 +2197,13 @@ __device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, i
 // levels agree), re-reads the block where it is crossed and finds the token
 // (inverse CDF over ascending id; if the weights sum to zero, over p'; if
 // rounding leaves no crossing, the largest id with w > 0).
-template <class LT, bool VEC>
+template <class LT, bool VEC, bool BAN>
 __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   typedef typename LT::T ET;
   typedef typename LT::Raw LR;
   __shared__ int s_last;
   __shared__ DrawSum s_blk[kDrawSpan * kWaves];
+  __shared__ int s_ban[BAN ? kBanMax : 1];
   const int i = blockIdx.x / (a.dparts + 1), part = blockIdx.x - i * (a.dparts + 1);
   const ReqRec rr = a.rec[i];
   const int gamma = rr.gamma;
@@ -2094,6 +2233,15 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   DrawSum* ds = a.dsum + (size_t)i * nsteps * kWaves;
   DrawSum* dt = a.dtot + (size_t)i * a.dparts;
   const int s0 = part * kDrawSpan, cnt = min(kDrawSpan, nsteps - s0);
+  // the request's banned tokens (checked by the row pass, which faults the
+  // request on a bad list)
+  int nban = 0;
+  if (BAN) {
+    const int b0 = a.ban_off[i];
+    nban = a.ban_off[i + 1] - b0;
+    for (int t = tid; t < nban; t += kBlock) s_ban[t] = a.ban_ids[(size_t)b0 + t];
+    __syncthreads();
+  }
   // all of this workgroup's loads first, then the sums (block sums go to LDS:
   // a global store here would count against the counter the loads wait on)
   LR lr[kDrawSpan];
@@ -2106,10 +2254,19 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
       qr[u] = (mode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
     }
   }
+  BanWalk bw;
+  if (BAN) bw = ban_start((const LDS_AS int*)s_ban, nban);
 #pragma unroll
   for (int u = 0; u < kDrawSpan; ++u) {
     if (u >= cnt) break;
     const int base = (s0 + u) * kStep + tid * kCh;
+    if (BAN) {
+      const uint32_t m = ban_mask(bw, (const LDS_AS int*)s_ban, (s0 + u) * kStep + wave * 512);
+      if (m) {
+        ban_logits(lr[u], m);
+        if (mode == 1) ban_apply(qr[u], m, 0u);
+      }
+    }
     float lv[8], qv[8], w[8], pw[8];
     LT::unpack(lr[u], lv);
     F32::unpack(qr[u], qv);
@@ -2213,8 +2370,20 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   } else {
     const int base = (rstar / kWaves) * kStep + (rstar % kWaves) * 512 + lane * kCh;
     float lv[8], qv[8], w[8], pw[8];
-    LT::unpack(load_logits<LT, VEC>(lrow, base, V), lv);
-    if (dmode == 1) F32::unpack(load_probs<VEC>(qrow, base, V), qv);
+    LR lb = load_logits<LT, VEC>(lrow, base, V);
+    F32::Raw qb = (dmode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
+    if (BAN) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (ban_has((const LDS_AS int*)s_ban, nban, base + e)) m |= 1u << e;
+      if (m) {
+        ban_logits(lb, m);
+        ban_apply(qb, m, 0u);
+      }
+    }
+    LT::unpack(lb, lv);
+    if (dmode == 1) F32::unpack(qb, qv);
     else
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[e] = 0.f;
@@ -2310,17 +2479,18 @@ struct Events {
   hipEvent_t start, mid, end;
 };
 
-template <class LT, bool VEC>
+template <class LT, bool VEC, bool BAN>
 hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
   const long rows = a.synthetic ? (long)a.N : (long)a.N * (a.G + 1);  // synthetic mode: row A only
   hipError_t e;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((row_kernel<LT, VEC>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
+  hipLaunchKernelGGL((row_kernel<LT, VEC, BAN>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.mid && (e = hipEventRecord(ev.mid, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((draw_kernel<LT, VEC>), dim3((unsigned)((long)a.N * (a.dparts + 1))), dim3(kBlock), 0, stream, a);
+  hipLaunchKernelGGL((draw_kernel<LT, VEC, BAN>), dim3((unsigned)((long)a.N * (a.dparts + 1))), dim3(kBlock), 0,
+                     stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.end && (e = hipEventRecord(ev.end, stream)) != hipSuccess) return e;
   return hipSuccess;
@@ -2333,7 +2503,8 @@ struct Layout {
   int T;
 };
 
-int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* srates, const int32_t* ids, const float* q, const void* logits, int dtype,
+int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* srates, const int32_t* ban_off,
+        const int32_t* ban_ids, const int32_t* ids, const float* q, const void* logits, int dtype,
         const float* temperature, const int32_t* top_k, const float* top_p, const float* u_accept,
         const float* u_sample, int32_t* out_tokens, int32_t* out_num, double* p_y, double* q_y, double* resid,
         int32_t* fault, void* workspace, size_t workspace_bytes, void* stream, const Events& ev) {
@@ -2402,6 +2573,8 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   a.cu = lay.cu;
   a.has_q = lay.has_q;
   a.T = lay.T;
+  a.ban_off = ban_off;
+  a.ban_ids = ban_ids;
   a.synthetic = synthetic ? 1 : 0;
   a.srates = srates;
 
@@ -2410,10 +2583,17 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   const bool vec = (V % 8 == 0) && ((uintptr_t)logits % 16 == 0) && (!q || (uintptr_t)q % 16 == 0);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if (dtype == SPEC_VERIFY_BF16)
-    e = vec ? launch<Bf16, true>(a, s, ev) : launch<Bf16, false>(a, s, ev);
-  else
-    e = vec ? launch<F32, true>(a, s, ev) : launch<F32, false>(a, s, ev);
+  if (ban_off) {
+    if (dtype == SPEC_VERIFY_BF16)
+      e = vec ? launch<Bf16, true, true>(a, s, ev) : launch<Bf16, false, true>(a, s, ev);
+    else
+      e = vec ? launch<F32, true, true>(a, s, ev) : launch<F32, false, true>(a, s, ev);
+  } else {
+    if (dtype == SPEC_VERIFY_BF16)
+      e = vec ? launch<Bf16, true, false>(a, s, ev) : launch<Bf16, false, false>(a, s, ev);
+    else
+      e = vec ? launch<F32, true, false>(a, s, ev) : launch<F32, false, false>(a, s, ev);
+  }
   return e == hipSuccess ? SPEC_VERIFY_OK : SPEC_VERIFY_ERR_HIP;
 }
 
@@ -2431,7 +2611,7 @@ int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* d
                 int logits_dtype, const float* temperature, const int32_t* top_k, const float* top_p,
                 const float* u_accept, const float* u_sample, int32_t* out_tokens, int32_t* out_num_accepted,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes,
              stream, Events{nullptr, nullptr, nullptr});
 }
@@ -2441,7 +2621,7 @@ int spec_verify_diag(int N, int gmax, int V, const int32_t* draft_ids, const flo
                      const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
                      int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{nullptr, nullptr, nullptr});
 }
@@ -2452,7 +2632,7 @@ int spec_verify_timed(int N, int gmax, int V, const int32_t* draft_ids, const fl
                       int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
                       void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_mid,
                       void* ev_end) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
                     reinterpret_cast<hipEvent_t>(ev_end)});
@@ -2464,7 +2644,7 @@ int spec_verify_flat(int N, int gmax, int V, int num_drafts, const int32_t* cu_n
                      const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
                      int32_t* out_num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
-  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, draft_ids, draft_probs,
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, nullptr, nullptr, draft_ids, draft_probs,
              target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens,
              out_num_accepted, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
              Events{nullptr, nullptr, nullptr});
@@ -2478,9 +2658,25 @@ int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t
                            double* resid_mass, int32_t* fault, void* workspace, size_t workspace_bytes, void* stream,
                            void* ev_start, void* ev_mid, void* ev_end) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
-  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, draft_ids, draft_probs,
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, nullptr, nullptr, draft_ids, draft_probs,
              target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens,
              out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
+             Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
+                    reinterpret_cast<hipEvent_t>(ev_end)});
+}
+
+int spec_verify_flat_banned(int N, int gmax, int V, int num_drafts, const int32_t* cu_num_draft_tokens,
+                            const int32_t* draft_ids, const float* draft_probs, const uint8_t* has_draft_probs,
+                            const void* target_logits, int logits_dtype, const float* temperature,
+                            const int32_t* top_k, const float* top_p, const int32_t* banned_offsets,
+                            const int32_t* banned_ids, const float* u_accept, const float* u_sample,
+                            int32_t* out_tokens, int32_t* out_num_accepted, double* p_y, double* q_y,
+                            double* resid_mass, int32_t* fault, void* workspace, size_t workspace_bytes,
+                            void* stream, void* ev_start, void* ev_mid, void* ev_end) {
+  if (N > 0 && (!cu_num_draft_tokens || !banned_offsets || !banned_ids)) return SPEC_VERIFY_ERR_NULL;
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, banned_offsets,
+             banned_ids, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+             u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
                     reinterpret_cast<hipEvent_t>(ev_end)});
 }
@@ -2494,7 +2690,7 @@ int spec_verify_flat_synthetic(int N, int gmax, int V, int num_drafts, const int
                                void* stream, void* ev_start, void* ev_mid, void* ev_end) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
   if (N > 0 && gmax > 0 && !synthetic_rates) return SPEC_VERIFY_ERR_NULL;
-  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, true, synthetic_rates, draft_ids, draft_probs, target_logits, logits_dtype,
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, true, synthetic_rates, nullptr, nullptr, draft_ids, draft_probs, target_logits, logits_dtype,
              temperature, top_k, top_p, u_accept, u_sample, out_tokens, out_num_accepted, nullptr, nullptr, nullptr,
              fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),

@@ -48,7 +48,7 @@ def gpu_run(batch, diag=True, stream=None):
     return res
 
 
-def gpu_run_flat(batch, diag=True, stream=None, synthetic_rates=None):
+def gpu_run_flat(batch, diag=True, stream=None, synthetic_rates=None, banned=None):
     """Run a numpy batch on cuda:0 as one call in the flattened layout (a mixed
     dense / draft-free batch included: the draft-row mask selects per request);
     with synthetic_rates, in the synthetic acceptance mode."""
@@ -59,6 +59,9 @@ def gpu_run_flat(batch, diag=True, stream=None, synthetic_rates=None):
     kw = {}
     if synthetic_rates is not None:
         kw["synthetic_rates"] = torch.from_numpy(np.ascontiguousarray(synthetic_rates, np.float32)).cuda()
+    if banned is not None:
+        kw["banned_offsets"] = torch.from_numpy(np.ascontiguousarray(banned[0], np.int32)).cuda()
+        kw["banned_ids"] = torch.from_numpy(np.ascontiguousarray(banned[1], np.int32)).cuda()
     if diag:
         t, n, dg = sv.verify_flat_batch(d, diag=True, stream=stream, **kw)
         out = dict(tokens=t, num_accepted=n, **dg)
@@ -69,15 +72,23 @@ def gpu_run_flat(batch, diag=True, stream=None, synthetic_rates=None):
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-def oracle_run(batch, threads=8, synthetic_rates=None):
+def oracle_run(batch, threads=8, synthetic_rates=None, banned=None):
     import oracle
     import workloads as W
     parts = [batch]
     if batch["draft_probs"] is not None and "has_q" in batch and not batch["has_q"].all():
         parts = W.split_by_q(batch)
+    bans = [None] * len(parts)
+    if banned is not None:  # the lists of each contiguous part
+        off, ids = np.asarray(banned[0], np.int64), np.asarray(banned[1])
+        lo, bans = 0, []
+        for p in parts:
+            hi = lo + p["draft_ids"].shape[0]
+            bans.append((off[lo:hi + 1] - off[lo], ids[off[lo]:off[hi]]))
+            lo = hi
     outs = [oracle.run(p["draft_ids"], p["draft_probs"], p["target_logits"], p["dtype"], p["temperature"],
                        p["top_k"], p["top_p"], p["u_accept"], p["u_sample"], threads=threads,
-                       synthetic_rates=synthetic_rates) for p in parts]
+                       synthetic_rates=synthetic_rates, banned=bn) for p, bn in zip(parts, bans)]
     return {k: np.concatenate([o[k] for o in outs], axis=0) for k in outs[0]}
 
 

@@ -539,3 +539,69 @@ def test_synthetic_parity(name):
     res = compare(g, oracle_run(b, synthetic_rates=rates), label=name)
     check_layout(b, g)
     log("[parity] %s ok %s" % (name, res))
+
+
+# ------------------------------------------------------------------------------------------
+# banned tokens (identical in p and q)
+# ------------------------------------------------------------------------------------------
+
+def _ban_lists(b, seed, n):
+    """n random banned ids per request, plus, for every third request, its first
+    draft token and, for every fifth, the argmax of its first target row."""
+    rng = np.random.default_rng(seed)
+    N, V = b["draft_ids"].shape[0], b["target_logits"].shape[-1]
+    tl = b["target_logits"]
+    lists = []
+    for i in range(N):
+        x = set(rng.choice(V, size=min(n, V), replace=False).tolist())
+        if i % 3 == 0 and b["draft_ids"].shape[1] and b["draft_ids"][i, 0] >= 0:
+            x.add(int(b["draft_ids"][i, 0]))
+        if i % 5 == 0:
+            row = W.bf16_bits_to_f32(tl[i, 0]) if b["dtype"] == "bf16" else tl[i, 0]
+            x.add(int(np.argmax(row)))
+        lists.append(np.array(sorted(x), np.int32))
+    off = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    return off, np.concatenate(lists).astype(np.int32)
+
+
+BAN = {
+    "ban_cfg3_small_topk": (W.config(3, N=16, V=12000), 60),
+    "ban_cfg2_tempered": (W.config(2, N=24, V=5000), 40),
+    "ban_cfg4_small_greedy": (W.config(4, N=40, V=7000, greedy_count=10), 30),
+    "ban_cfg5_small_mixed": (W.config(5, N=48, V=6144), 50),
+    "ban_top_p_only": (W.config(2, N=12, V=6000, top_p=0.8), 25),
+    "ban_unaligned_f32_topk": (W.config(3, N=10, V=3001, dtype="f32"), 20),
+    "ban_long_lists": (W.config(3, N=8, V=9000), 512),
+}
+
+
+@pytest.mark.parametrize("name", list(BAN))
+def test_banned_tokens_parity(name):
+    cfg, n = BAN[name]
+    b = W.generate(cfg)
+    banned = _ban_lists(b, 5, n)
+    log("[parity] %s: N=%d V=%d, %d banned ids" % (name, b["draft_ids"].shape[0], b["target_logits"].shape[-1],
+                                                      len(banned[1])))
+    g = gpu_run_flat(b, banned=banned)
+    res = compare(g, oracle_run(b, banned=banned), label=name)
+    off, ids = banned
+    for i in range(len(off) - 1):
+        A = g["num_accepted"][i]
+        if A >= 0:
+            assert not np.isin(g["tokens"][i, : A + 1], ids[off[i]:off[i + 1]]).any()
+    log("[parity] %s ok %s" % (name, res))
+
+
+def test_banned_list_faults_and_full_ban():
+    import rejection_sampling_verify_13_amd as sv
+    b = W.generate(W.config(1, N=6, gmax=2, V=16))
+    lists = [[3, 1], [16], [-1, 2], list(range(16)), [5, 5], [2, 9]]
+    off = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    ids = np.concatenate([np.array(x, np.int32) for x in lists])
+    log("[parity] malformed and full ban lists")
+    g = gpu_run_flat(b, banned=(off, ids))
+    o = oracle_run(b, banned=(off, ids))
+    np.testing.assert_array_equal(g["fault"], o["fault"])
+    assert (g["fault"][[0, 1, 2, 4]] == sv.FAULT_BAN_LIST).all() and g["fault"][3] == sv.FAULT_TARGET_ROW
+    assert g["fault"][5] == 0
+    compare(g, o, label="ban lists")

@@ -75,6 +75,7 @@ extern "C" {
 #define SPEC_VERIFY_FAULT_DRAFT_MASS 32
 #define SPEC_VERIFY_FAULT_DRAFT_COUNT 64 /* flattened layout: gamma_i outside [0, gmax] or past num_drafts */
 #define SPEC_VERIFY_FAULT_BAN_LIST 128   /* banned-token list longer than 512, not ascending, or an id outside [0, V) */
+#define SPEC_VERIFY_FAULT_ROW_INDEX 256  /* a target_logits row index outside [0, logits_rows) */
 
 /*
  * Bytes of device workspace one call with these sizes needs.  The layout is
@@ -195,27 +196,53 @@ int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t
                            void *ev_end);
 
 /*
- * spec_verify_flat_timed with banned tokens (zwjcode.cn page, section 06: p and
- * q must go through identical transforms, banned tokens among them): a banned
- * token of request i has logit -inf in every target row of the request and
- * probability 0 in every draft row, before temperature, top-k and top-p.  It
- * can therefore never be committed, and a draft of it is always rejected.
+ * spec_verify_flat_timed with the two options of the flattened call as vLLM
+ * feeds it; either may be NULL.
+ *
+ * Row indices (vLLM page, section "SpecDecodeMetadata：验证阶段的「索引地图」",
+ * fields target_logits_indices and bonus_logits_indices; the sampler's second
+ * step gathers the rows it verifies with them): the target model's logits
+ * tensor holds rows for other positions too, and these say which row holds
+ * each position, so that no gather copy is needed.
+ *   target_logits          f32/bf16 [logits_rows, V]
+ *   target_logits_indices  int32    [num_drafts]  row of flattened draft position t
+ *   bonus_logits_indices   int32    [N]           row of request i's bonus position
+ * bonus_logits_indices selects the option; target_logits_indices may then be
+ * NULL only when num_drafts is 0.  Without the option the rows are in request
+ * order as for spec_verify_flat and logits_rows must be at least
+ * num_drafts + N.  Rows
+ * no index names are never read.  An index outside [0, logits_rows) gives its
+ * request SPEC_VERIFY_FAULT_ROW_INDEX; an index is read only for a request
+ * whose count and parameters are valid.
+ *
+ * Banned tokens (zwjcode.cn page, section 06: p and q must go through
+ * identical transforms, banned tokens among them): a banned token of request i
+ * has logit -inf in every target row of the request and probability 0 in every
+ * draft row, before temperature, top-k and top-p.  It can therefore never be
+ * committed, and a draft of it is always rejected.
  *   banned_offsets  int32 [N + 1]   request i's list is banned_ids[off[i] .. off[i+1]-1]
  *   banned_ids      int32           strictly ascending per request, each in [0, V),
  *                                   at most 512 per request
- * A request whose list breaks those rules gets SPEC_VERIFY_FAULT_BAN_LIST.
- * Returns SPEC_VERIFY_ERR_NULL if either list pointer is NULL (N > 0).
+ * banned_offsets selects the option; banned_ids may then be NULL when every
+ * list is empty.  A request whose list breaks those rules (a nonempty list
+ * with NULL banned_ids among them) gets SPEC_VERIFY_FAULT_BAN_LIST.
+ *
+ * Returns SPEC_VERIFY_ERR_NULL (N > 0) for target_logits_indices without
+ * bonus_logits_indices, bonus_logits_indices without target_logits_indices
+ * when num_drafts > 0, or banned_ids without banned_offsets; and
+ * SPEC_VERIFY_ERR_SHAPE for logits_rows below 1, or below num_drafts + N
+ * without indices (N > 0).
  */
-int spec_verify_flat_banned(int N, int gmax, int V, int num_drafts, const int32_t *cu_num_draft_tokens,
-                            const int32_t *draft_ids, const float *draft_probs,
-                            const uint8_t *has_draft_probs, const void *target_logits,
-                            int logits_dtype, const float *temperature, const int32_t *top_k,
-                            const float *top_p, const int32_t *banned_offsets,
-                            const int32_t *banned_ids, const float *u_accept, const float *u_sample,
-                            int32_t *out_tokens, int32_t *out_num_accepted, double *p_y,
-                            double *q_y, double *resid_mass, int32_t *fault, void *workspace,
-                            size_t workspace_bytes, void *stream, void *ev_start, void *ev_mid,
-                            void *ev_end);
+int spec_verify_flat_ex(int N, int gmax, int V, int num_drafts, const int32_t *cu_num_draft_tokens,
+                        const int32_t *draft_ids, const float *draft_probs,
+                        const uint8_t *has_draft_probs, const void *target_logits, int logits_rows,
+                        const int32_t *target_logits_indices, const int32_t *bonus_logits_indices,
+                        int logits_dtype, const float *temperature, const int32_t *top_k,
+                        const float *top_p, const int32_t *banned_offsets, const int32_t *banned_ids,
+                        const float *u_accept, const float *u_sample, int32_t *out_tokens,
+                        int32_t *out_num_accepted, double *p_y, double *q_y, double *resid_mass,
+                        int32_t *fault, void *workspace, size_t workspace_bytes, void *stream,
+                        void *ev_start, void *ev_mid, void *ev_end);
 
 /*
  * The synthetic acceptance mode (vLLM page, section "关于 synthetic / block

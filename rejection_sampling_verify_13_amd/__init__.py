@@ -26,9 +26,10 @@ FAULT_DRAFT_ROW = 16
 FAULT_DRAFT_MASS = 32
 FAULT_DRAFT_COUNT = 64
 FAULT_BAN_LIST = 128
+FAULT_ROW_INDEX = 256
 
 EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_timed", "spec_verify_flat", "spec_verify_flat_timed",
-           "spec_verify_flat_synthetic", "spec_verify_flat_banned", "spec_verify_rollback", "spec_verify_workspace_size",
+           "spec_verify_flat_synthetic", "spec_verify_flat_ex", "spec_verify_rollback", "spec_verify_workspace_size",
            "spec_verify_status_string", "spec_verify_version")
 
 
@@ -57,9 +58,9 @@ def _load():
     lib.spec_verify_flat_synthetic.restype = I
     lib.spec_verify_flat_synthetic.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, Z, P,
                                                P, P, P]
-    lib.spec_verify_flat_banned.restype = I
-    lib.spec_verify_flat_banned.argtypes = ([I, I, I, I] + [P] * 5 + [I] + [P] * 3 + [P, P] + [P] * 4 + [P] * 4 +
-                                            [P, Z, P] + [P] * 3)
+    lib.spec_verify_flat_ex.restype = I
+    lib.spec_verify_flat_ex.argtypes = ([I, I, I, I] + [P] * 5 + [I, P, P, I] + [P] * 3 + [P, P] + [P] * 4 +
+                                        [P] * 4 + [P, Z, P] + [P] * 3)
     lib.spec_verify_rollback.restype = I
     lib.spec_verify_rollback.argtypes = [I, I, P, P, P, P, P, P, P]
     lib.spec_verify_workspace_size.restype = Z
@@ -173,7 +174,7 @@ def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, 
 def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, target_logits, gmax,
                 temperature=None, top_k=None, top_p=None, u_accept=None, u_sample=None, *, out_tokens=None,
                 out_num_accepted=None, workspace=None, stream=None, diag=False, events=None, synthetic_rates=None,
-                banned_offsets=None, banned_ids=None):
+                banned_offsets=None, banned_ids=None, target_logits_indices=None, bonus_logits_indices=None):
     """Verify a batch in the flattened layout (spec_verify_flat in include/spec_verify.h).
 
     cu_num_draft_tokens int32 [N] (inclusive prefix sums of the draft counts),
@@ -187,16 +188,25 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
     (float32 [gmax]) the synthetic acceptance mode runs (spec_verify_flat_synthetic):
     draft j is accepted iff u_accept < rate_j; diag then returns only ``fault``.
     With ``banned_offsets`` (int32 [N + 1]) and ``banned_ids`` (int32, ascending
-    per request) those tokens are banned in p and q alike (spec_verify_flat_banned).
+    per request) those tokens are banned in p and q alike.  With
+    ``target_logits_indices`` (int32 [T]) and ``bonus_logits_indices`` (int32
+    [N]) target_logits is any [R, V] tensor and those indices name the row of
+    each draft and bonus position.  Either option runs spec_verify_flat_ex.
     """
     if target_logits.dim() != 2:
-        raise ValueError("target_logits must be [T + N, V]")
+        raise ValueError("target_logits must be [T + N, V] (or [R, V] with row indices)")
     N = cu_num_draft_tokens.shape[0]
     G = int(gmax)
     R, V = target_logits.shape
-    T = R - N
-    if T < 0:
-        raise ValueError("target_logits has fewer rows than requests")
+    indexed = target_logits_indices is not None or bonus_logits_indices is not None
+    if indexed:
+        if draft_ids is None or draft_ids.dim() != 1:
+            raise ValueError("draft_ids must be a 1-d int32 tensor")
+        T = draft_ids.shape[0]
+    else:
+        T = R - N
+        if T < 0:
+            raise ValueError("target_logits has fewer rows than requests")
     dev = target_logits.device
     if target_logits.dtype == torch.bfloat16:
         dt = BF16
@@ -247,13 +257,15 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
         if rc != 0:
             raise SpecVerifyError("spec_verify_flat_synthetic failed: %s" % lib.spec_verify_status_string(rc).decode())
         return (out_tokens, out_num_accepted, d) if diag else (out_tokens, out_num_accepted)
-    if banned_offsets is not None or banned_ids is not None:
-        if synthetic_rates is not None:
-            raise ValueError("banned tokens are not supported together with the synthetic mode")
-        _check(banned_offsets, "banned_offsets", torch.int32, (N + 1,), dev)
-        if banned_ids is None or banned_ids.dim() != 1:
-            raise ValueError("banned_ids must be a 1-d int32 tensor")
-        _check(banned_ids, "banned_ids", torch.int32, tuple(banned_ids.shape), dev)
+    if banned_offsets is not None or banned_ids is not None or indexed:
+        if banned_offsets is not None or banned_ids is not None:
+            _check(banned_offsets, "banned_offsets", torch.int32, (N + 1,), dev)
+            if banned_ids is None or banned_ids.dim() != 1:
+                raise ValueError("banned_ids must be a 1-d int32 tensor")
+            _check(banned_ids, "banned_ids", torch.int32, tuple(banned_ids.shape), dev)
+        if indexed:
+            _check(target_logits_indices, "target_logits_indices", torch.int32, (T,), dev)
+            _check(bonus_logits_indices, "bonus_logits_indices", torch.int32, (N,), dev)
         if diag:
             d = dict(p_y=torch.empty((N, G), dtype=torch.float64, device=dev),
                      q_y=torch.empty((N, G), dtype=torch.float64, device=dev),
@@ -265,10 +277,11 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
         evp = (None, None, None) if events is None else tuple(
             None if e is None else ctypes.c_void_p(e.cuda_event) for e in events)
         with torch.cuda.device(dev):
-            rc = lib.spec_verify_flat_banned(*head[:13], _ptr(banned_offsets), _ptr(banned_ids), *head[13:], *dp,
-                                             _ptr(workspace), ws_bytes, sptr, *evp)
+            rc = lib.spec_verify_flat_ex(*head[:9], R, _ptr(target_logits_indices), _ptr(bonus_logits_indices),
+                                         *head[9:13], _ptr(banned_offsets), _ptr(banned_ids), *head[13:], *dp,
+                                         _ptr(workspace), ws_bytes, sptr, *evp)
         if rc != 0:
-            raise SpecVerifyError("spec_verify_flat_banned failed: %s" % lib.spec_verify_status_string(rc).decode())
+            raise SpecVerifyError("spec_verify_flat_ex failed: %s" % lib.spec_verify_status_string(rc).decode())
         return (out_tokens, out_num_accepted, d) if diag else (out_tokens, out_num_accepted)
     with torch.cuda.device(dev):
         if diag or events is not None:
@@ -319,7 +332,7 @@ def to_device_flat(flat: dict, device="cuda"):
     import numpy as np
     out = {"gmax": flat["gmax"]}
     for k in ("cu_num_draft_tokens", "draft_ids", "draft_probs", "has_draft_probs", "temperature", "top_k",
-              "top_p", "u_accept", "u_sample"):
+              "top_p", "u_accept", "u_sample", "target_logits_indices", "bonus_logits_indices"):
         v = flat.get(k)
         out[k] = None if v is None else torch.from_numpy(np.ascontiguousarray(v)).to(device)
     tl = flat["target_logits"]
@@ -335,7 +348,8 @@ def verify_flat_batch(dev_flat: dict, **kw):
     return verify_flat(dev_flat["cu_num_draft_tokens"], dev_flat["draft_ids"], dev_flat["draft_probs"],
                        dev_flat["has_draft_probs"], dev_flat["target_logits"], dev_flat["gmax"],
                        dev_flat["temperature"], dev_flat["top_k"], dev_flat["top_p"], dev_flat["u_accept"],
-                       dev_flat["u_sample"], **kw)
+                       dev_flat["u_sample"], target_logits_indices=dev_flat.get("target_logits_indices"),
+                       bonus_logits_indices=dev_flat.get("bonus_logits_indices"), **kw)
 
 
 def rollback(num_accepted, *, cu_num_draft_tokens=None, draft_ids=None, gmax=None, num_computed_tokens=None,

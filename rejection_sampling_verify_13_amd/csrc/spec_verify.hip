@@ -82,6 +82,7 @@ enum {
   kFaultDraftMass = SPEC_VERIFY_FAULT_DRAFT_MASS,
   kFaultDraftCount = SPEC_VERIFY_FAULT_DRAFT_COUNT,
   kFaultBanList = SPEC_VERIFY_FAULT_BAN_LIST,
+  kFaultRowIndex = SPEC_VERIFY_FAULT_ROW_INDEX,
 };
 constexpr int kBanMax = 512;            // banned tokens per request (ascending list kept in LDS)
 
@@ -156,8 +157,11 @@ struct Args {
   const int32_t* cu;    // [N] inclusive prefix sums of gamma_i
   const uint8_t* has_q; // [N] request i has draft rows iff nonzero; nullptr: all do (when q != nullptr)
   int T;                // number of drafts, cu[N - 1]
+  const int32_t* bidx;  // [N] target_logits row of each bonus position, or nullptr (rows in request order)
+  const int32_t* tidx;  // [T] target_logits row of each draft position (with bidx)
+  int R;                // rows of target_logits (with bidx)
   const int32_t* ban_off;  // [N + 1] banned-token list offsets, or nullptr
-  const int32_t* ban_ids;  // ascending ids per request
+  const int32_t* ban_ids;  // ascending ids per request; nullptr when every list is empty
   int synthetic;        // 1: the synthetic acceptance mode (draft j accepted iff u_j < srates[j])
   const float* srates;  // synthetic acceptance rates [G]
 };
@@ -514,7 +518,8 @@ __device__ inline int block_min_i(int v, int* red) {
 
 struct Req {
   int gamma;      // number of draft tokens
-  int tgt0;       // target_logits row of position 0
+  int tgt0;       // target_logits row of position 0 (rows in request order)
+  long long trow; // target_logits row of the row being processed (row kernel)
   int id0;        // index of draft 0 in draft_ids and u_accept
   int q0;         // draft_probs row of position 0; -1: no draft rows
   float T;        // temperature
@@ -1622,7 +1627,7 @@ __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, 
   typedef typename LT::T ET;
   const int G = a.G, V = a.V, tid = threadIdx.x;
   const size_t row = (size_t)i * (G + 1) + j;  // the row record
-  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + ((size_t)rq.tgt0 + j) * (size_t)V;
+  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + (size_t)rq.trow * (size_t)V;
   float best = -INFINITY, acc = 0.f;
   int bidx = -1;
   stream_greedy<LT, VEC, BAN>(lrow, V, best, bidx, acc, ban, nban);
@@ -1669,7 +1674,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   const int G = a.G, V = a.V;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const size_t row = (size_t)i * (G + 1) + j;  // the row record
-  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + ((size_t)rq.tgt0 + j) * (size_t)V;
+  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + (size_t)rq.trow * (size_t)V;
   const bool draft_pos = j < rq.gamma;
   const bool req_q = rq.q0 >= 0;  // the request carries draft rows
   const bool has_q = req_q && draft_pos;
@@ -2079,12 +2084,19 @@ __global__ __launch_bounds__(kBlock, sizeof(typename LT::T) == 2 ? 3 : 2) void r
   const int i = bonus ? bx - nd : (m >> 7);
   Req rq = load_req(a, i);
   const int j = bonus ? rq.gamma : (m & 127);
+  // the row's place in target_logits: request order, or the caller's indices
+  rq.trow = (long long)rq.tgt0 + j;
+  if (a.bidx && !rq.fault) {
+    const int r = j < rq.gamma ? a.tidx[(size_t)rq.id0 + j] : a.bidx[i];
+    if (r < 0 || r >= a.R) rq.fault |= kFaultRowIndex;
+    rq.trow = r;
+  }
   int nban = 0;
   if (BAN) {
     // the request's banned tokens into LDS: at most kBanMax, strictly
     // ascending, each in [0, V); otherwise the request faults
     const int b0 = a.ban_off[i], n = a.ban_off[i + 1] - b0;
-    int bad = (n < 0 || n > kBanMax) ? 1 : 0;
+    int bad = (n < 0 || n > kBanMax || (n > 0 && !a.ban_ids)) ? 1 : 0;
     if (!bad)
       for (int t = threadIdx.x; t < n; t += kBlock) {
         const int id = a.ban_ids[(size_t)b0 + t];
@@ -2227,7 +2239,9 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   const bool temper = T != 1.f;
   const float invZ = (float)(1.0 / sa.z);
   const float invR = (mode == 1) ? (float)(1.0 / sa.r) : 0.f;
-  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + ((size_t)rr.tgt0 + A) * (size_t)V;
+  // (row A's index was checked by the row pass: a bad one faults the request)
+  const size_t trow = !a.bidx ? (size_t)rr.tgt0 + A : (size_t)(A < gamma ? a.tidx[(size_t)rr.id0 + A] : a.bidx[i]);
+  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + trow * (size_t)V;
   const float* qrow = (mode == 1) ? a.q + ((size_t)rr.q0 + A) * (size_t)V : nullptr;
   const int nsteps = (V + kStep - 1) / kStep;
   DrawSum* ds = a.dsum + (size_t)i * nsteps * kWaves;
@@ -2504,7 +2518,7 @@ struct Layout {
 };
 
 int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* srates, const int32_t* ban_off,
-        const int32_t* ban_ids, const int32_t* ids, const float* q, const void* logits, int dtype,
+        const int32_t* ban_ids, const int32_t* tidx, const int32_t* bidx, int R, const int32_t* ids, const float* q, const void* logits, int dtype,
         const float* temperature, const int32_t* top_k, const float* top_p, const float* u_accept,
         const float* u_sample, int32_t* out_tokens, int32_t* out_num, double* p_y, double* q_y, double* resid,
         int32_t* fault, void* workspace, size_t workspace_bytes, void* stream, const Events& ev) {
@@ -2573,6 +2587,9 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   a.cu = lay.cu;
   a.has_q = lay.has_q;
   a.T = lay.T;
+  a.tidx = tidx;
+  a.bidx = bidx;
+  a.R = R;
   a.ban_off = ban_off;
   a.ban_ids = ban_ids;
   a.synthetic = synthetic ? 1 : 0;
@@ -2611,7 +2628,7 @@ int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* d
                 int logits_dtype, const float* temperature, const int32_t* top_k, const float* top_p,
                 const float* u_accept, const float* u_sample, int32_t* out_tokens, int32_t* out_num_accepted,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes,
              stream, Events{nullptr, nullptr, nullptr});
 }
@@ -2621,7 +2638,7 @@ int spec_verify_diag(int N, int gmax, int V, const int32_t* draft_ids, const flo
                      const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
                      int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{nullptr, nullptr, nullptr});
 }
@@ -2632,7 +2649,7 @@ int spec_verify_timed(int N, int gmax, int V, const int32_t* draft_ids, const fl
                       int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
                       void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_mid,
                       void* ev_end) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
                     reinterpret_cast<hipEvent_t>(ev_end)});
@@ -2644,7 +2661,7 @@ int spec_verify_flat(int N, int gmax, int V, int num_drafts, const int32_t* cu_n
                      const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
                      int32_t* out_num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
-  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, nullptr, nullptr, draft_ids, draft_probs,
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs,
              target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens,
              out_num_accepted, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
              Events{nullptr, nullptr, nullptr});
@@ -2658,25 +2675,34 @@ int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t
                            double* resid_mass, int32_t* fault, void* workspace, size_t workspace_bytes, void* stream,
                            void* ev_start, void* ev_mid, void* ev_end) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
-  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, nullptr, nullptr, draft_ids, draft_probs,
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs,
              target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens,
              out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
                     reinterpret_cast<hipEvent_t>(ev_end)});
 }
 
-int spec_verify_flat_banned(int N, int gmax, int V, int num_drafts, const int32_t* cu_num_draft_tokens,
-                            const int32_t* draft_ids, const float* draft_probs, const uint8_t* has_draft_probs,
-                            const void* target_logits, int logits_dtype, const float* temperature,
-                            const int32_t* top_k, const float* top_p, const int32_t* banned_offsets,
-                            const int32_t* banned_ids, const float* u_accept, const float* u_sample,
-                            int32_t* out_tokens, int32_t* out_num_accepted, double* p_y, double* q_y,
-                            double* resid_mass, int32_t* fault, void* workspace, size_t workspace_bytes,
-                            void* stream, void* ev_start, void* ev_mid, void* ev_end) {
-  if (N > 0 && (!cu_num_draft_tokens || !banned_offsets || !banned_ids)) return SPEC_VERIFY_ERR_NULL;
+int spec_verify_flat_ex(int N, int gmax, int V, int num_drafts, const int32_t* cu_num_draft_tokens,
+                        const int32_t* draft_ids, const float* draft_probs, const uint8_t* has_draft_probs,
+                        const void* target_logits, int logits_rows, const int32_t* target_logits_indices,
+                        const int32_t* bonus_logits_indices, int logits_dtype, const float* temperature,
+                        const int32_t* top_k, const float* top_p, const int32_t* banned_offsets,
+                        const int32_t* banned_ids, const float* u_accept, const float* u_sample, int32_t* out_tokens,
+                        int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
+                        void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_mid,
+                        void* ev_end) {
+  if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
+  // the bonus indices and the offsets select the options; their companions
+  // may be NULL only where nothing would be read through them
+  if (N > 0 && target_logits_indices && !bonus_logits_indices) return SPEC_VERIFY_ERR_NULL;
+  if (N > 0 && num_drafts > 0 && bonus_logits_indices && !target_logits_indices) return SPEC_VERIFY_ERR_NULL;
+  if (N > 0 && banned_ids && !banned_offsets) return SPEC_VERIFY_ERR_NULL;
+  if (N > 0 && (logits_rows < 1 || (!bonus_logits_indices && (long long)logits_rows < (long long)num_drafts + N)))
+    return SPEC_VERIFY_ERR_SHAPE;
   return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, banned_offsets,
-             banned_ids, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
-             u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
+             banned_ids, target_logits_indices, bonus_logits_indices, logits_rows, draft_ids, draft_probs,
+             target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens, out_num_accepted,
+             p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
                     reinterpret_cast<hipEvent_t>(ev_end)});
 }
@@ -2690,7 +2716,7 @@ int spec_verify_flat_synthetic(int N, int gmax, int V, int num_drafts, const int
                                void* stream, void* ev_start, void* ev_mid, void* ev_end) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
   if (N > 0 && gmax > 0 && !synthetic_rates) return SPEC_VERIFY_ERR_NULL;
-  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, true, synthetic_rates, nullptr, nullptr, draft_ids, draft_probs, target_logits, logits_dtype,
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, true, synthetic_rates, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype,
              temperature, top_k, top_p, u_accept, u_sample, out_tokens, out_num_accepted, nullptr, nullptr, nullptr,
              fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),

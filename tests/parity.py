@@ -48,14 +48,19 @@ def gpu_run(batch, diag=True, stream=None):
     return res
 
 
-def gpu_run_flat(batch, diag=True, stream=None, synthetic_rates=None, banned=None):
+def gpu_run_flat(batch, diag=True, stream=None, synthetic_rates=None, banned=None, scatter=None):
     """Run a numpy batch on cuda:0 as one call in the flattened layout (a mixed
     dense / draft-free batch included: the draft-row mask selects per request);
-    with synthetic_rates, in the synthetic acceptance mode."""
+    with synthetic_rates, in the synthetic acceptance mode; with scatter =
+    (seed, extra rows), its target rows scattered over a larger NaN-filled
+    logits tensor and addressed through row indices."""
     import torch
     import rejection_sampling_verify_13_amd as sv
     import workloads as W
-    d = sv.to_device_flat(W.flatten(batch))
+    flat = W.flatten(batch)
+    if scatter is not None:
+        flat = W.scatter_rows(flat, *scatter)
+    d = sv.to_device_flat(flat)
     kw = {}
     if synthetic_rates is not None:
         kw["synthetic_rates"] = torch.from_numpy(np.ascontiguousarray(synthetic_rates, np.float32)).cuda()

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_verify_diag", "spec_verify_workspace_size", "spec_verify_status_string",
               "spec_verify_version", "spec_verify_flat", "spec_verify_flat_timed", "spec_verify_rollback",
-              "spec_verify_flat_synthetic"):
+              "spec_verify_flat_synthetic", "spec_verify_flat_ex"):
         assert n in names
 
 
@@ -91,6 +91,27 @@ def test_flat_host_validation(lib):
     assert _flat(lib, T=0, ids=0, ua=0, logits=0) == 1   # ids may be NULL without drafts; logits may not
     assert _flat(lib, N=0, cu=0) == 0    # empty batch
     assert _flat(lib, G=65) == 2
+
+
+def _ex(lib, N=2, G=3, V=16, T=4, R=6, tidx=0, bidx=0, boff=0, bids=0):
+    P = lambda flag: ctypes.c_void_p(0x1000) if flag else None
+    # a 16-byte workspace: every accepted argument set stops at the workspace check
+    return lib.spec_verify_flat_ex(N, G, V, T, P(1), P(1), None, None, P(1), R, P(tidx), P(bidx), 1, None, None, None,
+                                   P(boff), P(bids), P(1), P(1), P(1), P(1), None, None, None, None, P(1), 16, None,
+                                   None, None, None)
+
+
+def test_flat_ex_host_validation(lib):
+    assert _ex(lib) == 4
+    assert _ex(lib, tidx=1) == 1               # draft-row indices without bonus-row indices
+    assert _ex(lib, bidx=1) == 1               # bonus-row indices without draft-row indices, with drafts
+    assert _ex(lib, T=0, R=1, bidx=1) == 4     # no drafts: the draft-row indices may be NULL
+    assert _ex(lib, R=5) == 2                  # fewer rows than num_drafts + N without indices
+    assert _ex(lib, R=0, tidx=1, bidx=1) == 2
+    assert _ex(lib, R=1, tidx=1, bidx=1) == 4  # any row count with indices
+    assert _ex(lib, bids=1) == 1               # banned ids without offsets
+    assert _ex(lib, boff=1) == 4               # offsets alone: every list empty
+    assert _ex(lib, N=0, T=0, R=0, tidx=1) == 0  # empty batch
 
 
 def test_synthetic_host_validation(lib):

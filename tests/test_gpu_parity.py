@@ -605,3 +605,56 @@ def test_banned_list_faults_and_full_ban():
     assert (g["fault"][[0, 1, 2, 4]] == sv.FAULT_BAN_LIST).all() and g["fault"][3] == sv.FAULT_TARGET_ROW
     assert g["fault"][5] == 0
     compare(g, o, label="ban lists")
+
+
+# ------------------------------------------------------------------------------------------
+# target rows addressed through row indices (vLLM's target_logits_indices and
+# bonus_logits_indices), inside a larger logits tensor whose other rows are NaN
+# ------------------------------------------------------------------------------------------
+
+SCAT = {
+    "rows_cfg3_small_topk": (W.config(3, N=24, V=12000), 0),
+    "rows_cfg5_small_mixed": (W.config(5, N=48, V=6144), 0),
+    "rows_cfg4_small_greedy": (W.config(4, N=40, V=7000, greedy_count=10), 0),
+    "rows_unaligned_f32_banned": (W.config(2, N=16, V=3001, dtype="f32"), 30),
+    "rows_cfg2_ragged": (W.config(2, N=20, V=5000), 0),
+}
+
+
+@pytest.mark.parametrize("name", list(SCAT))
+def test_row_indices_parity(name):
+    cfg, nban = SCAT[name]
+    b = W.generate(cfg)
+    N = b["draft_ids"].shape[0]
+    banned = _ban_lists(b, 9, nban) if nban else None
+    log("[parity] %s: N=%d V=%d, rows scattered over %d extra NaN rows" % (name, N, b["target_logits"].shape[-1],
+                                                                       N // 2 + 3))
+    g = gpu_run_flat(b, banned=banned, scatter=(11, N // 2 + 3))
+    res = compare(g, oracle_run(b, banned=banned), label=name)
+    log("[parity] %s ok %s" % (name, res))
+
+
+def test_row_index_faults():
+    """An index outside [0, R) faults its request alone; the others match the
+    oracle on the ordered rows."""
+    import torch
+    import rejection_sampling_verify_13_amd as sv
+    b = W.generate(W.config(3, N=8, V=4096))
+    flat = W.scatter_rows(W.flatten(b), 3, 5)
+    R = flat["target_logits"].shape[0]
+    cu = flat["cu_num_draft_tokens"]
+    assert cu[1] > cu[0] and cu[6] > cu[5]
+    flat["target_logits_indices"][cu[0]] = R           # request 1: first draft row past the end
+    flat["bonus_logits_indices"][4] = -1               # request 4: negative bonus row
+    flat["target_logits_indices"][cu[6] - 1] = R + 99  # request 6: last draft row
+    log("[parity] out-of-range row indices, R=%d" % R)
+    d = sv.to_device_flat(flat)
+    t, n, dg = sv.verify_flat_batch(d, diag=True)
+    torch.cuda.synchronize()
+    g = dict(tokens=t.cpu().numpy(), num_accepted=n.cpu().numpy(), **{k: v.cpu().numpy() for k, v in dg.items()})
+    o = oracle_run(b)
+    bad = [1, 4, 6]
+    assert (g["fault"][bad] == sv.FAULT_ROW_INDEX).all()
+    assert (g["tokens"][bad] == -1).all() and (g["num_accepted"][bad] == -1).all()
+    keep = np.setdiff1d(np.arange(8), bad)
+    compare({k: v[keep] for k, v in g.items()}, {k: v[keep] for k, v in o.items()}, label="row index faults")

@@ -276,3 +276,30 @@ def flatten(batch: dict) -> dict:
                 target_logits=logits, dtype=batch["dtype"], gmax=G, temperature=batch["temperature"],
                 top_k=batch["top_k"], top_p=batch["top_p"], u_accept=ua.astype(np.float32),
                 u_sample=batch["u_sample"])
+
+
+def scatter_rows(flat: dict, seed: int, extra: int) -> dict:
+    """The flattened batch with its target rows scattered over a larger logits
+    tensor, as a target model's output holds them among rows of other
+    positions: target_logits becomes [T + N + extra, V] with the rows at a
+    seeded random placement and NaN in every row no index names;
+    target_logits_indices [T] and bonus_logits_indices [N] give each draft and
+    bonus position's row.  Pure data movement."""
+    cu = np.asarray(flat["cu_num_draft_tokens"], np.int64)
+    N = cu.shape[0]
+    tl = flat["target_logits"]
+    R0, V = tl.shape
+    T = R0 - N
+    R = R0 + int(extra)
+    rng = np.random.default_rng(seed)
+    place = rng.permutation(R)[:R0].astype(np.int32)  # row r of the ordered layout goes to place[r]
+    nan = np.uint16(0x7FC0) if flat["dtype"] == "bf16" else np.float32(np.nan)
+    out = np.full((R, V), nan, tl.dtype)
+    out[place] = tl
+    # ordered-layout row of draft t of request i is t + i; of its bonus, cu[i] + i
+    req_of_t = np.searchsorted(cu, np.arange(T), side="right")
+    tidx = place[np.arange(T) + req_of_t].astype(np.int32)
+    bidx = place[cu + np.arange(N)].astype(np.int32) if N else np.zeros(0, np.int32)
+    res = dict(flat)
+    res.update(target_logits=out, target_logits_indices=tidx, bonus_logits_indices=bidx)
+    return res

@@ -34,7 +34,9 @@ FAULT_TARGET_ROW = 8
 FAULT_DRAFT_ROW = 16
 FAULT_DRAFT_MASS = 32
 FAULT_BAN_LIST = 128
+FAULT_PENALTY = 512
 BAN_MAX = 512
+PEN_MAX = 1024
 
 
 def build(force: bool = True) -> str:
@@ -86,7 +88,7 @@ def _c(a, dtype):
 
 def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=None, top_p=None,
         u_accept=None, u_sample=None, threads: int = 1, _lib_override=None, synthetic_rates=None,
-        banned=None) -> dict:
+        banned=None, penalties=None) -> dict:
     """Verify a batch on the CPU.
 
     ``dtype`` is "f32" (``target_logits`` float32) or "bf16" (``target_logits``
@@ -103,6 +105,23 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
     inputs changed that way.  A list longer than BAN_MAX, not strictly
     ascending, or with an id outside [0, V) faults its request (FAULT_BAN_LIST,
     with the request's parameter faults and no row read).
+
+    ``penalties`` = dict(lists=..., repetition=[N] or None, presence=[N] or
+    None, frequency=[N] or None): repetition penalties, the other transform
+    that section names.  lists[i][j] = (ids, counts) for each row j = 0 ..
+    gamma_i of request i: the tokens of the context that position j continues
+    (the draft tokens before j included) and how often each occurs in the
+    generated output (0: only in the prompt).  Each listed token's logit is
+    changed as ``penalize_logits`` states and its draft probability multiplied
+    by exp(-delta) (``penalty_deltas``), the same change on the probability
+    scale, before temperature, top-k and top-p.  A list longer than PEN_MAX,
+    not strictly ascending, with an id outside [0, V) or a negative count, a
+    repetition penalty that is not a positive finite number, a presence or
+    frequency penalty that is not finite, or a repetition penalty other than 1
+    on a request that carries draft rows and has a nonzero temperature (a
+    multiplicative change of logits has no counterpart on probabilities, whose
+    logits are fixed only up to a constant), faults the request
+    (FAULT_PENALTY, with its parameter faults).
     """
     lib = _lib_override or _load()
     ids = _c(draft_ids, np.int32)
@@ -114,6 +133,14 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
     q = _c(draft_probs, np.float32)
     if q is not None:
         assert q.shape == (N, gmax, V), q.shape
+    bad_pen = np.zeros(N, bool)
+    if penalties is not None:
+        tl = tl.copy()
+        q = None if q is None else q.copy()
+        neg = np.concatenate([ids < 0, np.ones((N, 1), bool)], axis=1)
+        gam = np.argmax(neg, axis=1)  # the first negative id, else gmax
+        for i in range(N):
+            bad_pen[i] = not _penalize_request(i, gam[i], penalties, tl, q, dtype, temperature, V)
     bad_list = np.zeros(N, bool)
     if banned is not None:
         off, bid = np.asarray(banned[0], np.int64), np.asarray(banned[1], np.int64)
@@ -170,8 +197,9 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
             rc = list(ex.map(lambda t: one(bounds[t], bounds[t + 1]), range(threads)))
     if any(rc):
         raise ValueError("oracle rejected the shapes or dtype")
-    for i in np.nonzero(bad_list)[0]:
-        out["fault"][i] = (out["fault"][i] & (FAULT_DRAFT_ID | FAULT_TEMPERATURE | FAULT_TOP_P)) | FAULT_BAN_LIST
+    for i in np.nonzero(bad_list | bad_pen)[0]:
+        out["fault"][i] = ((out["fault"][i] & (FAULT_DRAFT_ID | FAULT_TEMPERATURE | FAULT_TOP_P)) |
+                           (FAULT_BAN_LIST if bad_list[i] else 0) | (FAULT_PENALTY if bad_pen[i] else 0))
         out["tokens"][i] = -1
         out["num_accepted"][i] = -1
         out["p_y"][i] = np.nan
@@ -179,6 +207,68 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
         out["resid_mass"][i] = np.nan
         out["margin"][i] = np.inf
     return out
+
+
+def penalty_deltas(counts, presence, frequency):
+    """The additive penalty of each listed token, float32: frequency * count +
+    presence for a token that occurs in the generated output (count > 0), 0 for
+    one that occurs only in the prompt; the product and the sum are each
+    rounded to float32."""
+    c = np.asarray(counts, np.int64)
+    with np.errstate(all="ignore"):
+        d = np.float32(frequency) * c.astype(np.float32)
+        d = (d + np.float32(presence)).astype(np.float32)
+    return np.where(c > 0, d, np.float32(0.0)).astype(np.float32)
+
+
+def penalize_logits(values, dtype, theta, deltas):
+    """Penalised logits of listed tokens: a positive logit is divided by the
+    repetition penalty theta and any other multiplied by it, then the token's
+    delta is subtracted, in float32 with each operation rounded; bf16 logits
+    (uint16 bit patterns in and out) are rounded back to bf16, to nearest
+    even, NaN staying NaN."""
+    bf16 = dtype == "bf16"
+    v = np.asarray(values)
+    if bf16:
+        l = (v.astype(np.uint32) << 16).view(np.float32)
+    else:
+        l = v.astype(np.float32)
+    th = np.float32(theta)
+    with np.errstate(all="ignore"):
+        l1 = np.where(l > 0, l / th, l * th).astype(np.float32)
+        l2 = (l1 - np.asarray(deltas, np.float32)).astype(np.float32)
+    if not bf16:
+        return l2
+    u = l2.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return np.where(np.isnan(l2), np.uint16(0x7FC0), r).astype(np.uint16)
+
+
+def _penalize_request(i, gamma, pen, tl, q, dtype, temperature, V):
+    """Apply request i's penalties to its rows in place; False if they fault."""
+    def scalar(key, default):
+        a = pen.get(key)
+        return np.float32(default if a is None else a[i])
+    theta, pres, freq = scalar("repetition", 1.0), scalar("presence", 0.0), scalar("frequency", 0.0)
+    if not (np.isfinite(theta) and theta > 0 and np.isfinite(pres) and np.isfinite(freq)):
+        return False
+    T = 1.0 if temperature is None else np.float32(temperature[i])
+    if theta != 1 and q is not None and T != 0:
+        return False
+    rows = pen["lists"][i]
+    assert len(rows) == gamma + 1, "one list per row j = 0 .. gamma_i"
+    for pid, cnt in rows:
+        pid, cnt = np.asarray(pid, np.int64), np.asarray(cnt, np.int64)
+        if (len(pid) > PEN_MAX or len(cnt) != len(pid) or (pid < 0).any() or (pid >= V).any() or
+                (np.diff(pid) <= 0).any() or (cnt < 0).any()):
+            return False
+    for j, (pid, cnt) in enumerate(rows):
+        pid = np.asarray(pid, np.int64)
+        d = penalty_deltas(cnt, pres, freq)
+        tl[i, j, pid] = penalize_logits(tl[i, j, pid], dtype, theta, d)
+        if q is not None and j < gamma:
+            q[i, j, pid] = (q[i, j, pid].astype(np.float64) * np.exp(-d.astype(np.float64))).astype(np.float32)
+    return True
 
 
 def target_probs(row, dtype, T=1.0, top_k=0, top_p=1.0, _lib_override=None):

@@ -123,6 +123,9 @@ def main():
                          "(flattened layout; only row A of each request is read)")
     ap.add_argument("--banned", type=int, default=0,
                     help="ban this many seeded random token ids per request (flattened layout, identical in p and q)")
+    ap.add_argument("--penalties", type=int, default=0,
+                    help="repetition penalties over a seeded context of this many tokens per request (flattened "
+                         "layout; presence 0.5, frequency 0.25, repetition 1.2 on greedy and draft-free requests)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -151,13 +154,22 @@ def main():
         [float(x) for x in args.synthetic_rates.split(",")], np.float32)
     if rates is not None and len(rates) != spec.gmax:
         sys.exit("--synthetic-rates needs %d rates" % spec.gmax)
-    flat = args.layout == "flat" or (args.layout == "auto" and mixed) or rates is not None or args.banned > 0
+    flat = (args.layout == "flat" or (args.layout == "auto" and mixed) or rates is not None or args.banned > 0 or
+            args.penalties > 0)
     ban = None
     if args.banned > 0:
         brng = np.random.default_rng(7)
         lists = [np.sort(brng.choice(spec.V, size=args.banned, replace=False)) for _ in range(spec.N)]
         ban = (np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32),
                np.concatenate(lists).astype(np.int32))
+    pen = None
+    if args.penalties > 0:
+        off, pid, cnt = W.flatten_penalties(W.penalty_lists(batch, 8, args.penalties))
+        dense = batch["has_q"] if batch["draft_probs"] is not None else np.zeros(spec.N, bool)
+        theta = np.where(dense & (batch["temperature"] != 0), 1.0, 1.2).astype(np.float32)
+        pen = dict(penalty_offsets=off, penalty_ids=pid, penalty_counts=cnt, repetition_penalty=theta,
+                   presence_penalty=np.full(spec.N, 0.5, np.float32),
+                   frequency_penalty=np.full(spec.N, 0.25, np.float32))
     if flat:
         parts = [W.flatten(batch)]
     else:
@@ -193,6 +205,8 @@ def main():
             if ban is not None:
                 d["ban_off"] = torch.from_numpy(ban[0]).to(dev)
                 d["ban_ids"] = torch.from_numpy(ban[1]).to(dev)
+            if pen is not None:
+                d.update({k: torch.from_numpy(v).to(dev) for k, v in pen.items()})
             ps.append(d)
         sets.append(ps)
     del batch["target_logits"], batch["draft_probs"]
@@ -285,6 +299,7 @@ def main():
                    "kv_rollback_in_step": bool(args.rollback),
                    "synthetic_rates": None if rates is None else [float(x) for x in rates],
                    "banned_per_request": args.banned,
+                   "penalty_context_per_request": args.penalties,
                    "target_logits": spec.dtype, "draft_probs": "f32" if spec.q_mode != "null" else None,
                    "verified_positions_per_step": positions, "rows_per_step": rows,
                    "algorithmic_bytes_per_step": B_alg, "target_bytes": B_target, "draft_bytes": B_draft},

@@ -76,6 +76,7 @@ extern "C" {
 #define SPEC_VERIFY_FAULT_DRAFT_COUNT 64 /* flattened layout: gamma_i outside [0, gmax] or past num_drafts */
 #define SPEC_VERIFY_FAULT_BAN_LIST 128   /* banned-token list longer than 512, not ascending, or an id outside [0, V) */
 #define SPEC_VERIFY_FAULT_ROW_INDEX 256  /* a target_logits row index outside [0, logits_rows) */
+#define SPEC_VERIFY_FAULT_PENALTY 512    /* a penalty list or penalty value breaks the rules of spec_verify_flat_ex */
 
 /*
  * Bytes of device workspace one call with these sizes needs.  The layout is
@@ -196,8 +197,8 @@ int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t
                            void *ev_end);
 
 /*
- * spec_verify_flat_timed with the two options of the flattened call as vLLM
- * feeds it; either may be NULL.
+ * spec_verify_flat_timed with the three options of the flattened call as vLLM
+ * feeds it; each may be left out (NULL).
  *
  * Row indices (vLLM page, section "SpecDecodeMetadata：验证阶段的「索引地图」",
  * fields target_logits_indices and bonus_logits_indices; the sampler's second
@@ -227,9 +228,41 @@ int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t
  * list is empty.  A request whose list breaks those rules (a nonempty list
  * with NULL banned_ids among them) gets SPEC_VERIFY_FAULT_BAN_LIST.
  *
+ * Repetition penalties (zwjcode.cn page, section 06: the same transforms at
+ * the same position in p and q, repetition penalties among them; vLLM page,
+ * the sampler's second step: "penalty" logits processors): each position
+ * carries its own list, the tokens of the context it continues (the draft
+ * tokens before it included) with their counts in the generated output.
+ *   penalty_offsets     int32 [num_drafts + N + 1]  position j of request i
+ *                       (j = 0 .. gamma_i) has index cu[i-1] + i + j and its list
+ *                       is penalty_ids[off[p] .. off[p+1]-1]
+ *   penalty_ids         int32   strictly ascending per position, each in [0, V),
+ *                               at most 1024 per position
+ *   penalty_counts      int32   aligned with penalty_ids, >= 0 (0: the token is
+ *                               only in the prompt)
+ *   repetition_penalty  float32 [N] or NULL (1)    theta_i: positive and finite
+ *   presence_penalty    float32 [N] or NULL (0)    finite
+ *   frequency_penalty   float32 [N] or NULL (0)    finite
+ * A listed token with logit l reads as (l > 0 ? l / theta : l * theta) - d,
+ * with d = frequency * count + presence when count > 0, else 0: float32
+ * arithmetic, each operation rounded, and a bf16 result rounded back to bf16
+ * to nearest even.  Its draft probability reads as q * exp(-d) (d shifts the
+ * draft's logits alike; the draft rows are renormalised as always).  Both
+ * happen before temperature, top-k and top-p, and a banned token stays
+ * banned.  A repetition penalty other than 1 on a request that carries draft
+ * rows (has_draft_probs) and a nonzero temperature is a fault: draft
+ * probabilities fix the draft's logits only up to a constant, so the
+ * multiplicative change has no counterpart on them.  A list or value that
+ * breaks these rules gives its request SPEC_VERIFY_FAULT_PENALTY; the lists
+ * of a request with SPEC_VERIFY_FAULT_DRAFT_COUNT are not read.
+ * penalty_offsets selects the option; penalty_ids and penalty_counts are
+ * given together, and may both be NULL when every list is empty.
+ *
  * Returns SPEC_VERIFY_ERR_NULL (N > 0) for target_logits_indices without
  * bonus_logits_indices, bonus_logits_indices without target_logits_indices
- * when num_drafts > 0, or banned_ids without banned_offsets; and
+ * when num_drafts > 0, banned_ids without banned_offsets, any penalty
+ * argument without penalty_offsets, or only one of penalty_ids and
+ * penalty_counts; and
  * SPEC_VERIFY_ERR_SHAPE for logits_rows below 1, or below num_drafts + N
  * without indices (N > 0).
  */
@@ -239,6 +272,9 @@ int spec_verify_flat_ex(int N, int gmax, int V, int num_drafts, const int32_t *c
                         const int32_t *target_logits_indices, const int32_t *bonus_logits_indices,
                         int logits_dtype, const float *temperature, const int32_t *top_k,
                         const float *top_p, const int32_t *banned_offsets, const int32_t *banned_ids,
+                        const int32_t *penalty_offsets, const int32_t *penalty_ids,
+                        const int32_t *penalty_counts, const float *repetition_penalty,
+                        const float *presence_penalty, const float *frequency_penalty,
                         const float *u_accept, const float *u_sample, int32_t *out_tokens,
                         int32_t *out_num_accepted, double *p_y, double *q_y, double *resid_mass,
                         int32_t *fault, void *workspace, size_t workspace_bytes, void *stream,

@@ -27,6 +27,7 @@ FAULT_DRAFT_MASS = 32
 FAULT_DRAFT_COUNT = 64
 FAULT_BAN_LIST = 128
 FAULT_ROW_INDEX = 256
+FAULT_PENALTY = 512
 
 EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_timed", "spec_verify_flat", "spec_verify_flat_timed",
            "spec_verify_flat_synthetic", "spec_verify_flat_ex", "spec_verify_rollback", "spec_verify_workspace_size",
@@ -59,8 +60,8 @@ def _load():
     lib.spec_verify_flat_synthetic.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, Z, P,
                                                P, P, P]
     lib.spec_verify_flat_ex.restype = I
-    lib.spec_verify_flat_ex.argtypes = ([I, I, I, I] + [P] * 5 + [I, P, P, I] + [P] * 3 + [P, P] + [P] * 4 +
-                                        [P] * 4 + [P, Z, P] + [P] * 3)
+    lib.spec_verify_flat_ex.argtypes = ([I, I, I, I] + [P] * 5 + [I, P, P, I] + [P] * 3 + [P, P] + [P] * 6 +
+                                        [P] * 4 + [P] * 4 + [P, Z, P] + [P] * 3)
     lib.spec_verify_rollback.restype = I
     lib.spec_verify_rollback.argtypes = [I, I, P, P, P, P, P, P, P]
     lib.spec_verify_workspace_size.restype = Z
@@ -174,7 +175,9 @@ def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, 
 def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, target_logits, gmax,
                 temperature=None, top_k=None, top_p=None, u_accept=None, u_sample=None, *, out_tokens=None,
                 out_num_accepted=None, workspace=None, stream=None, diag=False, events=None, synthetic_rates=None,
-                banned_offsets=None, banned_ids=None, target_logits_indices=None, bonus_logits_indices=None):
+                banned_offsets=None, banned_ids=None, target_logits_indices=None, bonus_logits_indices=None,
+                penalty_offsets=None, penalty_ids=None, penalty_counts=None, repetition_penalty=None,
+                presence_penalty=None, frequency_penalty=None):
     """Verify a batch in the flattened layout (spec_verify_flat in include/spec_verify.h).
 
     cu_num_draft_tokens int32 [N] (inclusive prefix sums of the draft counts),
@@ -191,7 +194,11 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
     per request) those tokens are banned in p and q alike.  With
     ``target_logits_indices`` (int32 [T]) and ``bonus_logits_indices`` (int32
     [N]) target_logits is any [R, V] tensor and those indices name the row of
-    each draft and bonus position.  Either option runs spec_verify_flat_ex.
+    each draft and bonus position.  With ``penalty_offsets`` (int32 [T + N + 1],
+    one list per position in request order), ``penalty_ids`` / ``penalty_counts``
+    (int32) and the optional per-request ``repetition_penalty``,
+    ``presence_penalty`` and ``frequency_penalty`` (float32 [N]) the
+    penalties apply to p and q alike.  Any option runs spec_verify_flat_ex.
     """
     if target_logits.dim() != 2:
         raise ValueError("target_logits must be [T + N, V] (or [R, V] with row indices)")
@@ -257,7 +264,9 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
         if rc != 0:
             raise SpecVerifyError("spec_verify_flat_synthetic failed: %s" % lib.spec_verify_status_string(rc).decode())
         return (out_tokens, out_num_accepted, d) if diag else (out_tokens, out_num_accepted)
-    if banned_offsets is not None or banned_ids is not None or indexed:
+    pen_args = (penalty_offsets, penalty_ids, penalty_counts, repetition_penalty, presence_penalty, frequency_penalty)
+    penalised = any(x is not None for x in pen_args)
+    if banned_offsets is not None or banned_ids is not None or indexed or penalised:
         if banned_offsets is not None or banned_ids is not None:
             _check(banned_offsets, "banned_offsets", torch.int32, (N + 1,), dev)
             if banned_ids is None or banned_ids.dim() != 1:
@@ -266,6 +275,17 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
         if indexed:
             _check(target_logits_indices, "target_logits_indices", torch.int32, (T,), dev)
             _check(bonus_logits_indices, "bonus_logits_indices", torch.int32, (N,), dev)
+        if penalised:
+            _check(penalty_offsets, "penalty_offsets", torch.int32, (T + N + 1,), dev)
+            for name, t in (("penalty_ids", penalty_ids), ("penalty_counts", penalty_counts)):
+                if t is not None and t.dim() != 1:
+                    raise ValueError("%s must be a 1-d int32 tensor" % name)
+                _check(t, name, torch.int32, None if t is None else tuple(t.shape), dev)
+            if penalty_ids is not None and penalty_counts is not None and penalty_ids.shape != penalty_counts.shape:
+                raise ValueError("penalty_ids and penalty_counts must have the same length")
+            for name, t in (("repetition_penalty", repetition_penalty), ("presence_penalty", presence_penalty),
+                            ("frequency_penalty", frequency_penalty)):
+                _check(t, name, torch.float32, (N,), dev)
         if diag:
             d = dict(p_y=torch.empty((N, G), dtype=torch.float64, device=dev),
                      q_y=torch.empty((N, G), dtype=torch.float64, device=dev),
@@ -278,7 +298,8 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
             None if e is None else ctypes.c_void_p(e.cuda_event) for e in events)
         with torch.cuda.device(dev):
             rc = lib.spec_verify_flat_ex(*head[:9], R, _ptr(target_logits_indices), _ptr(bonus_logits_indices),
-                                         *head[9:13], _ptr(banned_offsets), _ptr(banned_ids), *head[13:], *dp,
+                                         *head[9:13], _ptr(banned_offsets), _ptr(banned_ids),
+                                         *[_ptr(x) for x in pen_args], *head[13:], *dp,
                                          _ptr(workspace), ws_bytes, sptr, *evp)
         if rc != 0:
             raise SpecVerifyError("spec_verify_flat_ex failed: %s" % lib.spec_verify_status_string(rc).decode())
@@ -332,7 +353,9 @@ def to_device_flat(flat: dict, device="cuda"):
     import numpy as np
     out = {"gmax": flat["gmax"]}
     for k in ("cu_num_draft_tokens", "draft_ids", "draft_probs", "has_draft_probs", "temperature", "top_k",
-              "top_p", "u_accept", "u_sample", "target_logits_indices", "bonus_logits_indices"):
+              "top_p", "u_accept", "u_sample", "target_logits_indices", "bonus_logits_indices",
+              "penalty_offsets", "penalty_ids", "penalty_counts", "repetition_penalty", "presence_penalty",
+              "frequency_penalty"):
         v = flat.get(k)
         out[k] = None if v is None else torch.from_numpy(np.ascontiguousarray(v)).to(device)
     tl = flat["target_logits"]
@@ -348,8 +371,11 @@ def verify_flat_batch(dev_flat: dict, **kw):
     return verify_flat(dev_flat["cu_num_draft_tokens"], dev_flat["draft_ids"], dev_flat["draft_probs"],
                        dev_flat["has_draft_probs"], dev_flat["target_logits"], dev_flat["gmax"],
                        dev_flat["temperature"], dev_flat["top_k"], dev_flat["top_p"], dev_flat["u_accept"],
-                       dev_flat["u_sample"], target_logits_indices=dev_flat.get("target_logits_indices"),
-                       bonus_logits_indices=dev_flat.get("bonus_logits_indices"), **kw)
+                       dev_flat["u_sample"], **dict({k: dev_flat.get(k) for k in _FLAT_OPTIONS}, **kw))
+
+
+_FLAT_OPTIONS = ("target_logits_indices", "bonus_logits_indices", "penalty_offsets", "penalty_ids", "penalty_counts",
+                 "repetition_penalty", "presence_penalty", "frequency_penalty")
 
 
 def rollback(num_accepted, *, cu_num_draft_tokens=None, draft_ids=None, gmax=None, num_computed_tokens=None,

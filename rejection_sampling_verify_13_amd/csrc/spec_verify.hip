@@ -44,6 +44,13 @@
 //                 crossing block).
 //   rollback_kernel  (own entry point, after a verify call) the KV bookkeeping
 //                 of the rejected drafts.
+//
+// Token lists (flattened entry point with options): the row and draw kernels
+// have instantiations that copy the request's banned tokens, and the
+// position's repetition-penalty list, into LDS and rewrite each step's raw
+// values as they arrive (a banned token: -inf / 0; a penalised one: the rule
+// of include/spec_verify.h), so every later step sees the transformed row;
+// the instantiation without lists is the one the plain entry points use.
 
 // Compile: hipcc --offload-arch=gfx950 -O3 -shared -fPIC
 //          -Xclang -target-feature -Xclang -packed-fp32-ops
@@ -83,8 +90,10 @@ enum {
   kFaultDraftCount = SPEC_VERIFY_FAULT_DRAFT_COUNT,
   kFaultBanList = SPEC_VERIFY_FAULT_BAN_LIST,
   kFaultRowIndex = SPEC_VERIFY_FAULT_ROW_INDEX,
+  kFaultPenalty = SPEC_VERIFY_FAULT_PENALTY,
 };
 constexpr int kBanMax = 512;            // banned tokens per request (ascending list kept in LDS)
+constexpr int kPenMax = 1024;           // penalised tokens per row (ascending list kept in LDS)
 
 // Per-row results (64 bytes).
 struct RowStats {
@@ -162,11 +171,18 @@ struct Args {
   int R;                // rows of target_logits (with bidx)
   const int32_t* ban_off;  // [N + 1] banned-token list offsets, or nullptr
   const int32_t* ban_ids;  // ascending ids per request; nullptr when every list is empty
+  const int32_t* pen_off;  // [T + N + 1] penalty list offsets per position, or nullptr
+  const int32_t* pen_ids;  // ascending ids per position; nullptr when every list is empty
+  const int32_t* pen_cnt;  // their counts in the generated output
+  const float* pen_rep;    // [N] repetition penalty, or nullptr (1)
+  const float* pen_pres;   // [N] presence penalty, or nullptr (0)
+  const float* pen_freq;   // [N] frequency penalty, or nullptr (0)
   int synthetic;        // 1: the synthetic acceptance mode (draft j accepted iff u_j < srates[j])
   const float* srates;  // synthetic acceptance rates [G]
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Row data is read through global-address-space pointers so that loads are
 // global (not flat) instructions: they then count only against the vector
@@ -893,6 +909,166 @@ __device__ inline void ban_logits(Bf16::Raw& r, uint32_t m) { ban_apply(r, m); }
 __device__ inline void ban_logits(F32::Raw& r, uint32_t m) { ban_apply(r, m, 0xff800000u); }
 
 // ------------------------------------------------------------------------------------------
+// repetition penalties: a row's ascending list in LDS with each token's
+// additive delta d.  A listed logit l reads as (l > 0 ? l / theta : l * theta)
+// - d, in float32 and rounded to the logits' type; a listed draft probability
+// q reads as q * exp(-d) (in double, then float), the same shift on the
+// probability scale.  A banned token still reads as -inf / 0.
+// ------------------------------------------------------------------------------------------
+
+// A row's token lists (wave-uniform).
+struct Toks {
+  const LDS_AS int* ban;    // banned tokens, ascending
+  int nban;
+  const LDS_AS int* pid;    // penalised tokens, ascending
+  const LDS_AS float* pd;   // their deltas
+  LDS_AS float* stage;      // this wave's 512 staging slots (NaN when empty)
+  int npen;
+  float theta;              // repetition penalty
+};
+
+__device__ inline float pen_logit(float l, float theta, float d) {
+#pragma clang fp contract(off)
+  const float l1 = l > 0.f ? l / theta : l * theta;
+  return l1 - d;
+}
+// float32 to bf16 bits, to nearest even; NaN stays NaN
+__device__ inline uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ inline float pen_value(Bf16*, float l, float theta, float d) {
+  return __uint_as_float(bf16_rne(pen_logit(l, theta, d)) << 16);
+}
+__device__ inline float pen_value(F32*, float l, float theta, float d) { return pen_logit(l, theta, d); }
+__device__ inline float pen_prob(float q, float d) { return (float)((double)q * exp(-(double)d)); }
+
+// Rewrites the listed tokens of one lane's raw step; d[e] is token e's delta
+// or NaN (not listed).
+__device__ inline void pen_apply(Bf16::Raw& r, const float d[8], float theta) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (d[e] == d[e]) {
+      const uint32_t w = r.a[e >> 1];
+      const uint32_t bits = (e & 1) ? (w >> 16) : (w & 0xffffu);
+      const uint32_t nb = bf16_rne(pen_logit(__uint_as_float(bits << 16), theta, d[e]));
+      r.a[e >> 1] = (e & 1) ? ((w & 0x0000ffffu) | (nb << 16)) : ((w & 0xffff0000u) | nb);
+    }
+}
+__device__ inline void pen_apply(F32::Raw& r, const float d[8], float theta) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (d[e] == d[e]) {
+      if (e < 4) r.a[e] = __float_as_uint(pen_logit(__uint_as_float(r.a[e]), theta, d[e]));
+      else r.b[e - 4] = __float_as_uint(pen_logit(__uint_as_float(r.b[e - 4]), theta, d[e]));
+    }
+}
+__device__ inline void pen_apply_q(F32::Raw& r, const float d[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (d[e] == d[e]) {
+      if (e < 4) r.a[e] = __float_as_uint(pen_prob(__uint_as_float(r.a[e]), d[e]));
+      else r.b[e - 4] = __float_as_uint(pen_prob(__uint_as_float(r.b[e - 4]), d[e]));
+    }
+}
+
+// Walks the penalty list along consecutive 512-token wave ranges as ban_mask
+// walks the ban list.  The ids of the range [lo, lo + 512) write their deltas
+// into the wave's staging slots (ids are distinct, so no two lanes share a
+// slot); each lane then reads the 8 slots of its tokens lo + 8 * lane .. + 7,
+// rewrites the listed ones (and their draft probabilities when q_on), and
+// resets those slots to NaN.  The cost per step does not grow with the number
+// of listed tokens in it.
+struct PenWalk {
+  int ptr, n;
+};
+__device__ inline PenWalk pen_start(int n) {
+  PenWalk b;
+  b.ptr = 0;
+  b.n = uni(n);
+  return b;
+}
+template <class LR>
+__device__ inline void pen_walk(PenWalk& b, const Toks& tk, int lo, LR& l, F32::Raw& q, bool q_on) {
+  const int lane = lane_id();
+  uint64_t wrote = 0ull;
+  while (b.ptr < b.n) {
+    const bool ok = b.ptr + lane < b.n;
+    const int id = ok ? tk.pid[b.ptr + lane] : INT_MAX;
+    const float d = ok ? tk.pd[b.ptr + lane] : 0.f;
+    const bool inr = id >= lo && id < lo + 512;
+    if (inr) tk.stage[id - lo] = d;
+    wrote |= __ballot(inr);
+    const int c = __popcll(__ballot(id < lo + 512));
+    b.ptr += c;
+    if (c < 64) break;
+  }
+  if (!wrote) return;
+  wave_lds_sync();
+  float dv[8];
+  {
+    const LDS_AS f32x4* sp = reinterpret_cast<const LDS_AS f32x4*>(tk.stage + lane * kCh);
+    const f32x4 x = sp[0], y = sp[1];
+    dv[0] = x.x; dv[1] = x.y; dv[2] = x.z; dv[3] = x.w;
+    dv[4] = y.x; dv[5] = y.y; dv[6] = y.z; dv[7] = y.w;
+  }
+  bool hit = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) hit |= dv[e] == dv[e];
+  if (hit) {
+    pen_apply(l, dv, tk.theta);
+    if (q_on) pen_apply_q(q, dv);
+    LDS_AS f32x4* sp = reinterpret_cast<LDS_AS f32x4*>(tk.stage + lane * kCh);
+    const float nan = __uint_as_float(0x7fffffffu);
+    sp[0] = f32x4{nan, nan, nan, nan};
+    sp[1] = f32x4{nan, nan, nan, nan};
+  }
+  wave_lds_sync();
+}
+
+// index of x in an ascending list, or -1
+__device__ inline int tok_find(const LDS_AS int* ids, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (ids[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return (lo < n && ids[lo] == x) ? lo : -1;
+}
+// token x's logit l / draft probability q as the row's lists make it
+template <class LT>
+__device__ inline float tok_logit(const Toks& tk, int x, float l) {
+  if (tk.npen) {
+    const int k = tok_find(tk.pid, tk.npen, x);
+    if (k >= 0) l = pen_value((LT*)nullptr, l, tk.theta, tk.pd[k]);
+  }
+  if (tk.nban && ban_has(tk.ban, tk.nban, x)) l = -INFINITY;
+  return l;
+}
+__device__ inline float tok_prob(const Toks& tk, int x, float q) {
+  if (tk.npen) {
+    const int k = tok_find(tk.pid, tk.npen, x);
+    if (k >= 0) q = pen_prob(q, tk.pd[k]);
+  }
+  if (tk.nban && ban_has(tk.ban, tk.nban, x)) q = 0.f;
+  return q;
+}
+__device__ inline Toks toks(const LDS_AS int* ban, int nban, const LDS_AS int* pid, const LDS_AS float* pd,
+                            LDS_AS float* stage, int npen, float theta) {
+  Toks t;
+  t.ban = ban;
+  t.nban = uni(nban);
+  t.pid = pid;
+  t.pd = pd;
+  t.stage = stage;
+  t.npen = uni(npen);
+  t.theta = uni(theta);
+  return t;
+}
+
+// ------------------------------------------------------------------------------------------
 // kept set from the candidate buffers (one wave per distribution)
 // ------------------------------------------------------------------------------------------
 
@@ -1239,7 +1415,7 @@ struct DrawOut {
 // kept tokens.
 __device__ __noinline__ DrawOut wave_draw(DrawIn in, const LDS_AS uint32_t* skey, const LDS_AS int* sid,
                                           const LDS_AS double* ke, LDS_AS double* wbuf, const LDS_AS int* ban,
-                                          int nban) {
+                                          int nban, const LDS_AS int* pid, const LDS_AS float* pd, int npen) {
   const int lane = lane_id();
   in.nk = uni(in.nk);
   in.cutkey = uni(in.cutkey);
@@ -1251,14 +1427,14 @@ __device__ __noinline__ DrawOut wave_draw(DrawIn in, const LDS_AS uint32_t* skey
   in.rk = uni(in.rk);
   in.y = uni(in.y);
   in.us = uni(in.us);
-  nban = uni(nban);
+  const Toks tk = toks(ban, nban, pid, pd, nullptr, npen, 1.f);
   auto weight = [&](bool keep, int id, double e, double& p) {
     p = keep ? e / in.zk : 0.0;
     double w = p;
     if (in.mode == 1) {
       double q = 0.0;
       if (keep) {
-        const float qx = (nban && ban_has(ban, nban, id)) ? 0.f : F32::at(in.qrow, (size_t)id);
+        const float qx = tok_prob(tk, id, F32::at(in.qrow, (size_t)id));
         q = (qx >= in.cut_q) ? temper_q(qx, in.T) / in.rk : 0.0;
       }
       w = p - q > 0.0 ? p - q : 0.0;
@@ -1359,7 +1535,8 @@ struct Filtered {
 
 __device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hist, LDS_AS double* sel_d,
                                                 LDS_AS uint32_t* sel_u, LDS_AS double* red, const LDS_AS int* ban,
-                                                int nban) {
+                                                int nban, const LDS_AS int* pid, const LDS_AS float* pd, int npen,
+                                                float theta) {
   g.row = uni(g.row);
   g.V = uni(g.V);
   g.bf16 = uni((int)g.bf16);
@@ -1373,7 +1550,7 @@ __device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hi
   g.top_p = uni(g.top_p);
   g.pact = uni((int)g.pact);
   g.total = uni(g.total);
-  nban = uni(nban);
+  const Toks tk = toks(ban, nban, pid, pd, nullptr, npen, theta);
   RowRef ka;
   ka.row = g.row;
   ka.V = g.V;
@@ -1383,8 +1560,9 @@ __device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hi
                    : (double)fast_exp2((v - g.m) * g.c);
   };
   auto value = [&](int x) -> float {
-    if (nban && ban_has(ban, nban, x)) return g.draft ? 0.f : -INFINITY;
-    return row_value(ka, x);
+    const float v = row_value(ka, x);
+    if (!tk.nban && !tk.npen) return v;
+    return g.draft ? tok_prob(tk, x, v) : (g.bf16 ? tok_logit<Bf16>(tk, x, v) : tok_logit<F32>(tk, x, v));
   };
   auto kw = [&](int x, uint32_t& key, double& w) {
     const float v = value(x);
@@ -1470,9 +1648,9 @@ struct StochState {
 };
 
 // QM: 0 no draft row, 1 draft row at T = 1, 2 draft row at T != 1.
-template <class LT, bool VEC, int QM, bool CAND, bool BAN>
+template <class LT, bool VEC, int QM, bool CAND, int TOK>
 __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, const float* qrow, int V, float c, float invT, int k,
-                                  RowShared<LT>& sh, StochState& st, const LDS_AS int* ban, int nban) {
+                                  RowShared<LT>& sh, StochState& st, const Toks& tk) {
   typedef typename LT::Raw LR;
   const int tid = threadIdx.x, w = tid >> 6;
   const int nsteps = (V + kStep - 1) / kStep;
@@ -1525,7 +1703,9 @@ __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, co
   const int nfull = VEC ? V / kStep : 0;
   const int base0 = tid * kCh;
   BanWalk bw;
-  if (BAN) bw = ban_start(ban, nban);
+  PenWalk pw;
+  if (TOK) bw = ban_start(tk.ban, tk.nban);
+  if (TOK == 2) pw = pen_start(tk.npen);
   ring_stream<QM ? 5 : 10, StepRaw<LR>>(
       nfull,
       [&](int s) {
@@ -1535,9 +1715,10 @@ __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, co
         return r;
       },
       [&](const StepRaw<LR>& r, int s) {
-        if (BAN) {
+        if (TOK) {
           StepRaw<LR> b = r;
-          const uint32_t m = ban_mask(bw, ban, s * kStep + w * 512);
+          if (TOK == 2) pen_walk(pw, tk, s * kStep + w * 512, b.l, b.q, QM != 0);
+          const uint32_t m = ban_mask(bw, tk.ban, s * kStep + w * 512);
           if (m) {
             ban_logits(b.l, m);
             if (QM) ban_apply(b.q, m, 0u);
@@ -1553,8 +1734,9 @@ __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, co
     LR lr = load_logits<LT, VEC>(lrow, base, V);
     F32::Raw qr{};
     if (QM) qr = load_probs<VEC>(qrow, base, V);
-    if (BAN) {
-      const uint32_t m = ban_mask(bw, ban, s * kStep + w * 512);
+    if (TOK == 2) pen_walk(pw, tk, s * kStep + w * 512, lr, qr, QM != 0);
+    if (TOK) {
+      const uint32_t m = ban_mask(bw, tk.ban, s * kStep + w * 512);
       if (m) {
         ban_logits(lr, m);
         if (QM) ban_apply(qr, m, 0u);
@@ -1567,9 +1749,9 @@ __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, co
 
 // Greedy rows: argmax (lowest id among equal maxima) and a running sum that
 // flags NaN / +inf for an exact re-check.
-template <class LT, bool VEC, bool BAN>
-__device__ void stream_greedy(const typename LT::T* lrow, int V, float& best, int& bidx, float& acc,
-                              const LDS_AS int* ban, int nban) {
+template <class LT, bool VEC, int TOK>
+__device__ __forceinline__ void stream_greedy(const typename LT::T* lrow, int V, float& best, int& bidx, float& acc,
+                                              const Toks& tk) {
   typedef typename LT::Raw LR;
   const int tid = threadIdx.x, w = tid >> 6;
   const int nsteps = (V + kStep - 1) / kStep;
@@ -1596,11 +1778,17 @@ __device__ void stream_greedy(const typename LT::T* lrow, int V, float& best, in
   const int nfull = VEC ? V / kStep : 0;
   const int base0 = tid * kCh;
   BanWalk bw;
-  if (BAN) bw = ban_start(ban, nban);
+  PenWalk pw;
+  if (TOK) bw = ban_start(tk.ban, tk.nban);
+  if (TOK == 2) pw = pen_start(tk.npen);
   auto masked = [&](const LR& r, int s, int base) {
-    if (BAN) {
+    if (TOK) {
       LR b = r;
-      const uint32_t m = ban_mask(bw, ban, s * kStep + w * 512);
+      if (TOK == 2) {
+        F32::Raw none;
+        pen_walk(pw, tk, s * kStep + w * 512, b, none, false);
+      }
+      const uint32_t m = ban_mask(bw, tk.ban, s * kStep + w * 512);
       if (m) ban_logits(b, m);
       process(b, base, m);
     } else {
@@ -1621,16 +1809,16 @@ __device__ void stream_greedy(const typename LT::T* lrow, int V, float& best, in
 // row processing
 // ------------------------------------------------------------------------------------------
 
-template <class LT, bool VEC, bool BAN>
+template <class LT, bool VEC, int TOK>
 __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, int j, RowShared<LT>& sh,
-                                           const LDS_AS int* ban, int nban) {
+                                           const Toks& tk) {
   typedef typename LT::T ET;
   const int G = a.G, V = a.V, tid = threadIdx.x;
   const size_t row = (size_t)i * (G + 1) + j;  // the row record
   const ET* lrow = reinterpret_cast<const ET*>(a.logits) + (size_t)rq.trow * (size_t)V;
   float best = -INFINITY, acc = 0.f;
   int bidx = -1;
-  stream_greedy<LT, VEC, BAN>(lrow, V, best, bidx, acc, ban, nban);
+  stream_greedy<LT, VEC, TOK>(lrow, V, best, bidx, acc, tk);
   __builtin_amdgcn_s_setprio(2);
   const float gbest = block_max_f(best, sh.red_f);
   int cand = (best == gbest && bidx >= 0) ? bidx : INT_MAX;
@@ -1641,8 +1829,8 @@ __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, 
   int bad = 0;
   if (suspicious) {
     for (int x = tid; x < V; x += kBlock) {
-      if (BAN && ban_has(ban, nban, x)) continue;  // a banned token reads as -inf
-      const float l = LT::at(lrow, (size_t)x);
+      float l = LT::at(lrow, (size_t)x);
+      if (TOK) l = tok_logit<LT>(tk, x, l);
       bad |= (l != l) || (l == INFINITY);
     }
     bad = block_max_i(bad, sh.red_i);
@@ -1667,9 +1855,9 @@ __device__ __forceinline__ void greedy_row(const Args& a, const Req& rq, int i, 
   }
 }
 
-template <class LT, bool VEC, bool BAN>
+template <class LT, bool VEC, int TOK>
 __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int i, int j, RowShared<LT>& sh,
-                                               const LDS_AS int* ban, int nban) {
+                                               const Toks& tk) {
   typedef typename LT::T ET;
   const int G = a.G, V = a.V;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -1693,9 +1881,9 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
     y = a.ids[(size_t)rq.id0 + j];
     ly = LT::at(lrow, (size_t)y);
     if (req_q) qyv = F32::at(qrow, (size_t)y);
-    if (BAN && ban_has(ban, nban, y)) {
-      ly = -INFINITY;
-      qyv = 0.f;
+    if (TOK) {
+      ly = tok_logit<LT>(tk, y, ly);
+      qyv = tok_prob(tk, y, qyv);
     }
   }
 
@@ -1709,9 +1897,9 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   st.qs = ChunkState{0, 0u, 0};
   const int qm = has_q ? (temper ? 2 : 1) : 0;
   if (cand) {
-    if (qm == 0) stream_stochastic<LT, VEC, 0, true, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
-    else if (qm == 1) stream_stochastic<LT, VEC, 1, true, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
-    else stream_stochastic<LT, VEC, 2, true, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
+    if (qm == 0) stream_stochastic<LT, VEC, 0, true, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
+    else if (qm == 1) stream_stochastic<LT, VEC, 1, true, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
+    else stream_stochastic<LT, VEC, 2, true, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
     // each wave cuts its own buffers down to its k-th largest chunk key and
     // copies the tokens at or above that threshold into its segment
     __builtin_amdgcn_s_setprio(2);
@@ -1731,9 +1919,9 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       if (lane == 0) sh.scnt[1][wave] = n;
     }
   } else {
-    if (qm == 0) stream_stochastic<LT, VEC, 0, false, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
-    else if (qm == 1) stream_stochastic<LT, VEC, 1, false, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
-    else stream_stochastic<LT, VEC, 2, false, BAN>(lrow, qrow, V, c, invT, rq.k, sh, st, ban, nban);
+    if (qm == 0) stream_stochastic<LT, VEC, 0, false, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
+    else if (qm == 1) stream_stochastic<LT, VEC, 1, false, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
+    else stream_stochastic<LT, VEC, 2, false, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
   }
 
   // the rest of the row is short serial work that holds this workgroup's
@@ -1873,7 +2061,8 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       g.pact = rq.pact;
       g.total = Z;
       const Filtered f = general_filter(g, (LDS_AS double*)sh.pb, (LDS_AS double*)sh.sel_d,
-                                        (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d, ban, BAN ? nban : 0);
+                                        (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d, tk.ban, TOK ? tk.nban : 0,
+                                        tk.pid, tk.pd, TOK == 2 ? tk.npen : 0, tk.theta);
       cut_p = f.cut;
       Zk = f.mass;
     }
@@ -1894,7 +2083,8 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       g.total = R;
       // (histogram in the draft buffers: the target weights stay for the draw)
       const Filtered f = general_filter(g, (LDS_AS double*)sh.qb, (LDS_AS double*)sh.sel_d,
-                                        (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d, ban, BAN ? nban : 0);
+                                        (LDS_AS uint32_t*)sh.sel_u, (LDS_AS double*)sh.red_d, tk.ban, TOK ? tk.nban : 0,
+                                        tk.pid, tk.pd, TOK == 2 ? tk.npen : 0, tk.theta);
       cut_q = f.cut;
       Rk = f.mass;
     }
@@ -1942,7 +2132,8 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       din.y = __builtin_amdgcn_readlane(y, 0);
       din.us = a.u_sample[i];
       d = wave_draw(din, (const LDS_AS uint32_t*)sh.skey[0], (const LDS_AS int*)sh.sid[0],
-                    (const LDS_AS double*)sh.pb, (LDS_AS double*)sh.qb, ban, BAN ? nban : 0);
+                    (const LDS_AS double*)sh.pb, (LDS_AS double*)sh.qb, tk.ban, TOK ? tk.nban : 0, tk.pid,
+                    tk.pd, TOK == 2 ? tk.npen : 0);
     }
     if (lane == 0) {
       s.s = d.s;
@@ -2068,10 +2259,54 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
   if (tid == 0) a.plan[0] = s_base[0];
 }
 
-template <class LT, bool VEC, bool BAN>
-__global__ __launch_bounds__(kBlock, sizeof(typename LT::T) == 2 ? 3 : 2) void row_kernel(Args a) {
+// presence / frequency part of a listed token's delta (count > 0), each
+// operation rounded to float32
+__device__ inline float pen_delta(float freq, int cnt, float pres) {
+#pragma clang fp contract(off)
+  const float f = freq * (float)cnt;
+  return f + pres;
+}
+
+// Position j of request i: its penalty list into LDS (ids, deltas), the
+// request's repetition penalty, and every staging slot set to NaN.  With `check` (the row pass) the
+// list and the penalties are validated: at most kPenMax ids, strictly
+// ascending, in [0, V), counts >= 0; a positive finite repetition penalty,
+// finite presence and frequency penalties, and a repetition penalty of 1 on a
+// request that carries draft rows and samples (its draft probabilities fix
+// the draft's logits only up to a constant).  Returns the list length, or -1
+// when a check fails.  Every thread of the workgroup calls it.
+__device__ inline int load_penalties(const Args& a, const Req& rq, int i, int j, LDS_AS int* pid, LDS_AS float* pd,
+                                     LDS_AS float* stage, float& theta, bool check) {
+  const int pos = rq.id0 + i + j;  // the position's index in the flattened layout
+  const int p0 = a.pen_off[pos], n = a.pen_off[pos + 1] - p0;
+  theta = a.pen_rep ? a.pen_rep[i] : 1.f;
+  const float pres = a.pen_pres ? a.pen_pres[i] : 0.f, freq = a.pen_freq ? a.pen_freq[i] : 0.f;
+  int bad = 0;
+  if (check)
+    bad = (n < 0 || n > kPenMax || (n > 0 && (!a.pen_ids || !a.pen_cnt)) || !(theta > 0.f) || isinf(theta) ||
+           !isfinite(pres) || !isfinite(freq) || (theta != 1.f && rq.q0 >= 0 && !rq.greedy))
+              ? 1
+              : 0;
+  if (!bad)
+    for (int t = threadIdx.x; t < n; t += kBlock) {
+      const int id = a.pen_ids[(size_t)p0 + t], cnt = a.pen_cnt[(size_t)p0 + t];
+      const float d = cnt > 0 ? pen_delta(freq, cnt, pres) : 0.f;
+      pid[t] = id;
+      pd[t] = d;
+      if (check) bad |= (id < 0 || id >= a.V || cnt < 0 || (t > 0 && a.pen_ids[(size_t)p0 + t - 1] >= id)) ? 1 : 0;
+    }
+  for (int t = threadIdx.x; t < kWaves * 512; t += kBlock) stage[t] = __uint_as_float(0x7fffffffu);
+  bad = __syncthreads_or(bad);
+  return bad ? -1 : n;
+}
+
+template <class LT, bool VEC, int TOK>
+__global__ __launch_bounds__(kBlock, TOK == 2 ? 2 : (sizeof(typename LT::T) == 2 ? 3 : 2)) void row_kernel(Args a) {
   __shared__ RowShared<LT> sh;
-  __shared__ int s_ban[BAN ? kBanMax : 1];
+  __shared__ int s_ban[TOK ? kBanMax : 1];
+  __shared__ int s_pid[TOK == 2 ? kPenMax : 1];
+  __shared__ float s_pd[TOK == 2 ? kPenMax : 1];
+  __shared__ float s_stage[TOK == 2 ? kWaves * 512 : 1];
   // the draft rows first (the larger rows; the plan lists them request-major,
   // so consecutive blocks, which dispatch round-robin over the XCDs, read
   // neighbouring rows), then one bonus row per request; the launch covers
@@ -2092,7 +2327,7 @@ __global__ __launch_bounds__(kBlock, sizeof(typename LT::T) == 2 ? 3 : 2) void r
     rq.trow = r;
   }
   int nban = 0;
-  if (BAN) {
+  if (TOK && a.ban_off) {
     // the request's banned tokens into LDS: at most kBanMax, strictly
     // ascending, each in [0, V); otherwise the request faults
     const int b0 = a.ban_off[i], n = a.ban_off[i + 1] - b0;
@@ -2107,12 +2342,21 @@ __global__ __launch_bounds__(kBlock, sizeof(typename LT::T) == 2 ? 3 : 2) void r
     if (bad) rq.fault |= kFaultBanList;
     else nban = n;
   }
+  int npen = 0;
+  float theta = 1.f;
+  // (a request whose draft count is out of range has no valid positions)
+  if (TOK == 2 && !(rq.fault & kFaultDraftCount)) {
+    npen = load_penalties(a, rq, i, j, (LDS_AS int*)s_pid, (LDS_AS float*)s_pd, (LDS_AS float*)s_stage, theta, true);
+    if (npen < 0) rq.fault |= kFaultPenalty;
+  }
   if (rq.fault) {
     if (threadIdx.x == 0) note_row(a, i, j, 0, rq.fault, false);
     return;
   }
-  if (rq.greedy) greedy_row<LT, VEC, BAN>(a, rq, i, j, sh, (const LDS_AS int*)s_ban, nban);
-  else stochastic_row<LT, VEC, BAN>(a, rq, i, j, sh, (const LDS_AS int*)s_ban, nban);
+  const Toks tk = toks((const LDS_AS int*)s_ban, nban, (const LDS_AS int*)s_pid, (const LDS_AS float*)s_pd,
+                       (LDS_AS float*)s_stage + (threadIdx.x >> 6) * 512, npen, theta);
+  if (rq.greedy) greedy_row<LT, VEC, TOK>(a, rq, i, j, sh, tk);
+  else stochastic_row<LT, VEC, TOK>(a, rq, i, j, sh, tk);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -2209,13 +2453,16 @@ __device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, i
 // levels agree), re-reads the block where it is crossed and finds the token
 // (inverse CDF over ascending id; if the weights sum to zero, over p'; if
 // rounding leaves no crossing, the largest id with w > 0).
-template <class LT, bool VEC, bool BAN>
+template <class LT, bool VEC, int TOK>
 __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   typedef typename LT::T ET;
   typedef typename LT::Raw LR;
   __shared__ int s_last;
   __shared__ DrawSum s_blk[kDrawSpan * kWaves];
-  __shared__ int s_ban[BAN ? kBanMax : 1];
+  __shared__ int s_ban[TOK ? kBanMax : 1];
+  __shared__ int s_pid[TOK == 2 ? kPenMax : 1];
+  __shared__ float s_pd[TOK == 2 ? kPenMax : 1];
+  __shared__ float s_stage[TOK == 2 ? kWaves * 512 : 1];
   const int i = blockIdx.x / (a.dparts + 1), part = blockIdx.x - i * (a.dparts + 1);
   const ReqRec rr = a.rec[i];
   const int gamma = rr.gamma;
@@ -2250,12 +2497,22 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   // the request's banned tokens (checked by the row pass, which faults the
   // request on a bad list)
   int nban = 0;
-  if (BAN) {
+  if (TOK && a.ban_off) {
     const int b0 = a.ban_off[i];
     nban = a.ban_off[i + 1] - b0;
     for (int t = tid; t < nban; t += kBlock) s_ban[t] = a.ban_ids[(size_t)b0 + t];
     __syncthreads();
   }
+  // row A's penalty list (checked by the row pass likewise)
+  int npen = 0;
+  float theta = 1.f;
+  if (TOK == 2) {
+    Req rq;
+    rq.id0 = rr.id0;
+    npen = load_penalties(a, rq, i, A, (LDS_AS int*)s_pid, (LDS_AS float*)s_pd, (LDS_AS float*)s_stage, theta, false);
+  }
+  const Toks tk = toks((const LDS_AS int*)s_ban, nban, (const LDS_AS int*)s_pid, (const LDS_AS float*)s_pd,
+                       (LDS_AS float*)s_stage + (threadIdx.x >> 6) * 512, npen, theta);
   // all of this workgroup's loads first, then the sums (block sums go to LDS:
   // a global store here would count against the counter the loads wait on)
   LR lr[kDrawSpan];
@@ -2269,13 +2526,16 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
     }
   }
   BanWalk bw;
-  if (BAN) bw = ban_start((const LDS_AS int*)s_ban, nban);
+  PenWalk pw;
+  if (TOK) bw = ban_start(tk.ban, tk.nban);
+  if (TOK == 2) pw = pen_start(tk.npen);
 #pragma unroll
   for (int u = 0; u < kDrawSpan; ++u) {
     if (u >= cnt) break;
     const int base = (s0 + u) * kStep + tid * kCh;
-    if (BAN) {
-      const uint32_t m = ban_mask(bw, (const LDS_AS int*)s_ban, (s0 + u) * kStep + wave * 512);
+    if (TOK == 2) pen_walk(pw, tk, (s0 + u) * kStep + wave * 512, lr[u], qr[u], mode == 1);
+    if (TOK) {
+      const uint32_t m = ban_mask(bw, tk.ban, (s0 + u) * kStep + wave * 512);
       if (m) {
         ban_logits(lr[u], m);
         if (mode == 1) ban_apply(qr[u], m, 0u);
@@ -2386,11 +2646,21 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
     float lv[8], qv[8], w[8], pw[8];
     LR lb = load_logits<LT, VEC>(lrow, base, V);
     F32::Raw qb = (dmode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
-    if (BAN) {
+    if (TOK == 2 && tk.npen) {
+      float dv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = tok_find(tk.pid, tk.npen, base + e);
+        dv[e] = k >= 0 ? tk.pd[k] : __uint_as_float(0x7fffffffu);
+      }
+      pen_apply(lb, dv, tk.theta);
+      if (dmode == 1) pen_apply_q(qb, dv);
+    }
+    if (TOK) {
       uint32_t m = 0u;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (ban_has((const LDS_AS int*)s_ban, nban, base + e)) m |= 1u << e;
+        if (ban_has(tk.ban, tk.nban, base + e)) m |= 1u << e;
       if (m) {
         ban_logits(lb, m);
         ban_apply(qb, m, 0u);
@@ -2493,17 +2763,17 @@ struct Events {
   hipEvent_t start, mid, end;
 };
 
-template <class LT, bool VEC, bool BAN>
+template <class LT, bool VEC, int TOK>
 hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
   const long rows = a.synthetic ? (long)a.N : (long)a.N * (a.G + 1);  // synthetic mode: row A only
   hipError_t e;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((row_kernel<LT, VEC, BAN>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
+  hipLaunchKernelGGL((row_kernel<LT, VEC, TOK>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.mid && (e = hipEventRecord(ev.mid, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((draw_kernel<LT, VEC, BAN>), dim3((unsigned)((long)a.N * (a.dparts + 1))), dim3(kBlock), 0,
+  hipLaunchKernelGGL((draw_kernel<LT, VEC, TOK>), dim3((unsigned)((long)a.N * (a.dparts + 1))), dim3(kBlock), 0,
                      stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.end && (e = hipEventRecord(ev.end, stream)) != hipSuccess) return e;
@@ -2517,8 +2787,14 @@ struct Layout {
   int T;
 };
 
+// Penalty lists per position and the per-request penalties (all nullptr: none).
+struct Penalties {
+  const int32_t *off, *ids, *cnt;
+  const float *rep, *pres, *freq;
+};
+
 int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* srates, const int32_t* ban_off,
-        const int32_t* ban_ids, const int32_t* tidx, const int32_t* bidx, int R, const int32_t* ids, const float* q, const void* logits, int dtype,
+        const int32_t* ban_ids, const Penalties& pen, const int32_t* tidx, const int32_t* bidx, int R, const int32_t* ids, const float* q, const void* logits, int dtype,
         const float* temperature, const int32_t* top_k, const float* top_p, const float* u_accept,
         const float* u_sample, int32_t* out_tokens, int32_t* out_num, double* p_y, double* q_y, double* resid,
         int32_t* fault, void* workspace, size_t workspace_bytes, void* stream, const Events& ev) {
@@ -2592,6 +2868,12 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   a.R = R;
   a.ban_off = ban_off;
   a.ban_ids = ban_ids;
+  a.pen_off = pen.off;
+  a.pen_ids = pen.ids;
+  a.pen_cnt = pen.cnt;
+  a.pen_rep = pen.rep;
+  a.pen_pres = pen.pres;
+  a.pen_freq = pen.freq;
   a.synthetic = synthetic ? 1 : 0;
   a.srates = srates;
 
@@ -2600,16 +2882,21 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   const bool vec = (V % 8 == 0) && ((uintptr_t)logits % 16 == 0) && (!q || (uintptr_t)q % 16 == 0);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if (ban_off) {
+  if (pen.off) {
     if (dtype == SPEC_VERIFY_BF16)
-      e = vec ? launch<Bf16, true, true>(a, s, ev) : launch<Bf16, false, true>(a, s, ev);
+      e = vec ? launch<Bf16, true, 2>(a, s, ev) : launch<Bf16, false, 2>(a, s, ev);
     else
-      e = vec ? launch<F32, true, true>(a, s, ev) : launch<F32, false, true>(a, s, ev);
+      e = vec ? launch<F32, true, 2>(a, s, ev) : launch<F32, false, 2>(a, s, ev);
+  } else if (ban_off) {
+    if (dtype == SPEC_VERIFY_BF16)
+      e = vec ? launch<Bf16, true, 1>(a, s, ev) : launch<Bf16, false, 1>(a, s, ev);
+    else
+      e = vec ? launch<F32, true, 1>(a, s, ev) : launch<F32, false, 1>(a, s, ev);
   } else {
     if (dtype == SPEC_VERIFY_BF16)
-      e = vec ? launch<Bf16, true, false>(a, s, ev) : launch<Bf16, false, false>(a, s, ev);
+      e = vec ? launch<Bf16, true, 0>(a, s, ev) : launch<Bf16, false, 0>(a, s, ev);
     else
-      e = vec ? launch<F32, true, false>(a, s, ev) : launch<F32, false, false>(a, s, ev);
+      e = vec ? launch<F32, true, 0>(a, s, ev) : launch<F32, false, 0>(a, s, ev);
   }
   return e == hipSuccess ? SPEC_VERIFY_OK : SPEC_VERIFY_ERR_HIP;
 }
@@ -2628,7 +2915,7 @@ int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* d
                 int logits_dtype, const float* temperature, const int32_t* top_k, const float* top_p,
                 const float* u_accept, const float* u_sample, int32_t* out_tokens, int32_t* out_num_accepted,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, Penalties{}, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes,
              stream, Events{nullptr, nullptr, nullptr});
 }
@@ -2638,7 +2925,7 @@ int spec_verify_diag(int N, int gmax, int V, const int32_t* draft_ids, const flo
                      const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
                      int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, Penalties{}, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{nullptr, nullptr, nullptr});
 }
@@ -2649,7 +2936,7 @@ int spec_verify_timed(int N, int gmax, int V, const int32_t* draft_ids, const fl
                       int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
                       void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_mid,
                       void* ev_end) {
-  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
+  return run(N, gmax, V, Layout{nullptr, nullptr, 0}, false, nullptr, nullptr, nullptr, Penalties{}, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p, u_accept,
              u_sample, out_tokens, out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
                     reinterpret_cast<hipEvent_t>(ev_end)});
@@ -2661,7 +2948,7 @@ int spec_verify_flat(int N, int gmax, int V, int num_drafts, const int32_t* cu_n
                      const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
                      int32_t* out_num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
-  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs,
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, nullptr, nullptr, Penalties{}, nullptr, nullptr, 0, draft_ids, draft_probs,
              target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens,
              out_num_accepted, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
              Events{nullptr, nullptr, nullptr});
@@ -2675,7 +2962,7 @@ int spec_verify_flat_timed(int N, int gmax, int V, int num_drafts, const int32_t
                            double* resid_mass, int32_t* fault, void* workspace, size_t workspace_bytes, void* stream,
                            void* ev_start, void* ev_mid, void* ev_end) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
-  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs,
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, nullptr, nullptr, Penalties{}, nullptr, nullptr, 0, draft_ids, draft_probs,
              target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens,
              out_num_accepted, p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
@@ -2687,20 +2974,28 @@ int spec_verify_flat_ex(int N, int gmax, int V, int num_drafts, const int32_t* c
                         const void* target_logits, int logits_rows, const int32_t* target_logits_indices,
                         const int32_t* bonus_logits_indices, int logits_dtype, const float* temperature,
                         const int32_t* top_k, const float* top_p, const int32_t* banned_offsets,
-                        const int32_t* banned_ids, const float* u_accept, const float* u_sample, int32_t* out_tokens,
-                        int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass, int32_t* fault,
-                        void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_mid,
-                        void* ev_end) {
+                        const int32_t* banned_ids, const int32_t* penalty_offsets, const int32_t* penalty_ids,
+                        const int32_t* penalty_counts, const float* repetition_penalty, const float* presence_penalty,
+                        const float* frequency_penalty, const float* u_accept, const float* u_sample,
+                        int32_t* out_tokens, int32_t* out_num_accepted, double* p_y, double* q_y, double* resid_mass,
+                        int32_t* fault, void* workspace, size_t workspace_bytes, void* stream, void* ev_start,
+                        void* ev_mid, void* ev_end) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
   // the bonus indices and the offsets select the options; their companions
   // may be NULL only where nothing would be read through them
   if (N > 0 && target_logits_indices && !bonus_logits_indices) return SPEC_VERIFY_ERR_NULL;
   if (N > 0 && num_drafts > 0 && bonus_logits_indices && !target_logits_indices) return SPEC_VERIFY_ERR_NULL;
   if (N > 0 && banned_ids && !banned_offsets) return SPEC_VERIFY_ERR_NULL;
+  if (N > 0 && !penalty_offsets && (penalty_ids || penalty_counts || repetition_penalty || presence_penalty ||
+                                    frequency_penalty))
+    return SPEC_VERIFY_ERR_NULL;
+  if (N > 0 && penalty_offsets && (penalty_ids != nullptr) != (penalty_counts != nullptr)) return SPEC_VERIFY_ERR_NULL;
   if (N > 0 && (logits_rows < 1 || (!bonus_logits_indices && (long long)logits_rows < (long long)num_drafts + N)))
     return SPEC_VERIFY_ERR_SHAPE;
+  const Penalties pen{penalty_offsets, penalty_ids, penalty_counts, repetition_penalty, presence_penalty,
+                      frequency_penalty};
   return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, false, nullptr, banned_offsets,
-             banned_ids, target_logits_indices, bonus_logits_indices, logits_rows, draft_ids, draft_probs,
+             banned_ids, pen, target_logits_indices, bonus_logits_indices, logits_rows, draft_ids, draft_probs,
              target_logits, logits_dtype, temperature, top_k, top_p, u_accept, u_sample, out_tokens, out_num_accepted,
              p_y, q_y, resid_mass, fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),
@@ -2716,7 +3011,7 @@ int spec_verify_flat_synthetic(int N, int gmax, int V, int num_drafts, const int
                                void* stream, void* ev_start, void* ev_mid, void* ev_end) {
   if (N > 0 && !cu_num_draft_tokens) return SPEC_VERIFY_ERR_NULL;
   if (N > 0 && gmax > 0 && !synthetic_rates) return SPEC_VERIFY_ERR_NULL;
-  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, true, synthetic_rates, nullptr, nullptr, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype,
+  return run(N, gmax, V, Layout{cu_num_draft_tokens, has_draft_probs, num_drafts}, true, synthetic_rates, nullptr, nullptr, Penalties{}, nullptr, nullptr, 0, draft_ids, draft_probs, target_logits, logits_dtype,
              temperature, top_k, top_p, u_accept, u_sample, out_tokens, out_num_accepted, nullptr, nullptr, nullptr,
              fault, workspace, workspace_bytes, stream,
              Events{reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_mid),

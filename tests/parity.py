@@ -48,12 +48,14 @@ def gpu_run(batch, diag=True, stream=None):
     return res
 
 
-def gpu_run_flat(batch, diag=True, stream=None, synthetic_rates=None, banned=None, scatter=None):
+def gpu_run_flat(batch, diag=True, stream=None, synthetic_rates=None, banned=None, scatter=None, penalties=None):
     """Run a numpy batch on cuda:0 as one call in the flattened layout (a mixed
     dense / draft-free batch included: the draft-row mask selects per request);
     with synthetic_rates, in the synthetic acceptance mode; with scatter =
     (seed, extra rows), its target rows scattered over a larger NaN-filled
-    logits tensor and addressed through row indices."""
+    logits tensor and addressed through row indices; with penalties (the
+    oracle's dict: lists, repetition, presence, frequency), repetition
+    penalties."""
     import torch
     import rejection_sampling_verify_13_amd as sv
     import workloads as W
@@ -67,6 +69,13 @@ def gpu_run_flat(batch, diag=True, stream=None, synthetic_rates=None, banned=Non
     if banned is not None:
         kw["banned_offsets"] = torch.from_numpy(np.ascontiguousarray(banned[0], np.int32)).cuda()
         kw["banned_ids"] = torch.from_numpy(np.ascontiguousarray(banned[1], np.int32)).cuda()
+    if penalties is not None:
+        off, pid, cnt = W.flatten_penalties(penalties["lists"])
+        for k, v in (("penalty_offsets", off), ("penalty_ids", pid), ("penalty_counts", cnt)):
+            kw[k] = torch.from_numpy(v).cuda()
+        for k in ("repetition", "presence", "frequency"):
+            if penalties.get(k) is not None:
+                kw[k + "_penalty"] = torch.from_numpy(np.ascontiguousarray(penalties[k], np.float32)).cuda()
     if diag:
         t, n, dg = sv.verify_flat_batch(d, diag=True, stream=stream, **kw)
         out = dict(tokens=t, num_accepted=n, **dg)
@@ -77,7 +86,7 @@ def gpu_run_flat(batch, diag=True, stream=None, synthetic_rates=None, banned=Non
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-def oracle_run(batch, threads=8, synthetic_rates=None, banned=None):
+def oracle_run(batch, threads=8, synthetic_rates=None, banned=None, penalties=None):
     import oracle
     import workloads as W
     parts = [batch]
@@ -91,9 +100,21 @@ def oracle_run(batch, threads=8, synthetic_rates=None, banned=None):
             hi = lo + p["draft_ids"].shape[0]
             bans.append((off[lo:hi + 1] - off[lo], ids[off[lo]:off[hi]]))
             lo = hi
+    pens = [None] * len(parts)
+    if penalties is not None:  # each contiguous part's requests
+        lo, pens = 0, []
+        for p in parts:
+            hi = lo + p["draft_ids"].shape[0]
+            d = dict(lists=penalties["lists"][lo:hi])
+            for k in ("repetition", "presence", "frequency"):
+                if penalties.get(k) is not None:
+                    d[k] = np.asarray(penalties[k])[lo:hi]
+            pens.append(d)
+            lo = hi
     outs = [oracle.run(p["draft_ids"], p["draft_probs"], p["target_logits"], p["dtype"], p["temperature"],
                        p["top_k"], p["top_p"], p["u_accept"], p["u_sample"], threads=threads,
-                       synthetic_rates=synthetic_rates, banned=bn) for p, bn in zip(parts, bans)]
+                       synthetic_rates=synthetic_rates, banned=bn, penalties=pn)
+            for p, bn, pn in zip(parts, bans, pens)]
     return {k: np.concatenate([o[k] for o in outs], axis=0) for k in outs[0]}
 
 

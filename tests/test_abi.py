@@ -93,12 +93,12 @@ def test_flat_host_validation(lib):
     assert _flat(lib, G=65) == 2
 
 
-def _ex(lib, N=2, G=3, V=16, T=4, R=6, tidx=0, bidx=0, boff=0, bids=0):
+def _ex(lib, N=2, G=3, V=16, T=4, R=6, tidx=0, bidx=0, boff=0, bids=0, pen=(0, 0, 0, 0, 0, 0)):
     P = lambda flag: ctypes.c_void_p(0x1000) if flag else None
     # a 16-byte workspace: every accepted argument set stops at the workspace check
     return lib.spec_verify_flat_ex(N, G, V, T, P(1), P(1), None, None, P(1), R, P(tidx), P(bidx), 1, None, None, None,
-                                   P(boff), P(bids), P(1), P(1), P(1), P(1), None, None, None, None, P(1), 16, None,
-                                   None, None, None)
+                                   P(boff), P(bids), *[P(x) for x in pen], P(1), P(1), P(1), P(1), None, None, None,
+                                   None, P(1), 16, None, None, None, None)
 
 
 def test_flat_ex_host_validation(lib):
@@ -112,6 +112,13 @@ def test_flat_ex_host_validation(lib):
     assert _ex(lib, bids=1) == 1               # banned ids without offsets
     assert _ex(lib, boff=1) == 4               # offsets alone: every list empty
     assert _ex(lib, N=0, T=0, R=0, tidx=1) == 0  # empty batch
+    # penalties: the offsets select the option; ids and counts go together
+    assert _ex(lib, pen=(1, 0, 0, 0, 0, 0)) == 4
+    assert _ex(lib, pen=(1, 1, 1, 1, 1, 1)) == 4
+    assert _ex(lib, pen=(1, 1, 0, 0, 0, 0)) == 1
+    assert _ex(lib, pen=(1, 0, 1, 0, 0, 0)) == 1
+    for k in range(1, 6):
+        assert _ex(lib, pen=tuple(int(t == k) for t in range(6))) == 1   # a penalty argument without offsets
 
 
 def test_synthetic_host_validation(lib):

@@ -658,3 +658,75 @@ def test_row_index_faults():
     assert (g["tokens"][bad] == -1).all() and (g["num_accepted"][bad] == -1).all()
     keep = np.setdiff1d(np.arange(8), bad)
     compare({k: v[keep] for k, v in g.items()}, {k: v[keep] for k, v in o.items()}, label="row index faults")
+
+
+# ------------------------------------------------------------------------------------------
+# repetition penalties (per-position lists, identical in p and q)
+# ------------------------------------------------------------------------------------------
+
+def _penalty_params(b, seed, lists):
+    """theta may differ from 1 only on greedy or draft-free requests; presence
+    and frequency anywhere."""
+    rng = np.random.default_rng(seed)
+    N = b["draft_ids"].shape[0]
+    if b["draft_probs"] is None:
+        dense = np.zeros(N, bool)
+    else:
+        dense = np.asarray(b.get("has_q", np.ones(N, bool)), bool)
+    stoch = b["temperature"] != 0
+    theta = np.where(dense & stoch, 1.0, rng.uniform(0.8, 1.6, N)).astype(np.float32)
+    return dict(lists=lists, repetition=theta, presence=rng.uniform(-0.3, 1.5, N).astype(np.float32),
+                frequency=rng.uniform(0.0, 0.8, N).astype(np.float32))
+
+
+PEN = {
+    "pen_cfg3_small_topk": (W.config(3, N=16, V=12000), 200, 0, None),
+    "pen_cfg5_small_mixed": (W.config(5, N=48, V=6144), 100, 0, None),
+    "pen_cfg4_small_greedy": (W.config(4, N=40, V=7000, greedy_count=10), 150, 0, None),
+    "pen_cfg2_tempered": (W.config(2, N=24, V=5000), 300, 0, None),
+    "pen_unaligned_f32_banned": (W.config(2, N=12, V=3001, dtype="f32"), 64, 20, None),
+    "pen_long_lists": (W.config(3, N=8, V=9000), 1024 - 5, 0, None),
+    "pen_rows_scattered": (W.config(3, N=12, V=8192), 120, 10, (13, 9)),
+}
+
+
+@pytest.mark.parametrize("name", list(PEN))
+def test_penalties_parity(name):
+    cfg, n_ctx, nban, scatter = PEN[name]
+    b = W.generate(cfg)
+    pen = _penalty_params(b, 21, W.penalty_lists(b, 22, n_ctx))
+    banned = _ban_lists(b, 23, nban) if nban else None
+    npen = sum(len(r[0]) for req in pen["lists"] for r in req)
+    log("[parity] %s: N=%d V=%d, %d penalty entries" % (name, b["draft_ids"].shape[0], b["target_logits"].shape[-1],
+                                                        npen))
+    g = gpu_run_flat(b, banned=banned, scatter=scatter, penalties=pen)
+    o = oracle_run(b, banned=banned, penalties=pen)
+    assert (o["fault"] == 0).all()
+    res = compare(g, o, label=name)
+    log("[parity] %s ok %s" % (name, res))
+
+
+def test_penalty_faults():
+    b = W.generate(W.config(1, N=10, gmax=2, V=16))
+    b["draft_ids"][:, :] = np.abs(b["draft_ids"])  # gamma = 2 everywhere
+    b["temperature"][8] = -1.0
+    ok = (np.array([1, 4], np.int32), np.array([0, 2], np.int32))
+    lists = [[ok, ok, ok] for _ in range(10)]
+    lists[1][2] = (np.array([4, 1], np.int32), np.array([0, 0], np.int32))    # not ascending
+    lists[2][0] = (np.array([16], np.int32), np.array([1], np.int32))         # outside [0, V)
+    lists[3][1] = (np.array([2, 3], np.int32), np.array([1, -1], np.int32))   # negative count
+    lists[4][0] = (np.arange(1025, dtype=np.int32) % 16, np.zeros(1025, np.int32))  # too long
+    theta = np.ones(10, np.float32)
+    pres = np.zeros(10, np.float32)
+    theta[5] = 1.5      # theta != 1 with draft rows at a nonzero temperature
+    theta[6] = 0.0
+    pres[7] = np.inf
+    theta[8] = 2.0      # and a temperature fault
+    pen = dict(lists=lists, repetition=theta, presence=pres)
+    log("[parity] malformed penalty lists and values")
+    g = gpu_run_flat(b, penalties=pen)
+    o = oracle_run(b, penalties=pen)
+    np.testing.assert_array_equal(g["fault"], o["fault"])
+    import rejection_sampling_verify_13_amd as sv
+    assert (g["fault"][1:8] == sv.FAULT_PENALTY).all() and g["fault"][0] == 0 and g["fault"][9] == 0
+    compare(g, o, label="penalty faults")

@@ -303,3 +303,50 @@ def scatter_rows(flat: dict, seed: int, extra: int) -> dict:
     res = dict(flat)
     res.update(target_logits=out, target_logits_indices=tidx, bonus_logits_indices=bidx)
     return res
+
+
+def penalty_lists(batch: dict, seed: int, n_ctx: int) -> list:
+    """Per-position repetition-penalty lists for a padded batch: request i
+    gets a context of n_ctx distinct tokens with output counts (0: prompt only,
+    else geometric), and position j's list is that context plus the draft
+    tokens y_0 .. y_{j-1} before it, each adding one to its count.  Every
+    third request's context also holds its first draft token and the argmax
+    of its first target row, so that penalties reach the tokens that decide.
+    lists[i][j] = (ids ascending, counts), int32."""
+    rng = np.random.default_rng(seed)
+    ids = batch["draft_ids"]
+    N, G = ids.shape
+    tl = batch["target_logits"]
+    V = tl.shape[-1]
+    neg = np.concatenate([ids < 0, np.ones((N, 1), bool)], axis=1)
+    gam = np.argmax(neg, axis=1)
+    out = []
+    for i in range(N):
+        ctx = set(rng.choice(V, size=min(n_ctx, V), replace=False).tolist())
+        if i % 3 == 0:
+            if gam[i] > 0:
+                ctx.add(int(ids[i, 0]))
+            row = bf16_bits_to_f32(tl[i, 0]) if batch["dtype"] == "bf16" else tl[i, 0]
+            ctx.add(int(np.argmax(row)))
+        ctx = sorted(ctx)[:n_ctx]
+        base = dict(zip(ctx, (rng.geometric(0.5, size=len(ctx)) - 1).tolist()))
+        rows = []
+        for j in range(gam[i] + 1):
+            d = dict(base)
+            for t in range(j):
+                d[int(ids[i, t])] = d.get(int(ids[i, t]), 0) + 1
+            keys = sorted(d)
+            rows.append((np.array(keys, np.int32), np.array([d[k] for k in keys], np.int32)))
+        out.append(rows)
+    return out
+
+
+def flatten_penalties(lists: list):
+    """The per-position lists in the flattened layout: positions in request
+    order (request i's positions 0 .. gamma_i), offsets [positions + 1], ids,
+    counts.  Pure data movement."""
+    rows = [r for req in lists for r in req]
+    off = np.concatenate([[0], np.cumsum([len(r[0]) for r in rows])]).astype(np.int32)
+    ids = np.concatenate([r[0] for r in rows] + [np.zeros(0, np.int32)]).astype(np.int32)
+    cnt = np.concatenate([r[1] for r in rows] + [np.zeros(0, np.int32)]).astype(np.int32)
+    return off, ids, cnt

@@ -269,9 +269,10 @@ def verify_flat(cu_num_draft_tokens, draft_ids, draft_probs, has_draft_probs, ta
     if banned_offsets is not None or banned_ids is not None or indexed or penalised:
         if banned_offsets is not None or banned_ids is not None:
             _check(banned_offsets, "banned_offsets", torch.int32, (N + 1,), dev)
-            if banned_ids is None or banned_ids.dim() != 1:
-                raise ValueError("banned_ids must be a 1-d int32 tensor")
-            _check(banned_ids, "banned_ids", torch.int32, tuple(banned_ids.shape), dev)
+            if banned_ids is not None:  # None: every list is empty
+                if banned_ids.dim() != 1:
+                    raise ValueError("banned_ids must be a 1-d int32 tensor")
+                _check(banned_ids, "banned_ids", torch.int32, tuple(banned_ids.shape), dev)
         if indexed:
             _check(target_logits_indices, "target_logits_indices", torch.int32, (T,), dev)
             _check(bonus_logits_indices, "bonus_logits_indices", torch.int32, (N,), dev)

@@ -730,3 +730,25 @@ def test_penalty_faults():
     import rejection_sampling_verify_13_amd as sv
     assert (g["fault"][1:8] == sv.FAULT_PENALTY).all() and g["fault"][0] == 0 and g["fault"][9] == 0
     compare(g, o, label="penalty faults")
+
+
+def test_empty_option_lists_change_nothing():
+    """Offsets whose lists are all empty, with the id arrays left NULL, give the
+    plain call's outputs bit for bit (the options' kernels, nothing to apply)."""
+    import torch
+    import rejection_sampling_verify_13_amd as sv
+    b = W.generate(W.config(5, N=32, V=4096))
+    d = sv.to_device_flat(W.flatten(b))
+    N = b["draft_ids"].shape[0]
+    T = d["draft_ids"].shape[0]
+    log("[parity] empty option lists, N=%d" % N)
+    t0, n0, g0 = sv.verify_flat_batch(d, diag=True)
+    z = lambda n: torch.zeros(n, dtype=torch.int32, device="cuda")
+    f = lambda v: torch.full((N,), v, dtype=torch.float32, device="cuda")
+    t1, n1, g1 = sv.verify_flat_batch(d, diag=True, banned_offsets=z(N + 1), penalty_offsets=z(T + N + 1),
+                                      repetition_penalty=f(1.0), presence_penalty=f(0.7),
+                                      frequency_penalty=f(0.3))
+    torch.cuda.synchronize()
+    assert torch.equal(t0, t1) and torch.equal(n0, n1)
+    for k in ("p_y", "q_y", "fault"):
+        assert torch.equal(torch.nan_to_num(g0[k], nan=-7.0), torch.nan_to_num(g1[k], nan=-7.0)), k

@@ -752,3 +752,38 @@ def test_empty_option_lists_change_nothing():
     assert torch.equal(t0, t1) and torch.equal(n0, n1)
     for k in ("p_y", "q_y", "fault"):
         assert torch.equal(torch.nan_to_num(g0[k], nan=-7.0), torch.nan_to_num(g1[k], nan=-7.0)), k
+
+
+
+# ------------------------------------------------------------------------------------------
+# brute force on tiny vocabularies: one request per cell of (y, u_accept,
+# u_sample) space at the cell's midpoint; the GPU matches the oracle request by
+# request and its law, summed over the cells, is the closed form
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("V,gam,T,k,p,null_q,seed", [
+    (3, 2, 1.0, 0, 1.0, False, 1), (4, 2, 0.7, 0, 1.0, False, 2), (4, 2, 1.0, 2, 1.0, False, 3),
+    (4, 2, 1.0, 0, 0.7, False, 4), (4, 1, 1.3, 3, 0.8, False, 5), (4, 2, 0.8, 0, 0.9, True, 7)])
+def test_enumerated_cells_on_gpu(V, gam, T, k, p, null_q, seed):
+    from scipy.special import softmax
+    from test_oracle_pins import closed_form_law, law_cells
+    rng = np.random.default_rng(seed)
+    logits = (rng.standard_normal((gam + 1, V)) * 1.5).astype(np.float32)
+    q = None if null_q else softmax(rng.standard_normal((gam, V)) * 1.5, axis=1).astype(np.float32)
+    ids_fixed = [int(x) for x in rng.integers(0, V, gam)] if null_q else None
+    b, cases, P, Qd = law_cells(logits, q, T, k, p, gam, V, ids_fixed)
+    log("[parity] enumerated cells V=%d gamma=%d T=%g k=%d p=%g null_q=%s: %d requests" % (
+        V, gam, T, k, p, null_q, len(cases)))
+    g = gpu_run(b)
+    o = oracle_run(b)
+    compare(g, o, label="cells")
+    amb = (o["margin"] < 1e-6)
+    law, slack = {}, 0.0
+    for t, c in enumerate(cases):
+        toks = tuple(int(x) for x in g["tokens"][t] if x >= 0)
+        law[toks] = law.get(toks, 0.0) + c[3]
+        if amb[t]:
+            slack += c[3]
+    want = closed_form_law(P, Qd, gam, ids_fixed)
+    for key in set(want) | set(law):
+        assert abs(law.get(key, 0.0) - want.get(key, 0.0)) <= 1e-9 + slack, key

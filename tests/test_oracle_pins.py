@@ -317,9 +317,10 @@ def closed_form_law(P, Q, gam, ids_fixed=None):
     return law
 
 
-def enumerate_law(oracle_mod, logits, q, T, k, p, gam, V, ids_fixed=None):
-    """Run the oracle at the midpoint of every cell of (y, u_accept, u_sample)
-    space and add up the cell measures by output.  Cells are cut at the
+def law_cells(logits, q, T, k, p, gam, V, ids_fixed=None):
+    """One request per cell of (y, u_accept, u_sample) space, placed at the
+    cell's midpoint: returns the batch, the cells (ids, ua, us, measure,
+    expected A) and the transformed rows P and Qd.  Cells are cut at the
     acceptance ratios and at the residual CDF boundaries, both computed here
     with numpy from the transformed rows."""
     P = np.array([np_target(logits[j], T, k, p) for j in range(gam + 1)])
@@ -371,6 +372,14 @@ def enumerate_law(oracle_mod, logits, q, T, k, p, gam, V, ids_fixed=None):
              temperature=np.full(n, T, np.float32), top_k=np.full(n, k, np.int32),
              top_p=np.full(n, p, np.float32), u_accept=np.array([c[1] for c in cases], np.float32).reshape(n, gam),
              u_sample=np.array([c[2] for c in cases], np.float32))
+    return b, cases, P, Qd
+
+
+def enumerate_law(oracle_mod, logits, q, T, k, p, gam, V, ids_fixed=None):
+    """Run the oracle at the midpoint of every cell (law_cells) and add up the
+    cell measures by output."""
+    b, cases, P, Qd = law_cells(logits, q, T, k, p, gam, V, ids_fixed)
+    n = len(cases)
     r = run(oracle_mod, b)
     law = {}
     for t in range(n):

@@ -5,9 +5,11 @@ the CPU-baseline leg of ``bench.py`` may import this package.  The product
 library never loads it, and it imports nothing from the product package.
 
 The arithmetic lives in ``spec_verify_oracle.c`` (plain C, fp64, single
-threaded); this module only compiles it with gcc and marshals numpy arrays,
-except for ``rollback``, the integer KV bookkeeping after a verify call,
-which is written out here in plain Python.
+threaded); this module compiles it with gcc and marshals numpy arrays.  Three
+parts are written out here in plain Python instead: ``rollback``, the integer
+KV bookkeeping after a verify call, and the two token-list transforms that
+``run`` applies to its inputs before calling the C routine (banned tokens, and
+the repetition penalties of ``penalty_deltas`` / ``penalize_logits``).
 ``run(..., threads=n)`` splits the batch into contiguous request ranges and
 calls the C routine on each range from a thread pool: requests are independent,
 so the result does not depend on ``n``.

@@ -19,6 +19,11 @@ FLAGS = [
 ]
 
 
+EXAMPLE_SRC = os.path.join(HERE, "examples", "verify_from_c.c")
+EXAMPLE = os.path.join(HERE, "verify_from_c")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC] + FLAGS + ["-o", tmp, SRC]
@@ -29,7 +34,24 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed for " + SRC)
     os.replace(tmp, LIB)
+    build_example(verbose)
     return LIB
+
+
+def build_example(verbose: bool = False) -> str:
+    """The plain-C caller of the library (a host program: gcc and the HIP runtime)."""
+    tmp = EXAMPLE + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c99", "-O2", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(ROCM, "include"), EXAMPLE_SRC, "-L", HERE, "-lspecverify",
+           "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN", "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("gcc failed for " + EXAMPLE_SRC)
+    os.replace(tmp, EXAMPLE)
+    return EXAMPLE
 
 
 if __name__ == "__main__":

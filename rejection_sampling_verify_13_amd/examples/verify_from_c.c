@@ -1,0 +1,82 @@
+/*
+ * Calling the verifier from plain C through include/spec_verify.h: device
+ * buffers from the HIP runtime, one spec_verify call on the default stream,
+ * results copied back.  The input is the two-token worked example of the
+ * zwjcode.cn page (section 05, and section 07's unit-test form): vocabulary
+ * {A = 0, B = 1}, draft q = (0.2, 0.8), target p = (0.6, 0.4) at the draft
+ * position and (0.3, 0.7) at the bonus position, draft token B, u = 0.7.
+ * p/q at B is 0.5, so B is rejected and the residual (0.4, 0) commits A:
+ * the outputs are tokens [0, -1] and 0 accepted drafts, for any u_sample.
+ *
+ * Build (the package build does this, next to libspecverify.so):
+ *   gcc -std=c99 -D__HIP_PLATFORM_AMD__ -I include -I /opt/rocm/include \
+ *       rejection_sampling_verify_13_amd/examples/verify_from_c.c -L rejection_sampling_verify_13_amd \
+ *       -lspecverify -L /opt/rocm/lib -lamdhip64 -lm -Wl,-rpath,'$ORIGIN' -o verify_from_c
+ * Exit status 0 when the outputs are as stated, 1 otherwise, 2 on an API error.
+ */
+#include <math.h>
+#include <stdio.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "spec_verify.h"
+
+#define CHECK(x)                                                   \
+  do {                                                             \
+    if ((x) != hipSuccess) {                                       \
+      fprintf(stderr, "HIP error at %s:%d\n", __FILE__, __LINE__); \
+      return 2;                                                    \
+    }                                                              \
+  } while (0)
+
+int main(void) {
+  const int N = 1, G = 1, V = 2;
+  const int32_t ids[1] = {1};
+  const float q[2] = {0.2f, 0.8f};
+  const float logits[4] = {logf(0.6f), logf(0.4f), logf(0.3f), logf(0.7f)};
+  const float temperature[1] = {1.0f};
+  const int32_t top_k[1] = {0};
+  const float top_p[1] = {1.0f};
+  const float u_accept[1] = {0.7f};
+  const float u_sample[1] = {0.9f};
+
+  int32_t *d_ids, *d_k, *d_out, *d_num;
+  float *d_q, *d_l, *d_t, *d_p, *d_ua, *d_us;
+  void* d_ws;
+  const size_t ws = spec_verify_workspace_size(N, G, V);
+  CHECK(hipMalloc((void**)&d_ids, sizeof ids));
+  CHECK(hipMalloc((void**)&d_q, sizeof q));
+  CHECK(hipMalloc((void**)&d_l, sizeof logits));
+  CHECK(hipMalloc((void**)&d_t, sizeof temperature));
+  CHECK(hipMalloc((void**)&d_k, sizeof top_k));
+  CHECK(hipMalloc((void**)&d_p, sizeof top_p));
+  CHECK(hipMalloc((void**)&d_ua, sizeof u_accept));
+  CHECK(hipMalloc((void**)&d_us, sizeof u_sample));
+  CHECK(hipMalloc((void**)&d_out, sizeof(int32_t) * N * (G + 1)));
+  CHECK(hipMalloc((void**)&d_num, sizeof(int32_t) * N));
+  CHECK(hipMalloc(&d_ws, ws));
+  CHECK(hipMemcpy(d_ids, ids, sizeof ids, hipMemcpyHostToDevice));
+  CHECK(hipMemcpy(d_q, q, sizeof q, hipMemcpyHostToDevice));
+  CHECK(hipMemcpy(d_l, logits, sizeof logits, hipMemcpyHostToDevice));
+  CHECK(hipMemcpy(d_t, temperature, sizeof temperature, hipMemcpyHostToDevice));
+  CHECK(hipMemcpy(d_k, top_k, sizeof top_k, hipMemcpyHostToDevice));
+  CHECK(hipMemcpy(d_p, top_p, sizeof top_p, hipMemcpyHostToDevice));
+  CHECK(hipMemcpy(d_ua, u_accept, sizeof u_accept, hipMemcpyHostToDevice));
+  CHECK(hipMemcpy(d_us, u_sample, sizeof u_sample, hipMemcpyHostToDevice));
+
+  const int rc = spec_verify(N, G, V, d_ids, d_q, d_l, SPEC_VERIFY_F32, d_t, d_k, d_p, d_ua, d_us, d_out, d_num,
+                             d_ws, ws, NULL);
+  if (rc != SPEC_VERIFY_OK) {
+    fprintf(stderr, "spec_verify: %s\n", spec_verify_status_string(rc));
+    return 2;
+  }
+  CHECK(hipDeviceSynchronize());
+  int32_t out[2], num[1];
+  CHECK(hipMemcpy(out, d_out, sizeof out, hipMemcpyDeviceToHost));
+  CHECK(hipMemcpy(num, d_num, sizeof num, hipMemcpyDeviceToHost));
+  printf("tokens [%d, %d], accepted %d\n", out[0], out[1], num[0]);
+  hipFree(d_ids); hipFree(d_q); hipFree(d_l); hipFree(d_t); hipFree(d_k); hipFree(d_p);
+  hipFree(d_ua); hipFree(d_us); hipFree(d_out); hipFree(d_num); hipFree(d_ws);
+  return (out[0] == 0 && out[1] == -1 && num[0] == 0) ? 0 : 1;
+}

@@ -109,7 +109,7 @@ def cpu_baseline(spec, n_req, threads, min_seconds=10.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
     ap.add_argument("--cpu-sample", type=int, default=256, help="requests timed on the CPU oracle (0: skip)")

@@ -100,9 +100,12 @@ struct RowStats {
   float m;        // max logit of the row
   float cut_p;    // target token kept iff logit >= cut_p
   float cut_q;    // draft token kept iff q >= cut_q
-  int argmax;     // greedy rows: lowest id of the max logit
+  union {
+    int argmax;   // greedy rows: lowest id of the max logit
+    float qinv;   // stochastic rows: 1 / qs, the scale of the tempered draft weights (q / qs)^(1/T)
+  };
   double z;       // sum over the kept set of 2^((l - m) * c), c = log2(e) / T in fp32
-  double r;       // sum over the kept set of q^(1/T)
+  double r;       // sum over the kept set of (q / qs)^(1/T) (of q at T = 1)
   double p_y;     // p'(y) at a draft position
   double q_y;     // q'(y) at a draft position
   double s;       // mass S of the draw made in the row (when draw >= 0)
@@ -305,9 +308,29 @@ __device__ inline uint32_t max8u(const uint32_t u[8]) {
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// q^(1/T) in fp64, the same expression wherever a single value is needed
-__device__ inline double temper_q(float q, float T) {
-  return T == 1.f ? (double)q : pow((double)q, 1.0 / (double)T);
+// Tempered draft weights are (q / qs)^(1/T) with qs = 2^(E - 126), E the
+// biased fp32 exponent of the row's largest q clamped to [1, 252]: the power
+// of two just above that q.  The factor qs^(-1/T) is common to every weight
+// and to their sum, so q' is unchanged, while q / qs is exact, the weights stay
+// within [0, 1] and the fp32 exponent log2(q / qs) / T stays small for the
+// tokens that carry the mass (at low T, log2(q) / T itself reaches hundreds,
+// where one fp32 ulp is ~1e-5).  Rows whose largest q is subnormal or above
+// 2^126 lie outside that scheme (the first read as zero mass).
+__device__ inline int scale_e(uint32_t qmax_bits) { return min(max((int)(qmax_bits >> 23), 1), 252); }
+__device__ inline float scale_qs(int e) { return __uint_as_float((uint32_t)(e + 1) << 23); }
+__device__ inline float scale_inv(int e) { return __uint_as_float((uint32_t)(253 - e) << 23); }
+// (qs(e0) / qs(e1))^(1/T)
+__device__ inline double scale_step(int e0, int e1, float invT) {
+  return exp2((double)(e0 - e1) * (double)invT);
+}
+// the weight in fp64, the same expression wherever a single value is needed
+// (qinv = 1 / qs is a power of two: the product is exact)
+__device__ inline double temper_q(float q, float T, float qinv) {
+  return T == 1.f ? (double)q : pow((double)q * (double)qinv, 1.0 / (double)T);
+}
+// the fp32 counterpart used by the streaming passes, with qinv = 1 / qs
+__device__ inline float temper_q32(float q, float invT, float qinv) {
+  return fast_exp2(fast_log2(q * qinv) * invT);
 }
 // 2^((l - m) * c) in fp64 with the fp32 scale c used by the streaming sums
 __device__ inline double mass_p(float l, float m, float c) {
@@ -1129,12 +1152,12 @@ struct MergeIn {
   int k;
   float top_p;
   int pact;
-  int draft;          // weights q^(1/T) (else 2^((l - m) * c))
-  float m, c, T;
+  int draft;          // weights (q / qs)^(1/T) (else 2^((l - m) * c))
+  float m, c, T, qinv;
 };
 
 __device__ inline double merge_weight(const MergeIn& in, float v) {
-  return in.draft ? temper_q(v, in.T) : mass_p(v, in.m, in.c);
+  return in.draft ? temper_q(v, in.T, in.qinv) : mass_p(v, in.m, in.c);
 }
 
 __device__ inline void unpack_raw(const Bf16::Raw& r, float v[8]) { Bf16::unpack(r, v); }
@@ -1196,6 +1219,7 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
   in.draft = uni(in.draft);
   in.top_p = uni(in.top_p);
   in.m = uni(in.m);
+  in.qinv = uni(in.qinv);
   in.c = uni(in.c);
   in.T = uni(in.T);
   MergeOut out;
@@ -1397,6 +1421,7 @@ struct DrawIn {
   int mode;           // 0: p'; 1: max(0, p' - q'); 2: p' with the draft token removed
   const float* qrow;  // mode 1: the draft row
   float cut_q, T;     // mode 1: draft cut and temperature
+  float qinv;         // mode 1: 1 / qs
   double rk;          // mode 1: kept draft mass
   int y;              // mode 2: the draft token
   float us;           // the request's draw uniform
@@ -1424,6 +1449,7 @@ __device__ __noinline__ DrawOut wave_draw(DrawIn in, const LDS_AS uint32_t* skey
   in.qrow = uni(in.qrow);
   in.cut_q = uni(in.cut_q);
   in.T = uni(in.T);
+  in.qinv = uni(in.qinv);
   in.rk = uni(in.rk);
   in.y = uni(in.y);
   in.us = uni(in.us);
@@ -1435,7 +1461,7 @@ __device__ __noinline__ DrawOut wave_draw(DrawIn in, const LDS_AS uint32_t* skey
       double q = 0.0;
       if (keep) {
         const float qx = tok_prob(tk, id, F32::at(in.qrow, (size_t)id));
-        q = (qx >= in.cut_q) ? temper_q(qx, in.T) / in.rk : 0.0;
+        q = (qx >= in.cut_q) ? temper_q(qx, in.T, in.qinv) / in.rk : 0.0;
       }
       w = p - q > 0.0 ? p - q : 0.0;
     } else if (in.mode == 2) {
@@ -1520,6 +1546,7 @@ struct GeneralArgs {
   int V;
   bool bf16, draft;
   float m, c, invT;
+  float qinv;     // draft rows: 1 / qs
   bool temper;
   int k;
   bool kact;
@@ -1544,6 +1571,7 @@ __device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hi
   g.m = uni(g.m);
   g.c = uni(g.c);
   g.invT = uni(g.invT);
+  g.qinv = uni(g.qinv);
   g.temper = uni((int)g.temper);
   g.k = uni(g.k);
   g.kact = uni((int)g.kact);
@@ -1556,7 +1584,7 @@ __device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hi
   ka.V = g.V;
   ka.bf16 = g.bf16;
   auto weight = [&](float v) -> double {
-    return g.draft ? (g.temper ? (double)fast_exp2(fast_log2(v) * g.invT) : (double)v)
+    return g.draft ? (g.temper ? (double)temper_q32(v, g.invT, g.qinv) : (double)v)
                    : (double)fast_exp2((v - g.m) * g.c);
   };
   auto value = [&](int x) -> float {
@@ -1641,7 +1669,8 @@ struct StepRaw {
 struct StochState {
   float m;          // running max of this thread's logits
   double z;         // sum of 2^((l - m) * c) over this thread's logits (no top-k)
-  double r;         // sum of q^(1/T) (no top-k)
+  double r;         // sum of q at T = 1, else of (q / qs)^(1/T) with qs = scale_qs(scale_e(qbad)) (no top-k)
+  float qinv;       // 1 / qs
   uint32_t qbad;    // max raw bits of q (>= 0x7f800000: NaN, inf or sign bit)
   uint32_t lbad;    // max bits of |l| (> 0x7f800000: NaN) (top-k)
   ChunkState ps, qs;
@@ -1681,13 +1710,21 @@ __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, co
       uint32_t u[8];
       F32::bits(qr, u);
       qmax = max8u(u);
+      if (QM == 2 && !CAND && qmax > st.qbad) {
+        const int e0 = scale_e(st.qbad), e1 = scale_e(qmax);
+        if (e1 > e0) {
+          // a q in a higher binade: move the running sum to the new scale
+          if (st.r != 0.0) st.r *= (double)fast_exp2((float)(e0 - e1) * invT);
+          st.qinv = scale_inv(e1);
+        }
+      }
       st.qbad = max(st.qbad, qmax);
       if (!CAND) {
         float r[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const float qv = __uint_as_float(u[t]);
-          r[t] = (QM == 1) ? qv : fast_exp2(fast_log2(qv) * invT);
+          r[t] = (QM == 1) ? qv : temper_q32(qv, invT, st.qinv);
         }
         st.r += (double)(((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7])));
       }
@@ -1891,6 +1928,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   st.m = cand ? -INFINITY : -FLT_MAX;
   st.z = 0.0;
   st.r = 0.0;
+  st.qinv = scale_inv(1);
   st.qbad = 0u;
   st.lbad = 0u;
   st.ps = ChunkState{0, 0u, 0};
@@ -1932,7 +1970,10 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
     const float mw = wave_max_f32(st.m);
     const uint32_t qbw = has_q ? wave_max_u32(st.qbad) : 0u;
     const uint32_t lbw = cand ? wave_max_u32(st.lbad) : 0u;
-    const double rw = (has_q && !cand) ? wave_sum_f64(st.r) : 0.0;
+    double rt = st.r;
+    if (has_q && !cand && temper && rt != 0.0 && scale_e(st.qbad) != scale_e(qbw))
+      rt *= scale_step(scale_e(st.qbad), scale_e(qbw), invT);
+    const double rw = (has_q && !cand) ? wave_sum_f64(rt) : 0.0;
     if (lane == 0) {
       sh.xm[wave] = mw;
       sh.xqb[wave] = qbw;
@@ -1944,8 +1985,17 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   }
   __syncthreads();
   const float m = __builtin_fmaxf(__builtin_fmaxf(sh.xm[0], sh.xm[1]), __builtin_fmaxf(sh.xm[2], sh.xm[3]));
-  const double R = (sh.xr[0] + sh.xr[1]) + (sh.xr[2] + sh.xr[3]);
   const uint32_t qb = max(max(sh.xqb[0], sh.xqb[1]), max(sh.xqb[2], sh.xqb[3]));
+  // the draft weight scale qs of the row (1 where the weights are q itself)
+  const float qinv = (has_q && temper) ? scale_inv(scale_e(qb)) : 1.f;
+  double xr[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    xr[w] = sh.xr[w];
+    if (has_q && !cand && temper && xr[w] != 0.0 && scale_e(sh.xqb[w]) != scale_e(qb))
+      xr[w] *= scale_step(scale_e(sh.xqb[w]), scale_e(qb), invT);
+  }
+  const double R = (xr[0] + xr[1]) + (xr[2] + xr[3]);
   const uint32_t lb = max(max(sh.xlb[0], sh.xlb[1]), max(sh.xlb[2], sh.xlb[3]));
   if (cand) {
     // a segment that overflowed is gathered again with the largest wave
@@ -2020,6 +2070,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
         in.m = m;
         in.c = c;
         in.T = T;
+        in.qinv = qinv;
         MergeOut mo;
         if (d == 0)
           mo = wave_merge<sizeof(ET) == 2>(in, (LDS_AS uint32_t*)sh.skey[0], (LDS_AS int*)sh.sid[0],
@@ -2054,6 +2105,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       g.m = m;
       g.c = c;
       g.invT = invT;
+      g.qinv = 1.f;
       g.temper = temper;
       g.k = rq.k;
       g.kact = rq.kact;
@@ -2075,6 +2127,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       g.m = m;
       g.c = c;
       g.invT = invT;
+      g.qinv = qinv;
       g.temper = temper;
       g.k = rq.k;
       g.kact = rq.kact;
@@ -2099,7 +2152,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
     s.m = m;
     s.cut_p = cut_p;
     s.cut_q = cut_q;
-    s.argmax = -1;
+    s.qinv = qinv;
     s.z = Zk;
     s.r = Rk;
     s.p_y = NAN;
@@ -2109,7 +2162,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       const double e = (ly >= cut_p) ? mass_p(ly, m, c) : 0.0;
       const double py = e / Zk;
       double qy = 1.0;
-      if (req_q) qy = (qyv >= cut_q) ? temper_q(qyv, T) / Rk : 0.0;
+      if (req_q) qy = (qyv >= cut_q) ? temper_q(qyv, T, qinv) / Rk : 0.0;
       const double u = (double)a.u_accept[(size_t)rq.id0 + j];
       acc = (!a.synthetic && u * qy < py) ? 1 : 0;  // synthetic mode: the listed draft row is A
       s.p_y = py;
@@ -2128,6 +2181,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       din.qrow = qrow;
       din.cut_q = cut_q;
       din.T = T;
+      din.qinv = qinv;
       din.rk = Rk;
       din.y = __builtin_amdgcn_readlane(y, 0);
       din.us = a.u_sample[i];
@@ -2378,14 +2432,15 @@ __device__ inline double wave_incl_scan_f64(double v) {
 // token removed) and p' of one lane's 8 tokens; tokens past the row end read
 // as -inf logits and zero probabilities, so both are zero there.
 __device__ inline void draw_weights(const float lv[8], const float qv[8], int base, int mode, float m, float c,
-                                    float invZ, float cut_p, float cut_q, float invR, float invT, bool temper, int yA,
+                                    float invZ, float cut_p, float cut_q, float invR, float invT, float qinv,
+                                    bool temper, int yA,
                                     float w[8], float p[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     p[e] = (lv[e] >= cut_p) ? fast_exp2((lv[e] - m) * c) * invZ : 0.f;
     float x = p[e];
     if (mode == 1) {
-      const float r = temper ? fast_exp2(fast_log2(qv[e]) * invT) : qv[e];
+      const float r = temper ? temper_q32(qv[e], invT, qinv) : qv[e];
       const float q = (qv[e] >= cut_q) ? r * invR : 0.f;
       x = __builtin_fmaxf(p[e] - q, 0.f);
     } else if (mode == 2) {
@@ -2486,6 +2541,7 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   const bool temper = T != 1.f;
   const float invZ = (float)(1.0 / sa.z);
   const float invR = (mode == 1) ? (float)(1.0 / sa.r) : 0.f;
+  const float qinv = (mode == 1 && temper) ? sa.qinv : 1.f;
   // (row A's index was checked by the row pass: a bad one faults the request)
   const size_t trow = !a.bidx ? (size_t)rr.tgt0 + A : (size_t)(A < gamma ? a.tidx[(size_t)rr.id0 + A] : a.bidx[i]);
   const ET* lrow = reinterpret_cast<const ET*>(a.logits) + trow * (size_t)V;
@@ -2544,7 +2600,7 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
     float lv[8], qv[8], w[8], pw[8];
     LT::unpack(lr[u], lv);
     F32::unpack(qr[u], qv);
-    draw_weights(lv, qv, base, mode, sa.m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w, pw);
+    draw_weights(lv, qv, base, mode, sa.m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, qinv, temper, yA, w, pw);
     double sw = 0.0, sp = 0.0;
     uint32_t lw = 0u, lp = 0u;
 #pragma unroll
@@ -2671,7 +2727,7 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
     else
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[e] = 0.f;
-    draw_weights(lv, qv, base, dmode, sa.m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, temper, yA, w, pw);
+    draw_weights(lv, qv, base, dmode, sa.m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, qinv, temper, yA, w, pw);
     double ls = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ls += (double)w[e];

@@ -139,7 +139,12 @@ def compare(g, o, rows=None, label=""):
     if "p_y" in g:
         for key in ("p_y", "q_y"):
             a, b = g[key], o[key]
-            both = ~np.isnan(b) & (o["fault"][:, None] == 0)
+            # The margin covers the rows that decide the outcome: positions up to the first rejection A.
+            # A row past A, or a row of an ambiguous request, may keep a different set at a top-p cut that
+            # lies within the margin, so the filtered probabilities are compared at positions j <= A of
+            # unambiguous requests.
+            decisive = np.arange(b.shape[1])[None, :] <= o["num_accepted"][:, None]
+            both = ~np.isnan(b) & (o["fault"][:, None] == 0) & ~amb[:, None] & decisive
             assert not np.isnan(a[both]).any(), "%s %s missing on GPU" % (label, key)
             if both.any():
                 d = np.abs(a[both] - b[both]).max()

@@ -128,6 +128,11 @@ SMALL = {
     "k_128_edge": W.config(3, N=8, V=4096, top_k=128, top_p=0.95),
     "greedy_all": W.config(4, N=24, V=5000, greedy_count=24),
     "low_temperature": W.config(2, N=16, V=4000, temperature=0.05),
+    # low temperature on each path that forms tempered draft weights in fp32
+    "low_temperature_general_topk": W.config(2, N=16, V=8000, gmax=8, top_k=65, top_p=0.5, temperature=0.05,
+                                             dtype="f32"),
+    "low_temperature_unfiltered": W.config(2, N=16, V=6000, top_k=0, top_p=1.0, temperature=0.08),
+    "low_temperature_top_p_only": W.config(3, N=12, V=9000, top_k=0, top_p=0.9, temperature=0.15, dtype="f32"),
     "high_temperature": W.config(2, N=16, V=4000, temperature=3.0),
     "gamma_zero": W.config(2, N=12, gmax=0, V=3000),
     "gamma_max_64": W.config(2, N=3, gmax=64, V=2048),

@@ -130,12 +130,14 @@ int spec_verify_diag(int N, int gmax, int V, const int32_t *draft_ids, const flo
 
 /*
  * spec_verify_diag plus three optional hipEvent_t handles (created by the
- * caller, may be NULL) that are recorded on `stream`: ev_start before the
- * row pass (every row's statistics and accept flag, and the draw of a row
- * that may be drawn from and kept its top-k set on chip), ev_mid after it,
- * ev_end after the draw pass (each request's first rejection and outputs,
- * and the draw for requests whose draw row made none).  For timing the two
- * phases; results are identical to spec_verify_diag.
+ * caller, may be NULL) that are recorded on `stream`: ev_start at the start
+ * of the row pass (every row's statistics and accept flag, and the draw of a
+ * row that may be drawn from and kept its top-k set on chip) and ev_mid at
+ * its end, both taken by the row pass's own dispatch (hipExtLaunchKernel),
+ * so they add no packets around it; ev_end after the draw pass (each
+ * request's first rejection and outputs, and the draw for requests whose
+ * draw row made none).  For timing the two phases; results are identical to
+ * spec_verify_diag.
  */
 int spec_verify_timed(int N, int gmax, int V, const int32_t *draft_ids, const float *draft_probs,
                       const void *target_logits, int logits_dtype, const float *temperature,

@@ -56,6 +56,7 @@
 //          -Xclang -target-feature -Xclang -packed-fp32-ops
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <float.h>
 #include <limits.h>
@@ -2825,10 +2826,14 @@ hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
   hipError_t e;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((row_kernel<LT, VEC, TOK>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
+  // the row pass's events travel in its own dispatch (start and end of the
+  // kernel), so timing it adds no packets before or after it on the stream
+  if (ev.start || ev.mid)
+    hipExtLaunchKernelGGL((row_kernel<LT, VEC, TOK>), dim3((unsigned)rows), dim3(kBlock), 0, stream, ev.start, ev.mid,
+                          0u, a);
+  else
+    hipLaunchKernelGGL((row_kernel<LT, VEC, TOK>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev.mid && (e = hipEventRecord(ev.mid, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((draw_kernel<LT, VEC, TOK>), dim3((unsigned)((long)a.N * (a.dparts + 1))), dim3(kBlock), 0,
                      stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

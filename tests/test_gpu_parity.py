@@ -577,6 +577,7 @@ BAN = {
     "ban_top_p_only": (W.config(2, N=12, V=6000, top_p=0.8), 25),
     "ban_unaligned_f32_topk": (W.config(3, N=10, V=3001, dtype="f32"), 20),
     "ban_long_lists": (W.config(3, N=8, V=9000), 512),
+    "ban_low_temperature_top_p": (W.config(2, N=12, V=6000, top_k=0, top_p=0.9, temperature=0.1), 40),
 }
 
 
@@ -692,6 +693,8 @@ PEN = {
     "pen_unaligned_f32_banned": (W.config(2, N=12, V=3001, dtype="f32"), 64, 20, None),
     "pen_long_lists": (W.config(3, N=8, V=9000), 1024 - 5, 0, None),
     "pen_rows_scattered": (W.config(3, N=12, V=8192), 120, 10, (13, 9)),
+    # penalised draft rows streamed unfiltered at low temperature
+    "pen_low_temperature": (W.config(2, N=16, V=6000, top_k=0, top_p=1.0, temperature=0.1), 200, 0, None),
 }
 
 

@@ -225,6 +225,33 @@ def test_draft_transform_matches_numpy(oracle_mod, seed):
         np.testing.assert_allclose(got, np_draft(q, T, k, p), rtol=1e-12, atol=1e-15)
 
 
+def np_draft_logdomain(q, T, k, p):
+    """q' from the logs: exp(log(q) / T - max), the route that stays in range at any T."""
+    q64 = q.astype(np.float64)
+    with np.errstate(divide="ignore"):
+        s = np.log(q64) / T
+    e = np.exp(s - s.max())
+    keep = np_filters(e, e, k, p)
+    w = np.where(keep, e, 0.0)
+    return w / w.sum()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_draft_transform_low_temperature(oracle_mod, seed):
+    # q^(1/T) / sum at T = 0.05 and 0.02 equals the log-domain form, and q' is unchanged when every q is
+    # scaled by the same power of two (exact in fp32): the normalisation removes any common factor
+    rng = np.random.default_rng(200 + seed)
+    V = int(rng.integers(50, 4000))
+    q = softmax(rng.standard_normal(V) * 1.5).astype(np.float32)
+    for T, k, p in [(0.05, 0, 1.0), (0.05, 0, 0.9), (0.02, 65, 1.0), (0.05, 5, 0.95)]:
+        got, f, _ = oracle_mod.draft_probs(q, T, k, p)
+        assert f == 0
+        np.testing.assert_allclose(got, np_draft_logdomain(q, T, k, p), rtol=1e-9, atol=1e-300)
+        scaled, f2, _ = oracle_mod.draft_probs((q * np.float32(2.0 ** -5)).astype(np.float32), T, k, p)
+        assert f2 == 0
+        np.testing.assert_allclose(scaled, got, rtol=1e-12, atol=1e-300)
+
+
 def test_top_k_keeps_ties(oracle_mod):
     l = np.array([5, 4, 4, 4, 3, 2, 4, 1], np.float32)
     got, _, _ = oracle_mod.target_probs(l, "f32", 1.0, 2, 1.0)

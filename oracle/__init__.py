@@ -36,6 +36,10 @@ FAULT_TARGET_ROW = 8
 FAULT_DRAFT_ROW = 16
 FAULT_DRAFT_MASS = 32
 FAULT_BAN_LIST = 128
+TOL = 1e-6  # decisions within it of their boundary may go either way
+AMB_ACCEPT = 1
+AMB_TOP_P = 2
+AMB_CDF = 4
 FAULT_PENALTY = 512
 BAN_MAX = 512
 PEN_MAX = 1024
@@ -57,10 +61,10 @@ def _bind(path):
     P = ctypes.c_void_p
     lib.oracle_spec_verify.restype = ctypes.c_int
     lib.oracle_spec_verify.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int] + [P] * 2 + \
-        [P, ctypes.c_int] + [P] * 12
+        [P, ctypes.c_int] + [P] * 12 + [P] * 8
     lib.oracle_spec_verify_synthetic.restype = ctypes.c_int
     lib.oracle_spec_verify_synthetic.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int] + [P] * 2 + \
-        [P, ctypes.c_int] + [P] * 11
+        [P, ctypes.c_int] + [P] * 11 + [P] * 8
     lib.oracle_target_probs.restype = ctypes.c_int
     lib.oracle_target_probs.argtypes = [ctypes.c_int, P, ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                         ctypes.c_double, P, P]
@@ -96,7 +100,17 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
     ``dtype`` is "f32" (``target_logits`` float32) or "bf16" (``target_logits``
     uint16 bit patterns).  Returns a dict with tokens [N,gmax+1], num_accepted
     [N], p_y / q_y [N,gmax] (NaN where not computed), resid_mass [N], margin [N]
-    and fault [N].  With ``synthetic_rates`` (float32 [gmax]) the synthetic
+    and fault [N], and per row (zwjcode.cn page, section 14: record the
+    filtered support set and its probability sum) row_margin [N,gmax+1] (the
+    top-p cut margin of the row's target and draft transforms, the smaller of
+    the two; +inf without top-p), kept_p [N,gmax+1] / kept_q [N,gmax] (kept-set
+    sizes) and frac_p / frac_q (kept mass over the tempered row's whole mass);
+    NaN / -1 for rows not computed.  Per request, amb_kind says which decisions
+    lie within TOL = 1e-6 of their boundary (AMB_ACCEPT: an accept ratio,
+    AMB_TOP_P: a top-p cut, AMB_CDF: the draw), and z_lo / z_hi bound the
+    draw window: the tokens drawn by inverse CDF at u_sample - TOL and
+    u_sample + TOL, between which every token with positive weight is an
+    equally valid draw when only the CDF margin is small.  With ``synthetic_rates`` (float32 [gmax]) the synthetic
     acceptance mode runs instead: draft j is accepted iff u_j < rate_j.
 
     ``banned`` = (offsets [N + 1], ids): request i's banned tokens are
@@ -165,7 +179,11 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
     out = dict(tokens=np.empty((N, gmax + 1), np.int32), num_accepted=np.empty((N,), np.int32),
                p_y=np.empty((N, gmax), np.float64), q_y=np.empty((N, gmax), np.float64),
                resid_mass=np.empty((N,), np.float64), margin=np.empty((N,), np.float64),
-               fault=np.empty((N,), np.int32))
+               fault=np.empty((N,), np.int32), row_margin=np.empty((N, gmax + 1), np.float64),
+               kept_p=np.empty((N, gmax + 1), np.int32), kept_q=np.empty((N, gmax), np.int32),
+               frac_p=np.empty((N, gmax + 1), np.float64), frac_q=np.empty((N, gmax), np.float64),
+               amb_kind=np.empty((N,), np.int32), z_lo=np.empty((N,), np.int32), z_hi=np.empty((N,), np.int32))
+    rows = [out[k] for k in ("row_margin", "kept_p", "kept_q", "frac_p", "frac_q", "amb_kind", "z_lo", "z_hi")]
 
     def sl(a, lo):
         return None if a is None else a[lo:].ctypes.data
@@ -184,11 +202,12 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
             return lib.oracle_spec_verify_synthetic(
                 n, gmax, V, sl(ids, lo), sl(q, lo), sl(tl, lo), dt, sl(T, lo), sl(k, lo), sl(p, lo),
                 rates.ctypes.data, sl(ua, lo), sl(us, lo), sl(out["tokens"], lo), sl(out["num_accepted"], lo),
-                sl(out["resid_mass"], lo), sl(out["margin"], lo), sl(out["fault"], lo))
+                sl(out["resid_mass"], lo), sl(out["margin"], lo), sl(out["fault"], lo), *[sl(a, lo) for a in rows])
         return lib.oracle_spec_verify(n, gmax, V, sl(ids, lo), sl(q, lo), sl(tl, lo), dt, sl(T, lo), sl(k, lo),
                                       sl(p, lo), sl(ua, lo), sl(us, lo), sl(out["tokens"], lo),
                                       sl(out["num_accepted"], lo), sl(out["p_y"], lo), sl(out["q_y"], lo),
-                                      sl(out["resid_mass"], lo), sl(out["margin"], lo), sl(out["fault"], lo))
+                                      sl(out["resid_mass"], lo), sl(out["margin"], lo), sl(out["fault"], lo),
+                                      *[sl(a, lo) for a in rows])
 
     threads = max(1, min(int(threads), N)) if N else 1
     if threads == 1:
@@ -208,6 +227,14 @@ def run(draft_ids, draft_probs, target_logits, dtype, temperature=None, top_k=No
         out["q_y"][i] = np.nan
         out["resid_mass"][i] = np.nan
         out["margin"][i] = np.inf
+        out["row_margin"][i] = np.nan
+        out["kept_p"][i] = -1
+        out["kept_q"][i] = -1
+        out["frac_p"][i] = np.nan
+        out["frac_q"][i] = np.nan
+        out["amb_kind"][i] = 0
+        out["z_lo"][i] = -1
+        out["z_hi"][i] = -1
     return out
 
 

@@ -56,6 +56,15 @@
 #define OF_DRAFT_ROW     16  /* NaN / inf / sign bit set in a read q row      */
 #define OF_DRAFT_MASS    32  /* kept q mass is zero in a read q row           */
 
+/* Tolerance of a comparison with another implementation: a decision whose
+ * margin is below it may go either way (an accept ratio within OR_TOL of u, a
+ * top-p cut within OR_TOL of top_p, u_sample within OR_TOL of a CDF boundary
+ * C_x / S). */
+#define OR_TOL 1e-6
+#define AMB_ACCEPT 1
+#define AMB_TOP_P  2
+#define AMB_CDF    4
+
 static double bf16_to_double(uint16_t b) {
     uint32_t u = (uint32_t)b << 16;
     float f;
@@ -157,7 +166,8 @@ static double apply_filters(long V, const double *order, const double *mass, int
  * or 0.  p_out receives V probabilities.
  */
 static int target_probs_row(long V, const void *row, int dtype, double T, int top_k,
-                            double top_p, double *p_out, double *topp_margin) {
+                            double top_p, double *p_out, double *topp_margin, long *kept,
+                            double *kept_frac) {
     double *s = (double *)malloc(sizeof(double) * V);
     double *e = (double *)malloc(sizeof(double) * V);
     unsigned char *keep = (unsigned char *)malloc(V);
@@ -172,9 +182,19 @@ static int target_probs_row(long V, const void *row, int dtype, double T, int to
     }
     if (m == -INFINITY) fault = OF_TARGET_ROW; /* no finite logit */
     if (!fault) {
-        for (x = 0; x < V; x++) e[x] = exp(s[x] - m);
+        double total = 0.0;
+        for (x = 0; x < V; x++) {
+            e[x] = exp(s[x] - m);
+            total += e[x];
+        }
         double z = apply_filters(V, s, e, top_k, top_p, keep, topp_margin);
-        for (x = 0; x < V; x++) p_out[x] = keep[x] ? e[x] / z : 0.0;
+        long n = 0;
+        for (x = 0; x < V; x++) {
+            p_out[x] = keep[x] ? e[x] / z : 0.0;
+            n += keep[x];
+        }
+        *kept = n;
+        *kept_frac = z / total;
     }
     free(s);
     free(e);
@@ -188,7 +208,7 @@ static int target_probs_row(long V, const void *row, int dtype, double T, int to
  * [SD §06: p and q must go through identical transforms].
  */
 static int draft_probs_row(long V, const float *q, double T, int top_k, double top_p,
-                           double *q_out, double *topp_margin) {
+                           double *q_out, double *topp_margin, long *kept, double *kept_frac) {
     double *r = (double *)malloc(sizeof(double) * V);
     unsigned char *keep = (unsigned char *)malloc(V);
     long x;
@@ -199,11 +219,19 @@ static int draft_probs_row(long V, const float *q, double T, int top_k, double t
         r[x] = (T == 1.0) ? (double)f : pow((double)f, 1.0 / T);
     }
     if (!fault) {
+        double total = 0.0;
+        for (x = 0; x < V; x++) total += r[x];
         double z = apply_filters(V, r, r, top_k, top_p, keep, topp_margin);
         if (z == 0.0) {
             fault = OF_DRAFT_MASS;
         } else {
-            for (x = 0; x < V; x++) q_out[x] = keep[x] ? r[x] / z : 0.0;
+            long n = 0;
+            for (x = 0; x < V; x++) {
+                q_out[x] = keep[x] ? r[x] / z : 0.0;
+                n += keep[x];
+            }
+            *kept = n;
+            *kept_frac = z / total;
         }
     }
     free(r);
@@ -270,7 +298,74 @@ typedef struct {
     double *p_y, *q_y;       /* [gmax] or NULL */
     double *resid_mass, *margin;
     int32_t *fault_out;
+    /* per-row diagnostics [SD §14: record the filtered support and its mass],
+     * each NULL or [gmax+1] (target rows) / [gmax] (draft rows): the top-p cut
+     * margin of the row (the smaller of its target and draft margins), the
+     * kept-set sizes, and the kept mass as a fraction of the tempered row's */
+    double *row_margin;
+    int32_t *kept_p, *kept_q;
+    double *frac_p, *frac_q;
+    /* per request, each NULL or one value: which decisions lie within OR_TOL of
+     * their boundary (AMB_* bits), and the draw window: the tokens whose CDF
+     * intervals meet [u - OR_TOL, u + OR_TOL] * S are those from z_lo to z_hi
+     * (both drawn by inverse CDF, at u - OR_TOL and u + OR_TOL) */
+    int32_t *amb_kind, *z_lo, *z_hi;
 } request_t;
+
+/* request i's slices of the batched per-row outputs ([N, gmax+1] / [N, gmax]) */
+static void set_row_outputs(request_t *r, int i, double *row_margin, int32_t *kept_p, int32_t *kept_q,
+                            double *frac_p, double *frac_q, int32_t *amb_kind, int32_t *z_lo, int32_t *z_hi) {
+    size_t g = (size_t)r->gmax;
+    r->amb_kind = amb_kind ? amb_kind + i : NULL;
+    r->z_lo = z_lo ? z_lo + i : NULL;
+    r->z_hi = z_hi ? z_hi + i : NULL;
+    r->row_margin = row_margin ? row_margin + (size_t)i * (g + 1) : NULL;
+    r->kept_p = kept_p ? kept_p + (size_t)i * (g + 1) : NULL;
+    r->frac_p = frac_p ? frac_p + (size_t)i * (g + 1) : NULL;
+    r->kept_q = kept_q ? kept_q + (size_t)i * g : NULL;
+    r->frac_q = frac_q ? frac_q + (size_t)i * g : NULL;
+}
+
+/* the request's ambiguity kinds and draw window (see request_t) */
+static void note_ambiguity(request_t *r, double mg_acc, double mg_topp, double mg_cdf, int32_t zlo, int32_t zhi) {
+    if (r->amb_kind)
+        *r->amb_kind = (mg_acc < OR_TOL ? AMB_ACCEPT : 0) | (mg_topp < OR_TOL ? AMB_TOP_P : 0) |
+                       (mg_cdf < OR_TOL ? AMB_CDF : 0);
+    if (r->z_lo) *r->z_lo = zlo;
+    if (r->z_hi) *r->z_hi = zhi;
+}
+
+/* per-row diagnostics: unset rows read NaN (margins, fractions) and -1 (sizes) */
+static void init_row_outputs(request_t *r) {
+    int j;
+    if (r->amb_kind) *r->amb_kind = 0;
+    if (r->z_lo) *r->z_lo = -1;
+    if (r->z_hi) *r->z_hi = -1;
+    for (j = 0; j <= r->gmax; j++) {
+        if (r->row_margin) r->row_margin[j] = NAN;
+        if (r->kept_p) r->kept_p[j] = -1;
+        if (r->frac_p) r->frac_p[j] = NAN;
+        if (j < r->gmax) {
+            if (r->kept_q) r->kept_q[j] = -1;
+            if (r->frac_q) r->frac_q[j] = NAN;
+        }
+    }
+}
+
+/* row j's filter outcome: draft = 0 for the target row, 1 for the draft row */
+static void note_row(request_t *r, int j, int draft, double topp_margin, long kept, double frac) {
+    if (r->row_margin) {
+        double m = r->row_margin[j];
+        r->row_margin[j] = (isnan(m) || topp_margin < m) ? topp_margin : m;
+    }
+    if (!draft) {
+        if (r->kept_p) r->kept_p[j] = (int32_t)kept;
+        if (r->frac_p) r->frac_p[j] = frac;
+    } else {
+        if (r->kept_q) r->kept_q[j] = (int32_t)kept;
+        if (r->frac_q) r->frac_q[j] = frac;
+    }
+}
 
 static const void *logit_row(const request_t *r, int j) {
     size_t esz = r->dtype == 1 ? 2 : 4;
@@ -293,7 +388,7 @@ static void write_fault(request_t *r, int fault) {
  * draft probabilities, P[g] for the bonus) must be filled.
  */
 static int32_t draw_token(const request_t *r, double *const *P, double *const *Q, int A, int g, double *S_out,
-                          double *cmargin) {
+                          double *cmargin, int32_t *zlo, int32_t *zhi) {
     const long V = r->V;
     double *w = (double *)malloc(sizeof(double) * V);
     double S = 0.0;
@@ -318,6 +413,9 @@ static int32_t draw_token(const request_t *r, double *const *P, double *const *Q
         }
     }
     int32_t z = inverse_cdf(V, w, S, r->u_sample, cmargin);
+    double unused;
+    *zlo = inverse_cdf(V, w, S, r->u_sample - OR_TOL, &unused);
+    *zhi = inverse_cdf(V, w, S, r->u_sample + OR_TOL, &unused);
     *S_out = S;
     free(w);
     return z;
@@ -348,6 +446,7 @@ static void verify_request(request_t *r) {
     if (r->resid_mass) *r->resid_mass = NAN;
     if (r->margin) *r->margin = INFINITY;
     if (r->fault_out) *r->fault_out = 0;
+    init_row_outputs(r);
 
     /* gamma_i: drafts run up to the first negative id (padding) */
     for (j = 0; j < r->gmax; j++)
@@ -388,26 +487,33 @@ static void verify_request(request_t *r) {
             }
         z = t[A];
         free(t);
+        note_ambiguity(r, INFINITY, INFINITY, INFINITY, z, z);
     } else {
         /* full distributions p'_0..p'_g and q'_0..q'_{g-1} */
         double **P = (double **)malloc(sizeof(double *) * (g + 1));
         double **Q = (double **)malloc(sizeof(double *) * (g + 1));
-        double mg = INFINITY, tm;
+        double mg = INFINITY, tm, mg_acc = INFINITY, mg_topp = INFINITY;
         for (j = 0; j <= g; j++) {
             P[j] = (double *)malloc(sizeof(double) * V);
             Q[j] = NULL;
         }
         double *topp_m = (double *)malloc(sizeof(double) * (2 * g + 2));
         for (j = 0; j <= g && !fault; j++) {
-            fault |= target_probs_row(V, logit_row(r, j), r->dtype, T, r->top_k, r->top_p, P[j], &tm);
+            long n = -1;
+            double f = NAN;
+            fault |= target_probs_row(V, logit_row(r, j), r->dtype, T, r->top_k, r->top_p, P[j], &tm, &n, &f);
             topp_m[2 * j] = tm;
             topp_m[2 * j + 1] = INFINITY;
+            note_row(r, j, 0, tm, n, f);
         }
         if (r->q)
             for (j = 0; j < g && !fault; j++) {
+                long n = -1;
+                double f = NAN;
                 Q[j] = (double *)malloc(sizeof(double) * V);
-                fault |= draft_probs_row(V, r->q + (size_t)j * V, T, r->top_k, r->top_p, Q[j], &tm);
+                fault |= draft_probs_row(V, r->q + (size_t)j * V, T, r->top_k, r->top_p, Q[j], &tm, &n, &f);
                 topp_m[2 * j + 1] = tm;
+                note_row(r, j, 1, tm, n, f);
             }
         if (fault) {
             for (j = 0; j <= g; j++) {
@@ -439,22 +545,25 @@ static void verify_request(request_t *r) {
             double u = (double)r->u_accept[j];
             if (qy > 0.0) {
                 double d = fabs(u - py / qy);
-                if (d < mg) mg = d;
+                if (d < mg_acc) mg_acc = d;
             }
-            if (topp_m[2 * j] < mg) mg = topp_m[2 * j];
-            if (topp_m[2 * j + 1] < mg) mg = topp_m[2 * j + 1];
+            if (topp_m[2 * j] < mg_topp) mg_topp = topp_m[2 * j];
+            if (topp_m[2 * j + 1] < mg_topp) mg_topp = topp_m[2 * j + 1];
             if (!(u * qy < py)) {
                 A = j;
                 break;
             }
         }
-        if (A == g && topp_m[2 * g] < mg) mg = topp_m[2 * g];
+        if (A == g && topp_m[2 * g] < mg_topp) mg_topp = topp_m[2 * g];
 
         double cm, S;
-        z = draw_token(r, P, Q, A, g, &S, &cm);
+        int32_t zlo, zhi;
+        z = draw_token(r, P, Q, A, g, &S, &cm, &zlo, &zhi);
+        mg = mg_acc < mg_topp ? mg_acc : mg_topp;
         if (cm < mg) mg = cm;
         if (r->resid_mass) *r->resid_mass = S;
         if (r->margin) *r->margin = mg;
+        note_ambiguity(r, mg_acc, mg_topp, cm, zlo, zhi);
         for (j = 0; j <= g; j++) {
             free(P[j]);
             free(Q[j]);
@@ -474,14 +583,17 @@ static void verify_request(request_t *r) {
  * with the vocabulary contiguous: draft_ids [N,gmax], draft_probs [N,gmax,V],
  * target_logits [N,gmax+1,V] (dtype 0 = fp32, 1 = bf16 bit patterns),
  * u_accept [N,gmax], u_sample [N], out_tokens [N,gmax+1], out_num_accepted [N],
- * p_y and q_y [N,gmax], resid_mass, margin [N], fault [N].
+ * p_y and q_y [N,gmax], resid_mass, margin [N], fault [N], and the per-row
+ * diagnostics row_margin, kept_p, frac_p [N,gmax+1] and kept_q, frac_q [N,gmax],
+ * and per request amb_kind, z_lo, z_hi [N] (see request_t).
  */
 int oracle_spec_verify(int N, int gmax, int V, const int32_t *draft_ids, const float *draft_probs,
                        const void *target_logits, int dtype, const float *temperature,
                        const int32_t *top_k, const float *top_p, const float *u_accept,
                        const float *u_sample, int32_t *out_tokens, int32_t *out_num_accepted,
                        double *p_y, double *q_y, double *resid_mass, double *margin,
-                       int32_t *fault) {
+                       int32_t *fault, double *row_margin, int32_t *kept_p, int32_t *kept_q,
+                       double *frac_p, double *frac_q, int32_t *amb_kind, int32_t *z_lo, int32_t *z_hi) {
     int i;
     if (N < 0 || gmax < 0 || V < 1 || (dtype != 0 && dtype != 1)) return 1;
     size_t esz = dtype == 1 ? 2 : 4;
@@ -505,6 +617,7 @@ int oracle_spec_verify(int N, int gmax, int V, const int32_t *draft_ids, const f
         r.resid_mass = resid_mass ? resid_mass + i : NULL;
         r.margin = margin ? margin + i : NULL;
         r.fault_out = fault ? fault + i : NULL;
+        set_row_outputs(&r, i, row_margin, kept_p, kept_q, frac_p, frac_q, amb_kind, z_lo, z_hi);
         verify_request(&r);
     }
     return 0;
@@ -531,6 +644,7 @@ static void verify_request_synthetic(request_t *r, const float *rates) {
     if (r->resid_mass) *r->resid_mass = NAN;
     if (r->margin) *r->margin = INFINITY;
     if (r->fault_out) *r->fault_out = 0;
+    init_row_outputs(r);
 
     for (j = 0; j < r->gmax; j++)
         if (r->ids[j] < 0) {
@@ -549,12 +663,14 @@ static void verify_request_synthetic(request_t *r, const float *rates) {
     }
 
     /* the synthetic accept test, position by position until the first rejection */
-    double mg = INFINITY;
+    double mg = INFINITY, mg_acc = INFINITY, mg_topp = INFINITY, cm = INFINITY;
+    int32_t zlo = -1, zhi = -1;
     int A = g;
     for (j = 0; j < g; j++) {
         double u = (double)r->u_accept[j], rate = (double)rates[j];
         double d = fabs(u - rate);
         if (d < mg) mg = d;
+        if (d < mg_acc) mg_acc = d;
         if (!(u < rate)) {
             A = j;
             break;
@@ -564,22 +680,28 @@ static void verify_request_synthetic(request_t *r, const float *rates) {
     int32_t z = -1;
     if (greedy) {
         fault |= greedy_row(V, logit_row(r, A), r->dtype, &z);
+        zlo = zhi = z;
     } else {
         /* only row A's distributions: P[A] (also P[g] when A = g), Q[A] */
         double **P = (double **)calloc((size_t)g + 1, sizeof(double *));
         double **Q = (double **)calloc((size_t)g + 1, sizeof(double *));
-        double tm;
+        double tm, f = NAN;
+        long n = -1;
         P[A] = (double *)malloc(sizeof(double) * V);
-        fault |= target_probs_row(V, logit_row(r, A), r->dtype, T, r->top_k, r->top_p, P[A], &tm);
+        fault |= target_probs_row(V, logit_row(r, A), r->dtype, T, r->top_k, r->top_p, P[A], &tm, &n, &f);
         if (tm < mg) mg = tm;
+        if (tm < mg_topp) mg_topp = tm;
+        note_row(r, A, 0, tm, n, f);
         if (!fault && A < g && r->q) {
             Q[A] = (double *)malloc(sizeof(double) * V);
-            fault |= draft_probs_row(V, r->q + (size_t)A * V, T, r->top_k, r->top_p, Q[A], &tm);
+            fault |= draft_probs_row(V, r->q + (size_t)A * V, T, r->top_k, r->top_p, Q[A], &tm, &n, &f);
             if (tm < mg) mg = tm;
+            if (tm < mg_topp) mg_topp = tm;
+            note_row(r, A, 1, tm, n, f);
         }
         if (!fault) {
-            double cm, S;
-            z = draw_token(r, P, Q, A, g, &S, &cm);
+            double S;
+            z = draw_token(r, P, Q, A, g, &S, &cm, &zlo, &zhi);
             if (cm < mg) mg = cm;
             if (r->resid_mass) *r->resid_mass = S;
         }
@@ -593,6 +715,7 @@ static void verify_request_synthetic(request_t *r, const float *rates) {
         return;
     }
     if (r->margin) *r->margin = mg;
+    note_ambiguity(r, mg_acc, mg_topp, cm, zlo, zhi);
     write_output(r, A, z);
 }
 
@@ -601,7 +724,9 @@ int oracle_spec_verify_synthetic(int N, int gmax, int V, const int32_t *draft_id
                                  const void *target_logits, int dtype, const float *temperature,
                                  const int32_t *top_k, const float *top_p, const float *rates,
                                  const float *u_accept, const float *u_sample, int32_t *out_tokens,
-                                 int32_t *out_num_accepted, double *resid_mass, double *margin, int32_t *fault) {
+                                 int32_t *out_num_accepted, double *resid_mass, double *margin, int32_t *fault,
+                                 double *row_margin, int32_t *kept_p, int32_t *kept_q, double *frac_p,
+                                 double *frac_q, int32_t *amb_kind, int32_t *z_lo, int32_t *z_hi) {
     int i;
     if (N < 0 || gmax < 0 || V < 1 || (dtype != 0 && dtype != 1) || (gmax > 0 && !rates)) return 1;
     size_t esz = dtype == 1 ? 2 : 4;
@@ -625,6 +750,7 @@ int oracle_spec_verify_synthetic(int N, int gmax, int V, const int32_t *draft_id
         r.resid_mass = resid_mass ? resid_mass + i : NULL;
         r.margin = margin ? margin + i : NULL;
         r.fault_out = fault ? fault + i : NULL;
+        set_row_outputs(&r, i, row_margin, kept_p, kept_q, frac_p, frac_q, amb_kind, z_lo, z_hi);
         verify_request_synthetic(&r, rates);
     }
     return 0;
@@ -633,16 +759,18 @@ int oracle_spec_verify_synthetic(int N, int gmax, int V, const int32_t *draft_id
 /* Single-row views of the two transforms, for checking them on their own. */
 int oracle_target_probs(int V, const void *logits, int dtype, double T, int top_k, double top_p,
                         double *p_out, double *topp_margin) {
-    double tm;
-    int f = target_probs_row(V, logits, dtype, T, top_k, top_p, p_out, &tm);
+    double tm, frac;
+    long n;
+    int f = target_probs_row(V, logits, dtype, T, top_k, top_p, p_out, &tm, &n, &frac);
     if (topp_margin) *topp_margin = tm;
     return f;
 }
 
 int oracle_draft_probs(int V, const float *q, double T, int top_k, double top_p, double *q_out,
                        double *topp_margin) {
-    double tm;
-    int f = draft_probs_row(V, q, T, top_k, top_p, q_out, &tm);
+    double tm, frac;
+    long n;
+    int f = draft_probs_row(V, q, T, top_k, top_p, q_out, &tm, &n, &frac);
     if (topp_margin) *topp_margin = tm;
     return f;
 }

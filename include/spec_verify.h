@@ -64,7 +64,7 @@ extern "C" {
  * 256 * N * (ceil(ceil(V / 2048) / 4) + 1) (draw pass). */
 #define SPEC_VERIFY_ERR_DTYPE 3     /* unknown logits_dtype                              */
 #define SPEC_VERIFY_ERR_WORKSPACE 4 /* workspace_bytes below spec_verify_workspace_size  */
-#define SPEC_VERIFY_ERR_HIP 5       /* a HIP runtime call failed (launch, allocation)     */
+#define SPEC_VERIFY_ERR_HIP 5       /* a HIP runtime call failed (launch, copy, wait)      */
 
 /* fault bits of the diagnostic fault output */
 #define SPEC_VERIFY_FAULT_DRAFT_ID 1
@@ -80,8 +80,9 @@ extern "C" {
 
 /*
  * Bytes of device workspace one call with these sizes needs.  The layout is
- * private to the library; its contents do not need initialising and are not
- * meaningful after the call.
+ * private to the library; its contents do not need initialising.  After a
+ * call it holds that call's count of faulted requests, read by
+ * spec_verify_device_errors; the rest is not meaningful.
  */
 size_t spec_verify_workspace_size(int N, int gmax, int V);
 
@@ -99,13 +100,12 @@ size_t spec_verify_workspace_size(int N, int gmax, int V);
  *   out_tokens        int32   [N, gmax+1]      written
  *   out_num_accepted  int32   [N]              written
  * workspace: device memory of at least spec_verify_workspace_size(N, gmax, V)
- * bytes, or NULL to let the library use a buffer it allocates once per device
- * (grown when needed and kept until the process ends; the allocation may
- * synchronise the device).  stream: a hipStream_t, or NULL for the default
- * stream.  The call only enqueues work on the stream and returns; it never
- * waits for the device.  Calls that share a workspace must be ordered on one
- * stream.  N == 0 is a valid empty batch.  Inputs are read only; outputs must
- * not alias inputs or the workspace.
+ * bytes, owned by the caller (SPEC_VERIFY_ERR_NULL if NULL and N > 0): the
+ * library allocates nothing and keeps no state between calls.  stream: a
+ * hipStream_t, or NULL for the default stream.  The call only enqueues kernels
+ * on the stream and returns; it never waits for the device.  Calls that share
+ * a workspace must be ordered on one stream.  N == 0 is a valid empty batch.
+ * Inputs are read only; outputs must not alias inputs or the workspace.
  */
 int spec_verify(int N, int gmax, int V, const int32_t *draft_ids, const float *draft_probs,
                 const void *target_logits, int logits_dtype, const float *temperature,
@@ -331,6 +331,22 @@ int spec_verify_rollback(int N, int gmax, const int32_t *cu_num_draft_tokens,
                          const int32_t *draft_ids, const int32_t *num_accepted,
                          int32_t *num_computed_tokens, int32_t *num_output_placeholders,
                          int32_t *slot_mapping, void *stream);
+
+/*
+ * The number of requests that the most recent call using `workspace` reported
+ * as faulted (out_num_accepted = -1; the plain entry points have no other
+ * fault output).  The call's first kernel sets the count to zero and its last
+ * kernel adds one per faulted request, so it is the count of that call alone.
+ * Enqueues a copy of the count on `stream` (the stream of that call) and waits
+ * for the stream to finish, then stores the count in *count (host memory).
+ * Returns SPEC_VERIFY_ERR_NULL for a NULL workspace or count,
+ * SPEC_VERIFY_ERR_WORKSPACE for workspace_bytes below 256, SPEC_VERIFY_ERR_HIP
+ * if the copy or the wait fails.  The count belongs to one call rather than
+ * accumulating over calls: the workspace is caller memory that no call
+ * requires to be initialised, so a count carried from call to call would start
+ * from whatever the memory held.
+ */
+int spec_verify_device_errors(const void *workspace, size_t workspace_bytes, void *stream, int32_t *count);
 
 /* Human-readable text of a return code (static storage). */
 const char *spec_verify_status_string(int status);

@@ -30,7 +30,8 @@ FAULT_ROW_INDEX = 256
 FAULT_PENALTY = 512
 
 EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_timed", "spec_verify_flat", "spec_verify_flat_timed",
-           "spec_verify_flat_synthetic", "spec_verify_flat_ex", "spec_verify_rollback", "spec_verify_workspace_size",
+           "spec_verify_flat_synthetic", "spec_verify_flat_ex", "spec_verify_rollback", "spec_verify_device_errors",
+           "spec_verify_workspace_size",
            "spec_verify_status_string", "spec_verify_version")
 
 
@@ -66,6 +67,8 @@ def _load():
     lib.spec_verify_rollback.argtypes = [I, I, P, P, P, P, P, P, P]
     lib.spec_verify_workspace_size.restype = Z
     lib.spec_verify_workspace_size.argtypes = [I, I, I]
+    lib.spec_verify_device_errors.restype = I
+    lib.spec_verify_device_errors.argtypes = [P, Z, P, P]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     lib.spec_verify_status_string.argtypes = [I]
     lib.spec_verify_version.restype = I
@@ -78,6 +81,21 @@ lib = _load()
 
 def workspace_size(N: int, gmax: int, V: int) -> int:
     return int(lib.spec_verify_workspace_size(N, gmax, V))
+
+
+def device_errors(workspace, stream=None) -> int:
+    """Number of requests the most recent call on ``workspace`` (a uint8 CUDA
+    tensor passed to that call) reported as faulted; waits for ``stream``
+    (default: torch's current stream on the workspace's device)."""
+    if stream is None:
+        stream = torch.cuda.current_stream(workspace.device)
+    n = ctypes.c_int32(-1)
+    with torch.cuda.device(workspace.device):
+        rc = lib.spec_verify_device_errors(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           ctypes.c_void_p(stream.cuda_stream), ctypes.byref(n))
+    if rc != 0:
+        raise SpecVerifyError("spec_verify_device_errors: %s" % STATUS.get(rc, rc))
+    return int(n.value)
 
 
 def _ptr(t):

@@ -63,8 +63,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <mutex>
-#include <vector>
+#include <type_traits>
 
 #include "spec_verify.h"
 
@@ -79,7 +78,6 @@ constexpr int kKFast = 64;              // largest top_k served by the candidate
 constexpr int kSeg = 128;               // gathered candidate tokens per wave and distribution (LDS)
 constexpr int kDrawSpan = 4;            // draw pass: 2048-token steps per workgroup, all loads in flight
 constexpr int kMaxGamma = 64;
-constexpr float kLog2e = 1.4426950408889634f;
 
 enum {
   kFaultDraftId = SPEC_VERIFY_FAULT_DRAFT_ID,
@@ -163,6 +161,7 @@ struct Args {
   ReqRec* rec;          // per request
   DrawSum* dsum;        // [N][steps][kWaves]
   unsigned int* ddone;  // completion counter per request (draw pass)
+  unsigned int* nfault; // faulted requests of this call (workspace head; cleared by the plan kernel)
   int* plan;            // [0]: number of listed rows D; then D entries i * 128 + j, request-major
   DrawSum* dtot;        // [N][dparts] sums of each draw workgroup's blocks
   int dparts;           // draw pass: workgroups per request (kDrawSpan steps each)
@@ -320,22 +319,134 @@ __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ inline int scale_e(uint32_t qmax_bits) { return min(max((int)(qmax_bits >> 23), 1), 252); }
 __device__ inline float scale_qs(int e) { return __uint_as_float((uint32_t)(e + 1) << 23); }
 __device__ inline float scale_inv(int e) { return __uint_as_float((uint32_t)(253 - e) << 23); }
-// (qs(e0) / qs(e1))^(1/T)
-__device__ inline double scale_step(int e0, int e1, float invT) {
-  return exp2((double)(e0 - e1) * (double)invT);
+// An exponent scale (c = log2(e) / T for the target, 1 / T for the draft) in
+// fp64 and as an fp32 pair hi + lo with hi strictly below the value, so lo > 0.
+// A streamed exponent d * c is then fma(d, hi, d * lo): the exact product
+// rounded about once.  Rounding c itself to fp32 would instead scale every
+// exponent by the same relative error (up to 6e-8), a bias proportional to
+// the exponent that does not cancel in the normalised weights.  With lo > 0,
+// d = -inf gives -inf (weight 0) and NaN stays NaN.
+struct Scale2 {
+  double d;
+  float hi, lo;
+};
+__device__ inline Scale2 scale2(double v) {
+  Scale2 s;
+  s.d = v;
+  s.hi = (float)v;
+  if ((double)s.hi >= v) s.hi = __uint_as_float(__float_as_uint(s.hi) - 1u);  // v > 0
+  s.lo = (float)(v - (double)s.hi);
+  return s;
+}
+__device__ inline float smul(float x, const Scale2& s) { return __builtin_fmaf(x, s.hi, x * s.lo); }
+__device__ inline Scale2 target_scale(float T) { return scale2(1.4426950408889634 / (double)T); }
+__device__ inline Scale2 draft_scale(float T) { return scale2(1.0 / (double)T); }
+
+// (qs(e0) / qs(e1))^(1/T), e0 <= e1: in fp64 where wave and block sums are
+// combined; inside the streaming loop (a thread's running sum meeting a q in
+// a higher binade, a few times per row) the exponent is rounded once and the
+// power formed in fp32
+__device__ inline double scale_step(int e0, int e1, const Scale2& invT) {
+  return exp2((double)(e0 - e1) * invT.d);
+}
+__device__ inline double scale_step32(int e0, int e1, const Scale2& invT) {
+  return (double)fast_exp2(smul((float)(e0 - e1), invT));
 }
 // the weight in fp64, the same expression wherever a single value is needed
 // (qinv = 1 / qs is a power of two: the product is exact)
 __device__ inline double temper_q(float q, float T, float qinv) {
   return T == 1.f ? (double)q : pow((double)q * (double)qinv, 1.0 / (double)T);
 }
-// the fp32 counterpart used by the streaming passes, with qinv = 1 / qs
-__device__ inline float temper_q32(float q, float invT, float qinv) {
-  return fast_exp2(fast_log2(q * qinv) * invT);
+// The streamed tempered weight.  In fp32 the exponent log2(q / qs) / T carries
+// the hardware log2's error (about 6e-8 absolute) times 1/T, and is rounded to
+// fp32: at T = 0.05 a weight near the row's largest is off by ~1e-6.  So when
+// 1/T exceeds kPreciseInvT, the weights that can carry mass are formed in fp64
+// instead: those whose fp32 exponent is above thr = -(1/T + 24).  The largest
+// weight is at least 2^(-1/T) (qs is within a factor 2 of the largest q), so
+// the tokens left in fp32 each weigh under 2^-24 of it.
+constexpr double kPreciseInvT = 2.0;
+struct DraftW {
+  Scale2 invT;
+  float thr;      // exponent above which the weight is formed in fp64
+  bool precise;   // 1/T > kPreciseInvT
+};
+__device__ inline DraftW draft_w(float T) {
+  DraftW w;
+  w.invT = draft_scale(T);
+  w.precise = w.invT.d > kPreciseInvT;
+  w.thr = -(float)(w.invT.d + 24.0);
+  return w;
 }
-// 2^((l - m) * c) in fp64 with the fp32 scale c used by the streaming sums
-__device__ inline double mass_p(float l, float m, float c) {
-  return exp2(((double)l - (double)m) * (double)c);
+// r^(1/T) in fp64 for a positive float r (r = q / qs, exact), to about 1e-13
+// relative, in straight-line code (no library call).  r = m 2^E with
+// m in [sqrt(1/2), sqrt(2)); log2(m) = (2 / ln 2) atanh(t), t = (m - 1) / (m + 1),
+// |t| < 0.1716, from the series t + t^3/3 + ... + t^17/17; then x = (E +
+// log2 m) / T = n + f with n an integer and |f| <= 1/2, and 2^f = e^(f ln 2)
+// from its Taylor series to the 13th power.
+__device__ inline double precise_weight(float r, double invT) {
+  int E;
+  double m = 2.0 * (double)frexpf(r, &E);  // r = m 2^(E - 1), m in [1, 2)
+  E -= 1;
+  if (m > 1.4142135623730951) {
+    m *= 0.5;
+    E += 1;
+  }
+  const double t = (m - 1.0) / (m + 1.0), t2 = t * t;
+  double a = 1.0 / 17;
+  a = fma(a, t2, 1.0 / 15);
+  a = fma(a, t2, 1.0 / 13);
+  a = fma(a, t2, 1.0 / 11);
+  a = fma(a, t2, 1.0 / 9);
+  a = fma(a, t2, 1.0 / 7);
+  a = fma(a, t2, 1.0 / 5);
+  a = fma(a, t2, 1.0 / 3);
+  a = fma(a, t2, 1.0);
+  const double x = ((double)E + 2.8853900817779268 * t * a) * invT;  // 2 / ln 2
+  const double n = fmax(rint(x), -2000.0);
+  const double f = (x - n) * 0.6931471805599453;  // ln 2
+  double e = 1.0 / 6227020800.0;                 // 1 / 13!
+  e = fma(e, f, 1.0 / 479001600.0);
+  e = fma(e, f, 1.0 / 39916800.0);
+  e = fma(e, f, 1.0 / 3628800.0);
+  e = fma(e, f, 1.0 / 362880.0);
+  e = fma(e, f, 1.0 / 40320.0);
+  e = fma(e, f, 1.0 / 5040.0);
+  e = fma(e, f, 1.0 / 720.0);
+  e = fma(e, f, 1.0 / 120.0);
+  e = fma(e, f, 1.0 / 24.0);
+  e = fma(e, f, 1.0 / 6.0);
+  e = fma(e, f, 0.5);
+  e = fma(e, f, 1.0);
+  e = fma(e, f, 1.0);
+  return ldexp(e, (int)n);
+}
+// The same, out of line: the streaming loops and the draw pass call it from
+// rarely taken branches, and keep their registers (inlined there, its fp64
+// temporaries made the row kernel spill in its hot loops).
+__device__ __noinline__ double precise_weight_call(float r, double invT) { return precise_weight(r, invT); }
+// fp32 weight of q with qinv = 1 / qs, or (precise tokens) 0 with the fp64
+// weight added to acc
+__device__ inline float temper_w32(float q, const DraftW& dw, float qinv, double& acc) {
+  const float r = q * qinv;
+  const float x = smul(fast_log2(r), dw.invT);
+  if (dw.precise && x > dw.thr) {
+    acc += precise_weight_call(r, dw.invT.d);
+    return 0.f;
+  }
+  return fast_exp2(x);
+}
+__device__ inline double temper_w64(float q, const DraftW& dw, float qinv) {
+  const float r = q * qinv;
+  const float x = smul(fast_log2(r), dw.invT);
+  if (dw.precise && x > dw.thr) return precise_weight_call(r, dw.invT.d);
+  return (double)fast_exp2(x);
+}
+// streamed target weight 2^((l - m) * c); the largest is 1, so a token's
+// absolute error stays near 2^x * |x| * 2^-25, small wherever 2^x is not
+__device__ inline float mass_p32(float l, float m, const Scale2& c) { return fast_exp2(smul(l - m, c)); }
+// 2^((l - m) * c) in fp64
+__device__ inline double mass_p(float l, float m, const Scale2& c) {
+  return exp2(((double)l - (double)m) * c.d);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -555,6 +666,20 @@ __device__ inline int block_min_i(int v, int* red) {
 // ------------------------------------------------------------------------------------------
 // request parameters
 // ------------------------------------------------------------------------------------------
+
+// wave-uniform copies (scalar registers) of scale pairs and draft-weight settings
+__device__ inline Scale2 uni_s2(Scale2 v) {
+  v.d = uni(v.d);
+  v.hi = uni(v.hi);
+  v.lo = uni(v.lo);
+  return v;
+}
+__device__ inline DraftW uni_dw(DraftW d) {
+  d.invT = uni_s2(d.invT);
+  d.thr = uni(d.thr);
+  d.precise = uni((int)d.precise);
+  return d;
+}
 
 struct Req {
   int gamma;      // number of draft tokens
@@ -1154,11 +1279,12 @@ struct MergeIn {
   float top_p;
   int pact;
   int draft;          // weights (q / qs)^(1/T) (else 2^((l - m) * c))
-  float m, c, T, qinv;
+  float m, T, qinv;
+  double cd;          // log2(e) / T in fp64 (target weights)
 };
 
 __device__ inline double merge_weight(const MergeIn& in, float v) {
-  return in.draft ? temper_q(v, in.T, in.qinv) : mass_p(v, in.m, in.c);
+  return in.draft ? temper_q(v, in.T, in.qinv) : exp2(((double)v - (double)in.m) * in.cd);
 }
 
 __device__ inline void unpack_raw(const Bf16::Raw& r, float v[8]) { Bf16::unpack(r, v); }
@@ -1221,7 +1347,7 @@ __device__ __noinline__ MergeOut wave_merge(MergeIn in, LDS_AS uint32_t* skey, L
   in.top_p = uni(in.top_p);
   in.m = uni(in.m);
   in.qinv = uni(in.qinv);
-  in.c = uni(in.c);
+  in.cd = uni(in.cd);
   in.T = uni(in.T);
   MergeOut out;
   out.ok = 0;
@@ -1546,7 +1672,8 @@ struct GeneralArgs {
   const void* row;
   int V;
   bool bf16, draft;
-  float m, c, invT;
+  float m;
+  float T;        // temperature
   float qinv;     // draft rows: 1 / qs
   bool temper;
   int k;
@@ -1570,10 +1697,11 @@ __device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hi
   g.bf16 = uni((int)g.bf16);
   g.draft = uni((int)g.draft);
   g.m = uni(g.m);
-  g.c = uni(g.c);
-  g.invT = uni(g.invT);
+  g.T = uni(g.T);
   g.qinv = uni(g.qinv);
   g.temper = uni((int)g.temper);
+  const Scale2 c = uni_s2(target_scale(g.T));
+  const DraftW dw = uni_dw(draft_w(g.T));
   g.k = uni(g.k);
   g.kact = uni((int)g.kact);
   g.top_p = uni(g.top_p);
@@ -1585,8 +1713,7 @@ __device__ __noinline__ Filtered general_filter(GeneralArgs g, LDS_AS double* hi
   ka.V = g.V;
   ka.bf16 = g.bf16;
   auto weight = [&](float v) -> double {
-    return g.draft ? (g.temper ? (double)temper_q32(v, g.invT, g.qinv) : (double)v)
-                   : (double)fast_exp2((v - g.m) * g.c);
+    return g.draft ? (g.temper ? temper_w64(v, dw, g.qinv) : (double)v) : (double)mass_p32(v, g.m, c);
   };
   auto value = [&](int x) -> float {
     const float v = row_value(ka, x);
@@ -1677,10 +1804,13 @@ struct StochState {
   ChunkState ps, qs;
 };
 
-// QM: 0 no draft row, 1 draft row at T = 1, 2 draft row at T != 1.
+// QM: 0 no draft row, 1 draft row at T = 1, 2 draft row at T != 1, 3 draft row at
+// 1/T above kPreciseInvT (without top-k: the weights that carry mass in fp64, a
+// code path of its own so that the others keep their registers).
 template <class LT, bool VEC, int QM, bool CAND, int TOK>
-__device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, const float* qrow, int V, float c, float invT, int k,
-                                  RowShared<LT>& sh, StochState& st, const Toks& tk) {
+__device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, const float* qrow, int V, const Scale2& c,
+                                                  const DraftW& dw, int k, RowShared<LT>& sh, StochState& st,
+                                                  const Toks& tk) {
   typedef typename LT::Raw LR;
   const int tid = threadIdx.x, w = tid >> 6;
   const int nsteps = (V + kStep - 1) / kStep;
@@ -1698,12 +1828,12 @@ __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, co
       st.lbad = max(st.lbad, max8u(a));
     } else {
       if (cm > st.m) {
-        st.z *= (double)fast_exp2((st.m - cm) * c);
+        st.z *= (double)mass_p32(st.m, cm, c);
         st.m = cm;
       }
       float e[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) e[t] = fast_exp2((v[t] - st.m) * c);
+      for (int t = 0; t < 8; ++t) e[t] = mass_p32(v[t], st.m, c);
       st.z += (double)(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
     }
     uint32_t qmax = 0u;
@@ -1711,23 +1841,27 @@ __device__ __forceinline__ void stream_stochastic(const typename LT::T* lrow, co
       uint32_t u[8];
       F32::bits(qr, u);
       qmax = max8u(u);
-      if (QM == 2 && !CAND && qmax > st.qbad) {
+      if (QM >= 2 && !CAND && qmax > st.qbad) {
         const int e0 = scale_e(st.qbad), e1 = scale_e(qmax);
         if (e1 > e0) {
           // a q in a higher binade: move the running sum to the new scale
-          if (st.r != 0.0) st.r *= (double)fast_exp2((float)(e0 - e1) * invT);
+          if (st.r != 0.0) st.r *= scale_step32(e0, e1, dw.invT);
           st.qinv = scale_inv(e1);
         }
       }
       st.qbad = max(st.qbad, qmax);
       if (!CAND) {
         float r[8];
+        double hi = 0.0;  // weights formed in fp64 (QM 3)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const float qv = __uint_as_float(u[t]);
-          r[t] = (QM == 1) ? qv : temper_q32(qv, invT, st.qinv);
+          if (QM == 1) r[t] = qv;
+          else if (QM == 2) r[t] = fast_exp2(smul(fast_log2(qv * st.qinv), dw.invT));
+          else r[t] = temper_w32(qv, dw, st.qinv, hi);
         }
         st.r += (double)(((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7])));
+        if (QM == 3) st.r += hi;
       }
     }
     if (CAND) {
@@ -1905,9 +2039,9 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   const bool req_q = rq.q0 >= 0;  // the request carries draft rows
   const bool has_q = req_q && draft_pos;
   const float* qrow = has_q ? a.q + ((size_t)rq.q0 + j) * (size_t)V : nullptr;
-  const float T = rq.T;
-  const float c = kLog2e / T;
-  const float invT = 1.f / T;
+  const float T = uni(rq.T);
+  const Scale2 c = uni_s2(target_scale(T));
+  const DraftW dw = uni_dw(draft_w(T));
   const bool temper = T != 1.f;
   const bool filt = rq.kact || rq.pact;
   const bool cand = rq.kact && rq.k <= kKFast;
@@ -1934,11 +2068,11 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   st.lbad = 0u;
   st.ps = ChunkState{0, 0u, 0};
   st.qs = ChunkState{0, 0u, 0};
-  const int qm = has_q ? (temper ? 2 : 1) : 0;
+  const int qm = has_q ? (temper ? ((dw.precise && !cand) ? 3 : 2) : 1) : 0;
   if (cand) {
-    if (qm == 0) stream_stochastic<LT, VEC, 0, true, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
-    else if (qm == 1) stream_stochastic<LT, VEC, 1, true, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
-    else stream_stochastic<LT, VEC, 2, true, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
+    if (qm == 0) stream_stochastic<LT, VEC, 0, true, TOK>(lrow, qrow, V, c, dw, rq.k, sh, st, tk);
+    else if (qm == 1) stream_stochastic<LT, VEC, 1, true, TOK>(lrow, qrow, V, c, dw, rq.k, sh, st, tk);
+    else stream_stochastic<LT, VEC, 2, true, TOK>(lrow, qrow, V, c, dw, rq.k, sh, st, tk);
     // each wave cuts its own buffers down to its k-th largest chunk key and
     // copies the tokens at or above that threshold into its segment
     __builtin_amdgcn_s_setprio(2);
@@ -1958,9 +2092,10 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       if (lane == 0) sh.scnt[1][wave] = n;
     }
   } else {
-    if (qm == 0) stream_stochastic<LT, VEC, 0, false, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
-    else if (qm == 1) stream_stochastic<LT, VEC, 1, false, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
-    else stream_stochastic<LT, VEC, 2, false, TOK>(lrow, qrow, V, c, invT, rq.k, sh, st, tk);
+    if (qm == 0) stream_stochastic<LT, VEC, 0, false, TOK>(lrow, qrow, V, c, dw, rq.k, sh, st, tk);
+    else if (qm == 1) stream_stochastic<LT, VEC, 1, false, TOK>(lrow, qrow, V, c, dw, rq.k, sh, st, tk);
+    else if (qm == 2) stream_stochastic<LT, VEC, 2, false, TOK>(lrow, qrow, V, c, dw, rq.k, sh, st, tk);
+    else stream_stochastic<LT, VEC, 3, false, TOK>(lrow, qrow, V, c, dw, rq.k, sh, st, tk);
   }
 
   // the rest of the row is short serial work that holds this workgroup's
@@ -1973,7 +2108,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
     const uint32_t lbw = cand ? wave_max_u32(st.lbad) : 0u;
     double rt = st.r;
     if (has_q && !cand && temper && rt != 0.0 && scale_e(st.qbad) != scale_e(qbw))
-      rt *= scale_step(scale_e(st.qbad), scale_e(qbw), invT);
+      rt *= scale_step(scale_e(st.qbad), scale_e(qbw), dw.invT);
     const double rw = (has_q && !cand) ? wave_sum_f64(rt) : 0.0;
     if (lane == 0) {
       sh.xm[wave] = mw;
@@ -1994,7 +2129,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   for (int w = 0; w < kWaves; ++w) {
     xr[w] = sh.xr[w];
     if (has_q && !cand && temper && xr[w] != 0.0 && scale_e(sh.xqb[w]) != scale_e(qb))
-      xr[w] *= scale_step(scale_e(sh.xqb[w]), scale_e(qb), invT);
+      xr[w] *= scale_step(scale_e(sh.xqb[w]), scale_e(qb), dw.invT);
   }
   const double R = (xr[0] + xr[1]) + (xr[2] + xr[3]);
   const uint32_t lb = max(max(sh.xlb[0], sh.xlb[1]), max(sh.xlb[2], sh.xlb[3]));
@@ -2037,7 +2172,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
   // without top-k: Z = sum over the row; with it the kept mass is found below
   double Z = 1.0;
   if (!cand) {
-    const double zw = wave_sum_f64(st.z * exp2(((double)st.m - (double)m) * (double)c));
+    const double zw = wave_sum_f64(st.z * exp2(((double)st.m - (double)m) * c.d));
     if (lane == 0) sh.xz[wave] = zw;
     __syncthreads();
     Z = (sh.xz[0] + sh.xz[1]) + (sh.xz[2] + sh.xz[3]);
@@ -2069,7 +2204,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
         in.pact = rq.pact;
         in.draft = d;
         in.m = m;
-        in.c = c;
+        in.cd = c.d;
         in.T = T;
         in.qinv = qinv;
         MergeOut mo;
@@ -2104,8 +2239,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       g.bf16 = sizeof(ET) == 2;
       g.draft = false;
       g.m = m;
-      g.c = c;
-      g.invT = invT;
+      g.T = T;
       g.qinv = 1.f;
       g.temper = temper;
       g.k = rq.k;
@@ -2126,8 +2260,7 @@ __device__ __forceinline__ void stochastic_row(const Args& a, const Req& rq, int
       g.bf16 = false;
       g.draft = true;
       g.m = m;
-      g.c = c;
-      g.invT = invT;
+      g.T = T;
       g.qinv = qinv;
       g.temper = temper;
       g.k = rq.k;
@@ -2219,6 +2352,7 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
   const int tid = threadIdx.x, wave = tid >> 6;
   constexpr int kPer = 4;  // requests per thread and round
   if (tid < 2) s_base[tid] = 0;
+  if (tid == 0) *a.nfault = 0u;  // the draw pass counts this call's faulted requests
   __syncthreads();
   for (int r0 = 0; r0 < a.N; r0 += kBlock * kPer) {
     int gam[kPer], nl[kPer], gq[kPer], id0[kPer];
@@ -2429,26 +2563,69 @@ __device__ inline double wave_incl_scan_f64(double v) {
   return v;
 }
 
-// Draw weights w (mode 0: p'; 1: max(0, p' - q'); 2: p' with the draft
-// token removed) and p' of one lane's 8 tokens; tokens past the row end read
-// as -inf logits and zero probabilities, so both are zero there.
-__device__ inline void draw_weights(const float lv[8], const float qv[8], int base, int mode, float m, float c,
-                                    float invZ, float cut_p, float cut_q, float invR, float invT, float qinv,
-                                    bool temper, int yA,
-                                    float w[8], float p[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    p[e] = (lv[e] >= cut_p) ? fast_exp2((lv[e] - m) * c) * invZ : 0.f;
-    float x = p[e];
-    if (mode == 1) {
-      const float r = temper ? temper_q32(qv[e], invT, qinv) : qv[e];
-      const float q = (qv[e] >= cut_q) ? r * invR : 0.f;
-      x = __builtin_fmaxf(p[e] - q, 0.f);
-    } else if (mode == 2) {
-      x = (base + e == yA) ? 0.f : p[e];
+// What the draw pass needs to weigh row A's tokens.
+struct DrawW {
+  float m;          // max logit of the row
+  float cut_p;      // target token kept iff logit >= cut_p
+  float cut_q;      // draft token kept iff q >= cut_q
+  float qinv;       // 1 / qs of the tempered draft weights
+  float invZf;      // 1 / kept target mass, fp32
+  float invRf;      // 1 / kept draft mass, fp32
+  Scale2 c;         // log2(e) / T
+  DraftW dw;        // tempered draft weights
+  double invZ;      // 1 / kept target mass, fp64 (weights formed in fp64)
+  double invR;      // 1 / kept draft mass, fp64
+  bool temper;      // T != 1
+  int mode;         // 0: p'; 1: max(0, p' - q'); 2: p' with the draft token removed
+  int yA;           // mode 2: the draft token
+};
+
+// wave-uniform copies (scalar registers) of the draw parameters
+__device__ inline DrawW uni_draw(DrawW d) {
+  d.m = uni(d.m);
+  d.cut_p = uni(d.cut_p);
+  d.cut_q = uni(d.cut_q);
+  d.qinv = uni(d.qinv);
+  d.invZf = uni(d.invZf);
+  d.invRf = uni(d.invRf);
+  d.c = uni_s2(d.c);
+  d.dw = uni_dw(d.dw);
+  d.invZ = uni(d.invZ);
+  d.invR = uni(d.invR);
+  d.temper = uni((int)d.temper);
+  d.mode = uni(d.mode);
+  d.yA = uni(d.yA);
+  return d;
+}
+
+// Draw weight w and p' of token x (lv its logit, qv its draft probability);
+// tokens past the row end read as -inf logits and zero probabilities, so both
+// are zero there.  The exponents are formed as in the row pass's sums, so
+// that each p' is its weight over the very sum that weight entered.
+// PRECISE (a tempered residual at 1/T above kPreciseInvT): the draft weights
+// that carry mass are formed in fp64 as in the row pass, then normalised and
+// subtracted in fp64 (inline: the draw pass runs that case one step at a
+// time, with registers to spare).
+template <bool PRECISE>
+__device__ inline float draw_weight(float lv, float qv, int x, const DrawW& d, float& p) {
+  const float e = (lv >= d.cut_p) ? mass_p32(lv, d.m, d.c) : 0.f;
+  p = e * d.invZf;
+  if (d.mode == 1) {
+    float r = qv;
+    if (d.temper) {
+      const float rr = qv * d.qinv;
+      const float xq = smul(fast_log2(rr), d.dw.invT);
+      if (PRECISE && xq > d.dw.thr && qv >= d.cut_q) {
+        const double w = (double)e * d.invZ - precise_weight(rr, d.dw.invT.d) * d.invR;
+        return w > 0.0 ? (float)w : 0.f;
+      }
+      r = fast_exp2(xq);
     }
-    w[e] = x;
+    const float q = (qv >= d.cut_q) ? r * d.invRf : 0.f;
+    return __builtin_fmaxf(p - q, 0.f);
   }
+  if (d.mode == 2) return x == d.yA ? 0.f : p;
+  return p;
 }
 
 // Request i's outputs from its record: the accepted drafts before the first
@@ -2463,6 +2640,7 @@ __device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, i
   if (fault) {
     for (int t = tid; t <= G; t += kBlock) out[t] = -1;
     if (tid == 0) {
+      __hip_atomic_fetch_add(a.nfault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       a.out_num[i] = -1;
       if (a.d_fault) a.d_fault[i] = (int)fault;
       if (a.d_resid) a.d_resid[i] = NAN;
@@ -2538,11 +2716,21 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   const size_t row = (size_t)i * (G + 1) + A;  // the row record
   const RowStats sa = a.stats[row];
   const float T = a.temperature ? a.temperature[i] : 1.f;
-  const float c = kLog2e / T, invT = 1.f / T;
-  const bool temper = T != 1.f;
-  const float invZ = (float)(1.0 / sa.z);
-  const float invR = (mode == 1) ? (float)(1.0 / sa.r) : 0.f;
-  const float qinv = (mode == 1 && temper) ? sa.qinv : 1.f;
+  DrawW dwt;
+  dwt.m = sa.m;
+  dwt.cut_p = sa.cut_p;
+  dwt.cut_q = sa.cut_q;
+  dwt.temper = T != 1.f;
+  dwt.qinv = (mode == 1 && dwt.temper) ? sa.qinv : 1.f;
+  dwt.c = target_scale(T);
+  dwt.dw = draft_w(T);
+  dwt.invZ = 1.0 / sa.z;
+  dwt.invR = (mode == 1) ? 1.0 / sa.r : 0.0;
+  dwt.invZf = (float)dwt.invZ;
+  dwt.invRf = (float)dwt.invR;
+  dwt.mode = mode;
+  dwt.yA = yA;
+  dwt = uni_draw(dwt);
   // (row A's index was checked by the row pass: a bad one faults the request)
   const size_t trow = !a.bidx ? (size_t)rr.tgt0 + A : (size_t)(A < gamma ? a.tidx[(size_t)rr.id0 + A] : a.bidx[i]);
   const ET* lrow = reinterpret_cast<const ET*>(a.logits) + trow * (size_t)V;
@@ -2570,6 +2758,52 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   }
   const Toks tk = toks((const LDS_AS int*)s_ban, nban, (const LDS_AS int*)s_pid, (const LDS_AS float*)s_pd,
                        (LDS_AS float*)s_stage + (threadIdx.x >> 6) * 512, npen, theta);
+  // the block sums of one lane's step u (raw values lr, qr) into s_blk
+  auto block_sums = [&](LR& l, F32::Raw& q, int u, BanWalk& bw, PenWalk& pw, auto precise) {
+    const int base = (s0 + u) * kStep + tid * kCh;
+    if (TOK == 2) pen_walk(pw, tk, (s0 + u) * kStep + wave * 512, l, q, mode == 1);
+    if (TOK) {
+      const uint32_t m = ban_mask(bw, tk.ban, (s0 + u) * kStep + wave * 512);
+      if (m) {
+        ban_logits(l, m);
+        if (mode == 1) ban_apply(q, m, 0u);
+      }
+    }
+    float lv[8], qv[8];
+    LT::unpack(l, lv);
+    F32::unpack(q, qv);
+    double sw = 0.0, sp = 0.0;
+    uint32_t lw = 0u, lp = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float pe;
+      const float we = draw_weight<decltype(precise)::value>(lv[e], qv[e], base + e, dwt, pe);
+      sw += (double)we;
+      sp += (double)pe;
+      if (we > 0.f) lw = (uint32_t)(base + e + 1);
+      if (pe > 0.f) lp = (uint32_t)(base + e + 1);
+    }
+    DrawSum d;
+    d.sw = wave_sum_f64(sw);
+    d.sp = wave_sum_f64(sp);
+    d.lastw = (int)wave_max_u32(lw);
+    d.lastp = (int)wave_max_u32(lp);
+    d.pad[0] = d.pad[1] = 0;
+    if (lane == 0) __builtin_memcpy((DrawSum*)&s_blk[u * kWaves + wave], &d, sizeof(DrawSum));
+  };
+  BanWalk bw;
+  PenWalk pw;
+  if (TOK) bw = ban_start(tk.ban, tk.nban);
+  if (TOK == 2) pw = pen_start(tk.npen);
+  if (mode == 1 && dwt.temper && dwt.dw.precise) {
+    // tempered residual at large 1/T: one step at a time
+    for (int u = 0; u < cnt; ++u) {
+      const int base = (s0 + u) * kStep + tid * kCh;
+      LR l = load_logits<LT, VEC>(lrow, base, V);
+      F32::Raw q = load_probs<VEC>(qrow, base, V);
+      block_sums(l, q, u, bw, pw, std::true_type{});
+    }
+  } else {
   // all of this workgroup's loads first, then the sums (block sums go to LDS:
   // a global store here would count against the counter the loads wait on)
   LR lr[kDrawSpan];
@@ -2582,42 +2816,11 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
       qr[u] = (mode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
     }
   }
-  BanWalk bw;
-  PenWalk pw;
-  if (TOK) bw = ban_start(tk.ban, tk.nban);
-  if (TOK == 2) pw = pen_start(tk.npen);
 #pragma unroll
   for (int u = 0; u < kDrawSpan; ++u) {
     if (u >= cnt) break;
-    const int base = (s0 + u) * kStep + tid * kCh;
-    if (TOK == 2) pen_walk(pw, tk, (s0 + u) * kStep + wave * 512, lr[u], qr[u], mode == 1);
-    if (TOK) {
-      const uint32_t m = ban_mask(bw, tk.ban, (s0 + u) * kStep + wave * 512);
-      if (m) {
-        ban_logits(lr[u], m);
-        if (mode == 1) ban_apply(qr[u], m, 0u);
-      }
-    }
-    float lv[8], qv[8], w[8], pw[8];
-    LT::unpack(lr[u], lv);
-    F32::unpack(qr[u], qv);
-    draw_weights(lv, qv, base, mode, sa.m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, qinv, temper, yA, w, pw);
-    double sw = 0.0, sp = 0.0;
-    uint32_t lw = 0u, lp = 0u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sw += (double)w[e];
-      sp += (double)pw[e];
-      if (w[e] > 0.f) lw = (uint32_t)(base + e + 1);
-      if (pw[e] > 0.f) lp = (uint32_t)(base + e + 1);
-    }
-    DrawSum d;
-    d.sw = wave_sum_f64(sw);
-    d.sp = wave_sum_f64(sp);
-    d.lastw = (int)wave_max_u32(lw);
-    d.lastp = (int)wave_max_u32(lp);
-    d.pad[0] = d.pad[1] = 0;
-    if (lane == 0) __builtin_memcpy((DrawSum*)&s_blk[u * kWaves + wave], &d, sizeof(DrawSum));
+    block_sums(lr[u], qr[u], u, bw, pw, std::false_type{});
+  }
   }
   __syncthreads();
   if (tid < cnt * kWaves) {
@@ -2700,7 +2903,7 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
     z = (int)(usep ? lastp : lastw) - 1;
   } else {
     const int base = (rstar / kWaves) * kStep + (rstar % kWaves) * 512 + lane * kCh;
-    float lv[8], qv[8], w[8], pw[8];
+    float lv[8], qv[8], w[8];
     LR lb = load_logits<LT, VEC>(lrow, base, V);
     F32::Raw qb = (dmode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
     if (TOK == 2 && tk.npen) {
@@ -2728,7 +2931,14 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
     else
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[e] = 0.f;
-    draw_weights(lv, qv, base, dmode, sa.m, c, invZ, sa.cut_p, sa.cut_q, invR, invT, qinv, temper, yA, w, pw);
+    DrawW dd = dwt;
+    dd.mode = dmode;
+    const bool prec = dd.mode == 1 && dd.temper && dd.dw.precise;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float pe;
+      w[e] = prec ? draw_weight<true>(lv[e], qv[e], base + e, dd, pe) : draw_weight<false>(lv[e], qv[e], base + e, dd, pe);
+    }
     double ls = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ls += (double)w[e];
@@ -2799,6 +3009,8 @@ __global__ __launch_bounds__(kBlock) void rollback_kernel(RollbackArgs r) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// the workspace starts with this call's fault count (one 256-byte block)
+constexpr size_t kHeadBytes = 256;
 size_t stats_bytes(int N, int G) { return align_up((size_t)N * (G + 1) * sizeof(RowStats), 256); }
 size_t done_bytes(int N) { return align_up((size_t)N * sizeof(unsigned int), 256); }
 size_t rec_bytes(int N) { return align_up((size_t)N * sizeof(ReqRec), 256); }
@@ -2808,13 +3020,6 @@ size_t dsum_bytes(int N, int V) {
 }
 size_t draw_parts(int V) { return ((size_t)(V + kStep - 1) / kStep + kDrawSpan - 1) / kDrawSpan; }
 size_t dtot_bytes(int N, int V) { return align_up((size_t)N * draw_parts(V) * sizeof(DrawSum), 256); }
-
-struct DeviceBuffer {
-  void* ptr = nullptr;
-  size_t bytes = 0;
-};
-std::mutex g_ws_mutex;
-std::vector<DeviceBuffer> g_ws;  // one per device, grown on demand, kept until exit
 
 struct Events {
   hipEvent_t start, mid, end;
@@ -2872,22 +3077,7 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   if (!logits || !u_sample || !out_tokens || !out_num) return SPEC_VERIFY_ERR_NULL;
   if ((flat ? lay.T : G) > 0 && (!ids || !u_accept)) return SPEC_VERIFY_ERR_NULL;
   const size_t need = spec_verify_workspace_size(N, G, V);
-  if (!workspace) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return SPEC_VERIFY_ERR_HIP;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-    DeviceBuffer& b = g_ws[dev];
-    if (b.bytes < need) {
-      void* p = nullptr;
-      // a smaller earlier buffer may still be read by queued work: it is kept
-      if (hipMalloc(&p, need) != hipSuccess) return SPEC_VERIFY_ERR_HIP;
-      b.ptr = p;
-      b.bytes = need;
-    }
-    workspace = b.ptr;
-    workspace_bytes = b.bytes;
-  }
+  if (!workspace) return SPEC_VERIFY_ERR_NULL;
   if (workspace_bytes < need) return SPEC_VERIFY_ERR_WORKSPACE;
 
   Args a;
@@ -2909,8 +3099,9 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   a.d_resid = resid;
   a.d_fault = fault;
   char* ws = reinterpret_cast<char*>(workspace);
-  a.stats = reinterpret_cast<RowStats*>(ws);
-  size_t off = stats_bytes(N, G);
+  a.nfault = reinterpret_cast<unsigned int*>(ws);
+  a.stats = reinterpret_cast<RowStats*>(ws + kHeadBytes);
+  size_t off = kHeadBytes + stats_bytes(N, G);
   a.rec = reinterpret_cast<ReqRec*>(ws + off);
   off += rec_bytes(N);
   a.ddone = reinterpret_cast<unsigned int*>(ws + off);
@@ -2968,7 +3159,7 @@ extern "C" {
 
 size_t spec_verify_workspace_size(int N, int gmax, int V) {
   if (N <= 0 || gmax < 0 || V <= 0) return 256;
-  return stats_bytes(N, gmax) + rec_bytes(N) + done_bytes(N) + dsum_bytes(N, V) + dtot_bytes(N, V) +
+  return kHeadBytes + stats_bytes(N, gmax) + rec_bytes(N) + done_bytes(N) + dsum_bytes(N, V) + dtot_bytes(N, V) +
          plan_bytes(N, gmax);
 }
 
@@ -3098,6 +3289,17 @@ int spec_verify_rollback(int N, int gmax, const int32_t* cu_num_draft_tokens, co
   hipLaunchKernelGGL(rollback_kernel, dim3((unsigned)((N + kBlock - 1) / kBlock)), dim3(kBlock), 0,
                      reinterpret_cast<hipStream_t>(stream), r);
   return hipGetLastError() == hipSuccess ? SPEC_VERIFY_OK : SPEC_VERIFY_ERR_HIP;
+}
+
+int spec_verify_device_errors(const void* workspace, size_t workspace_bytes, void* stream, int32_t* count) {
+  if (!workspace || !count) return SPEC_VERIFY_ERR_NULL;
+  if (workspace_bytes < kHeadBytes) return SPEC_VERIFY_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned int n = 0u;
+  if (hipMemcpyAsync(&n, workspace, sizeof(n), hipMemcpyDeviceToHost, s) != hipSuccess) return SPEC_VERIFY_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return SPEC_VERIFY_ERR_HIP;
+  *count = (int32_t)n;
+  return SPEC_VERIFY_OK;
 }
 
 const char* spec_verify_status_string(int status) {

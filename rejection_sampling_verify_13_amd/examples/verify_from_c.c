@@ -71,12 +71,18 @@ int main(void) {
     fprintf(stderr, "spec_verify: %s\n", spec_verify_status_string(rc));
     return 2;
   }
-  CHECK(hipDeviceSynchronize());
+  /* waits for the call on its stream and reads how many requests faulted */
+  int32_t faults = -1;
+  const int rf = spec_verify_device_errors(d_ws, ws, NULL, &faults);
+  if (rf != SPEC_VERIFY_OK) {
+    fprintf(stderr, "spec_verify_device_errors: %s\n", spec_verify_status_string(rf));
+    return 2;
+  }
   int32_t out[2], num[1];
   CHECK(hipMemcpy(out, d_out, sizeof out, hipMemcpyDeviceToHost));
   CHECK(hipMemcpy(num, d_num, sizeof num, hipMemcpyDeviceToHost));
-  printf("tokens [%d, %d], accepted %d\n", out[0], out[1], num[0]);
+  printf("tokens [%d, %d], accepted %d, faulted requests %d\n", out[0], out[1], num[0], faults);
   hipFree(d_ids); hipFree(d_q); hipFree(d_l); hipFree(d_t); hipFree(d_k); hipFree(d_p);
   hipFree(d_ua); hipFree(d_us); hipFree(d_out); hipFree(d_num); hipFree(d_ws);
-  return (out[0] == 0 && out[1] == -1 && num[0] == 0) ? 0 : 1;
+  return (out[0] == 0 && out[1] == -1 && num[0] == 0 && faults == 0) ? 0 : 1;
 }

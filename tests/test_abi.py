@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_verify_diag", "spec_verify_workspace_size", "spec_verify_status_string",
               "spec_verify_version", "spec_verify_flat", "spec_verify_flat_timed", "spec_verify_rollback",
-              "spec_verify_flat_synthetic", "spec_verify_flat_ex"):
+              "spec_verify_flat_synthetic", "spec_verify_flat_ex", "spec_verify_device_errors"):
         assert n in names
 
 
@@ -74,6 +74,19 @@ def test_host_validation(lib):
     assert _call(lib, N=(1 << 24) // 2 - 1, G=0, V=16, logits=0) == 1  # just inside: the next check fires
     small = ctypes.c_void_p(0x1000)
     assert _call(lib, ws=small, wsb=16) == 4
+    # the workspace is the caller's: a NULL one is refused, nothing is allocated
+    assert _call(lib) == 1
+    assert _call(lib, N=0) == 0
+
+
+def test_device_errors_host_validation(lib):
+    n = ctypes.c_int32(7)
+    ws = ctypes.c_void_p(0x1000)
+    assert lib.spec_verify_device_errors(None, 4096, None, ctypes.byref(n)) == 1
+    assert lib.spec_verify_device_errors(ws, 4096, None, None) == 1
+    assert lib.spec_verify_device_errors(ws, 255, None, ctypes.byref(n)) == 4
+    assert n.value == 7  # untouched when refused
+    assert lib.spec_verify_workspace_size(0, 0, 1) >= 256
 
 
 def _flat(lib, N=2, G=3, V=16, T=4, cu=1, ids=1, logits=1, ua=1, us=1, out=1, num=1):

@@ -2,7 +2,8 @@
 verify_from_c.c, built next to the library by the package build): the
 two-token worked example of the zwjcode.cn page, section 05, through
 spec_verify with device buffers from the HIP runtime, must commit [A] = [0, -1]
-with no draft accepted."""
+with no draft accepted, and spec_verify_device_errors must report no faulted
+request."""
 import os
 import subprocess
 
@@ -23,4 +24,4 @@ def test_worked_example_from_c():
     r = subprocess.run([EXE], capture_output=True, text=True, timeout=60)
     log("[c] %s" % r.stdout.strip())
     assert r.returncode == 0, r.stdout + r.stderr
-    assert r.stdout.strip() == "tokens [0, -1], accepted 0"
+    assert r.stdout.strip() == "tokens [0, -1], accepted 0, faulted requests 0"

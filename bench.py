@@ -83,6 +83,41 @@ def traffic_from_profile(digest, workload):
     return int(m.group(1))
 
 
+def host_threads():
+    """Threads for the host-side work (input generation, the CPU oracle): the
+    CPUs this process may run on, limited by OMP_NUM_THREADS when that is set
+    (the share of a shared host that one GPU's job is given)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    lim = os.environ.get("OMP_NUM_THREADS", "")
+    if lim.isdigit() and int(lim) > 0:
+        n = min(n, int(lim))
+    return max(1, n)
+
+
+def acceptance_stats(num_accepted, gamma, temperature):
+    """What the zwjcode.cn page, section 12, asks to record with the
+    throughput: how far each request advanced (the distribution of the
+    rejection position A_i, i.e. of the accepted draft count), the mean
+    accepted length and committed tokens per target step, and the acceptance
+    rate over the drafts proposed."""
+    import numpy as np
+    A = np.asarray(num_accepted, np.int64)
+    gam = np.asarray(gamma, np.int64)
+    ok = A >= 0
+    G = int(gam.max()) if len(gam) else 0
+    hist = np.bincount(A[ok], minlength=G + 1)[: G + 1]
+    all_acc = ok & (A == gam)
+    return {
+        "requests": int(len(A)), "faulted": int((~ok).sum()),
+        "accepted_count_histogram": [int(x) for x in hist],
+        "all_drafts_accepted": int(all_acc.sum()),
+        "mean_accepted_length": round(float(A[ok].mean()), 4) if ok.any() else None,
+        "mean_committed_per_step": round(float((A[ok] + 1).mean()), 4) if ok.any() else None,
+        "acceptance_rate": round(float(A[ok].sum() / max(1, gam[ok].sum())), 4),
+        "greedy_requests": int((np.asarray(temperature) == 0).sum()),
+    }
+
+
 def cpu_baseline(spec, n_req, threads, min_seconds=10.0):
     """The fp64 C oracle timed on the host over the first n_req requests of
     the same workload, repeated until about min_seconds have passed."""
@@ -102,6 +137,7 @@ def cpu_baseline(spec, n_req, threads, min_seconds=10.0):
         if dt >= min_seconds:
             break
     return dict(value=pos * passes / dt, unit="positions/s", cores=threads, kind="oracle",
+                host_cpus=os.cpu_count(), threads=threads,
                 sample="first %d of %d requests of the same workload (%d verified positions) x %d passes, "
                        "fp64 C oracle, %d threads over requests, %.1f s wall" % (n_req, spec.N, pos, passes, threads, dt))
 
@@ -127,9 +163,10 @@ def main():
     ap.add_argument("--penalties", type=int, default=0,
                     help="repetition penalties over a seeded context of this many tokens per request (flattened "
                          "layout; presence 0.5, frequency 0.25, repetition 1.2 on greedy and draft-free requests)")
-    ap.add_argument("--time-every", type=int, default=4,
-                    help="time the row kernel with HIP events on every Nth timed step (each event is a packet in "
-                         "the stream, about 2 us per step; the wall-clock throughput covers every step)")
+    ap.add_argument("--time-every", type=int, default=0,
+                    help="time the row kernel with HIP events on every Nth timed step (the events travel in the "
+                         "row kernel's own dispatch; the wall-clock throughput covers every step); default: every "
+                         "step when --steps is below 100, else every 4th")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -149,7 +186,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     spec = W.config(args.config)
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_threads()
     print("[bench] generating workload %d (N=%d gmax=%d V=%d)" % (args.config, spec.N, spec.gmax, spec.V),
           file=sys.stderr, flush=True)
     batch = W.generate(spec, threads=threads)
@@ -242,7 +279,7 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    every = max(1, args.time_every)
+    every = args.time_every if args.time_every > 0 else (1 if args.steps < 100 else 4)
     timed = list(range(0, K, every))
     # start and end of the row kernel (the third event of the entry point, after the draw pass, is not used)
     evs = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), None) for _ in parts]
@@ -261,6 +298,9 @@ def main():
     row_ms = np.array([sum(e[0].elapsed_time(e[1]) for e in evs[k]) for k in timed])
     ms_per_step = wall * 1e3 / K
     value = positions * K / wall
+    # every input set holds the same batch: the outputs of the first one stand for all steps
+    acc = acceptance_stats(np.concatenate([d["out_n"].cpu().numpy() for d in sets[0]]), batch["gamma"],
+                           batch["temperature"])
 
     digest = source_digest()
     workload_name = "cfg%d" % args.config
@@ -272,7 +312,10 @@ def main():
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel="row_kernel", kernel_avg_us=round(row_avg_s * 1e6, 2),
                     kernel_us_p10_p50_p90=row_pct, input_sets_rotated=n_sets, launches_timed=len(timed),
-                    algorithmic_bytes_per_launch=B_alg)
+                    algorithmic_bytes_per_launch=B_alg,
+                    fetch_gbps=None if traffic is None else round(traffic / row_avg_s / 1e9, 1),
+                    scope="the row kernel alone (the dominant kernel); the whole verify step (plan, row and "
+                          "draw kernels) is hbm_gbps_step / hbm_frac_step")
 
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
@@ -318,6 +361,8 @@ def main():
         "hbm_gbps_step": round(B_alg / (ms_per_step * 1e-3) / 1e9, 1),
         "hbm_frac_step": round(B_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "rows_per_s": round(rows * K / wall, 1),
+        "bytes_per_verified_position": round(B_alg / max(1, positions), 1),
+        "acceptance": acc,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source": digest,

@@ -65,6 +65,7 @@ extern "C" {
 #define SPEC_VERIFY_ERR_DTYPE 3     /* unknown logits_dtype                              */
 #define SPEC_VERIFY_ERR_WORKSPACE 4 /* workspace_bytes below spec_verify_workspace_size  */
 #define SPEC_VERIFY_ERR_HIP 5       /* a HIP runtime call failed (launch, copy, wait)      */
+#define SPEC_VERIFY_ERR_SCRATCH 6   /* spec_verify_static: sizes need more workspace than its scratch */
 
 /* fault bits of the diagnostic fault output */
 #define SPEC_VERIFY_FAULT_DRAFT_ID 1
@@ -347,6 +348,33 @@ int spec_verify_rollback(int N, int gmax, const int32_t *cu_num_draft_tokens,
  * from whatever the memory held.
  */
 int spec_verify_device_errors(const void *workspace, size_t workspace_bytes, void *stream, int32_t *count);
+
+/*
+ * spec_verify for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc.  The
+ * arguments and the method are those of spec_verify, without the workspace:
+ * the library's own scratch array in device memory (a file-scope array of
+ * spec_verify_static_scratch_bytes() = 16 MiB, 256-byte aligned; each GPU the
+ * library runs on holds its own copy until the process ends) serves as the
+ * workspace.  The call allocates nothing and calls no allocating routine; its
+ * first call on a device looks up that device's address of the array, with
+ * the device current.  Sizes whose spec_verify_workspace_size exceeds the
+ * scratch are refused with SPEC_VERIFY_ERR_SCRATCH (N = 1024, gmax = 8,
+ * V = 128256 needs under 10 MiB).  Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (different streams, or host threads
+ * without ordering) race and their results are undefined; calls ordered on
+ * one stream are safe, since each call resets what it reads from the array.
+ * Faults show as out_num_accepted = -1 (spec_verify_device_errors needs the
+ * caller's workspace and does not apply).
+ */
+int spec_verify_static(int N, int gmax, int V, const int32_t *draft_ids, const float *draft_probs,
+                       const void *target_logits, int logits_dtype, const float *temperature,
+                       const int32_t *top_k, const float *top_p, const float *u_accept,
+                       const float *u_sample, int32_t *out_tokens, int32_t *out_num_accepted,
+                       void *stream);
+
+/* Bytes of the scratch array spec_verify_static uses as its workspace. */
+size_t spec_verify_static_scratch_bytes(void);
 
 /* Human-readable text of a return code (static storage). */
 const char *spec_verify_status_string(int status);

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 F32 = 0
 BF16 = 1
-STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "bad dtype", 4: "workspace too small", 5: "HIP error"}
+STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "bad dtype", 4: "workspace too small", 5: "HIP error",
+          6: "sizes exceed the static scratch"}
 FAULT_DRAFT_ID = 1
 FAULT_TEMPERATURE = 2
 FAULT_TOP_P = 4
@@ -31,7 +32,7 @@ FAULT_PENALTY = 512
 
 EXPORTS = ("spec_verify", "spec_verify_diag", "spec_verify_timed", "spec_verify_flat", "spec_verify_flat_timed",
            "spec_verify_flat_synthetic", "spec_verify_flat_ex", "spec_verify_rollback", "spec_verify_device_errors",
-           "spec_verify_workspace_size",
+           "spec_verify_static", "spec_verify_static_scratch_bytes", "spec_verify_workspace_size",
            "spec_verify_status_string", "spec_verify_version")
 
 
@@ -69,6 +70,10 @@ def _load():
     lib.spec_verify_workspace_size.argtypes = [I, I, I]
     lib.spec_verify_device_errors.restype = I
     lib.spec_verify_device_errors.argtypes = [P, Z, P, P]
+    lib.spec_verify_static.restype = I
+    lib.spec_verify_static.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P, P, P, P]
+    lib.spec_verify_static_scratch_bytes.restype = Z
+    lib.spec_verify_static_scratch_bytes.argtypes = []
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     lib.spec_verify_status_string.argtypes = [I]
     lib.spec_verify_version.restype = I
@@ -117,7 +122,7 @@ def _check(t, name, dtype, shape, device):
 
 def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, top_p=None, u_accept=None,
            u_sample=None, *, out_tokens=None, out_num_accepted=None, workspace=None, stream=None, diag=False,
-           events=None):
+           events=None, static=False):
     """Verify a batch on the GPU.
 
     draft_ids int32 [N, gmax] (-1 padded), draft_probs float32 [N, gmax, V] or
@@ -129,7 +134,10 @@ def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, 
     float64 and fault [N] int32.  The work is enqueued on ``stream`` (default:
     torch's current stream); nothing synchronises.  ``events`` = (start, mid,
     end) torch.cuda.Event objects (or None) are recorded on the stream before
-    the row pass, between the two kernels and after the finish kernel.
+    the row pass, between the two kernels and after the finish kernel.  With
+    static=True the call goes to spec_verify_static, which uses the library's
+    own device scratch array instead of a workspace and allocates nothing
+    (the outputs must then be passed in for no allocation at all).
     """
     if target_logits.dim() != 3:
         raise ValueError("target_logits must be [N, gmax+1, V]")
@@ -157,14 +165,20 @@ def verify(draft_ids, draft_probs, target_logits, temperature=None, top_k=None, 
         out_num_accepted = torch.empty((N,), dtype=torch.int32, device=dev)
     _check(out_tokens, "out_tokens", torch.int32, (N, G + 1), dev)
     _check(out_num_accepted, "out_num_accepted", torch.int32, (N,), dev)
-    if workspace is None:
+    if static and (workspace is not None or diag or events is not None):
+        raise ValueError("static=True takes no workspace, diag or events")
+    if workspace is None and not static:
         workspace = torch.empty((workspace_size(N, G, V),), dtype=torch.uint8, device=dev)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = 0 if static else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
     with torch.cuda.device(dev):
-        if events is not None:
+        if static:
+            rc = lib.spec_verify_static(N, G, V, _ptr(draft_ids), _ptr(draft_probs), _ptr(target_logits), dt,
+                                        _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(u_accept),
+                                        _ptr(u_sample), _ptr(out_tokens), _ptr(out_num_accepted), sptr)
+        elif events is not None:
             evp = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in events]
             rc = lib.spec_verify_timed(N, G, V, _ptr(draft_ids), _ptr(draft_probs), _ptr(target_logits), dt,
                                        _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(u_accept), _ptr(u_sample),

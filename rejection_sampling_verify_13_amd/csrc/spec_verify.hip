@@ -63,6 +63,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "spec_verify.h"
@@ -3153,6 +3154,36 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   return e == hipSuccess ? SPEC_VERIFY_OK : SPEC_VERIFY_ERR_HIP;
 }
 
+// ------------------------------------------------------------------------------------------
+// the entry point that allocates nothing: a file-scope scratch array as its workspace
+// ------------------------------------------------------------------------------------------
+
+// Every GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: only the
+// address hipGetSymbolAddress returns for the current device is ever passed to
+// a kernel.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, set on first use
+
+// The current device's address of `scratch` (looked up once per device, with
+// that device current).
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPEC_VERIFY_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPEC_VERIFY_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_VERIFY_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -3291,6 +3322,23 @@ int spec_verify_rollback(int N, int gmax, const int32_t* cu_num_draft_tokens, co
   return hipGetLastError() == hipSuccess ? SPEC_VERIFY_OK : SPEC_VERIFY_ERR_HIP;
 }
 
+int spec_verify_static(int N, int gmax, int V, const int32_t* draft_ids, const float* draft_probs,
+                       const void* target_logits, int logits_dtype, const float* temperature, const int32_t* top_k,
+                       const float* top_p, const float* u_accept, const float* u_sample, int32_t* out_tokens,
+                       int32_t* out_num_accepted, void* stream) {
+  // the size checks come first, so that a refused call touches no device state
+  if (N < 0 || gmax < 0 || gmax > kMaxGamma || V < 1) return SPEC_VERIFY_ERR_SHAPE;
+  if (N == 0) return SPEC_VERIFY_OK;
+  if (spec_verify_workspace_size(N, gmax, V) > kStaticScratchBytes) return SPEC_VERIFY_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc != SPEC_VERIFY_OK) return rc;
+  return spec_verify(N, gmax, V, draft_ids, draft_probs, target_logits, logits_dtype, temperature, top_k, top_p,
+                     u_accept, u_sample, out_tokens, out_num_accepted, ws, kStaticScratchBytes, stream);
+}
+
+size_t spec_verify_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
 int spec_verify_device_errors(const void* workspace, size_t workspace_bytes, void* stream, int32_t* count) {
   if (!workspace || !count) return SPEC_VERIFY_ERR_NULL;
   if (workspace_bytes < kHeadBytes) return SPEC_VERIFY_ERR_WORKSPACE;
@@ -3310,6 +3358,7 @@ const char* spec_verify_status_string(int status) {
     case SPEC_VERIFY_ERR_DTYPE: return "unknown logits dtype";
     case SPEC_VERIFY_ERR_WORKSPACE: return "workspace smaller than spec_verify_workspace_size";
     case SPEC_VERIFY_ERR_HIP: return "HIP runtime error";
+    case SPEC_VERIFY_ERR_SCRATCH: return "workspace for these sizes exceeds the static scratch of spec_verify_static";
     default: return "unknown status";
   }
 }

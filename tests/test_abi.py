@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_verify_diag", "spec_verify_workspace_size", "spec_verify_status_string",
               "spec_verify_version", "spec_verify_flat", "spec_verify_flat_timed", "spec_verify_rollback",
-              "spec_verify_flat_synthetic", "spec_verify_flat_ex", "spec_verify_device_errors"):
+              "spec_verify_flat_synthetic", "spec_verify_flat_ex", "spec_verify_device_errors",
+              "spec_verify_static", "spec_verify_static_scratch_bytes"):
         assert n in names
 
 
@@ -44,8 +45,21 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.spec_verify_version() == 1
-    for code in range(6):
+    for code in range(7):
         assert lib.spec_verify_status_string(code)
+
+
+def test_static_entry_point_host_validation(lib):
+    # sizes are checked before any device state is touched
+    P = ctypes.c_void_p(0x1000)
+    call = lambda N, G, V: lib.spec_verify_static(N, G, V, P, P, P, 1, None, None, None, P, P, P, P, None)
+    assert lib.spec_verify_static_scratch_bytes() == 16 << 20
+    assert call(-1, 4, 100) == 2
+    assert call(4, 65, 100) == 2
+    assert call(0, 4, 100) == 0
+    assert lib.spec_verify_workspace_size(4096, 8, 151936) > lib.spec_verify_static_scratch_bytes()
+    assert call(4096, 8, 151936) == 6
+    assert lib.spec_verify_workspace_size(1024, 8, 128256) <= lib.spec_verify_static_scratch_bytes()
 
 
 def _call(lib, N=2, G=3, V=16, ids=1, q=0, logits=1, dtype=1, ua=1, us=1, out=1, num=1, ws=None, wsb=0):

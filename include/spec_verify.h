@@ -61,7 +61,7 @@ extern "C" {
 #define SPEC_VERIFY_ERR_SHAPE 2     /* N < 0, gmax outside [0, 64], V < 1, or too large  */
 /* "Too large": V * (gmax + 1) above 2^40, V above 2^31 - 4097, or either
  * launch grid reaching 2^32 work-items: 256 * N * (gmax + 1) (row pass) or
- * 256 * N * (ceil(ceil(V / 2048) / 4) + 1) (draw pass). */
+ * 256 * N * ceil(ceil(V / 2048) / 4) (draw pass). */
 #define SPEC_VERIFY_ERR_DTYPE 3     /* unknown logits_dtype                              */
 #define SPEC_VERIFY_ERR_WORKSPACE 4 /* workspace_bytes below spec_verify_workspace_size  */
 #define SPEC_VERIFY_ERR_HIP 5       /* a HIP runtime call failed (launch, copy, wait)      */
@@ -359,8 +359,8 @@ int spec_verify_device_errors(const void *workspace, size_t workspace_bytes, voi
  * workspace.  The call allocates nothing and calls no allocating routine; its
  * first call on a device looks up that device's address of the array, with
  * the device current.  Sizes whose spec_verify_workspace_size exceeds the
- * scratch are refused with SPEC_VERIFY_ERR_SCRATCH (N = 1024, gmax = 8,
- * V = 128256 needs under 10 MiB).  Every call on a GPU shares that GPU's
+ * scratch are refused with SPEC_VERIFY_ERR_SCRATCH (N = 4096, gmax = 8,
+ * V = 151936 needs 12.6 MiB).  Every call on a GPU shares that GPU's
  * array: calls that overlap on one GPU (different streams, or host threads
  * without ordering) race and their results are undefined; calls ordered on
  * one stream are safe, since each call resets what it reads from the array.

@@ -37,11 +37,14 @@
 //                 its top-k set in LDS also draws its token there.  Each row
 //                 ORs its accept bit, fault bits and whether it drew into the
 //                 request's record.
-//   draw_kernel   per request: the first rejection A from the record, the
+//   draw_kernel   per request whose row A made no draw of its own: the sums
+//                 of row A's draw weights per 512-token block and per part,
+//                 the parts spread over workgroups.
+//   find_kernel   per request: the first rejection A from the record, the
 //                 outputs (-1 padded), and, where row A made no draw of its
-//                 own, the draw by inverse CDF over ascending token id with
-//                 two passes over row A (block sums and part totals, then the
-//                 crossing block).
+//                 own, the draw by inverse CDF over ascending token id from
+//                 the part and block sums (two levels, then the crossing
+//                 block re-read).
 //   rollback_kernel  (own entry point, after a verify call) the KV bookkeeping
 //                 of the rejected drafts.
 //
@@ -132,15 +135,12 @@ struct ReqRec {
 };
 static_assert(sizeof(ReqRec) == 48, "ReqRec layout");
 
-// Sums of one 512-token block (one wave's tokens of one step) of row A.
+// Sum of the draw weights w of one 512-token block (one wave's tokens of one
+// step) of row A, or of one draw workgroup's blocks.
 struct DrawSum {
-  double sw;      // sum of the draw weights w
-  double sp;      // sum of p' (the weights if w sums to zero)
-  int lastw;      // largest id with w > 0, plus one (0: none)
-  int lastp;      // largest id with p' > 0, plus one
-  int pad[2];
+  double sw;
 };
-static_assert(sizeof(DrawSum) == 32, "DrawSum layout");
+static_assert(sizeof(DrawSum) == 8, "DrawSum layout");
 
 struct Args {
   int N, G, V;
@@ -161,7 +161,6 @@ struct Args {
   RowStats* stats;
   ReqRec* rec;          // per request
   DrawSum* dsum;        // [N][steps][kWaves]
-  unsigned int* ddone;  // completion counter per request (draw pass)
   unsigned int* nfault; // faulted requests of this call (workspace head; cleared by the plan kernel)
   int* plan;            // [0]: number of listed rows D; then D entries i * 128 + j, request-major
   DrawSum* dtot;        // [N][dparts] sums of each draw workgroup's blocks
@@ -2367,7 +2366,6 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(Args a) {
       lf[u] = 0u;
       hq[u] = false;
       if (i < a.N) {
-        a.ddone[i] = 0u;
         if (a.cu) {
           const int prev = i ? a.cu[i - 1] : 0, cur = a.cu[i];
           const long long g = (long long)cur - prev;
@@ -2676,46 +2674,39 @@ __device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, i
   }
 }
 
-// Grid: dparts + 1 workgroups per request.  Each reads the request's record
-// and finds the first rejection A; the last one writes the outputs.  If row
-// A made no draw of its own (no kept list in LDS), each of the other dparts
-// workgroups loads kDrawSpan steps of row A (all of them in flight at once)
-// and stores the sums of the draw weights and of p' per 512-token block (one
-// wave's tokens of one step), then its own total: the last lane of
-// a wave prefix scan over its blocks in token order.  The last of them to
-// finish scans the part totals in token order, repeats the scan of the part
-// where the running sum first exceeds u * S (the same arithmetic, so the two
-// levels agree), re-reads the block where it is crossed and finds the token
-// (inverse CDF over ascending id; if the weights sum to zero, over p'; if
-// rounding leaves no crossing, the largest id with w > 0).
-template <class LT, bool VEC, int TOK>
-__global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
+// Where request i's draw happens: its record, the first rejection A, whether
+// row A left the draw to this pass, and how row A is weighed.
+template <class LT>
+struct DrawCtx {
+  ReqRec rr;
+  int A, mode, nsteps;
+  bool defer;
+  DrawW dwt;
+  const typename LT::T* lrow;
+  const float* qrow;
+  DrawSum* ds;  // [nsteps * kWaves] block sums
+  DrawSum* dt;  // [dparts] part totals
+};
+
+template <class LT>
+__device__ inline DrawCtx<LT> draw_ctx(const Args& a, int i) {
   typedef typename LT::T ET;
-  typedef typename LT::Raw LR;
-  __shared__ int s_last;
-  __shared__ DrawSum s_blk[kDrawSpan * kWaves];
-  __shared__ int s_ban[TOK ? kBanMax : 1];
-  __shared__ int s_pid[TOK == 2 ? kPenMax : 1];
-  __shared__ float s_pd[TOK == 2 ? kPenMax : 1];
-  __shared__ float s_stage[TOK == 2 ? kWaves * 512 : 1];
-  const int i = blockIdx.x / (a.dparts + 1), part = blockIdx.x - i * (a.dparts + 1);
-  const ReqRec rr = a.rec[i];
+  DrawCtx<LT> x;
+  x.rr = a.rec[i];
+  const ReqRec& rr = x.rr;
   const int gamma = rr.gamma;
   const uint64_t within = gamma >= 64 ? ~0ull : ((1ull << gamma) - 1ull);
   const uint64_t rej = ~rr.acc & within;
-  const int A = rej ? (__ffsll((unsigned long long)rej) - 1) : gamma;
-  const bool defer = !(rr.fault | rr.lfault) && (A >= 64 ? rr.nodraw64 != 0u : ((rr.nodraw >> A) & 1ull) != 0ull);
-  if (part == a.dparts) {
-    request_outputs(a, i, rr, A, defer);
-    return;
-  }
-  if (!defer) return;
-  const int G = a.G, V = a.V;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int mode = A < gamma ? (rr.q0 >= 0 ? 1 : 2) : 0;
-  const int yA = mode == 2 ? a.ids[(size_t)rr.id0 + A] : -1;
-  const size_t row = (size_t)i * (G + 1) + A;  // the row record
-  const RowStats sa = a.stats[row];
+  x.A = rej ? (__ffsll((unsigned long long)rej) - 1) : gamma;
+  const int A = x.A;
+  x.defer = !(rr.fault | rr.lfault) && (A >= 64 ? rr.nodraw64 != 0u : ((rr.nodraw >> A) & 1ull) != 0ull);
+  x.mode = A < gamma ? (rr.q0 >= 0 ? 1 : 2) : 0;
+  x.nsteps = (a.V + kStep - 1) / kStep;
+  x.ds = a.dsum + (size_t)i * x.nsteps * kWaves;
+  x.dt = a.dtot + (size_t)i * a.dparts;
+  if (!x.defer) return x;
+  const int mode = x.mode;
+  const RowStats sa = a.stats[(size_t)i * (a.G + 1) + A];  // row A's record
   const float T = a.temperature ? a.temperature[i] : 1.f;
   DrawW dwt;
   dwt.m = sa.m;
@@ -2730,15 +2721,42 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   dwt.invZf = (float)dwt.invZ;
   dwt.invRf = (float)dwt.invR;
   dwt.mode = mode;
-  dwt.yA = yA;
-  dwt = uni_draw(dwt);
+  dwt.yA = mode == 2 ? a.ids[(size_t)rr.id0 + A] : -1;
+  x.dwt = uni_draw(dwt);
   // (row A's index was checked by the row pass: a bad one faults the request)
   const size_t trow = !a.bidx ? (size_t)rr.tgt0 + A : (size_t)(A < gamma ? a.tidx[(size_t)rr.id0 + A] : a.bidx[i]);
-  const ET* lrow = reinterpret_cast<const ET*>(a.logits) + trow * (size_t)V;
-  const float* qrow = (mode == 1) ? a.q + ((size_t)rr.q0 + A) * (size_t)V : nullptr;
-  const int nsteps = (V + kStep - 1) / kStep;
-  DrawSum* ds = a.dsum + (size_t)i * nsteps * kWaves;
-  DrawSum* dt = a.dtot + (size_t)i * a.dparts;
+  x.lrow = reinterpret_cast<const ET*>(a.logits) + trow * (size_t)a.V;
+  x.qrow = (mode == 1) ? a.q + ((size_t)rr.q0 + A) * (size_t)a.V : nullptr;
+  return x;
+}
+
+// Draw pass, part 1 (grid: dparts workgroups per request).  Each reads the
+// request's record and finds the first rejection A.  If row A made no draw
+// of its own (no kept list in LDS), the workgroup loads kDrawSpan steps of
+// row A (all of them in flight at once) and stores the sum of the draw
+// weights of each 512-token block (one wave's tokens of one step), then its
+// own total: the last lane of a wave prefix scan over its blocks in token
+// order.  The next launch reads them: the kernel boundary orders the stores
+// before the reads, with no hand-off between workgroups of one launch.
+template <class LT, bool VEC, int TOK>
+__global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
+  typedef typename LT::Raw LR;
+  __shared__ double s_blk[kDrawSpan * kWaves];
+  __shared__ int s_ban[TOK ? kBanMax : 1];
+  __shared__ int s_pid[TOK == 2 ? kPenMax : 1];
+  __shared__ float s_pd[TOK == 2 ? kPenMax : 1];
+  __shared__ float s_stage[TOK == 2 ? kWaves * 512 : 1];
+  const int i = blockIdx.x / a.dparts, part = blockIdx.x - i * a.dparts;
+  const DrawCtx<LT> cx = draw_ctx<LT>(a, i);
+  if (!cx.defer) return;
+  const int V = a.V, A = cx.A, mode = cx.mode, nsteps = cx.nsteps;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const ReqRec& rr = cx.rr;
+  const DrawW& dwt = cx.dwt;
+  const typename LT::T* lrow = cx.lrow;
+  const float* qrow = cx.qrow;
+  DrawSum* ds = cx.ds;
+  DrawSum* dt = cx.dt;
   const int s0 = part * kDrawSpan, cnt = min(kDrawSpan, nsteps - s0);
   // the request's banned tokens (checked by the row pass, which faults the
   // request on a bad list)
@@ -2759,8 +2777,9 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   }
   const Toks tk = toks((const LDS_AS int*)s_ban, nban, (const LDS_AS int*)s_pid, (const LDS_AS float*)s_pd,
                        (LDS_AS float*)s_stage + (threadIdx.x >> 6) * 512, npen, theta);
-  // the block sums of one lane's step u (raw values lr, qr) into s_blk
-  auto block_sums = [&](LR& l, F32::Raw& q, int u, BanWalk& bw, PenWalk& pw, auto precise) {
+  // Sum of one lane's 8 draw weights (raw values l, q of step u); the lists
+  // walk ascending 512-token wave ranges, so steps come in order.
+  auto lane_sum = [&](LR& l, F32::Raw& q, int u, BanWalk& bw, PenWalk& pw, auto precise) {
     const int base = (s0 + u) * kStep + tid * kCh;
     if (TOK == 2) pen_walk(pw, tk, (s0 + u) * kStep + wave * 512, l, q, mode == 1);
     if (TOK) {
@@ -2773,24 +2792,13 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
     float lv[8], qv[8];
     LT::unpack(l, lv);
     F32::unpack(q, qv);
-    double sw = 0.0, sp = 0.0;
-    uint32_t lw = 0u, lp = 0u;
+    double sw = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float pe;
-      const float we = draw_weight<decltype(precise)::value>(lv[e], qv[e], base + e, dwt, pe);
-      sw += (double)we;
-      sp += (double)pe;
-      if (we > 0.f) lw = (uint32_t)(base + e + 1);
-      if (pe > 0.f) lp = (uint32_t)(base + e + 1);
+      sw += (double)draw_weight<decltype(precise)::value>(lv[e], qv[e], base + e, dwt, pe);
     }
-    DrawSum d;
-    d.sw = wave_sum_f64(sw);
-    d.sp = wave_sum_f64(sp);
-    d.lastw = (int)wave_max_u32(lw);
-    d.lastp = (int)wave_max_u32(lp);
-    d.pad[0] = d.pad[1] = 0;
-    if (lane == 0) __builtin_memcpy((DrawSum*)&s_blk[u * kWaves + wave], &d, sizeof(DrawSum));
+    return sw;
   };
   BanWalk bw;
   PenWalk pw;
@@ -2802,111 +2810,96 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
       const int base = (s0 + u) * kStep + tid * kCh;
       LR l = load_logits<LT, VEC>(lrow, base, V);
       F32::Raw q = load_probs<VEC>(qrow, base, V);
-      block_sums(l, q, u, bw, pw, std::true_type{});
+      const double sw = wave_sum_f64(lane_sum(l, q, u, bw, pw, std::true_type{}));
+      if (lane == 0) s_blk[u * kWaves + wave] = sw;
     }
   } else {
-  // all of this workgroup's loads first, then the sums (block sums go to LDS:
-  // a global store here would count against the counter the loads wait on)
-  LR lr[kDrawSpan];
-  F32::Raw qr[kDrawSpan];
+    // all of this workgroup's loads first, then the sums (block sums go to
+    // LDS: a global store here would count against the counter the loads
+    // wait on)
+    LR lr[kDrawSpan];
+    F32::Raw qr[kDrawSpan];
 #pragma unroll
-  for (int u = 0; u < kDrawSpan; ++u) {
-    const int base = (s0 + u) * kStep + tid * kCh;
-    if (u < cnt) {
-      lr[u] = load_logits<LT, VEC>(lrow, base, V);
-      qr[u] = (mode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
+    for (int u = 0; u < kDrawSpan; ++u) {
+      const int base = (s0 + u) * kStep + tid * kCh;
+      if (u < cnt) {
+        lr[u] = load_logits<LT, VEC>(lrow, base, V);
+        qr[u] = (mode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
+      }
     }
-  }
 #pragma unroll
-  for (int u = 0; u < kDrawSpan; ++u) {
-    if (u >= cnt) break;
-    block_sums(lr[u], qr[u], u, bw, pw, std::false_type{});
-  }
+    for (int u = 0; u < kDrawSpan; ++u) {
+      if (u >= cnt) break;
+      const double sw = wave_sum_f64(lane_sum(lr[u], qr[u], u, bw, pw, std::false_type{}));
+      if (lane == 0) s_blk[u * kWaves + wave] = sw;
+    }
   }
   __syncthreads();
   if (tid < cnt * kWaves) {
     DrawSum d;
-    __builtin_memcpy(&d, (const DrawSum*)&s_blk[tid], sizeof(DrawSum));
-    publish(ds + (size_t)s0 * kWaves + tid, d);
+    d.sw = s_blk[tid];
+    ds[(size_t)s0 * kWaves + tid] = d;
   }
   if (wave == 0) {
     // this part's total: the last lane of the scan over its blocks in order
-    DrawSum b{};
-    if (lane < cnt * kWaves) __builtin_memcpy(&b, (const DrawSum*)&s_blk[lane], sizeof(DrawSum));
+    const double b = lane < cnt * kWaves ? s_blk[lane] : 0.0;
     DrawSum t;
-    t.sw = readlane_d(wave_incl_scan_f64(b.sw), 63);
-    t.sp = readlane_d(wave_incl_scan_f64(b.sp), 63);
-    t.lastw = (int)wave_max_u32((uint32_t)b.lastw);
-    t.lastp = (int)wave_max_u32((uint32_t)b.lastp);
-    t.pad[0] = t.pad[1] = 0;
-    if (lane == 0) publish(dt + part, t);
+    t.sw = readlane_d(wave_incl_scan_f64(b), 63);
+    if (lane == 0) dt[part] = t;
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0)
-    s_last = (__hip_atomic_fetch_add(&a.ddone[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              (unsigned int)(a.dparts - 1));
-  __syncthreads();
-  if (!s_last || wave != 0) return;
+}
 
-  // the totals over the parts, in part order
-  double tw = 0.0, tp = 0.0;
-  uint32_t lastw = 0u, lastp = 0u;
-  for (int p0 = 0; p0 < a.dparts; p0 += 64) {
-    DrawSum d{};
-    if (p0 + lane < a.dparts) d = fetch(dt + p0 + lane);
-    tw += readlane_d(wave_incl_scan_f64(d.sw), 63);
-    tp += readlane_d(wave_incl_scan_f64(d.sp), 63);
-    lastw = max(lastw, wave_max_u32((uint32_t)d.lastw));
-    lastp = max(lastp, wave_max_u32((uint32_t)d.lastp));
+// Draw pass, part 2 (grid: one workgroup per request): the outputs, and the
+// draw left to this pass.  Wave 0 scans the part totals in token order,
+// repeats the scan of the part where the running sum first exceeds u * S
+// (the same arithmetic, so the two levels agree), re-reads the block where it
+// is crossed and finds the token (inverse CDF over ascending id; if rounding
+// leaves no crossing, the largest id with w > 0; if the weights sum to zero,
+// the same over p', whose sums the workgroup forms itself).
+template <class LT, bool VEC, int TOK>
+__global__ __launch_bounds__(kBlock) void find_kernel(Args a) {
+  typedef typename LT::Raw LR;
+  __shared__ int s_ban[TOK ? kBanMax : 1];
+  __shared__ int s_pid[TOK == 2 ? kPenMax : 1];
+  __shared__ float s_pd[TOK == 2 ? kPenMax : 1];
+  __shared__ float s_stage[TOK == 2 ? kWaves * 512 : 1];
+  const int i = blockIdx.x;
+  const DrawCtx<LT> cx = draw_ctx<LT>(a, i);
+  request_outputs(a, i, cx.rr, cx.A, cx.defer);
+  if (!cx.defer) return;
+  const int G = a.G, V = a.V, A = cx.A, mode = cx.mode, nsteps = cx.nsteps;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const ReqRec& rr = cx.rr;
+  const DrawW& dwt = cx.dwt;
+  const typename LT::T* lrow = cx.lrow;
+  const float* qrow = cx.qrow;
+  DrawSum* ds = cx.ds;
+  DrawSum* dt = cx.dt;
+  // the request's banned tokens (checked by the row pass, which faults the
+  // request on a bad list)
+  int nban = 0;
+  if (TOK && a.ban_off) {
+    const int b0 = a.ban_off[i];
+    nban = a.ban_off[i + 1] - b0;
+    for (int t = tid; t < nban; t += kBlock) s_ban[t] = a.ban_ids[(size_t)b0 + t];
+    __syncthreads();
   }
-  const bool usep = !(tw > 0.0);  // zero residual: draw from p'
-  const double S = usep ? tp : tw;
-  const int dmode = usep ? 0 : mode;
-  const double tau = (double)a.u_sample[i] * S;
-  // the part, then the block within it, where the running sum first exceeds tau
-  double pre = 0.0, pstar = 0.0;
-  int kstar = -1;
-  for (int p0 = 0; p0 < a.dparts && kstar < 0; p0 += 64) {
-    double x = 0.0;
-    if (p0 + lane < a.dparts) {
-      const DrawSum d = fetch(dt + p0 + lane);
-      x = usep ? d.sp : d.sw;
-    }
-    const double incl = wave_incl_scan_f64(x);
-    const uint64_t hit = __ballot(p0 + lane < a.dparts && x > 0.0 && pre + incl > tau);
-    if (hit) {
-      const int l = __ffsll((unsigned long long)hit) - 1;
-      kstar = p0 + l;
-      pstar = pre + (l > 0 ? readlane_d(incl, l - 1) : 0.0);
-    } else {
-      pre += readlane_d(incl, 63);
-    }
+  // row A's penalty list (checked by the row pass likewise)
+  int npen = 0;
+  float theta = 1.f;
+  if (TOK == 2) {
+    Req rq;
+    rq.id0 = rr.id0;
+    npen = load_penalties(a, rq, i, A, (LDS_AS int*)s_pid, (LDS_AS float*)s_pd, (LDS_AS float*)s_stage, theta, false);
   }
-  int rstar = -1;
-  if (kstar >= 0) {
-    const int k0 = kstar * kDrawSpan, kc = min(kDrawSpan, nsteps - k0);
-    double x = 0.0;
-    if (lane < kc * kWaves) {
-      const DrawSum d = fetch(ds + (size_t)k0 * kWaves + lane);
-      x = usep ? d.sp : d.sw;
-    }
-    const double incl = wave_incl_scan_f64(x);
-    const uint64_t hit = __ballot(lane < kc * kWaves && x > 0.0 && pstar + incl > tau);
-    if (hit) {
-      const int l = __ffsll((unsigned long long)hit) - 1;
-      rstar = k0 * kWaves + l;
-      pstar += (l > 0 ? readlane_d(incl, l - 1) : 0.0);
-    }
-  }
-  int z;
-  if (rstar < 0) {
-    z = (int)(usep ? lastp : lastw) - 1;
-  } else {
-    const int base = (rstar / kWaves) * kStep + (rstar % kWaves) * 512 + lane * kCh;
-    float lv[8], qv[8], w[8];
+  const Toks tk = toks((const LDS_AS int*)s_ban, nban, (const LDS_AS int*)s_pid, (const LDS_AS float*)s_pd,
+                       (LDS_AS float*)s_stage + (threadIdx.x >> 6) * 512, npen, theta);
+  // Weights of one lane's 8 tokens in block blk (512 tokens: step blk / 4,
+  // wave range blk % 4) under draw mode md; lists applied token by token.
+  auto block_weights = [&](int blk, int md, float w[8], int& base) {
+    base = (blk / kWaves) * kStep + (blk % kWaves) * 512 + lane * kCh;
     LR lb = load_logits<LT, VEC>(lrow, base, V);
-    F32::Raw qb = (dmode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
+    F32::Raw qb = (md == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
     if (TOK == 2 && tk.npen) {
       float dv[8];
 #pragma unroll
@@ -2915,7 +2908,7 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
         dv[e] = k >= 0 ? tk.pd[k] : __uint_as_float(0x7fffffffu);
       }
       pen_apply(lb, dv, tk.theta);
-      if (dmode == 1) pen_apply_q(qb, dv);
+      if (md == 1) pen_apply_q(qb, dv);
     }
     if (TOK) {
       uint32_t m = 0u;
@@ -2927,19 +2920,114 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
         ban_apply(qb, m, 0u);
       }
     }
+    float lv[8], qv[8];
     LT::unpack(lb, lv);
-    if (dmode == 1) F32::unpack(qb, qv);
+    if (md == 1) F32::unpack(qb, qv);
     else
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[e] = 0.f;
     DrawW dd = dwt;
-    dd.mode = dmode;
-    const bool prec = dd.mode == 1 && dd.temper && dd.dw.precise;
+    dd.mode = md;
+    const bool prec = md == 1 && dd.temper && dd.dw.precise;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float pe;
-      w[e] = prec ? draw_weight<true>(lv[e], qv[e], base + e, dd, pe) : draw_weight<false>(lv[e], qv[e], base + e, dd, pe);
+      w[e] = prec ? draw_weight<true>(lv[e], qv[e], base + e, dd, pe)
+                  : draw_weight<false>(lv[e], qv[e], base + e, dd, pe);
     }
+  };
+
+  // the total over the parts, in part order (wave 0; the other waves wait)
+  __shared__ double s_tw;
+  if (wave == 0) {
+    double tw = 0.0;
+    for (int p0 = 0; p0 < a.dparts; p0 += 64) {
+      const double x = p0 + lane < a.dparts ? dt[p0 + lane].sw : 0.0;
+      tw += readlane_d(wave_incl_scan_f64(x), 63);
+    }
+    if (lane == 0) s_tw = tw;
+  }
+  __syncthreads();
+  int dmode = mode;
+  if (!(s_tw > 0.0)) {
+    // Zero residual (p' and q' agree and the draft token lies outside both
+    // kept sets): the draw is from p'.  Rare: the block and part sums of p'
+    // are formed here, by this workgroup alone.
+    dmode = 0;
+    const int nblk = nsteps * kWaves;
+    for (int blk = wave; blk < nblk; blk += kWaves) {
+      float w[8];
+      int base;
+      block_weights(blk, 0, w, base);
+      double ls = 0.0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ls += (double)w[e];
+      DrawSum d;
+      d.sw = wave_sum_f64(ls);
+      if (lane == 0) ds[blk] = d;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      double tw = 0.0;
+      for (int p = 0; p < a.dparts; ++p) {
+        const int k0 = p * kDrawSpan, kc = min(kDrawSpan, nsteps - k0);
+        const double x = lane < kc * kWaves ? ds[(size_t)k0 * kWaves + lane].sw : 0.0;
+        DrawSum t;
+        t.sw = readlane_d(wave_incl_scan_f64(x), 63);
+        tw += t.sw;
+        if (lane == 0) dt[p] = t;
+      }
+      if (lane == 0) s_tw = tw;
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  const double S = s_tw;
+  const double tau = (double)a.u_sample[i] * S;
+  // the part, then the block within it, where the running sum first exceeds
+  // tau; where rounding leaves tau at or past the total, the last part and
+  // block of positive weight, and there the last token of positive weight
+  double pre = 0.0, pstar = 0.0;
+  int kstar = -1, klast = -1;
+  for (int p0 = 0; p0 < a.dparts; p0 += 64) {
+    const double x = p0 + lane < a.dparts ? dt[p0 + lane].sw : 0.0;
+    const double incl = wave_incl_scan_f64(x);
+    const uint64_t pos = __ballot(x > 0.0);
+    if (pos) klast = p0 + 63 - __clzll((long long)pos);
+    if (kstar < 0) {
+      const uint64_t hit = __ballot(x > 0.0 && pre + incl > tau);
+      if (hit) {
+        const int l = __ffsll((unsigned long long)hit) - 1;
+        kstar = p0 + l;
+        pstar = pre + (l > 0 ? readlane_d(incl, l - 1) : 0.0);
+      } else {
+        pre += readlane_d(incl, 63);
+      }
+    }
+  }
+  bool last = kstar < 0;
+  const int kp = last ? klast : kstar;
+  int rstar = -1;
+  if (kp >= 0) {
+    const int k0 = kp * kDrawSpan, kc = min(kDrawSpan, nsteps - k0);
+    const double x = lane < kc * kWaves ? ds[(size_t)k0 * kWaves + lane].sw : 0.0;
+    const double incl = wave_incl_scan_f64(x);
+    const uint64_t pos = __ballot(x > 0.0);
+    const uint64_t hit = last ? 0ull : __ballot(x > 0.0 && pstar + incl > tau);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      rstar = k0 * kWaves + l;
+      pstar += (l > 0 ? readlane_d(incl, l - 1) : 0.0);
+    } else if (pos) {
+      last = true;
+      rstar = k0 * kWaves + 63 - __clzll((long long)pos);
+    }
+  }
+  int z = -1;
+  if (rstar >= 0) {
+    float w[8];
+    int base;
+    block_weights(rstar, dmode, w, base);
     double ls = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ls += (double)w[e];
@@ -2951,9 +3039,8 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
       acc += (double)w[e];
       if (zz == INT_MAX && w[e] > 0.f && acc > tau) zz = base + e;
     }
-    const int best = -wave_max_i(-zz);
-    const int lastb = wave_max_i(lastpos);
-    z = best != INT_MAX ? best : lastb;
+    const int best = last ? INT_MAX : -wave_max_i(-zz);
+    z = best != INT_MAX ? best : wave_max_i(lastpos);
   }
   if (lane == 0) {
     a.out_tokens[(size_t)i * (G + 1) + A] = z;
@@ -3013,7 +3100,6 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // the workspace starts with this call's fault count (one 256-byte block)
 constexpr size_t kHeadBytes = 256;
 size_t stats_bytes(int N, int G) { return align_up((size_t)N * (G + 1) * sizeof(RowStats), 256); }
-size_t done_bytes(int N) { return align_up((size_t)N * sizeof(unsigned int), 256); }
 size_t rec_bytes(int N) { return align_up((size_t)N * sizeof(ReqRec), 256); }
 size_t plan_bytes(int N, int G) { return align_up(((size_t)N * G + 1) * sizeof(int), 256); }
 size_t dsum_bytes(int N, int V) {
@@ -3040,8 +3126,9 @@ hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
   else
     hipLaunchKernelGGL((row_kernel<LT, VEC, TOK>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((draw_kernel<LT, VEC, TOK>), dim3((unsigned)((long)a.N * (a.dparts + 1))), dim3(kBlock), 0,
-                     stream, a);
+  hipLaunchKernelGGL((draw_kernel<LT, VEC, TOK>), dim3((unsigned)((long)a.N * a.dparts)), dim3(kBlock), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((find_kernel<LT, VEC, TOK>), dim3((unsigned)a.N), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev.end && (e = hipEventRecord(ev.end, stream)) != hipSuccess) return e;
   return hipSuccess;
@@ -3072,7 +3159,7 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   if ((long long)V * (G + 1) > (1LL << 40) || V > 0x7fffffff - 2 * kStep) return SPEC_VERIFY_ERR_SHAPE;
   // a dispatch holds its grid size in work-items as a 32-bit number
   const long long dparts = (long long)draw_parts(V);
-  if ((long long)N * (G + 1) * kBlock > 0xffffffffLL || (long long)N * (dparts + 1) * kBlock > 0xffffffffLL)
+  if ((long long)N * (G + 1) * kBlock > 0xffffffffLL || (long long)N * dparts * kBlock > 0xffffffffLL)
     return SPEC_VERIFY_ERR_SHAPE;
   if (N == 0) return SPEC_VERIFY_OK;
   if (!logits || !u_sample || !out_tokens || !out_num) return SPEC_VERIFY_ERR_NULL;
@@ -3105,8 +3192,6 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   size_t off = kHeadBytes + stats_bytes(N, G);
   a.rec = reinterpret_cast<ReqRec*>(ws + off);
   off += rec_bytes(N);
-  a.ddone = reinterpret_cast<unsigned int*>(ws + off);
-  off += done_bytes(N);
   a.dsum = reinterpret_cast<DrawSum*>(ws + off);
   off += dsum_bytes(N, V);
   a.dtot = reinterpret_cast<DrawSum*>(ws + off);
@@ -3190,7 +3275,7 @@ extern "C" {
 
 size_t spec_verify_workspace_size(int N, int gmax, int V) {
   if (N <= 0 || gmax < 0 || V <= 0) return 256;
-  return kHeadBytes + stats_bytes(N, gmax) + rec_bytes(N) + done_bytes(N) + dsum_bytes(N, V) + dtot_bytes(N, V) +
+  return kHeadBytes + stats_bytes(N, gmax) + rec_bytes(N) + dsum_bytes(N, V) + dtot_bytes(N, V) +
          plan_bytes(N, gmax);
 }
 

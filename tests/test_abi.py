@@ -57,8 +57,8 @@ def test_static_entry_point_host_validation(lib):
     assert call(-1, 4, 100) == 2
     assert call(4, 65, 100) == 2
     assert call(0, 4, 100) == 0
-    assert lib.spec_verify_workspace_size(4096, 8, 151936) > lib.spec_verify_static_scratch_bytes()
-    assert call(4096, 8, 151936) == 6
+    assert lib.spec_verify_workspace_size(8192, 8, 151936) > lib.spec_verify_static_scratch_bytes()
+    assert call(8192, 8, 151936) == 6
     assert lib.spec_verify_workspace_size(1024, 8, 128256) <= lib.spec_verify_static_scratch_bytes()
 
 
@@ -84,8 +84,9 @@ def test_host_validation(lib):
     assert _call(lib, N=0) == 0  # empty batch: nothing to do
     # grids whose size in work-items (256 per workgroup) needs more than 32 bits
     assert _call(lib, N=(1 << 24) // 65 + 1, G=64) == 2     # row pass: N * (gmax + 1) workgroups
-    assert _call(lib, N=(1 << 24) // 2, G=0, V=16) == 2      # draw pass: N * 2 workgroups at V <= 8192
-    assert _call(lib, N=(1 << 24) // 2 - 1, G=0, V=16, logits=0) == 1  # just inside: the next check fires
+    assert _call(lib, N=(1 << 24) // 2, G=0, V=16384) == 2   # draw pass: N * 2 workgroups at 8192 < V <= 16384
+    assert _call(lib, N=(1 << 24) // 2 - 1, G=0, V=16384, logits=0) == 1  # just inside: the next check fires
+    assert _call(lib, N=(1 << 24), G=0, V=16) == 2           # row pass: N workgroups
     small = ctypes.c_void_p(0x1000)
     assert _call(lib, ws=small, wsb=16) == 4
     # the workspace is the caller's: a NULL one is refused, nothing is allocated

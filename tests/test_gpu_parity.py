@@ -250,6 +250,30 @@ def test_fault_injection():
     assert sv.device_errors(ws) == int((n.cpu().numpy() == -1).sum())
 
 
+def test_zero_residual_falls_back_to_target():
+    """p' and q' both keep only the common argmax (top-p 0.05 alone, so the
+    radix path and the draw pass serve it) and the draft token lies outside:
+    it is rejected, max(0, p' - q') is zero everywhere, and the token is drawn
+    from p' (zwjcode.cn page, section 04, residual; the zero-mass case is this
+    build's reading), i.e. the argmax, for every u_sample."""
+    rng = np.random.default_rng(31)
+    V, reqs = 3000, []
+    for r in range(12):
+        l = rng.standard_normal((2, V)).astype(np.float32)
+        a = int(rng.integers(V))
+        l[:, a] = 6.0
+        d = l[0].astype(np.float64) + 0.05 * rng.standard_normal(V)
+        q = np.exp(d - d.max())
+        q = (q / q.sum()).astype(np.float32)
+        y = (a + 1 + int(rng.integers(V - 1))) % V
+        reqs.append(one_request([y], q[None], l, p=0.05, ua=[float(rng.uniform())], us=float(rng.uniform())))
+    b = stack(reqs)
+    g, o, _ = parity(b, "zero residual")
+    assert (g["num_accepted"] == 0).all()
+    for r in range(12):
+        assert g["tokens"][r, 0] == int(np.argmax(b["target_logits"][r, 0]))
+
+
 def test_special_rows():
     V = 2048
     rng = np.random.default_rng(9)

@@ -59,7 +59,7 @@ def test_static_entry_point_refuses_sizes_beyond_its_scratch():
     import rejection_sampling_verify_13_amd as sv
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    big_n = 4096
+    big_n = 8192
     assert sv.lib.spec_verify_workspace_size(big_n, 8, 151936) > sv.lib.spec_verify_static_scratch_bytes()
     P = ctypes.c_void_p(0x1000)  # never dereferenced: the size check comes first
     rc = sv.lib.spec_verify_static(big_n, 8, 151936, P, P, P, 1, None, None, None, P, P, P, P, None)

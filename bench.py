@@ -77,10 +77,10 @@ def traffic_from_profile(digest, workload):
     if not os.path.exists(COUNTERS):
         return None
     text = open(COUNTERS).read()
-    m = re.search(r"traffic_bytes_per_launch:\s*(\d+)\s+source:\s*(\w+)\s+workload:\s*(\S+)", text)
-    if not m or m.group(2) != digest or m.group(3) != workload:
-        return None
-    return int(m.group(1))
+    for b, src, wl in re.findall(r"traffic_bytes_per_launch:\s*(\d+)\s+source:\s*(\w+)\s+workload:\s*(\S+)", text):
+        if src == digest and wl == workload:
+            return int(b)
+    return None
 
 
 def host_threads():
@@ -314,8 +314,8 @@ def main():
                     kernel_us_p10_p50_p90=row_pct, input_sets_rotated=n_sets, launches_timed=len(timed),
                     algorithmic_bytes_per_launch=B_alg,
                     fetch_gbps=None if traffic is None else round(traffic / row_avg_s / 1e9, 1),
-                    scope="the row kernel alone (the dominant kernel); the whole verify step (plan, row and "
-                          "draw kernels) is hbm_gbps_step / hbm_frac_step")
+                    scope="the row kernel alone (the dominant kernel); the whole verify step (plan, row, draw "
+                          "and find kernels) is hbm_gbps_step / hbm_frac_step")
 
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4

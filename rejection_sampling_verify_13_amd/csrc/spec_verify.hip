@@ -10,13 +10,16 @@
 // token's cell removed).  The exact contract is stated in include/spec_verify.h.
 //
 // Work per call, all on the caller's stream:
-//   plan_kernel   stores gamma_i and where the request's rows and drafts sit
-//                 (padded or flattened layout), clears the outcome bits of each
-//                 request's record, and lists the draft rows (request,
+//   plan_kernel   (flattened layout, synthetic mode) stores gamma_i and where
+//                 the request's rows and drafts sit, clears the outcome bits of
+//                 each request's record, and lists the draft rows (request,
 //                 position < gamma_i) request-major; in the synthetic
 //                 acceptance mode it finds the first rejection A from the
-//                 uniforms and lists row A alone.
-//   row_kernel    one 256-thread workgroup per real row: the listed rows, then
+//                 uniforms and lists row A alone.  The padded layout in the
+//                 standard mode needs no plan: each row workgroup finds gamma_i
+//                 from the request's ids (one load per lane) and the request's
+//                 outcome is read back from its rows' records.
+//   row_kernel    one 256-thread workgroup per real row: the draft rows, then
 //                 (standard mode) one bonus row per request.  It streams the target-logit
 //                 row and, at draft positions of sampled requests, the
 //                 draft-probability row once (16-byte nontemporal loads,
@@ -35,16 +38,16 @@
 //                 and the flag u * q'(y) < p'(y) stored; a row that may be the
 //                 one drawn from (the bonus row, or a rejected draft row) with
 //                 its top-k set in LDS also draws its token there.  Each row
-//                 ORs its accept bit, fault bits and whether it drew into the
-//                 request's record.
+//                 writes its accept bit, fault bits and draw to its own record
+//                 (and, with a plan, ORs them into the request's record).
 //   draw_kernel   per request whose row A made no draw of its own: the sums
-//                 of row A's draw weights per 512-token block and per part,
-//                 the parts spread over workgroups.
+//                 of row A's draw weights per 512-token block, the row spread
+//                 over workgroups of kDrawSpan steps.
 //   find_kernel   per request: the first rejection A from the record, the
 //                 outputs (-1 padded), and, where row A made no draw of its
 //                 own, the draw by inverse CDF over ascending token id from
-//                 the part and block sums (two levels, then the crossing
-//                 block re-read).
+//                 the block sums (one scan over all of them, then the
+//                 crossing block re-read).
 //   rollback_kernel  (own entry point, after a verify call) the KV bookkeeping
 //                 of the rejected drafts.
 //
@@ -80,7 +83,9 @@ constexpr int kStep = kBlock * kCh;     // tokens per workgroup step (2048)
 constexpr int kCap = 160;               // buffered candidate chunks per wave and distribution
 constexpr int kKFast = 64;              // largest top_k served by the candidate buffers
 constexpr int kSeg = 128;               // gathered candidate tokens per wave and distribution (LDS)
-constexpr int kDrawSpan = 4;            // draw pass: 2048-token steps per workgroup, all loads in flight
+constexpr int kDrawSpan = 4;            // draw pass: 2048-token steps per workgroup
+constexpr int kDrawWin = 4;             // draw pass: steps in flight per workgroup
+constexpr int kFindPer = 8;             // draw search: block sums per lane and load round
 constexpr int kMaxGamma = 64;
 
 enum {
@@ -136,7 +141,7 @@ struct ReqRec {
 static_assert(sizeof(ReqRec) == 48, "ReqRec layout");
 
 // Sum of the draw weights w of one 512-token block (one wave's tokens of one
-// step) of row A, or of one draw workgroup's blocks.
+// step) of row A.
 struct DrawSum {
   double sw;
 };
@@ -163,7 +168,6 @@ struct Args {
   DrawSum* dsum;        // [N][steps][kWaves]
   unsigned int* nfault; // faulted requests of this call (workspace head; cleared by the plan kernel)
   int* plan;            // [0]: number of listed rows D; then D entries i * 128 + j, request-major
-  DrawSum* dtot;        // [N][dparts] sums of each draw workgroup's blocks
   int dparts;           // draw pass: workgroups per request (kDrawSpan steps each)
   // flattened layout (cu == nullptr: the padded [N, G] layout)
   const int32_t* cu;    // [N] inclusive prefix sums of gamma_i
@@ -180,6 +184,8 @@ struct Args {
   const float* pen_rep;    // [N] repetition penalty, or nullptr (1)
   const float* pen_pres;   // [N] presence penalty, or nullptr (0)
   const float* pen_freq;   // [N] frequency penalty, or nullptr (0)
+  int direct;           // 1: padded layout, standard mode: no plan kernel; each row workgroup finds
+                        // gamma_i from the ids and the outcome lives in the rows' records
   int synthetic;        // 1: the synthetic acceptance mode (draft j accepted iff u_j < srates[j])
   const float* srates;  // synthetic acceptance rates [G]
 };
@@ -450,39 +456,28 @@ __device__ inline double mass_p(float l, float m, const Scale2& c) {
 }
 
 // ------------------------------------------------------------------------------------------
-// hand-off of partial results between workgroups of one launch
+// per-row records
 //
-// Records are written with agent-scope atomic stores and read back with
-// agent-scope atomic loads: on gfx950 these are global stores / loads with
-// the device-coherence bit, which write through and read past the per-XCD L2,
-// so the consuming workgroup (possibly on another XCD) sees them without a
-// cache-wide write-back or invalidate.  Each writer waits for its stores to
-// complete before the workgroup barrier that precedes the counter increment.
+// A row's record is written by its own workgroup and read only by later
+// launches on the same stream (the draw and find kernels): the end of one
+// kernel and the start of the next order the writes before the reads, so the
+// records are plain stores and no workgroup waits on another within a launch.
 // ------------------------------------------------------------------------------------------
 
 template <class T>
 __device__ inline void publish(T* dst, const T& v) {
-  static_assert(sizeof(T) % 8 == 0, "published records are whole 8-byte words");
+  static_assert(sizeof(T) % 8 == 0, "records are whole 8-byte words");
   const uint64_t* src = reinterpret_cast<const uint64_t*>(&v);
   uint64_t* d = reinterpret_cast<uint64_t*>(dst);
 #pragma unroll
-  for (int t = 0; t < (int)(sizeof(T) / 8); ++t) __hip_atomic_store(d + t, src[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <class T>
-__device__ inline T fetch(const T* src) {
-  static_assert(sizeof(T) % 8 == 0, "published records are whole 8-byte words");
-  T v;
-  uint64_t* d = reinterpret_cast<uint64_t*>(&v);
-  const uint64_t* s = reinterpret_cast<const uint64_t*>(src);
-#pragma unroll
-  for (int t = 0; t < (int)(sizeof(T) / 8); ++t) d[t] = __hip_atomic_load(s + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return v;
+  for (int t = 0; t < (int)(sizeof(T) / 8); ++t) d[t] = src[t];
 }
 
-// Adds row j's outcome to request i's record (one thread).  The ORs return
-// nothing, so the workgroup does not wait for them; the draw pass, a later
-// launch, reads the record.
+// Adds row j's outcome to request i's record (one thread; plan mode).  The
+// ORs return nothing, so the workgroup does not wait for them; the draw
+// pass, a later launch, reads the record.
 __device__ inline void note_row(const Args& a, int i, int j, int acc, int fault, bool nodraw) {
+  if (a.direct) return;  // direct mode: the row's own record carries the outcome
   ReqRec* r = a.rec + i;
   if (acc) __hip_atomic_fetch_or(&r->acc, 1ull << j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (fault) __hip_atomic_fetch_or(&r->fault, (unsigned int)fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -696,23 +691,36 @@ struct Req {
   bool pact;      // top-p filter active
 };
 
-// The request's layout (from the plan kernel's record) and parameters, and
-// the draft-id check; every wave of the block evaluates this redundantly
-// (gamma_i <= 64 ids).
+// The request's layout and parameters, and the draft-id check; every wave of
+// the block evaluates this redundantly (gamma_i <= 64 ids).  Plan mode: the
+// layout from the plan kernel's record.  Direct mode (padded layout): gamma_i
+// is the index of the first negative id, found from one load per lane, and
+// the rest follows from i; the parameters load alongside.
 __device__ inline Req load_req(const Args& a, int i) {
   Req r;
   const int lane = lane_id();
-  const ReqRec* rr = a.rec + i;
-  r.gamma = rr->gamma;
-  r.tgt0 = rr->tgt0;
-  r.id0 = rr->id0;
-  r.q0 = rr->q0;
-  r.fault = (int)rr->lfault;
-  const int id = lane < r.gamma ? a.ids[(size_t)r.id0 + lane] : 0;
-  if (__ballot(lane < r.gamma && (id < 0 || id >= a.V))) r.fault |= kFaultDraftId;
   r.T = a.temperature ? a.temperature[i] : 1.f;
   r.k = a.top_k ? a.top_k[i] : 0;
   r.p = a.top_p ? a.top_p[i] : 1.f;
+  int id;
+  if (a.direct) {
+    r.tgt0 = i * (a.G + 1);
+    r.id0 = i * a.G;
+    r.q0 = a.q ? i * a.G : -1;
+    r.fault = 0;
+    id = lane < a.G ? a.ids[(size_t)r.id0 + lane] : 0;
+    const uint64_t neg = __ballot(lane < a.G && id < 0);
+    r.gamma = neg ? __ffsll((unsigned long long)neg) - 1 : a.G;
+  } else {
+    const ReqRec* rr = a.rec + i;
+    r.gamma = rr->gamma;
+    r.tgt0 = rr->tgt0;
+    r.id0 = rr->id0;
+    r.q0 = rr->q0;
+    r.fault = (int)rr->lfault;
+    id = lane < r.gamma ? a.ids[(size_t)r.id0 + lane] : 0;
+  }
+  if (__ballot(lane < r.gamma && (id < 0 || id >= a.V))) r.fault |= kFaultDraftId;
   const float T = r.T;
   if (isnan(T) || T < 0.f || isinf(T) || (T > 0.f && T < FLT_MIN)) r.fault |= kFaultTemperature;
   r.greedy = (T == 0.f);
@@ -2495,18 +2503,32 @@ __global__ __launch_bounds__(kBlock, TOK == 2 ? 2 : (sizeof(typename LT::T) == 2
   __shared__ int s_pid[TOK == 2 ? kPenMax : 1];
   __shared__ float s_pd[TOK == 2 ? kPenMax : 1];
   __shared__ float s_stage[TOK == 2 ? kWaves * 512 : 1];
-  // the draft rows first (the larger rows; the plan lists them request-major,
-  // so consecutive blocks, which dispatch round-robin over the XCDs, read
-  // neighbouring rows), then one bonus row per request; the launch covers
-  // N * (gmax + 1) blocks and the ones past the real rows exit at once
-  const int nd = a.plan[0];
+  // the draft rows first (the larger rows, request-major, so consecutive
+  // blocks, which dispatch round-robin over the XCDs, read neighbouring
+  // rows), then one bonus row per request.  Plan mode: the plan lists the
+  // draft rows and the launch's blocks past the real rows exit at once.
+  // Direct mode: block b < N * gmax is draft position (b / gmax, b % gmax),
+  // and exits at once if that is a padding position; the rest are bonus rows.
   const int bx = (int)blockIdx.x;
-  if (bx >= nd + (a.synthetic ? 0 : a.N)) return;
-  const bool bonus = bx >= nd;
-  const int m = bonus ? 0 : a.plan[1 + bx];
-  const int i = bonus ? bx - nd : (m >> 7);
-  Req rq = load_req(a, i);
-  const int j = bonus ? rq.gamma : (m & 127);
+  int i, j;
+  Req rq;
+  if (a.direct) {
+    if (bx == 0 && threadIdx.x == 0) *a.nfault = 0u;  // the find kernel counts this call's faulted requests
+    const int nd = a.N * a.G;
+    const bool bonus = bx >= nd;
+    i = bonus ? bx - nd : bx / a.G;
+    rq = load_req(a, i);
+    j = bonus ? rq.gamma : bx - i * a.G;
+    if (!bonus && j >= rq.gamma) return;
+  } else {
+    const int nd = a.plan[0];
+    if (bx >= nd + (a.synthetic ? 0 : a.N)) return;
+    const bool bonus = bx >= nd;
+    const int m = bonus ? 0 : a.plan[1 + bx];
+    i = bonus ? bx - nd : (m >> 7);
+    rq = load_req(a, i);
+    j = bonus ? rq.gamma : (m & 127);
+  }
   // the row's place in target_logits: request order, or the caller's indices
   rq.trow = (long long)rq.tgt0 + j;
   if (a.bidx && !rq.fault) {
@@ -2538,7 +2560,20 @@ __global__ __launch_bounds__(kBlock, TOK == 2 ? 2 : (sizeof(typename LT::T) == 2
     if (npen < 0) rq.fault |= kFaultPenalty;
   }
   if (rq.fault) {
-    if (threadIdx.x == 0) note_row(a, i, j, 0, rq.fault, false);
+    if (threadIdx.x == 0) {
+      if (a.direct) {
+        RowStats s;
+        s.m = NAN;
+        s.cut_p = -INFINITY;
+        s.cut_q = -INFINITY;
+        s.argmax = -1;
+        s.z = s.r = s.p_y = s.q_y = s.s = NAN;
+        s.flags = rq.fault << 8;
+        s.draw = -1;
+        publish(a.stats + (size_t)i * (a.G + 1) + j, s);
+      }
+      note_row(a, i, j, 0, rq.fault, false);
+    }
     return;
   }
   const Toks tk = toks((const LDS_AS int*)s_ban, nban, (const LDS_AS int*)s_pid, (const LDS_AS float*)s_pd,
@@ -2597,34 +2632,64 @@ __device__ inline DrawW uni_draw(DrawW d) {
   return d;
 }
 
-// Draw weight w and p' of token x (lv its logit, qv its draft probability);
-// tokens past the row end read as -inf logits and zero probabilities, so both
-// are zero there.  The exponents are formed as in the row pass's sums, so
-// that each p' is its weight over the very sum that weight entered.
+// Draw weight of token x (lv its logit, qv its draft probability) under draw
+// mode MODE (0: p'; 1: max(0, p' - q'); 2: p' with the draft token's cell
+// removed); tokens past the row end read as -inf logits and zero
+// probabilities, so their weight is zero.  The exponents are formed as in the
+// row pass's sums, so that each p' is its weight over the very sum that
+// weight entered; p' - q' is one fused multiply-add.  TEMPER: T != 1.  FILT:
+// the row kept a top-k / top-p set (cuts above -inf); without one every
+// token is kept, the row pass having faulted any NaN or negative value.
 // PRECISE (a tempered residual at 1/T above kPreciseInvT): the draft weights
 // that carry mass are formed in fp64 as in the row pass, then normalised and
-// subtracted in fp64 (inline: the draw pass runs that case one step at a
-// time, with registers to spare).
-template <bool PRECISE>
-__device__ inline float draw_weight(float lv, float qv, int x, const DrawW& d, float& p) {
-  const float e = (lv >= d.cut_p) ? mass_p32(lv, d.m, d.c) : 0.f;
-  p = e * d.invZf;
-  if (d.mode == 1) {
+// subtracted in fp64.  Contraction is off, so every caller forms the same
+// weight.
+template <int MODE, bool TEMPER, bool FILT, bool PRECISE>
+__device__ inline float draw_w(float lv, float qv, int x, const DrawW& d) {
+#pragma clang fp contract(off)
+  float e = mass_p32(lv, d.m, d.c);
+  if (FILT && !(lv >= d.cut_p)) e = 0.f;
+  if (MODE == 1) {
     float r = qv;
-    if (d.temper) {
+    if (TEMPER) {
       const float rr = qv * d.qinv;
       const float xq = smul(fast_log2(rr), d.dw.invT);
-      if (PRECISE && xq > d.dw.thr && qv >= d.cut_q) {
-        const double w = (double)e * d.invZ - precise_weight(rr, d.dw.invT.d) * d.invR;
+      if (PRECISE && xq > d.dw.thr && (!FILT || qv >= d.cut_q)) {
+        const double w = (double)e * d.invZ - precise_weight_call(rr, d.dw.invT.d) * d.invR;
         return w > 0.0 ? (float)w : 0.f;
       }
       r = fast_exp2(xq);
     }
-    const float q = (qv >= d.cut_q) ? r * d.invRf : 0.f;
-    return __builtin_fmaxf(p - q, 0.f);
+    float q = r * d.invRf;
+    if (FILT && !(qv >= d.cut_q)) q = 0.f;
+    return __builtin_fmaxf(__builtin_fmaf(e, d.invZf, -q), 0.f);
   }
-  if (d.mode == 2) return x == d.yA ? 0.f : p;
+  const float p = e * d.invZf;
+  if (MODE == 2) return x == d.yA ? 0.f : p;
   return p;
+}
+
+// The same weight with the mode chosen at run time (the find kernel, one
+// block per request); FILT = true equals FILT = false on rows without a cut.
+template <bool PRECISE>
+__device__ inline float draw_weight(float lv, float qv, int x, const DrawW& d) {
+  if (d.mode == 1)
+    return d.temper ? draw_w<1, true, true, PRECISE>(lv, qv, x, d) : draw_w<1, false, true, false>(lv, qv, x, d);
+  if (d.mode == 2) return draw_w<2, false, true, false>(lv, qv, x, d);
+  return draw_w<0, false, true, false>(lv, qv, x, d);
+}
+
+// A lane's 8 weights summed pairwise in fp32 (the row pass sums its exponent
+// terms the same way), widened to fp64 for the block and row sums; the fp64
+// weights of the precise form are summed in fp64, in token order.
+__device__ inline double lane_sum8(const float w[8]) {
+  return (double)(((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7])));
+}
+__device__ inline double lane_sum8_seq(const float w[8]) {
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += (double)w[e];
+  return s;
 }
 
 // Request i's outputs from its record: the accepted drafts before the first
@@ -2675,24 +2740,55 @@ __device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, i
 }
 
 // Where request i's draw happens: its record, the first rejection A, whether
-// row A left the draw to this pass, and how row A is weighed.
+// row A left the draw to this pass, and where row A sits.  The record and the
+// request's temperature are loaded together.
 template <class LT>
 struct DrawCtx {
   ReqRec rr;
   int A, mode, nsteps;
   bool defer;
-  DrawW dwt;
+  float T;
   const typename LT::T* lrow;
   const float* qrow;
-  DrawSum* ds;  // [nsteps * kWaves] block sums
-  DrawSum* dt;  // [dparts] part totals
+  DrawSum* ds;  // [nsteps * kWaves] block sums of row A
 };
+
+// Direct mode: request i's record rebuilt from its draft ids (gamma_i: the
+// first negative one) and its rows' records (accept flag, fault bits, whether
+// the row drew), one load of each per lane; row 64 (gmax = 64) separately.
+__device__ inline ReqRec direct_rec(const Args& a, int i) {
+  const int lane = lane_id(), G = a.G;
+  const RowStats* st = a.stats + (size_t)i * (G + 1);
+  const int id = lane < G ? a.ids[(size_t)i * G + lane] : 0;
+  const int fl = lane <= G ? st[lane].flags : 0;
+  const int dr = lane <= G ? st[lane].draw : 0;
+  const int fl64 = G == 64 ? st[64].flags : 0;
+  const int dr64 = G == 64 ? st[64].draw : 0;
+  const uint64_t neg = __ballot(lane < G && id < 0);
+  ReqRec r;
+  r.gamma = neg ? __ffsll((unsigned long long)neg) - 1 : G;
+  const int gamma = r.gamma;
+  r.acc = __ballot(lane < gamma && (fl & 1));
+  r.nodraw = __ballot(lane <= gamma && dr < 0);
+  r.nodraw64 = (gamma == 64 && dr64 < 0) ? 1u : 0u;
+  int f = lane <= gamma ? (fl >> 8) : 0;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) f |= __shfl_xor(f, o);
+  r.fault = (unsigned int)(__builtin_amdgcn_readfirstlane(f) | (gamma == 64 ? (fl64 >> 8) : 0));
+  r.tgt0 = i * (G + 1);
+  r.id0 = i * G;
+  r.q0 = a.q ? i * G : -1;
+  r.lfault = 0u;
+  r.pad = 0;
+  return r;
+}
 
 template <class LT>
 __device__ inline DrawCtx<LT> draw_ctx(const Args& a, int i) {
   typedef typename LT::T ET;
   DrawCtx<LT> x;
-  x.rr = a.rec[i];
+  x.rr = a.direct ? direct_rec(a, i) : a.rec[i];
+  x.T = a.temperature ? a.temperature[i] : 1.f;
   const ReqRec& rr = x.rr;
   const int gamma = rr.gamma;
   const uint64_t within = gamma >= 64 ? ~0ull : ((1ull << gamma) - 1ull);
@@ -2703,44 +2799,50 @@ __device__ inline DrawCtx<LT> draw_ctx(const Args& a, int i) {
   x.mode = A < gamma ? (rr.q0 >= 0 ? 1 : 2) : 0;
   x.nsteps = (a.V + kStep - 1) / kStep;
   x.ds = a.dsum + (size_t)i * x.nsteps * kWaves;
-  x.dt = a.dtot + (size_t)i * a.dparts;
+  x.lrow = nullptr;
+  x.qrow = nullptr;
   if (!x.defer) return x;
-  const int mode = x.mode;
-  const RowStats sa = a.stats[(size_t)i * (a.G + 1) + A];  // row A's record
-  const float T = a.temperature ? a.temperature[i] : 1.f;
+  // (row A's index was checked by the row pass: a bad one faults the request)
+  const size_t trow = !a.bidx ? (size_t)rr.tgt0 + A : (size_t)(A < gamma ? a.tidx[(size_t)rr.id0 + A] : a.bidx[i]);
+  x.lrow = reinterpret_cast<const ET*>(a.logits) + trow * (size_t)a.V;
+  x.qrow = (x.mode == 1) ? a.q + ((size_t)rr.q0 + A) * (size_t)a.V : nullptr;
+  return x;
+}
+
+// How row A's tokens are weighed: from row A's statistics (wave-uniform).
+template <class LT>
+__device__ inline DrawW draw_weights(const Args& a, int i, const DrawCtx<LT>& x) {
+  const int A = x.A, mode = x.mode;
+  const RowStats sa = a.stats[(size_t)i * (a.G + 1) + A];
   DrawW dwt;
   dwt.m = sa.m;
   dwt.cut_p = sa.cut_p;
   dwt.cut_q = sa.cut_q;
-  dwt.temper = T != 1.f;
+  dwt.temper = x.T != 1.f;
   dwt.qinv = (mode == 1 && dwt.temper) ? sa.qinv : 1.f;
-  dwt.c = target_scale(T);
-  dwt.dw = draft_w(T);
+  dwt.c = target_scale(x.T);
+  dwt.dw = draft_w(x.T);
   dwt.invZ = 1.0 / sa.z;
   dwt.invR = (mode == 1) ? 1.0 / sa.r : 0.0;
   dwt.invZf = (float)dwt.invZ;
   dwt.invRf = (float)dwt.invR;
   dwt.mode = mode;
-  dwt.yA = mode == 2 ? a.ids[(size_t)rr.id0 + A] : -1;
-  x.dwt = uni_draw(dwt);
-  // (row A's index was checked by the row pass: a bad one faults the request)
-  const size_t trow = !a.bidx ? (size_t)rr.tgt0 + A : (size_t)(A < gamma ? a.tidx[(size_t)rr.id0 + A] : a.bidx[i]);
-  x.lrow = reinterpret_cast<const ET*>(a.logits) + trow * (size_t)a.V;
-  x.qrow = (mode == 1) ? a.q + ((size_t)rr.q0 + A) * (size_t)a.V : nullptr;
-  return x;
+  dwt.yA = mode == 2 ? a.ids[(size_t)x.rr.id0 + A] : -1;
+  return uni_draw(dwt);
 }
 
-// Draw pass, part 1 (grid: dparts workgroups per request).  Each reads the
-// request's record and finds the first rejection A.  If row A made no draw
-// of its own (no kept list in LDS), the workgroup loads kDrawSpan steps of
-// row A (all of them in flight at once) and stores the sum of the draw
-// weights of each 512-token block (one wave's tokens of one step), then its
-// own total: the last lane of a wave prefix scan over its blocks in token
-// order.  The next launch reads them: the kernel boundary orders the stores
-// before the reads, with no hand-off between workgroups of one launch.
+// Draw pass, part 1 (grid: dparts workgroups per request, kDrawSpan steps of
+// row A each).  Each reads the request's record, finds the first rejection A
+// and, if row A made no draw of its own (no kept list in LDS), stores the sum
+// of the draw weights of each 512-token block (one wave's tokens of one step)
+// of its steps.  Row A's loads start as soon as the record is in: kDrawWin
+// steps stay in flight, the first window while row A's statistics and lists
+// are read.  The next launch reads the sums: the kernel boundary orders the
+// stores before the reads, with no hand-off between workgroups of one launch.
 template <class LT, bool VEC, int TOK>
-__global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
+__global__ __launch_bounds__(kBlock, (TOK || !VEC || sizeof(typename LT::T) == 4) ? 4 : 6) void draw_kernel(Args a) {
   typedef typename LT::Raw LR;
+  constexpr int kWin = sizeof(typename LT::T) == 2 ? kDrawWin : kDrawWin / 2;  // the same bytes in flight
   __shared__ double s_blk[kDrawSpan * kWaves];
   __shared__ int s_ban[TOK ? kBanMax : 1];
   __shared__ int s_pid[TOK == 2 ? kPenMax : 1];
@@ -2752,12 +2854,24 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   const int V = a.V, A = cx.A, mode = cx.mode, nsteps = cx.nsteps;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const ReqRec& rr = cx.rr;
-  const DrawW& dwt = cx.dwt;
   const typename LT::T* lrow = cx.lrow;
   const float* qrow = cx.qrow;
   DrawSum* ds = cx.ds;
-  DrawSum* dt = cx.dt;
   const int s0 = part * kDrawSpan, cnt = min(kDrawSpan, nsteps - s0);
+  // a tempered residual at large 1/T: fp64 draft weights, one step at a time
+  const bool precise = mode == 1 && cx.T != 1.f && draft_w(cx.T).precise;
+  // the first window of steps (steps past the row end load nothing and weigh zero)
+  LR lr[kWin];
+  F32::Raw qr[kWin];
+  if (!precise) {
+#pragma unroll
+    for (int u = 0; u < kWin; ++u) {
+      const int base = (s0 + u) * kStep + tid * kCh;
+      lr[u] = load_logits<LT, VEC>(lrow, base, V);
+      qr[u] = (mode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
+    }
+  }
+  const DrawW dwt = draw_weights<LT>(a, i, cx);
   // the request's banned tokens (checked by the row pass, which faults the
   // request on a bad list)
   int nban = 0;
@@ -2777,9 +2891,10 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
   }
   const Toks tk = toks((const LDS_AS int*)s_ban, nban, (const LDS_AS int*)s_pid, (const LDS_AS float*)s_pd,
                        (LDS_AS float*)s_stage + (threadIdx.x >> 6) * 512, npen, theta);
-  // Sum of one lane's 8 draw weights (raw values l, q of step u); the lists
-  // walk ascending 512-token wave ranges, so steps come in order.
-  auto lane_sum = [&](LR& l, F32::Raw& q, int u, BanWalk& bw, PenWalk& pw, auto precise) {
+  // Sum of one lane's 8 draw weights (raw values l, q of step u) under the
+  // compile-time draw form f = (MODE, TEMPER, FILT, PRECISE); the lists walk
+  // ascending 512-token wave ranges, so steps come in order.
+  auto lane_sum = [&](LR& l, F32::Raw& q, int u, BanWalk& bw, PenWalk& pw, auto md, auto tp, auto ft, auto pr) {
     const int base = (s0 + u) * kStep + tid * kCh;
     if (TOK == 2) pen_walk(pw, tk, (s0 + u) * kStep + wave * 512, l, q, mode == 1);
     if (TOK) {
@@ -2789,49 +2904,76 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
         if (mode == 1) ban_apply(q, m, 0u);
       }
     }
-    float lv[8], qv[8];
+    float lv[8], qv[8], w[8];
     LT::unpack(l, lv);
-    F32::unpack(q, qv);
-    double sw = 0.0;
+    if (decltype(md)::value == 1) F32::unpack(q, qv);
+    if constexpr (decltype(pr)::value) {
+      // fp64 weights: summed as they come (eight interleaved would not fit the registers)
+      double sw = 0.0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float pe;
-      sw += (double)draw_weight<decltype(precise)::value>(lv[e], qv[e], base + e, dwt, pe);
+      for (int e = 0; e < 8; ++e)
+        sw += (double)draw_w<1, true, decltype(ft)::value, true>(lv[e], qv[e], base + e, dwt);
+      return sw;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        w[e] = draw_w<decltype(md)::value, decltype(tp)::value, decltype(ft)::value, false>(
+            lv[e], decltype(md)::value == 1 ? qv[e] : 0.f, base + e, dwt);
+      return lane_sum8(w);
     }
-    return sw;
   };
   BanWalk bw;
   PenWalk pw;
   if (TOK) bw = ban_start(tk.ban, tk.nban);
   if (TOK == 2) pw = pen_start(tk.npen);
-  if (mode == 1 && dwt.temper && dwt.dw.precise) {
-    // tempered residual at large 1/T: one step at a time
+  const bool filt = dwt.cut_p > -INFINITY || dwt.cut_q > -INFINITY;
+  typedef std::integral_constant<int, 0> M0;
+  typedef std::integral_constant<int, 1> M1;
+  typedef std::integral_constant<int, 2> M2;
+  typedef std::true_type Y;
+  typedef std::false_type N;
+  if (precise) {
     for (int u = 0; u < cnt; ++u) {
       const int base = (s0 + u) * kStep + tid * kCh;
       LR l = load_logits<LT, VEC>(lrow, base, V);
       F32::Raw q = load_probs<VEC>(qrow, base, V);
-      const double sw = wave_sum_f64(lane_sum(l, q, u, bw, pw, std::true_type{}));
+      const double sw = filt ? wave_sum_f64(lane_sum(l, q, u, bw, pw, M1{}, Y{}, Y{}, Y{}))
+                             : wave_sum_f64(lane_sum(l, q, u, bw, pw, M1{}, Y{}, N{}, Y{}));
       if (lane == 0) s_blk[u * kWaves + wave] = sw;
     }
   } else {
-    // all of this workgroup's loads first, then the sums (block sums go to
-    // LDS: a global store here would count against the counter the loads
-    // wait on)
-    LR lr[kDrawSpan];
-    F32::Raw qr[kDrawSpan];
+    // step u is reduced while steps u + 1 .. u + kWin are in flight (block
+    // sums go to LDS: a global store here would count against the counter the
+    // loads wait on); one loop per draw form, chosen once
+    auto stream = [&](auto md, auto tp, auto ft) {
 #pragma unroll
-    for (int u = 0; u < kDrawSpan; ++u) {
-      const int base = (s0 + u) * kStep + tid * kCh;
-      if (u < cnt) {
-        lr[u] = load_logits<LT, VEC>(lrow, base, V);
-        qr[u] = (mode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
+      for (int u = 0; u < kDrawSpan; ++u) {
+        if (u >= cnt) break;
+        LR l = lr[u % kWin];
+        F32::Raw q = qr[u % kWin];
+        if (u + kWin < kDrawSpan) {
+          const int base = (s0 + u + kWin) * kStep + tid * kCh;
+          lr[u % kWin] = load_logits<LT, VEC>(lrow, base, V);
+          if (decltype(md)::value == 1) qr[u % kWin] = load_probs<VEC>(qrow, base, V);
+        }
+        const double sw = wave_sum_f64(lane_sum(l, q, u, bw, pw, md, tp, ft, N{}));
+        if (lane == 0) s_blk[u * kWaves + wave] = sw;
       }
-    }
-#pragma unroll
-    for (int u = 0; u < kDrawSpan; ++u) {
-      if (u >= cnt) break;
-      const double sw = wave_sum_f64(lane_sum(lr[u], qr[u], u, bw, pw, std::false_type{}));
-      if (lane == 0) s_blk[u * kWaves + wave] = sw;
+    };
+    if (mode == 1) {
+      if (dwt.temper) {
+        if (filt) stream(M1{}, Y{}, Y{});
+        else stream(M1{}, Y{}, N{});
+      } else {
+        if (filt) stream(M1{}, N{}, Y{});
+        else stream(M1{}, N{}, N{});
+      }
+    } else if (mode == 2) {
+      if (filt) stream(M2{}, N{}, Y{});
+      else stream(M2{}, N{}, N{});
+    } else {
+      if (filt) stream(M0{}, N{}, Y{});
+      else stream(M0{}, N{}, N{});
     }
   }
   __syncthreads();
@@ -2840,22 +2982,16 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Args a) {
     d.sw = s_blk[tid];
     ds[(size_t)s0 * kWaves + tid] = d;
   }
-  if (wave == 0) {
-    // this part's total: the last lane of the scan over its blocks in order
-    const double b = lane < cnt * kWaves ? s_blk[lane] : 0.0;
-    DrawSum t;
-    t.sw = readlane_d(wave_incl_scan_f64(b), 63);
-    if (lane == 0) dt[part] = t;
-  }
 }
 
 // Draw pass, part 2 (grid: one workgroup per request): the outputs, and the
-// draw left to this pass.  Wave 0 scans the part totals in token order,
-// repeats the scan of the part where the running sum first exceeds u * S
-// (the same arithmetic, so the two levels agree), re-reads the block where it
-// is crossed and finds the token (inverse CDF over ascending id; if rounding
-// leaves no crossing, the largest id with w > 0; if the weights sum to zero,
-// the same over p', whose sums the workgroup forms itself).
+// draw left to this pass.  Wave 0 loads every block sum of row A (kFindPer
+// consecutive blocks per lane, all in flight), forms S = their sum in token
+// order (lane sums, then a wave scan), finds the lane, then the block, where
+// the running sum first exceeds u * S, re-reads that block and finds the
+// token (inverse CDF over ascending id).  Where rounding leaves no crossing:
+// the last block, then the last token, of positive weight.  If the weights
+// sum to zero, the same over p', whose block sums the workgroup forms itself.
 template <class LT, bool VEC, int TOK>
 __global__ __launch_bounds__(kBlock) void find_kernel(Args a) {
   typedef typename LT::Raw LR;
@@ -2863,18 +2999,47 @@ __global__ __launch_bounds__(kBlock) void find_kernel(Args a) {
   __shared__ int s_pid[TOK == 2 ? kPenMax : 1];
   __shared__ float s_pd[TOK == 2 ? kPenMax : 1];
   __shared__ float s_stage[TOK == 2 ? kWaves * 512 : 1];
+  __shared__ double s_tw;
   const int i = blockIdx.x;
   const DrawCtx<LT> cx = draw_ctx<LT>(a, i);
+  const float us = a.u_sample[i];
   request_outputs(a, i, cx.rr, cx.A, cx.defer);
   if (!cx.defer) return;
   const int G = a.G, V = a.V, A = cx.A, mode = cx.mode, nsteps = cx.nsteps;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const ReqRec& rr = cx.rr;
-  const DrawW& dwt = cx.dwt;
   const typename LT::T* lrow = cx.lrow;
   const float* qrow = cx.qrow;
   DrawSum* ds = cx.ds;
-  DrawSum* dt = cx.dt;
+  const int nb = nsteps * kWaves;
+  constexpr int kChunk = 64 * kFindPer;
+  // one chunk of block sums: this lane's kFindPer consecutive blocks and the
+  // wave's inclusive scan of the lane sums (summed in block order)
+  auto chunk = [&](int c0, double (&xs)[kFindPer], double& is) {
+#pragma unroll
+    for (int t = 0; t < kFindPer; ++t) {
+      const int b = c0 + lane * kFindPer + t;
+      xs[t] = b < nb ? ds[b].sw : 0.0;
+    }
+    double ls = 0.0;
+#pragma unroll
+    for (int t = 0; t < kFindPer; ++t) ls += xs[t];
+    is = wave_incl_scan_f64(ls);
+  };
+  // the total, chunk totals summed in order (wave 0); the first chunk stays in registers
+  double x[kFindPer], incl = 0.0;
+  auto total = [&]() {
+    chunk(0, x, incl);
+    double s = readlane_d(incl, 63);
+    for (int c0 = kChunk; c0 < nb; c0 += kChunk) {
+      double y[kFindPer], iy;
+      chunk(c0, y, iy);
+      s += readlane_d(iy, 63);
+    }
+    if (lane == 0) s_tw = s;
+  };
+  if (wave == 0) total();
+  const DrawW dwt = draw_weights<LT>(a, i, cx);
   // the request's banned tokens (checked by the row pass, which faults the
   // request on a bad list)
   int nban = 0;
@@ -2882,8 +3047,8 @@ __global__ __launch_bounds__(kBlock) void find_kernel(Args a) {
     const int b0 = a.ban_off[i];
     nban = a.ban_off[i + 1] - b0;
     for (int t = tid; t < nban; t += kBlock) s_ban[t] = a.ban_ids[(size_t)b0 + t];
-    __syncthreads();
   }
+  __syncthreads();
   // row A's penalty list (checked by the row pass likewise)
   int npen = 0;
   float theta = 1.f;
@@ -2896,7 +3061,7 @@ __global__ __launch_bounds__(kBlock) void find_kernel(Args a) {
                        (LDS_AS float*)s_stage + (threadIdx.x >> 6) * 512, npen, theta);
   // Weights of one lane's 8 tokens in block blk (512 tokens: step blk / 4,
   // wave range blk % 4) under draw mode md; lists applied token by token.
-  auto block_weights = [&](int blk, int md, float w[8], int& base) {
+  auto block_weights = [&](int blk, int md, float w[8], int& base) -> bool {
     base = (blk / kWaves) * kStep + (blk % kWaves) * 512 + lane * kCh;
     LR lb = load_logits<LT, VEC>(lrow, base, V);
     F32::Raw qb = (md == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
@@ -2930,107 +3095,82 @@ __global__ __launch_bounds__(kBlock) void find_kernel(Args a) {
     dd.mode = md;
     const bool prec = md == 1 && dd.temper && dd.dw.precise;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float pe;
-      w[e] = prec ? draw_weight<true>(lv[e], qv[e], base + e, dd, pe)
-                  : draw_weight<false>(lv[e], qv[e], base + e, dd, pe);
-    }
+    for (int e = 0; e < 8; ++e)
+      w[e] = prec ? draw_weight<true>(lv[e], qv[e], base + e, dd) : draw_weight<false>(lv[e], qv[e], base + e, dd);
+    return prec;
   };
 
-  // the total over the parts, in part order (wave 0; the other waves wait)
-  __shared__ double s_tw;
-  if (wave == 0) {
-    double tw = 0.0;
-    for (int p0 = 0; p0 < a.dparts; p0 += 64) {
-      const double x = p0 + lane < a.dparts ? dt[p0 + lane].sw : 0.0;
-      tw += readlane_d(wave_incl_scan_f64(x), 63);
-    }
-    if (lane == 0) s_tw = tw;
-  }
-  __syncthreads();
   int dmode = mode;
+  bool held = nb <= kChunk;  // wave 0 holds every block sum in registers
   if (!(s_tw > 0.0)) {
     // Zero residual (p' and q' agree and the draft token lies outside both
-    // kept sets): the draw is from p'.  Rare: the block and part sums of p'
-    // are formed here, by this workgroup alone.
+    // kept sets): the draw is from p'.  Rare: the block sums of p' are
+    // formed here, by this workgroup alone.
     dmode = 0;
-    const int nblk = nsteps * kWaves;
-    for (int blk = wave; blk < nblk; blk += kWaves) {
+    held = false;
+    for (int blk = wave; blk < nb; blk += kWaves) {
       float w[8];
       int base;
-      block_weights(blk, 0, w, base);
-      double ls = 0.0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ls += (double)w[e];
+      block_weights(blk, 0, w, base);  // (mode 0: never the precise form)
       DrawSum d;
-      d.sw = wave_sum_f64(ls);
+      d.sw = wave_sum_f64(lane_sum8(w));
       if (lane == 0) ds[blk] = d;
     }
     __syncthreads();
-    if (wave == 0) {
-      double tw = 0.0;
-      for (int p = 0; p < a.dparts; ++p) {
-        const int k0 = p * kDrawSpan, kc = min(kDrawSpan, nsteps - k0);
-        const double x = lane < kc * kWaves ? ds[(size_t)k0 * kWaves + lane].sw : 0.0;
-        DrawSum t;
-        t.sw = readlane_d(wave_incl_scan_f64(x), 63);
-        tw += t.sw;
-        if (lane == 0) dt[p] = t;
-      }
-      if (lane == 0) s_tw = tw;
-    }
-    __syncthreads();
+    if (wave == 0) total();
   }
   if (wave != 0) return;
-  const double S = s_tw;
-  const double tau = (double)a.u_sample[i] * S;
-  // the part, then the block within it, where the running sum first exceeds
-  // tau; where rounding leaves tau at or past the total, the last part and
-  // block of positive weight, and there the last token of positive weight
+  const double S = readlane_d(s_tw, 0);
+  const double tau = (double)us * S;
+  // the lane, then its block, where the running sum first exceeds tau; where
+  // rounding leaves tau at or past the total, the last block of positive
+  // weight, and there the last token of positive weight
   double pre = 0.0, pstar = 0.0;
-  int kstar = -1, klast = -1;
-  for (int p0 = 0; p0 < a.dparts; p0 += 64) {
-    const double x = p0 + lane < a.dparts ? dt[p0 + lane].sw : 0.0;
-    const double incl = wave_incl_scan_f64(x);
-    const uint64_t pos = __ballot(x > 0.0);
-    if (pos) klast = p0 + 63 - __clzll((long long)pos);
-    if (kstar < 0) {
-      const uint64_t hit = __ballot(x > 0.0 && pre + incl > tau);
+  int bstar = -1, blast = -1;
+  for (int c0 = 0; c0 < nb; c0 += kChunk) {
+    if (!held) chunk(c0, x, incl);
+    int lp = -1;
+#pragma unroll
+    for (int t = 0; t < kFindPer; ++t)
+      if (x[t] > 0.0) lp = c0 + lane * kFindPer + t;
+    blast = max(blast, wave_max_i(lp));
+    if (bstar < 0) {
+      const uint64_t hit = __ballot(lp >= 0 && pre + incl > tau);
       if (hit) {
         const int l = __ffsll((unsigned long long)hit) - 1;
-        kstar = p0 + l;
-        pstar = pre + (l > 0 ? readlane_d(incl, l - 1) : 0.0);
+        double run = pre + (l > 0 ? readlane_d(incl, l - 1) : 0.0);
+        int bl = -1, blp = -1;
+        double pb = 0.0, pbp = 0.0;
+#pragma unroll
+        for (int t = 0; t < kFindPer; ++t) {
+          if (x[t] > 0.0) {
+            if (bl < 0 && run + x[t] > tau) {
+              bl = t;
+              pb = run;
+            }
+            blp = t;
+            pbp = run;
+          }
+          run += x[t];
+        }
+        if (bl < 0) {
+          bl = blp;
+          pb = pbp;
+        }
+        bstar = c0 + l * kFindPer + __builtin_amdgcn_readlane(bl, l);
+        pstar = readlane_d(pb, l);
       } else {
         pre += readlane_d(incl, 63);
       }
     }
   }
-  bool last = kstar < 0;
-  const int kp = last ? klast : kstar;
-  int rstar = -1;
-  if (kp >= 0) {
-    const int k0 = kp * kDrawSpan, kc = min(kDrawSpan, nsteps - k0);
-    const double x = lane < kc * kWaves ? ds[(size_t)k0 * kWaves + lane].sw : 0.0;
-    const double incl = wave_incl_scan_f64(x);
-    const uint64_t pos = __ballot(x > 0.0);
-    const uint64_t hit = last ? 0ull : __ballot(x > 0.0 && pstar + incl > tau);
-    if (hit) {
-      const int l = __ffsll((unsigned long long)hit) - 1;
-      rstar = k0 * kWaves + l;
-      pstar += (l > 0 ? readlane_d(incl, l - 1) : 0.0);
-    } else if (pos) {
-      last = true;
-      rstar = k0 * kWaves + 63 - __clzll((long long)pos);
-    }
-  }
+  const bool last = bstar < 0;
+  const int rstar = last ? blast : bstar;
   int z = -1;
   if (rstar >= 0) {
     float w[8];
     int base;
-    block_weights(rstar, dmode, w, base);
-    double ls = 0.0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ls += (double)w[e];
+    const double ls = block_weights(rstar, dmode, w, base) ? lane_sum8_seq(w) : lane_sum8(w);
     double acc = pstar + (wave_incl_scan_f64(ls) - ls);
     int zz = INT_MAX, lastpos = -1;
 #pragma unroll
@@ -3106,7 +3246,6 @@ size_t dsum_bytes(int N, int V) {
   return align_up((size_t)N * ((V + kStep - 1) / kStep) * kWaves * sizeof(DrawSum), 256);
 }
 size_t draw_parts(int V) { return ((size_t)(V + kStep - 1) / kStep + kDrawSpan - 1) / kDrawSpan; }
-size_t dtot_bytes(int N, int V) { return align_up((size_t)N * draw_parts(V) * sizeof(DrawSum), 256); }
 
 struct Events {
   hipEvent_t start, mid, end;
@@ -3116,8 +3255,10 @@ template <class LT, bool VEC, int TOK>
 hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
   const long rows = a.synthetic ? (long)a.N : (long)a.N * (a.G + 1);  // synthetic mode: row A only
   hipError_t e;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kBlock), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!a.direct) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kBlock), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   // the row pass's events travel in its own dispatch (start and end of the
   // kernel), so timing it adds no packets before or after it on the stream
   if (ev.start || ev.mid)
@@ -3194,8 +3335,6 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   off += rec_bytes(N);
   a.dsum = reinterpret_cast<DrawSum*>(ws + off);
   off += dsum_bytes(N, V);
-  a.dtot = reinterpret_cast<DrawSum*>(ws + off);
-  off += dtot_bytes(N, V);
   a.plan = reinterpret_cast<int*>(ws + off);
   a.dparts = (int)dparts;
   a.cu = lay.cu;
@@ -3213,6 +3352,7 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   a.pen_pres = pen.pres;
   a.pen_freq = pen.freq;
   a.synthetic = synthetic ? 1 : 0;
+  a.direct = (!lay.cu && !synthetic) ? 1 : 0;
   a.srates = srates;
 
   // 16-byte vector loads need every row start aligned: V a multiple of 8 and
@@ -3275,8 +3415,7 @@ extern "C" {
 
 size_t spec_verify_workspace_size(int N, int gmax, int V) {
   if (N <= 0 || gmax < 0 || V <= 0) return 256;
-  return kHeadBytes + stats_bytes(N, gmax) + rec_bytes(N) + dsum_bytes(N, V) + dtot_bytes(N, V) +
-         plan_bytes(N, gmax);
+  return kHeadBytes + stats_bytes(N, gmax) + rec_bytes(N) + dsum_bytes(N, V) + plan_bytes(N, gmax);
 }
 
 int spec_verify(int N, int gmax, int V, const int32_t* draft_ids, const float* draft_probs, const void* target_logits,

@@ -60,8 +60,10 @@ extern "C" {
 #define SPEC_VERIFY_ERR_NULL 1      /* a required pointer is NULL                        */
 #define SPEC_VERIFY_ERR_SHAPE 2     /* N < 0, gmax outside [0, 64], V < 1, or too large  */
 /* "Too large": V * (gmax + 1) above 2^40, V above 2^31 - 4097, or either
- * launch grid reaching 2^32 work-items: 256 * N * (gmax + 1) (row pass) or
- * 256 * N * ceil(ceil(V / 2048) / 4) (draw pass). */
+ * launch grid reaching 2^32 work-items: 256 * N * (gmax + 1) (row pass; in
+ * the padded layout 256 * N * (gmax + 2) when gmax is a positive multiple of
+ * 8, and 256 * N in the synthetic mode) or 256 * N * ceil(ceil(V / 2048) / 4)
+ * (draw pass). */
 #define SPEC_VERIFY_ERR_DTYPE 3     /* unknown logits_dtype                              */
 #define SPEC_VERIFY_ERR_WORKSPACE 4 /* workspace_bytes below spec_verify_workspace_size  */
 #define SPEC_VERIFY_ERR_HIP 5       /* a HIP runtime call failed (launch, copy, wait)      */

@@ -184,11 +184,21 @@ struct Args {
   const float* pen_rep;    // [N] repetition penalty, or nullptr (1)
   const float* pen_pres;   // [N] presence penalty, or nullptr (0)
   const float* pen_freq;   // [N] frequency penalty, or nullptr (0)
+  int dslots;           // direct mode: row-pass blocks per request for its draft positions
   int direct;           // 1: padded layout, standard mode: no plan kernel; each row workgroup finds
                         // gamma_i from the ids and the outcome lives in the rows' records
   int synthetic;        // 1: the synthetic acceptance mode (draft j accepted iff u_j < srates[j])
   const float* srates;  // synthetic acceptance rates [G]
 };
+
+// Direct mode: row-pass blocks per request for its draft positions (gmax,
+// one more when gmax is a multiple of 8, so that a request's positions do
+// not each land on one XCD), and the row pass's grid.
+__host__ __device__ inline int direct_slots(int G) { return (G > 0 && G % 8 == 0) ? G + 1 : G; }
+__host__ __device__ inline long long row_blocks(int N, int G, bool synthetic, bool direct) {
+  if (synthetic) return N;  // row A only
+  return (long long)N * ((direct ? direct_slots(G) : G) + 1);
+}
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -2503,22 +2513,28 @@ __global__ __launch_bounds__(kBlock, TOK == 2 ? 2 : (sizeof(typename LT::T) == 2
   __shared__ int s_pid[TOK == 2 ? kPenMax : 1];
   __shared__ float s_pd[TOK == 2 ? kPenMax : 1];
   __shared__ float s_stage[TOK == 2 ? kWaves * 512 : 1];
-  // the draft rows first (the larger rows, request-major, so consecutive
-  // blocks, which dispatch round-robin over the XCDs, read neighbouring
-  // rows), then one bonus row per request.  Plan mode: the plan lists the
-  // draft rows and the launch's blocks past the real rows exit at once.
-  // Direct mode: block b < N * gmax is draft position (b / gmax, b % gmax),
-  // and exits at once if that is a padding position; the rest are bonus rows.
+  // The draft rows first (the larger rows), request-major (consecutive
+  // blocks, which dispatch round-robin over the 8 XCDs, read neighbouring
+  // rows, in memory order), then one bonus row per request.  Plan mode: the
+  // plan lists the draft rows and the launch's blocks past the real rows exit
+  // at once.  Direct mode: request i owns `dslots` consecutive blocks, slot
+  // j < gmax being position j (a padding position exits at once).  With
+  // gmax a multiple of 8 there is one more slot, which exits without a load:
+  // otherwise block i * gmax + j would sit on XCD j for every request, and a
+  // ragged batch's mostly-padding high positions would leave XCDs idle.
   const int bx = (int)blockIdx.x;
   int i, j;
   Req rq;
   if (a.direct) {
     if (bx == 0 && threadIdx.x == 0) *a.nfault = 0u;  // the find kernel counts this call's faulted requests
-    const int nd = a.N * a.G;
+    const int ns = a.dslots;
+    const int nd = a.N * ns;
     const bool bonus = bx >= nd;
-    i = bonus ? bx - nd : bx / a.G;
+    i = bonus ? bx - nd : bx / ns;
+    const int slot = bonus ? 0 : bx - i * ns;
+    if (!bonus && slot >= a.G) return;
     rq = load_req(a, i);
-    j = bonus ? rq.gamma : bx - i * a.G;
+    j = bonus ? rq.gamma : slot;
     if (!bonus && j >= rq.gamma) return;
   } else {
     const int nd = a.plan[0];
@@ -3253,7 +3269,7 @@ struct Events {
 
 template <class LT, bool VEC, int TOK>
 hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
-  const long rows = a.synthetic ? (long)a.N : (long)a.N * (a.G + 1);  // synthetic mode: row A only
+  const long rows = row_blocks(a.N, a.G, a.synthetic, a.direct);
   hipError_t e;
   if (!a.direct) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kBlock), 0, stream, a);
@@ -3300,7 +3316,8 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   if ((long long)V * (G + 1) > (1LL << 40) || V > 0x7fffffff - 2 * kStep) return SPEC_VERIFY_ERR_SHAPE;
   // a dispatch holds its grid size in work-items as a 32-bit number
   const long long dparts = (long long)draw_parts(V);
-  if ((long long)N * (G + 1) * kBlock > 0xffffffffLL || (long long)N * dparts * kBlock > 0xffffffffLL)
+  if ((long long)row_blocks(N, G, synthetic, !lay.cu && !synthetic) * kBlock > 0xffffffffLL ||
+      (long long)N * dparts * kBlock > 0xffffffffLL)
     return SPEC_VERIFY_ERR_SHAPE;
   if (N == 0) return SPEC_VERIFY_OK;
   if (!logits || !u_sample || !out_tokens || !out_num) return SPEC_VERIFY_ERR_NULL;
@@ -3353,6 +3370,7 @@ int run(int N, int G, int V, const Layout& lay, bool synthetic, const float* sra
   a.pen_freq = pen.freq;
   a.synthetic = synthetic ? 1 : 0;
   a.direct = (!lay.cu && !synthetic) ? 1 : 0;
+  a.dslots = direct_slots(G);
   a.srates = srates;
 
   // 16-byte vector loads need every row start aligned: V a multiple of 8 and

@@ -83,7 +83,11 @@ def test_host_validation(lib):
     assert _call(lib, ua=0) == 1
     assert _call(lib, N=0) == 0  # empty batch: nothing to do
     # grids whose size in work-items (256 per workgroup) needs more than 32 bits
-    assert _call(lib, N=(1 << 24) // 65 + 1, G=64) == 2     # row pass: N * (gmax + 1) workgroups
+    assert _call(lib, N=(1 << 24) // 65 + 1, G=64) == 2     # row pass: N * (gmax + 2) workgroups
+    # padded layout, gmax a multiple of 8: one more row-pass workgroup per request
+    assert _call(lib, N=(1 << 32) // 2560 + 1, G=8) == 2     # N * 10 * 256 reaches 2^32
+    assert _call(lib, N=(1 << 32) // 2560, G=8, logits=0) == 1  # just inside: the next check fires
+    assert _call(lib, N=(1 << 32) // 2560 + 1, G=7, logits=0) == 1  # gmax = 7: N * 8 workgroups
     assert _call(lib, N=(1 << 24) // 2, G=0, V=16384) == 2   # draw pass: N * 2 workgroups at 8192 < V <= 16384
     assert _call(lib, N=(1 << 24) // 2 - 1, G=0, V=16384, logits=0) == 1  # just inside: the next check fires
     assert _call(lib, N=(1 << 24), G=0, V=16) == 2           # row pass: N workgroups

@@ -362,7 +362,7 @@ int spec_verify_device_errors(const void *workspace, size_t workspace_bytes, voi
  * first call on a device looks up that device's address of the array, with
  * the device current.  Sizes whose spec_verify_workspace_size exceeds the
  * scratch are refused with SPEC_VERIFY_ERR_SCRATCH (N = 4096, gmax = 8,
- * V = 151936 needs 12.6 MiB).  Every call on a GPU shares that GPU's
+ * V = 151936 needs 11.9 MiB).  Every call on a GPU shares that GPU's
  * array: calls that overlap on one GPU (different streams, or host threads
  * without ordering) race and their results are undefined; calls ordered on
  * one stream are safe, since each call resets what it reads from the array.

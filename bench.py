@@ -10,12 +10,20 @@ the timed region; ceil(512 MB / bytes per step) copies of them (at least 2, at
 most 64) rotate between steps so that no step reads data an earlier step left
 in the 256 MB Infinity Cache.
 
+Before the timed steps the step runs at least --warmup times and for at
+least --warmup-ms of wall time, so that the GPU's clocks have settled.  The
+padded call is bound once (rejection_sampling_verify_13_amd.Prepared), so a
+step costs the host one C call.  The row kernel is timed with HIP events
+carried by its own dispatch, created without a system-scope release
+(hipEventDisableSystemFence), so timing a step does not slow the next one.
+
 Prints one JSON line: verified draft positions per second (sum of gamma_i per
 step / time), the roofline of the dominant kernel (the row pass, timed with
 HIP events on its stream), and the CPU oracle timed on a bounded sample of the
 same workload.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -81,6 +89,43 @@ def traffic_from_profile(digest, workload):
         if src == digest and wl == workload:
             return int(b)
     return None
+
+
+class TimingEvent:
+    """A HIP event that only times the row kernel, created through the HIP
+    runtime this process already loaded (found by its path in
+    /proc/self/maps, so no second runtime is loaded).  With
+    hipEventDisableSystemFence (the default here) recording it makes no
+    system-scope release: a default event's release writes back and
+    invalidates the caches, which costs the step after it a few microseconds.
+    elapsed_time() is read only after a device-wide synchronisation."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+            hip = ctypes.CDLL(path)
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self, fence=False):
+        h = ctypes.c_void_p()
+        rc = self._runtime().hipEventCreateWithFlags(ctypes.byref(h), 0 if fence else self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
+        self.cuda_event = h.value
+
+    def elapsed_time(self, end):
+        ms = ctypes.c_float()
+        rc = self._runtime().hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.cuda_event),
+                                                 ctypes.c_void_p(end.cuda_event))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return ms.value
 
 
 def host_threads():
@@ -167,6 +212,11 @@ def main():
                     help="time the row kernel with HIP events on every Nth timed step (the events travel in the "
                          "row kernel's own dispatch; the wall-clock throughput covers every step); default: every "
                          "step when --steps is below 100, else every 4th")
+    ap.add_argument("--warmup-ms", type=float, default=250.0,
+                    help="keep warming up past --warmup steps until this much wall time has passed")
+    ap.add_argument("--timing-events", choices=("nofence", "fence"), default="nofence",
+                    help="the row kernel's HIP events: without a system-scope release (default) or with one "
+                         "(hipEventDefault)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -250,6 +300,12 @@ def main():
                 d["ban_ids"] = torch.from_numpy(ban[1]).to(dev)
             if pen is not None:
                 d.update({k: torch.from_numpy(v).to(dev) for k, v in pen.items()})
+            if not flat and rates is None and ban is None and pen is None:
+                # the padded call bound once: one C call per step on the host
+                d["call"] = sv.Prepared(d["draft_ids"], d["draft_probs"], d["target_logits"], d["temperature"],
+                                        d["top_k"], d["top_p"], d["u_accept"], d["u_sample"],
+                                        out_tokens=d["out_t"], out_num_accepted=d["out_n"], workspace=d["ws"],
+                                        stream=torch.cuda.current_stream(dev))
             ps.append(d)
         sets.append(ps)
     del batch["target_logits"], batch["draft_probs"]
@@ -260,6 +316,12 @@ def main():
             ev = None
             if events is not None:
                 ev = events[pi]
+            if "call" in d:
+                d["call"](ev)
+                if args.rollback:
+                    sv.rollback(d["out_n"], num_computed_tokens=d["nct"], slot_mapping=d["slots"], stream=stream,
+                                draft_ids=d["draft_ids"])
+                continue
             kw = dict(out_tokens=d["out_t"], out_num_accepted=d["out_n"], workspace=d["ws"], stream=stream, events=ev)
             if rates is not None:
                 kw.update(synthetic_rates=d["rates"])
@@ -274,20 +336,25 @@ def main():
                     dict(draft_ids=d["draft_ids"])
                 sv.rollback(d["out_n"], num_computed_tokens=d["nct"], slot_mapping=d["slots"], stream=stream, **lay)
 
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-
     K = args.steps
     every = args.time_every if args.time_every > 0 else (1 if args.steps < 100 else 4)
     timed = list(range(0, K, every))
-    # start and end of the row kernel (the third event of the entry point, after the draw pass, is not used)
-    evs = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), None) for _ in parts]
-           for k in timed}
-    for per_step in evs.values():  # torch creates an event's handle on its first record
-        for pair in per_step:
-            for e in pair[:2]:
-                e.record(stream)
+    # start and end of the row kernel (the third event of the entry point, after the draw pass, is not used),
+    # created before the warm-up so that no host work separates it from the timed steps
+    fence = args.timing_events == "fence"
+    evs = {k: [(TimingEvent(fence), TimingEvent(fence), None) for _ in parts] for k in timed}
+
+    # warm-up: the requested steps, and more until the GPU has run the step for
+    # at least --warmup-ms (its clocks settle over tens of milliseconds of
+    # load: a 20-step run right after 5 warm-up steps measured its row kernel
+    # 3 % slower than after 2000)
+    t_w = time.perf_counter()
+    warm = 0
+    while warm < args.warmup or (time.perf_counter() - t_w) * 1e3 < args.warmup_ms:
+        step(warm)
+        warm += 1
+        if warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
@@ -312,6 +379,8 @@ def main():
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel="row_kernel", kernel_avg_us=round(row_avg_s * 1e6, 2),
                     kernel_us_p10_p50_p90=row_pct, input_sets_rotated=n_sets, launches_timed=len(timed),
+                    timing_events=("hipEventDefault" if args.timing_events == "fence" else
+                                   "hipEventDisableSystemFence"),
                     algorithmic_bytes_per_launch=B_alg,
                     fetch_gbps=None if traffic is None else round(traffic / row_avg_s / 1e9, 1),
                     scope="the row kernel alone (the dominant kernel); the whole verify step (plan, row, draw "
@@ -343,6 +412,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_steps_run": warm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -374,6 +374,66 @@ def to_device(batch: dict, device="cuda"):
     return out
 
 
+class Prepared:
+    """A padded-layout verify call bound once to its buffers.
+
+    The arguments are those of verify() (outputs, workspace and stream
+    allocated or taken as there) and are checked and marshalled here, once;
+    each call then makes one C call, spec_verify (spec_verify_timed with
+    ``events``), with no checks or allocations on the host.  For loops that
+    refill the same input buffers in place every step.  The tensors must stay
+    alive and in place while the object is used, and calls are made with
+    their device current (one GPU per process)."""
+
+    def __init__(self, draft_ids, draft_probs, target_logits, temperature=None, top_k=None, top_p=None,
+                 u_accept=None, u_sample=None, *, out_tokens=None, out_num_accepted=None, workspace=None,
+                 stream=None):
+        if target_logits.dim() != 3 or not target_logits.is_contiguous():
+            raise ValueError("target_logits must be a contiguous [N, gmax+1, V] tensor")
+        N, G1, V = target_logits.shape
+        G = G1 - 1
+        dev = target_logits.device
+        if target_logits.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("target_logits must be bfloat16 or float32")
+        dt = BF16 if target_logits.dtype == torch.bfloat16 else F32
+        _check(draft_ids, "draft_ids", torch.int32, (N, G), dev)
+        _check(draft_probs, "draft_probs", torch.float32, (N, G, V), dev)
+        _check(temperature, "temperature", torch.float32, (N,), dev)
+        _check(top_k, "top_k", torch.int32, (N,), dev)
+        _check(top_p, "top_p", torch.float32, (N,), dev)
+        _check(u_accept, "u_accept", torch.float32, (N, G), dev)
+        _check(u_sample, "u_sample", torch.float32, (N,), dev)
+        if out_tokens is None:
+            out_tokens = torch.empty((N, G + 1), dtype=torch.int32, device=dev)
+        if out_num_accepted is None:
+            out_num_accepted = torch.empty((N,), dtype=torch.int32, device=dev)
+        _check(out_tokens, "out_tokens", torch.int32, (N, G + 1), dev)
+        _check(out_num_accepted, "out_num_accepted", torch.int32, (N,), dev)
+        if workspace is None:
+            workspace = torch.empty((workspace_size(N, G, V),), dtype=torch.uint8, device=dev)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        self.out_tokens, self.out_num_accepted = out_tokens, out_num_accepted
+        self._keep = (draft_ids, draft_probs, target_logits, temperature, top_k, top_p, u_accept, u_sample,
+                      workspace, stream)
+        self._head = (N, G, V, _ptr(draft_ids), _ptr(draft_probs), _ptr(target_logits), dt, _ptr(temperature),
+                      _ptr(top_k), _ptr(top_p), _ptr(u_accept), _ptr(u_sample), _ptr(out_tokens),
+                      _ptr(out_num_accepted))
+        self._tail = (_ptr(workspace), workspace.numel() * workspace.element_size(),
+                      ctypes.c_void_p(stream.cuda_stream))
+
+    def __call__(self, events=None):
+        """Enqueue the call; ``events`` = (start, mid, end) as for verify()."""
+        if events is None:
+            rc = lib.spec_verify(*self._head, *self._tail)
+        else:
+            evp = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in events]
+            rc = lib.spec_verify_timed(*self._head, None, None, None, None, *self._tail, *evp)
+        if rc != 0:
+            raise SpecVerifyError("spec_verify failed: %s" % lib.spec_verify_status_string(rc).decode())
+        return self.out_tokens, self.out_num_accepted
+
+
 def verify_batch(dev_batch: dict, **kw):
     """verify() with the arguments taken from a to_device() dict."""
     return verify(dev_batch["draft_ids"], dev_batch["draft_probs"], dev_batch["target_logits"],

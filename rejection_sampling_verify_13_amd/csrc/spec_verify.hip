@@ -2712,7 +2712,11 @@ __device__ inline double lane_sum8_seq(const float w[8]) {
 // rejection A, the token at A (drawn in the row pass, or a greedy row's
 // argmax; left to the draw below when `defer`), -1 after it, and the
 // diagnostics.  Run by one workgroup per request.
-__device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, int A, bool defer) {
+// In direct mode (`lanes`) lane t of each wave already holds draft id t
+// (lid) and row t's draw (ldr; row 64's in dr64) from rebuilding the record,
+// so the outputs need no loads of their own.
+__device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, int A, bool defer, bool lanes,
+                                       int lid, int ldr, int dr64) {
   const int G = a.G, tid = threadIdx.x;
   int32_t* out = a.out_tokens + (size_t)i * (G + 1);
   const RowStats* st = a.stats + (size_t)i * (G + 1);
@@ -2734,12 +2738,13 @@ __device__ inline void request_outputs(const Args& a, int i, const ReqRec& rr, i
   int z = -1;
   double S = NAN;
   if (!defer) {
-    z = st[A].draw;
-    S = st[A].s;
+    z = lanes ? (A < 64 ? __builtin_amdgcn_readlane(ldr, A) : dr64) : st[A].draw;
+    if (a.d_resid) S = st[A].s;
   }
   for (int t = tid; t <= G; t += kBlock) {
     if (defer && t == A) continue;
-    out[t] = t < A ? a.ids[(size_t)rr.id0 + t] : (t == A ? z : -1);
+    // (t < 64: this thread is lane t of wave 0)
+    out[t] = t < A ? ((lanes && t < 64) ? lid : a.ids[(size_t)rr.id0 + t]) : (t == A ? z : -1);
   }
   if (tid == 0) {
     a.out_num[i] = A;
@@ -2767,12 +2772,14 @@ struct DrawCtx {
   const typename LT::T* lrow;
   const float* qrow;
   DrawSum* ds;  // [nsteps * kWaves] block sums of row A
+  bool lanes;   // direct mode: lane t holds draft id t and row t's draw
+  int lid, ldr, ldr64;
 };
 
 // Direct mode: request i's record rebuilt from its draft ids (gamma_i: the
 // first negative one) and its rows' records (accept flag, fault bits, whether
 // the row drew), one load of each per lane; row 64 (gmax = 64) separately.
-__device__ inline ReqRec direct_rec(const Args& a, int i) {
+__device__ inline ReqRec direct_rec(const Args& a, int i, int& lid, int& ldr, int& ldr64) {
   const int lane = lane_id(), G = a.G;
   const RowStats* st = a.stats + (size_t)i * (G + 1);
   const int id = lane < G ? a.ids[(size_t)i * G + lane] : 0;
@@ -2796,6 +2803,9 @@ __device__ inline ReqRec direct_rec(const Args& a, int i) {
   r.q0 = a.q ? i * G : -1;
   r.lfault = 0u;
   r.pad = 0;
+  lid = id;
+  ldr = dr;
+  ldr64 = dr64;
   return r;
 }
 
@@ -2803,7 +2813,10 @@ template <class LT>
 __device__ inline DrawCtx<LT> draw_ctx(const Args& a, int i) {
   typedef typename LT::T ET;
   DrawCtx<LT> x;
-  x.rr = a.direct ? direct_rec(a, i) : a.rec[i];
+  x.lanes = a.direct != 0;
+  x.lid = x.ldr = x.ldr64 = 0;
+  if (a.direct) x.rr = direct_rec(a, i, x.lid, x.ldr, x.ldr64);
+  else x.rr = a.rec[i];
   x.T = a.temperature ? a.temperature[i] : 1.f;
   const ReqRec& rr = x.rr;
   const int gamma = rr.gamma;
@@ -2827,9 +2840,8 @@ __device__ inline DrawCtx<LT> draw_ctx(const Args& a, int i) {
 
 // How row A's tokens are weighed: from row A's statistics (wave-uniform).
 template <class LT>
-__device__ inline DrawW draw_weights(const Args& a, int i, const DrawCtx<LT>& x) {
+__device__ inline DrawW draw_weights(const Args& a, int i, const DrawCtx<LT>& x, const RowStats& sa) {
   const int A = x.A, mode = x.mode;
-  const RowStats sa = a.stats[(size_t)i * (a.G + 1) + A];
   DrawW dwt;
   dwt.m = sa.m;
   dwt.cut_p = sa.cut_p;
@@ -2887,7 +2899,7 @@ __global__ __launch_bounds__(kBlock, (TOK || !VEC || sizeof(typename LT::T) == 4
       qr[u] = (mode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
     }
   }
-  const DrawW dwt = draw_weights<LT>(a, i, cx);
+  const DrawW dwt = draw_weights<LT>(a, i, cx, a.stats[(size_t)i * (a.G + 1) + A]);
   // the request's banned tokens (checked by the row pass, which faults the
   // request on a bad list)
   int nban = 0;
@@ -3019,7 +3031,7 @@ __global__ __launch_bounds__(kBlock) void find_kernel(Args a) {
   const int i = blockIdx.x;
   const DrawCtx<LT> cx = draw_ctx<LT>(a, i);
   const float us = a.u_sample[i];
-  request_outputs(a, i, cx.rr, cx.A, cx.defer);
+  request_outputs(a, i, cx.rr, cx.A, cx.defer, cx.lanes, cx.lid, cx.ldr, cx.ldr64);
   if (!cx.defer) return;
   const int G = a.G, V = a.V, A = cx.A, mode = cx.mode, nsteps = cx.nsteps;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -3054,8 +3066,10 @@ __global__ __launch_bounds__(kBlock) void find_kernel(Args a) {
     }
     if (lane == 0) s_tw = s;
   };
+  // row A's record is requested before the block sums, so both arrive in one round trip
+  const RowStats sa = a.stats[(size_t)i * (G + 1) + A];
   if (wave == 0) total();
-  const DrawW dwt = draw_weights<LT>(a, i, cx);
+  const DrawW dwt = draw_weights<LT>(a, i, cx, sa);
   // the request's banned tokens (checked by the row pass, which faults the
   // request on a bad list)
   int nban = 0;

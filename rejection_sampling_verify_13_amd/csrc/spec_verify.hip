@@ -48,6 +48,9 @@
 //                 own, the draw by inverse CDF over ascending token id from
 //                 the block sums (one scan over all of them, then the
 //                 crossing block re-read).
+//   finish_kernel (instead of the two above, for calls without token lists
+//                 and with 128 to 384 requests) one 512-thread workgroup per
+//                 request: the outputs, row A's block sums in LDS, the search.
 //   rollback_kernel  (own entry point, after a verify call) the KV bookkeeping
 //                 of the rejected drafts.
 //
@@ -86,6 +89,12 @@ constexpr int kSeg = 128;               // gathered candidate tokens per wave an
 constexpr int kDrawSpan = 4;            // draw pass: 2048-token steps per workgroup
 constexpr int kDrawWin = 4;             // draw pass: steps in flight per workgroup
 constexpr int kFindPer = 8;             // draw search: block sums per lane and load round
+constexpr int kFinBlock = 512;          // fused draw pass: threads per workgroup (one workgroup per request)
+constexpr int kFinWaves = kFinBlock / 64;
+constexpr int kFinWin = 4;              // fused draw pass: 512-token blocks in flight per wave
+constexpr int kFinMinN = 128;           // fused draw pass from this many requests (half the CUs) ...
+constexpr int kFinMaxN = 384;           // ... to this many (1.5 per CU): one request per workgroup
+                                        // balances the draws left to the pass only in that range
 constexpr int kMaxGamma = 64;
 
 enum {
@@ -3218,6 +3227,222 @@ __global__ __launch_bounds__(kBlock) void find_kernel(Args a) {
   }
 }
 
+// One launch for the draw pass (calls without token lists and with kFinMinN
+// to kFinMaxN requests): one kFinBlock-thread workgroup per request writes the
+// outputs and, where row A made no draw of its own, forms the sum of the draw
+// weights of each 512-token block of row A in LDS (wave w takes blocks w,
+// w + kFinWaves, ..., kFinWin of them in flight), then searches them as the
+// find kernel does.  Every block sum and the search stay in one workgroup:
+// no hand-off between workgroups and no second launch.  The weights and lane
+// sums are the draw kernel's (draw_w), so the block re-read for the token
+// matches the sums.
+template <class LT, bool VEC>
+__global__ __launch_bounds__(kFinBlock) void finish_kernel(Args a) {
+  typedef typename LT::Raw LR;
+  extern __shared__ double s_fin[];  // [nb] block sums of row A
+  __shared__ double s_tw;
+  const int i = blockIdx.x;
+  const DrawCtx<LT> cx = draw_ctx<LT>(a, i);
+  const float us = a.u_sample[i];
+  request_outputs(a, i, cx.rr, cx.A, cx.defer, cx.lanes, cx.lid, cx.ldr, cx.ldr64);
+  if (!cx.defer) return;
+  const int G = a.G, V = a.V, A = cx.A, mode = cx.mode;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const typename LT::T* lrow = cx.lrow;
+  const float* qrow = cx.qrow;
+  const int nb = cx.nsteps * kWaves;
+  const DrawW dwt = draw_weights<LT>(a, i, cx, a.stats[(size_t)i * (G + 1) + A]);
+  const bool precise = mode == 1 && dwt.temper && dwt.dw.precise;
+  const bool filt = dwt.cut_p > -INFINITY || dwt.cut_q > -INFINITY;
+  typedef std::integral_constant<int, 0> M0;
+  typedef std::integral_constant<int, 1> M1;
+  typedef std::integral_constant<int, 2> M2;
+  typedef std::true_type Y;
+  typedef std::false_type N;
+  // Block sums of row A under the compile-time draw form (MODE, TEMPER, FILT,
+  // PRECISE); W blocks of each wave in flight (tokens past the row end load
+  // nothing and weigh zero).
+  auto sums = [&](auto md, auto tp, auto ft, auto pr) {
+    constexpr int M = decltype(md)::value;
+    constexpr bool P = decltype(pr)::value;
+    constexpr int W = P ? 1 : kFinWin;
+    for (int b0 = wave; b0 < nb; b0 += kFinWaves * W) {
+      LR l[W];
+      F32::Raw q[W];
+#pragma unroll
+      for (int u = 0; u < W; ++u) {
+        const int b = b0 + u * kFinWaves;
+        const int base = b < nb ? b * 512 + lane * kCh : V;
+        l[u] = load_logits<LT, VEC>(lrow, base, V);
+        if (M == 1) q[u] = load_probs<VEC>(qrow, base, V);
+      }
+#pragma unroll
+      for (int u = 0; u < W; ++u) {
+        const int b = b0 + u * kFinWaves;
+        if (b >= nb) break;
+        const int base = b * 512 + lane * kCh;
+        float lv[8], qv[8], w[8];
+        LT::unpack(l[u], lv);
+        if (M == 1) F32::unpack(q[u], qv);
+        double ls;
+        if constexpr (P) {
+          ls = 0.0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ls += (double)draw_w<1, true, decltype(ft)::value, true>(lv[e], qv[e], base + e, dwt);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            w[e] = draw_w<M, decltype(tp)::value, decltype(ft)::value, false>(lv[e], M == 1 ? qv[e] : 0.f, base + e,
+                                                                              dwt);
+          ls = lane_sum8(w);
+        }
+        const double sw = wave_sum_f64(ls);
+        if (lane == 0) s_fin[b] = sw;
+      }
+    }
+  };
+  if (precise) {
+    if (filt) sums(M1{}, Y{}, Y{}, Y{});
+    else sums(M1{}, Y{}, N{}, Y{});
+  } else if (mode == 1) {
+    if (dwt.temper) {
+      if (filt) sums(M1{}, Y{}, Y{}, N{});
+      else sums(M1{}, Y{}, N{}, N{});
+    } else {
+      if (filt) sums(M1{}, N{}, Y{}, N{});
+      else sums(M1{}, N{}, N{}, N{});
+    }
+  } else if (mode == 2) {
+    if (filt) sums(M2{}, N{}, Y{}, N{});
+    else sums(M2{}, N{}, N{}, N{});
+  } else {
+    if (filt) sums(M0{}, N{}, Y{}, N{});
+    else sums(M0{}, N{}, N{}, N{});
+  }
+  __syncthreads();
+  constexpr int kChunk = 64 * kFindPer;
+  // one chunk of block sums: this lane's kFindPer consecutive blocks and the
+  // wave's inclusive scan of the lane sums (summed in block order)
+  auto chunk = [&](int c0, double (&xs)[kFindPer], double& is) {
+#pragma unroll
+    for (int t = 0; t < kFindPer; ++t) {
+      const int b = c0 + lane * kFindPer + t;
+      xs[t] = b < nb ? s_fin[b] : 0.0;
+    }
+    double ls = 0.0;
+#pragma unroll
+    for (int t = 0; t < kFindPer; ++t) ls += xs[t];
+    is = wave_incl_scan_f64(ls);
+  };
+  double x[kFindPer], incl = 0.0;
+  auto total = [&]() {
+    chunk(0, x, incl);
+    double s = readlane_d(incl, 63);
+    for (int c0 = kChunk; c0 < nb; c0 += kChunk) {
+      double y[kFindPer], iy;
+      chunk(c0, y, iy);
+      s += readlane_d(iy, 63);
+    }
+    if (lane == 0) s_tw = s;
+  };
+  if (wave == 0) total();
+  __syncthreads();
+  // weights of one lane's 8 tokens in block blk under draw mode md
+  auto block_weights = [&](int blk, int md, float w[8], int& base) -> bool {
+    base = blk * 512 + lane * kCh;
+    LR lb = load_logits<LT, VEC>(lrow, base, V);
+    F32::Raw qb = (md == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
+    float lv[8], qv[8];
+    LT::unpack(lb, lv);
+    if (md == 1) F32::unpack(qb, qv);
+    else
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = 0.f;
+    DrawW dd = dwt;
+    dd.mode = md;
+    const bool prec = md == 1 && dd.temper && dd.dw.precise;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      w[e] = prec ? draw_weight<true>(lv[e], qv[e], base + e, dd) : draw_weight<false>(lv[e], qv[e], base + e, dd);
+    return prec;
+  };
+  int dmode = mode;
+  bool held = nb <= kChunk;  // wave 0 holds every block sum in registers
+  if (!(s_tw > 0.0)) {
+    // Zero residual: the draw is from p'; its block sums replace the residual's.
+    dmode = 0;
+    held = false;
+    if (filt) sums(M0{}, N{}, Y{}, N{});
+    else sums(M0{}, N{}, N{}, N{});
+    __syncthreads();
+    if (wave == 0) total();
+  }
+  if (wave != 0) return;
+  const double S = readlane_d(s_tw, 0);
+  const double tau = (double)us * S;
+  double pre = 0.0, pstar = 0.0;
+  int bstar = -1, blast = -1;
+  for (int c0 = 0; c0 < nb; c0 += kChunk) {
+    if (!held) chunk(c0, x, incl);
+    int lp = -1;
+#pragma unroll
+    for (int t = 0; t < kFindPer; ++t)
+      if (x[t] > 0.0) lp = c0 + lane * kFindPer + t;
+    blast = max(blast, wave_max_i(lp));
+    if (bstar < 0) {
+      const uint64_t hit = __ballot(lp >= 0 && pre + incl > tau);
+      if (hit) {
+        const int l = __ffsll((unsigned long long)hit) - 1;
+        double run = pre + (l > 0 ? readlane_d(incl, l - 1) : 0.0);
+        int bl = -1, blp = -1;
+        double pb = 0.0, pbp = 0.0;
+#pragma unroll
+        for (int t = 0; t < kFindPer; ++t) {
+          if (x[t] > 0.0) {
+            if (bl < 0 && run + x[t] > tau) {
+              bl = t;
+              pb = run;
+            }
+            blp = t;
+            pbp = run;
+          }
+          run += x[t];
+        }
+        if (bl < 0) {
+          bl = blp;
+          pb = pbp;
+        }
+        bstar = c0 + l * kFindPer + __builtin_amdgcn_readlane(bl, l);
+        pstar = readlane_d(pb, l);
+      } else {
+        pre += readlane_d(incl, 63);
+      }
+    }
+  }
+  const bool last = bstar < 0;
+  const int rstar = last ? blast : bstar;
+  int z = -1;
+  if (rstar >= 0) {
+    float w[8];
+    int base;
+    const double ls = block_weights(rstar, dmode, w, base) ? lane_sum8_seq(w) : lane_sum8(w);
+    double acc = pstar + (wave_incl_scan_f64(ls) - ls);
+    int zz = INT_MAX, lastpos = -1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (w[e] > 0.f) lastpos = base + e;
+      acc += (double)w[e];
+      if (zz == INT_MAX && w[e] > 0.f && acc > tau) zz = base + e;
+    }
+    const int best = last ? INT_MAX : -wave_max_i(-zz);
+    z = best != INT_MAX ? best : wave_max_i(lastpos);
+  }
+  if (lane == 0) {
+    a.out_tokens[(size_t)i * (G + 1) + A] = z;
+    if (a.d_resid) a.d_resid[i] = S;
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // KV bookkeeping after a verify call
 // ------------------------------------------------------------------------------------------
@@ -3297,10 +3522,23 @@ hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
   else
     hipLaunchKernelGGL((row_kernel<LT, VEC, TOK>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((draw_kernel<LT, VEC, TOK>), dim3((unsigned)((long)a.N * a.dparts)), dim3(kBlock), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((find_kernel<LT, VEC, TOK>), dim3((unsigned)a.N), dim3(kBlock), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // the draw pass: one fused launch for calls without token lists and with
+  // kFinMinN to kFinMaxN requests (row A's block sums in LDS, at most 64 KB of
+  // them); otherwise block sums over many workgroups, then the search.  The
+  // fused launch saves a launch, but gives each request's draw to one
+  // workgroup: with fewer requests it leaves CUs idle, with more it loads
+  // some CUs with two deferred rows and others with one.
+  const size_t fin_lds = (size_t)((a.V + kStep - 1) / kStep) * kWaves * sizeof(double);
+  if (TOK == 0 && a.N >= kFinMinN && a.N <= kFinMaxN && fin_lds <= 65536) {
+    hipLaunchKernelGGL((finish_kernel<LT, VEC>), dim3((unsigned)a.N), dim3(kFinBlock), fin_lds, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((draw_kernel<LT, VEC, TOK>), dim3((unsigned)((long)a.N * a.dparts)), dim3(kBlock), 0, stream,
+                       a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((find_kernel<LT, VEC, TOK>), dim3((unsigned)a.N), dim3(kBlock), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev.end && (e = hipEventRecord(ev.end, stream)) != hipSuccess) return e;
   return hipSuccess;
 }

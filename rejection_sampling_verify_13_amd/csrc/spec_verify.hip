@@ -2897,122 +2897,144 @@ __global__ __launch_bounds__(kBlock, (TOK || !VEC || sizeof(typename LT::T) == 4
   const int s0 = part * kDrawSpan, cnt = min(kDrawSpan, nsteps - s0);
   // a tempered residual at large 1/T: fp64 draft weights, one step at a time
   const bool precise = mode == 1 && cx.T != 1.f && draft_w(cx.T).precise;
-  // the first window of steps (steps past the row end load nothing and weigh zero)
-  LR lr[kWin];
-  F32::Raw qr[kWin];
-  if (!precise) {
-#pragma unroll
-    for (int u = 0; u < kWin; ++u) {
-      const int base = (s0 + u) * kStep + tid * kCh;
-      lr[u] = load_logits<LT, VEC>(lrow, base, V);
-      qr[u] = (mode == 1) ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
-    }
-  }
-  const DrawW dwt = draw_weights<LT>(a, i, cx, a.stats[(size_t)i * (a.G + 1) + A]);
-  // the request's banned tokens (checked by the row pass, which faults the
-  // request on a bad list)
-  int nban = 0;
-  if (TOK && a.ban_off) {
-    const int b0 = a.ban_off[i];
-    nban = a.ban_off[i + 1] - b0;
-    for (int t = tid; t < nban; t += kBlock) s_ban[t] = a.ban_ids[(size_t)b0 + t];
-    __syncthreads();
-  }
-  // row A's penalty list (checked by the row pass likewise)
-  int npen = 0;
-  float theta = 1.f;
-  if (TOK == 2) {
-    Req rq;
-    rq.id0 = rr.id0;
-    npen = load_penalties(a, rq, i, A, (LDS_AS int*)s_pid, (LDS_AS float*)s_pd, (LDS_AS float*)s_stage, theta, false);
-  }
-  const Toks tk = toks((const LDS_AS int*)s_ban, nban, (const LDS_AS int*)s_pid, (const LDS_AS float*)s_pd,
-                       (LDS_AS float*)s_stage + (threadIdx.x >> 6) * 512, npen, theta);
-  // Sum of one lane's 8 draw weights (raw values l, q of step u) under the
-  // compile-time draw form f = (MODE, TEMPER, FILT, PRECISE); the lists walk
-  // ascending 512-token wave ranges, so steps come in order.
-  auto lane_sum = [&](LR& l, F32::Raw& q, int u, BanWalk& bw, PenWalk& pw, auto md, auto tp, auto ft, auto pr) {
-    const int base = (s0 + u) * kStep + tid * kCh;
-    if (TOK == 2) pen_walk(pw, tk, (s0 + u) * kStep + wave * 512, l, q, mode == 1);
-    if (TOK) {
-      const uint32_t m = ban_mask(bw, tk.ban, (s0 + u) * kStep + wave * 512);
-      if (m) {
-        ban_logits(l, m);
-        if (mode == 1) ban_apply(q, m, 0u);
-      }
-    }
-    float lv[8], qv[8], w[8];
-    LT::unpack(l, lv);
-    if (decltype(md)::value == 1) F32::unpack(q, qv);
-    if constexpr (decltype(pr)::value) {
-      // fp64 weights: summed as they come (eight interleaved would not fit the registers)
-      double sw = 0.0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sw += (double)draw_w<1, true, decltype(ft)::value, true>(lv[e], qv[e], base + e, dwt);
-      return sw;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        w[e] = draw_w<decltype(md)::value, decltype(tp)::value, decltype(ft)::value, false>(
-            lv[e], decltype(md)::value == 1 ? qv[e] : 0.f, base + e, dwt);
-      return lane_sum8(w);
-    }
-  };
-  BanWalk bw;
-  PenWalk pw;
-  if (TOK) bw = ban_start(tk.ban, tk.nban);
-  if (TOK == 2) pw = pen_start(tk.npen);
-  const bool filt = dwt.cut_p > -INFINITY || dwt.cut_q > -INFINITY;
+  // Steps that lie wholly inside the row are loaded with unconditional
+  // 16-byte loads, so all of a window's loads are in flight together (a load
+  // that may fall back to element loads for the row's tail puts a wait for
+  // every outstanding load at each of its branches).  The row's partial last
+  // step, rows without 16-byte alignment and the precise form go one step at
+  // a time through the element-wise path.
+  const bool unit = !VEC || precise || (s0 + cnt) * kStep > V;
   typedef std::integral_constant<int, 0> M0;
   typedef std::integral_constant<int, 1> M1;
   typedef std::integral_constant<int, 2> M2;
   typedef std::true_type Y;
   typedef std::false_type N;
-  if (precise) {
-    for (int u = 0; u < cnt; ++u) {
-      const int base = (s0 + u) * kStep + tid * kCh;
-      LR l = load_logits<LT, VEC>(lrow, base, V);
-      F32::Raw q = load_probs<VEC>(qrow, base, V);
-      const double sw = filt ? wave_sum_f64(lane_sum(l, q, u, bw, pw, M1{}, Y{}, Y{}, Y{}))
-                             : wave_sum_f64(lane_sum(l, q, u, bw, pw, M1{}, Y{}, N{}, Y{}));
-      if (lane == 0) s_blk[u * kWaves + wave] = sw;
+  // everything from the first loads on, with the draw mode fixed at compile time
+  auto run = [&](auto md) {
+    constexpr int M = decltype(md)::value;
+    LR lr[kWin];
+    F32::Raw qr[kWin];
+    if constexpr (VEC) {
+      if (!unit) {
+        // the first window (past this workgroup's last step: that step again, whose weights are not used)
+#pragma unroll
+        for (int u = 0; u < kWin; ++u) {
+          const int base = (s0 + min(u, cnt - 1)) * kStep + tid * kCh;
+          lr[u] = LT::load(lrow + base);
+          if (M == 1) qr[u] = F32::load(qrow + base);
+        }
+      }
     }
-  } else {
+    const DrawW dwt = draw_weights<LT>(a, i, cx, a.stats[(size_t)i * (a.G + 1) + A]);
+    // the request's banned tokens (checked by the row pass, which faults the
+    // request on a bad list)
+    int nban = 0;
+    if (TOK && a.ban_off) {
+      const int b0 = a.ban_off[i];
+      nban = a.ban_off[i + 1] - b0;
+      for (int t = tid; t < nban; t += kBlock) s_ban[t] = a.ban_ids[(size_t)b0 + t];
+      __syncthreads();
+    }
+    // row A's penalty list (checked by the row pass likewise)
+    int npen = 0;
+    float theta = 1.f;
+    if (TOK == 2) {
+      Req rq;
+      rq.id0 = rr.id0;
+      npen = load_penalties(a, rq, i, A, (LDS_AS int*)s_pid, (LDS_AS float*)s_pd, (LDS_AS float*)s_stage, theta,
+                            false);
+    }
+    const Toks tk = toks((const LDS_AS int*)s_ban, nban, (const LDS_AS int*)s_pid, (const LDS_AS float*)s_pd,
+                         (LDS_AS float*)s_stage + (threadIdx.x >> 6) * 512, npen, theta);
+    // Sum of one lane's 8 draw weights (raw values l, q of step u) under the
+    // compile-time draw form (M, TEMPER, FILT, PRECISE); the lists walk
+    // ascending 512-token wave ranges, so steps come in order.
+    auto lane_sum = [&](LR& l, F32::Raw& q, int u, BanWalk& bw, PenWalk& pw, auto tp, auto ft, auto pr) {
+      const int base = (s0 + u) * kStep + tid * kCh;
+      if (TOK == 2) pen_walk(pw, tk, (s0 + u) * kStep + wave * 512, l, q, M == 1);
+      if (TOK) {
+        const uint32_t m = ban_mask(bw, tk.ban, (s0 + u) * kStep + wave * 512);
+        if (m) {
+          ban_logits(l, m);
+          if (M == 1) ban_apply(q, m, 0u);
+        }
+      }
+      float lv[8], qv[8], w[8];
+      LT::unpack(l, lv);
+      if (M == 1) F32::unpack(q, qv);
+      if constexpr (decltype(pr)::value) {
+        // fp64 weights: summed as they come (eight interleaved would not fit the registers)
+        double sw = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sw += (double)draw_w<1, true, decltype(ft)::value, true>(lv[e], qv[e], base + e, dwt);
+        return sw;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          w[e] = draw_w<M, decltype(tp)::value, decltype(ft)::value, false>(lv[e], M == 1 ? qv[e] : 0.f, base + e,
+                                                                            dwt);
+        return lane_sum8(w);
+      }
+    };
+    BanWalk bw;
+    PenWalk pw;
+    if (TOK) bw = ban_start(tk.ban, tk.nban);
+    if (TOK == 2) pw = pen_start(tk.npen);
+    const bool filt = dwt.cut_p > -INFINITY || dwt.cut_q > -INFINITY;
+    // one step at a time, element loads at the row's tail
+    auto per_step = [&](auto tp, auto ft, auto pr) {
+      for (int u = 0; u < cnt; ++u) {
+        const int base = (s0 + u) * kStep + tid * kCh;
+        LR l = load_logits<LT, VEC>(lrow, base, V);
+        F32::Raw q = M == 1 ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
+        const double sw = wave_sum_f64(lane_sum(l, q, u, bw, pw, tp, ft, pr));
+        if (lane == 0) s_blk[u * kWaves + wave] = sw;
+      }
+    };
     // step u is reduced while steps u + 1 .. u + kWin are in flight (block
     // sums go to LDS: a global store here would count against the counter the
-    // loads wait on); one loop per draw form, chosen once
-    auto stream = [&](auto md, auto tp, auto ft) {
+    // loads wait on)
+    auto stream = [&](auto tp, auto ft) {
 #pragma unroll
       for (int u = 0; u < kDrawSpan; ++u) {
         if (u >= cnt) break;
         LR l = lr[u % kWin];
         F32::Raw q = qr[u % kWin];
         if (u + kWin < kDrawSpan) {
-          const int base = (s0 + u + kWin) * kStep + tid * kCh;
-          lr[u % kWin] = load_logits<LT, VEC>(lrow, base, V);
-          if (decltype(md)::value == 1) qr[u % kWin] = load_probs<VEC>(qrow, base, V);
+          const int base = (s0 + min(u + kWin, cnt - 1)) * kStep + tid * kCh;
+          lr[u % kWin] = LT::load(lrow + base);
+          if (M == 1) qr[u % kWin] = F32::load(qrow + base);
         }
-        const double sw = wave_sum_f64(lane_sum(l, q, u, bw, pw, md, tp, ft, N{}));
+        const double sw = wave_sum_f64(lane_sum(l, q, u, bw, pw, tp, ft, N{}));
         if (lane == 0) s_blk[u * kWaves + wave] = sw;
       }
     };
-    if (mode == 1) {
-      if (dwt.temper) {
-        if (filt) stream(M1{}, Y{}, Y{});
-        else stream(M1{}, Y{}, N{});
+    auto forms = [&](auto body) {  // the (TEMPER, FILT) forms of mode M
+      if (M == 1 && dwt.temper) {
+        if (filt) body(Y{}, Y{});
+        else body(Y{}, N{});
       } else {
-        if (filt) stream(M1{}, N{}, Y{});
-        else stream(M1{}, N{}, N{});
+        if (filt) body(N{}, Y{});
+        else body(N{}, N{});
       }
-    } else if (mode == 2) {
-      if (filt) stream(M2{}, N{}, Y{});
-      else stream(M2{}, N{}, N{});
-    } else {
-      if (filt) stream(M0{}, N{}, Y{});
-      else stream(M0{}, N{}, N{});
+    };
+    if constexpr (M == 1) {
+      if (precise) {
+        if (filt) per_step(Y{}, Y{}, Y{});
+        else per_step(Y{}, N{}, Y{});
+        return;
+      }
     }
-  }
+    if (unit) {
+      forms([&](auto tp, auto ft) { per_step(tp, ft, N{}); });
+    } else {
+      if constexpr (VEC) forms([&](auto tp, auto ft) { stream(tp, ft); });
+    }
+  };
+  if (mode == 1) run(M1{});
+  else if (mode == 2) run(M2{});
+  else run(M0{});
   __syncthreads();
   if (tid < cnt * kWaves) {
     DrawSum d;
@@ -3260,45 +3282,61 @@ __global__ __launch_bounds__(kFinBlock) void finish_kernel(Args a) {
   typedef std::true_type Y;
   typedef std::false_type N;
   // Block sums of row A under the compile-time draw form (MODE, TEMPER, FILT,
-  // PRECISE); W blocks of each wave in flight (tokens past the row end load
-  // nothing and weigh zero).
+  // PRECISE).  Blocks wholly inside the row: unconditional 16-byte loads, W
+  // blocks of each wave in flight (a load that may fall back to element loads
+  // puts a wait for every outstanding load at each of its branches).  The
+  // row's partial last block, and every block without 16-byte loads or in the
+  // precise form: one at a time through the element-wise path.
+  const int nfull = VEC ? V / 512 : 0;
   auto sums = [&](auto md, auto tp, auto ft, auto pr) {
     constexpr int M = decltype(md)::value;
     constexpr bool P = decltype(pr)::value;
-    constexpr int W = P ? 1 : kFinWin;
-    for (int b0 = wave; b0 < nb; b0 += kFinWaves * W) {
-      LR l[W];
-      F32::Raw q[W];
+    auto weigh = [&](LR& l, F32::Raw& q, int b) -> double {
+      const int base = b * 512 + lane * kCh;
+      float lv[8], qv[8], w[8];
+      LT::unpack(l, lv);
+      if (M == 1) F32::unpack(q, qv);
+      if constexpr (P) {
+        double ls = 0.0;
 #pragma unroll
-      for (int u = 0; u < W; ++u) {
-        const int b = b0 + u * kFinWaves;
-        const int base = b < nb ? b * 512 + lane * kCh : V;
-        l[u] = load_logits<LT, VEC>(lrow, base, V);
-        if (M == 1) q[u] = load_probs<VEC>(qrow, base, V);
+        for (int e = 0; e < 8; ++e) ls += (double)draw_w<1, true, decltype(ft)::value, true>(lv[e], qv[e], base + e, dwt);
+        return ls;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          w[e] = draw_w<M, decltype(tp)::value, decltype(ft)::value, false>(lv[e], M == 1 ? qv[e] : 0.f, base + e,
+                                                                            dwt);
+        return lane_sum8(w);
       }
+    };
+    int first = 0;  // the first block of the element-wise path
+    if constexpr (VEC && !P) {
+      first = nfull;
+      for (int b0 = wave; b0 < nfull; b0 += kFinWaves * kFinWin) {
+        LR l[kFinWin];
+        F32::Raw q[kFinWin];
 #pragma unroll
-      for (int u = 0; u < W; ++u) {
-        const int b = b0 + u * kFinWaves;
-        if (b >= nb) break;
-        const int base = b * 512 + lane * kCh;
-        float lv[8], qv[8], w[8];
-        LT::unpack(l[u], lv);
-        if (M == 1) F32::unpack(q[u], qv);
-        double ls;
-        if constexpr (P) {
-          ls = 0.0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ls += (double)draw_w<1, true, decltype(ft)::value, true>(lv[e], qv[e], base + e, dwt);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            w[e] = draw_w<M, decltype(tp)::value, decltype(ft)::value, false>(lv[e], M == 1 ? qv[e] : 0.f, base + e,
-                                                                              dwt);
-          ls = lane_sum8(w);
+        for (int u = 0; u < kFinWin; ++u) {
+          const int b = b0 + u * kFinWaves;
+          const int base = (b < nfull ? b : b0) * 512 + lane * kCh;  // (past the last: b0 again, not used)
+          l[u] = LT::load(lrow + base);
+          if (M == 1) q[u] = F32::load(qrow + base);
         }
-        const double sw = wave_sum_f64(ls);
-        if (lane == 0) s_fin[b] = sw;
+#pragma unroll
+        for (int u = 0; u < kFinWin; ++u) {
+          const int b = b0 + u * kFinWaves;
+          if (b >= nfull) break;
+          const double sw = wave_sum_f64(weigh(l[u], q[u], b));
+          if (lane == 0) s_fin[b] = sw;
+        }
       }
+    }
+    for (int b = first + wave; b < nb; b += kFinWaves) {
+      const int base = b * 512 + lane * kCh;
+      LR l = load_logits<LT, VEC>(lrow, base, V);
+      F32::Raw q = M == 1 ? load_probs<VEC>(qrow, base, V) : F32::Raw{};
+      const double sw = wave_sum_f64(weigh(l, q, b));
+      if (lane == 0) s_fin[b] = sw;
     }
   };
   if (precise) {

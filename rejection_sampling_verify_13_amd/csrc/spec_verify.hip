@@ -342,7 +342,6 @@ __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 // where one fp32 ulp is ~1e-5).  Rows whose largest q is subnormal or above
 // 2^126 lie outside that scheme (the first read as zero mass).
 __device__ inline int scale_e(uint32_t qmax_bits) { return min(max((int)(qmax_bits >> 23), 1), 252); }
-__device__ inline float scale_qs(int e) { return __uint_as_float((uint32_t)(e + 1) << 23); }
 __device__ inline float scale_inv(int e) { return __uint_as_float((uint32_t)(253 - e) << 23); }
 // An exponent scale (c = log2(e) / T for the target, 1 / T for the draft) in
 // fp64 and as an fp32 pair hi + lo with hi strictly below the value, so lo > 0.
@@ -1824,7 +1823,7 @@ struct StepRaw {
 struct StochState {
   float m;          // running max of this thread's logits
   double z;         // sum of 2^((l - m) * c) over this thread's logits (no top-k)
-  double r;         // sum of q at T = 1, else of (q / qs)^(1/T) with qs = scale_qs(scale_e(qbad)) (no top-k)
+  double r;         // sum of q at T = 1, else of (q / qs)^(1/T), qs = 2^(scale_e(qbad) - 126) (no top-k)
   float qinv;       // 1 / qs
   uint32_t qbad;    // max raw bits of q (>= 0x7f800000: NaN, inf or sign bit)
   uint32_t lbad;    // max bits of |l| (> 0x7f800000: NaN) (top-k)

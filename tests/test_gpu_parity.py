@@ -141,6 +141,10 @@ SMALL = {
     "vocab_one": W.config(1, N=6, V=1),
     # more requests than the row planner lists per round, ragged drafts
     "many_requests_ragged": W.config(5, N=1500, gmax=3, V=1024, q_mode="dense"),
+    # padded, ragged, gmax a multiple of 8: each request's draft positions take gmax + 1 row-pass slots
+    "ragged_gmax_16": W.config(5, N=40, gmax=16, V=3000, q_mode="dense"),
+    # 128 to 384 requests without token lists: the fused draw pass, unfiltered rows (every draw left to it)
+    "fused_draw_unfiltered": W.config(2, N=160, gmax=3, V=5000),
 }
 
 

@@ -3560,13 +3560,13 @@ hipError_t launch(const Args& a, hipStream_t stream, const Events& ev) {
     hipLaunchKernelGGL((row_kernel<LT, VEC, TOK>), dim3((unsigned)rows), dim3(kBlock), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // the draw pass: one fused launch for calls without token lists and with
-  // kFinMinN to kFinMaxN requests (row A's block sums in LDS, at most 64 KB of
-  // them); otherwise block sums over many workgroups, then the search.  The
+  // kFinMinN to kFinMaxN requests (row A's block sums in LDS, at most 48 KB of
+  // them: V up to 3,145,728); otherwise block sums over many workgroups, then the search.  The
   // fused launch saves a launch, but gives each request's draw to one
   // workgroup: with fewer requests it leaves CUs idle, with more it loads
   // some CUs with two deferred rows and others with one.
   const size_t fin_lds = (size_t)((a.V + kStep - 1) / kStep) * kWaves * sizeof(double);
-  if (TOK == 0 && a.N >= kFinMinN && a.N <= kFinMaxN && fin_lds <= 65536) {
+  if (TOK == 0 && a.N >= kFinMinN && a.N <= kFinMaxN && fin_lds <= 48 * 1024) {
     hipLaunchKernelGGL((finish_kernel<LT, VEC>), dim3((unsigned)a.N), dim3(kFinBlock), fin_lds, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {
